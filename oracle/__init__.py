@@ -1,0 +1,133 @@
+"""Plain CPU oracle (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it
+and shares no code with it.
+
+The arithmetic lives in ``oracle.c`` (double-precision seven-loop
+convolution and two-pass GroupNorm, see the header of that file for the
+passages it follows).  This module compiles it with gcc, loads it with
+ctypes and marshals numpy arrays.
+
+Parity status: every function here is pinned by ``tests/test_oracle.py``
+(delta kernel, all-ones tap counts, per-channel 2-D correlation from scipy,
+explicit im2col x matmul, scatter-form brute force, torch float64 conv and
+group_norm on the CPU, GroupNorm closed-form invariants, the pages' printed
+geometry in ``tests/golden/``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c -> liboracle.so with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i, p, d = ctypes.c_int, ctypes.c_void_p, ctypes.c_double
+        lib.oracle_out_dim.argtypes = [i, i, i, i, i]
+        lib.oracle_out_dim.restype = i
+        lib.oracle_conv2d.argtypes = [i] * 11 + [p, p, p, p, p, i]
+        lib.oracle_conv2d.restype = i
+        lib.oracle_conv2d_points.argtypes = [i] * 11 + [p, p, p, ctypes.c_int64, p, p, p, i]
+        lib.oracle_conv2d_points.restype = i
+        lib.oracle_fused_gn.argtypes = [i] * 11 + [p] * 6 + [i, d, p, p, i]
+        lib.oracle_fused_gn.restype = i
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+def _f32(a):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def out_dim(n: int, k: int, stride: int, pad: int, dil: int) -> int:
+    return _load().oracle_out_dim(n, k, stride, pad, dil)
+
+
+def _geom(x, w, groups):
+    N, C, H, W = x.shape
+    K, cin, R, S = w.shape
+    if cin * groups != C:
+        raise ValueError("weight shape %s does not match C=%d, groups=%d" % (w.shape, C, groups))
+    return N, C, H, W, K, R, S
+
+
+def conv2d(x, w, bias=None, stride=1, pad=0, dil=1, groups=1, threads=None, want_bound=True):
+    """Returns (y, A): y the float64 conv output, A = sum |x*w| per output."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    N, C, H, W, K, R, S = _geom(x, w, groups)
+    Ho, Wo = out_dim(H, R, stride, pad, dil), out_dim(W, S, stride, pad, dil)
+    y = np.empty((N, K, Ho, Wo), dtype=np.float64)
+    A = np.empty_like(y) if want_bound else None
+    rc = _load().oracle_conv2d(N, C, H, W, K, R, S, stride, pad, dil, groups,
+                               _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(A),
+                               threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_conv2d rejected the geometry (rc=%d)" % rc)
+    return y, A
+
+
+def conv2d_points(x, w, idx, bias=None, stride=1, pad=0, dil=1, groups=1, threads=None):
+    """Conv output and bound at flat NCHW output indices `idx` (int64)."""
+    x, w, bias = _f32(x), _f32(w), _f32(bias)
+    N, C, H, W, K, R, S = _geom(x, w, groups)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    y = np.empty(idx.shape, dtype=np.float64)
+    A = np.empty_like(y)
+    rc = _load().oracle_conv2d_points(N, C, H, W, K, R, S, stride, pad, dil, groups,
+                                      _ptr(x), _ptr(w), _ptr(bias), idx.size, _ptr(idx),
+                                      _ptr(y), _ptr(A), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_conv2d_points rejected the input (rc=%d)" % rc)
+    return y, A
+
+
+def fused_gn(x, w, bias, scale, gamma, beta, gn_groups, eps=1e-5, stride=1, pad=0, dil=1,
+             groups=1, threads=None, want_v=False):
+    """conv -> +bias -> *scale -> sigmoid -> GroupNorm.  Returns out (and v)."""
+    x, w = _f32(x), _f32(w)
+    bias, scale, gamma, beta = _f32(bias), _f32(scale), _f32(gamma), _f32(beta)
+    N, C, H, W, K, R, S = _geom(x, w, groups)
+    Ho, Wo = out_dim(H, R, stride, pad, dil), out_dim(W, S, stride, pad, dil)
+    out = np.empty((N, K, Ho, Wo), dtype=np.float64)
+    v = np.empty_like(out) if want_v else None
+    rc = _load().oracle_fused_gn(N, C, H, W, K, R, S, stride, pad, dil, groups,
+                                 _ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(gamma),
+                                 _ptr(beta), gn_groups, float(eps), _ptr(v), _ptr(out),
+                                 threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_fused_gn rejected the input (rc=%d)" % rc)
+    return (out, v) if want_v else out

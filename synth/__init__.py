@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs shared by the tests, the smoke entry and the benchmark.
+
+This module only draws random numbers: it holds no convolution or
+normalisation arithmetic, so the oracle and the HIP path can both consume
+its buffers without sharing any of the method.
+
+Every tensor comes from its own numpy PCG64 stream, seeded with
+``seed * 16 + slot`` (slot 0 = x, 1 = w, 2 = bias, 3 = scale), so a tensor
+does not change when another tensor of the same workload changes shape.
+Uniform draws are ``lo + (hi - lo) * u`` with ``u`` in [0, 1) in float64,
+normal draws are ``std * z``; both are rounded once to float32.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+import numpy as np
+
+SLOT_X, SLOT_W, SLOT_BIAS, SLOT_SCALE = 0, 1, 2, 3
+
+
+def _rng(seed: int, slot: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed * 16 + slot))
+
+
+def uniform(shape, lo: float, hi: float, seed: int, slot: int) -> np.ndarray:
+    u = _rng(seed, slot).random(int(np.prod(shape)), dtype=np.float64)
+    return (lo + (hi - lo) * u).astype(np.float32).reshape(shape)
+
+
+def normal(shape, std: float, seed: int, slot: int) -> np.ndarray:
+    z = _rng(seed, slot).standard_normal(int(np.prod(shape)), dtype=np.float64)
+    return (std * z).astype(np.float32).reshape(shape)
+
+
+def integers(shape, lo: int, hi: int, seed: int, slot: int) -> np.ndarray:
+    """Small integers in [lo, hi] as float32 (exact sums for parity-by-bits)."""
+    v = _rng(seed, slot).integers(lo, hi + 1, size=int(np.prod(shape)))
+    return v.astype(np.float32).reshape(shape)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One convolution problem with its input recipe.
+
+    x_dist / w_dist / bias_dist / scale_dist are ("uniform", lo, hi) or
+    ("normal", std).  gn_groups > 0 marks the fused GroupNorm chain.
+    """
+    name: str
+    N: int
+    C: int
+    H: int
+    W: int
+    K: int
+    R: int
+    S: int
+    stride: int
+    pad: int
+    dil: int
+    groups: int
+    seed: int
+    x_dist: Tuple
+    w_dist: Tuple
+    bias_dist: Optional[Tuple] = None
+    scale_dist: Optional[Tuple] = None
+    gn_groups: int = 0
+    eps: float = 1e-5
+    note: str = field(default="", compare=False)
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+    @property
+    def fused(self) -> bool:
+        return self.gn_groups > 0
+
+
+def _draw(dist, shape, seed, slot):
+    if dist is None:
+        return None
+    if dist[0] == "uniform":
+        return uniform(shape, dist[1], dist[2], seed, slot)
+    if dist[0] == "normal":
+        return normal(shape, dist[1], seed, slot)
+    if dist[0] == "int":
+        return integers(shape, dist[1], dist[2], seed, slot)
+    raise ValueError(dist)
+
+
+def make_inputs(wl: Workload) -> dict:
+    """x, w (and bias, scale, gamma, beta for the fused chain) as float32."""
+    out = {
+        "x": _draw(wl.x_dist, (wl.N, wl.C, wl.H, wl.W), wl.seed, SLOT_X),
+        "w": _draw(wl.w_dist, (wl.K, wl.C // wl.groups, wl.R, wl.S), wl.seed, SLOT_W),
+        "bias": _draw(wl.bias_dist, (wl.K,), wl.seed, SLOT_BIAS),
+        "scale": _draw(wl.scale_dist, (wl.K,), wl.seed, SLOT_SCALE),
+    }
+    if wl.fused:
+        out["gamma"] = np.ones((wl.K,), dtype=np.float32)
+        out["beta"] = np.zeros((wl.K,), dtype=np.float32)
+    return out
+
+
+def _u(b):
+    return ("uniform", -b, b)
+
+
+# The five workloads (seven shape rows).  Weight bounds are +-1/sqrt(fan_in)
+# with fan_in = (C/groups)*R*S.
+WORKLOADS = {
+    "c1_grouped_cpg4": Workload("c1_grouped_cpg4", 1, 8, 16, 16, 8, 3, 3, 1, 1, 1, 2, 1001,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(36))),
+    "c2_depthwise_144": Workload("c2_depthwise_144", 4, 144, 56, 56, 144, 3, 3, 1, 1, 1, 144, 1002,
+                                 ("normal", 1.0), _u(1 / 3)),
+    "c3a_grouped_g64": Workload("c3a_grouped_g64", 32, 256, 64, 64, 256, 3, 3, 1, 1, 1, 64, 1003,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(36))),
+    "c3b_grouped_g128": Workload("c3b_grouped_g128", 32, 256, 64, 64, 256, 3, 3, 1, 1, 1, 128, 1004,
+                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(18))),
+    "c3c_depthwise_g256": Workload("c3c_depthwise_g256", 32, 256, 64, 64, 256, 3, 3, 1, 1, 1, 256, 1005,
+                                   ("uniform", -1.0, 1.0), _u(1 / 3)),
+    "c4_dense_5x9": Workload("c4_dense_5x9", 8, 32, 256, 256, 64, 5, 9, 1, 0, 1, 1, 1006,
+                             ("uniform", 0.0, 1.0), _u(1 / math.sqrt(1440))),
+    "c5_fused_gn": Workload("c5_fused_gn", 64, 8, 256, 256, 32, 3, 3, 1, 0, 1, 1, 1007,
+                            ("uniform", 0.0, 1.0), _u(1 / math.sqrt(72)),
+                            bias_dist=("normal", 0.1), scale_dist=("normal", 0.1),
+                            gn_groups=8, eps=1e-5),
+}
+
+ROW_ORDER = list(WORKLOADS)
