@@ -1,0 +1,352 @@
+"""Benchmark of the FP32 NCHW convolution library on one MI355X.
+
+One step = one pass of the whole hot path over the seven shape rows of the
+five workloads (grouped 3x3 cpg 4, depthwise 144, grouped 64/128/256 groups,
+dense 5x9, fused conv+bias+scale+sigmoid+GroupNorm), one library call per
+row, with inputs resident in HBM and rotated over B buffer sets so that
+every row streams at least ~512 MB per rotation (cold-cache honesty for
+rows that fit the 256 MB Infinity Cache).
+
+Timing boundaries:
+  step      K steps launched back to back; HIP events recorded on the launch
+            stream around every row give each row's device time per launch.
+  graph     per row, R launches captured in one HIP graph; device events
+            around each replay, 10 batches x 30 samples; time / R.
+  sync      per row, host clock around (library call + stream sync),
+            10 batches x 30 samples.
+Medians come with a 95% bootstrap interval (10,000 resamples).
+
+The printed JSON line's `value` is the geometric mean over the seven rows
+of algorithmic GB/s (compulsory bytes x + w + y [+ per-channel vectors],
+divided by the step-boundary device time).  `roofline` is reported for the
+kernel that takes the most device time per step; `cpu_baseline` times the
+CPU oracle on a bounded sample of every row on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "per-shape GB/s + GFLOP/s, % roofline, geomean; hipGraph vs sync-API timing"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense FP32 matrix, published
+FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FP32)
+COLD_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rows", default="", help="comma-separated subset of rows (default: all)")
+    ap.add_argument("--batches", type=int, default=10)
+    ap.add_argument("--samples", type=int, default=30)
+    ap.add_argument("--no-boundaries", action="store_true", help="skip the graph/sync tables")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm", action="store_true", help="one buffer set per row (cache-warm)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ work accounting
+
+
+def row_accounting(wl, ho, wo):
+    """Algorithmic bytes and flops of one launch (the method's compulsory traffic)."""
+    x = wl.N * wl.C * wl.H * wl.W
+    w = wl.K * (wl.C // wl.groups) * wl.R * wl.S
+    y = wl.N * wl.K * ho * wo
+    vec = 4 * wl.K if wl.fused else 0          # bias, scale, gamma, beta
+    macs = y * (wl.C // wl.groups) * wl.R * wl.S
+    flops = 2 * macs
+    byts = 4 * (x + w + y + vec)
+    # dense rows run on FP32 MFMA, grouped rows on the (non-packed) FP32 VALU
+    peak = FP32_MFMA_PEAK_TFLOPS if wl.groups == 1 else FP32_VALU_PEAK_TFLOPS
+    t_mem, t_cmp = byts / (HBM_PEAK_GBS * 1e9), flops / (peak * 1e12)
+    if t_mem >= t_cmp:
+        bound = "hbm"
+    else:
+        bound = "mfma" if wl.groups == 1 else "alu"
+    return dict(bytes=byts, flops=flops, bound=bound, floor_s=max(t_mem, t_cmp), compute_peak_tflops=peak)
+
+
+def boot_ci(samples, n_boot=10000, seed=0):
+    a = np.asarray(samples, dtype=np.float64)
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, a.size, size=(n_boot, a.size))
+    meds = np.median(a[idx], axis=1)
+    return float(np.median(a)), float(np.percentile(meds, 2.5)), float(np.percentile(meds, 97.5))
+
+
+def geomean(v):
+    v = [x for x in v if x and x > 0]
+    return float(math.exp(sum(math.log(x) for x in v) / len(v))) if v else None
+
+
+# ------------------------------------------------------------------ rows
+
+
+class Row:
+    def __init__(self, name, wl, gc, torch, warm):
+        import synth
+        self.name, self.wl = name, wl
+        self.gc, self.torch = gc, torch
+        self.desc = gc.conv_desc_create(wl.N, wl.C, wl.H, wl.W, wl.K, wl.R, wl.S, wl.stride, wl.pad,
+                                        wl.dil, wl.groups)
+        self.ho, self.wo = gc.conv_desc_get_output_dims(self.desc)
+        self.algo = gc.ALGO_NAMES[gc.conv_desc_get_algo(self.desc)]
+        self.acct = row_accounting(wl, self.ho, self.wo)
+        inp = synth.make_inputs(wl)
+        dev = "cuda"
+        nsets = 1 if warm else max(1, int(math.ceil(COLD_BYTES / self.acct["bytes"])))
+        if self.acct["bytes"] < (1 << 20):
+            nsets = 1  # launch-bound row: rotation would not change what is measured
+        self.nsets = nsets
+        x0 = torch.from_numpy(inp["x"]).to(dev)
+        self.x = [x0] + [x0.clone() for _ in range(nsets - 1)]
+        self.w = torch.from_numpy(inp["w"]).to(dev)
+        self.y = [torch.empty((wl.N, wl.K, self.ho, self.wo), device=dev) for _ in range(nsets)]
+        self.vec = {k: (torch.from_numpy(inp[k]).to(dev) if inp.get(k) is not None else None)
+                    for k in ("bias", "scale", "gamma", "beta")}
+        if wl.fused:
+            nb = gc.conv_fused_gn_workspace_size(self.desc, wl.gn_groups)
+            self.ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        self.inputs_host = inp
+
+    def launch(self, i, stream=None):
+        s = i % self.nsets
+        gc = self.gc
+        if self.wl.fused:
+            v = self.vec
+            gc.conv_fused_gn_fwd(self.desc, self.x[s], self.w, v["bias"], v["scale"], v["gamma"], v["beta"],
+                                 self.wl.gn_groups, self.wl.eps, self.y[s], self.ws, stream=stream)
+        else:
+            gc.conv_fwd(self.desc, self.x[s], self.w, None, self.y[s], stream=stream)
+
+    def figures(self, seconds):
+        a = self.acct
+        return dict(ms=seconds * 1e3, gbs=a["bytes"] / seconds / 1e9, gflops=a["flops"] / seconds / 1e9,
+                    roofline_frac=a["floor_s"] / seconds)
+
+
+def graph_boundary(row, torch, batches, samples):
+    """R launches captured in one graph; per-launch device time of each replay."""
+    per = row.acct["bytes"] / (HBM_PEAK_GBS * 1e9) + row.acct["flops"] / 100e12
+    R = int(min(500, max(2, math.ceil(1e-3 / max(per, 2e-6)))))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        row.launch(0, stream=s)          # warm the code objects before capture
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(R):
+                row.launch(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    out = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
+    for _ in range(batches):
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        out += [a.elapsed_time(b) / 1e3 / R for a, b in ev]
+    del g
+    return out, R
+
+
+def sync_boundary(row, torch, batches, samples):
+    out = []
+    for i in range(3):
+        row.launch(i)
+    torch.cuda.synchronize()
+    k = 0
+    for _ in range(batches):
+        for _ in range(samples):
+            t0 = time.perf_counter()
+            row.launch(k)
+            torch.cuda.synchronize()
+            out.append(time.perf_counter() - t0)
+            k += 1
+    return out
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+CPU_SAMPLE_N = {"c1_grouped_cpg4": 1, "c2_depthwise_144": 4, "c3a_grouped_g64": 4, "c3b_grouped_g128": 4,
+                "c3c_depthwise_g256": 4, "c4_dense_5x9": 2, "c5_fused_gn": 4}
+
+
+def cpu_baseline(rows):
+    import oracle
+    threads = oracle.default_threads()
+    per_row = {}
+    total = 0.0
+    for r in rows:
+        wl = r.wl
+        n = min(wl.N, CPU_SAMPLE_N.get(r.name, 1))
+        inp = r.inputs_host
+        x = inp["x"][:n]
+        t0 = time.perf_counter()
+        if wl.fused:
+            oracle.fused_gn(x, inp["w"], inp["bias"], inp["scale"], inp["gamma"], inp["beta"], wl.gn_groups,
+                            wl.eps, wl.stride, wl.pad, wl.dil, wl.groups, threads=threads)
+        else:
+            oracle.conv2d(x, inp["w"], None, wl.stride, wl.pad, wl.dil, wl.groups, threads=threads,
+                          want_bound=False)
+        dt = time.perf_counter() - t0
+        total += dt
+        a = row_accounting(wl.with_(N=n), r.ho, r.wo)
+        per_row[r.name] = dict(samples_n=n, seconds=dt, gbs=a["bytes"] / dt / 1e9, gflops=a["flops"] / dt / 1e9)
+        log("[cpu] %-20s N=%d  %.2f s  %.3f GB/s" % (r.name, n, dt, per_row[r.name]["gbs"]))
+    return dict(value=geomean([v["gbs"] for v in per_row.values()]),
+                unit="GB/s (geomean of rows, oracle fp64 on the host)", cores=threads, kind="oracle",
+                sample="each row on its first N images: " + ", ".join("%s N=%d" % (k, v["samples_n"])
+                                                                       for k, v in per_row.items()),
+                seconds=total, rows=per_row)
+
+
+# ------------------------------------------------------------------ main
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of this build "
+              "(got --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import grouped_convolution_conv_amd as gc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    names = [n for n in synth.ROW_ORDER if not args.rows or n in args.rows.split(",")]
+    log("[bench] device:", torch.cuda.get_device_name(0))
+    rows = []
+    for n in names:
+        rows.append(Row(n, synth.WORKLOADS[n], gc, torch, args.warm))
+        log("[bench] row %-20s algo=%-10s sets=%d bytes=%d flops=%d" % (n, rows[-1].algo, rows[-1].nsets,
+                                                                      rows[-1].acct["bytes"], rows[-1].acct["flops"]))
+    torch.cuda.synchronize()
+
+    # ---- warmup
+    for i in range(args.warmup):
+        for r in rows:
+            r.launch(i)
+    torch.cuda.synchronize()
+
+    # ---- timed steps
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in rows]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for j, r in enumerate(rows):
+            ev[i][j][0].record()
+            r.launch(i)
+            ev[i][j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / K * 1e3
+    step_times = {r.name: [ev[i][j][0].elapsed_time(ev[i][j][1]) / 1e3 for i in range(K)]
+                  for j, r in enumerate(rows)}
+    log("[bench] %d steps in %.3f s (%.3f ms/step)" % (K, wall, ms_per_step))
+
+    out_rows = []
+    for r in rows:
+        med = float(np.median(step_times[r.name]))
+        rec = dict(name=r.name, algo=r.algo, bound=r.acct["bound"], bytes=r.acct["bytes"], flops=r.acct["flops"],
+                   floor_us=r.acct["floor_s"] * 1e6, buffer_sets=r.nsets)
+        rec["step"] = r.figures(med)
+        rec["step"]["mean_ms"] = float(np.mean(step_times[r.name])) * 1e3
+        out_rows.append(rec)
+        log("[bench] %-20s step  %.4f ms  %8.1f GB/s  %8.1f GFLOP/s  frac %.3f"
+            % (r.name, rec["step"]["ms"], rec["step"]["gbs"], rec["step"]["gflops"], rec["step"]["roofline_frac"]))
+
+    if not args.no_boundaries:
+        for r, rec in zip(rows, out_rows):
+            gs, R = graph_boundary(r, torch, args.batches, args.samples)
+            ss = sync_boundary(r, torch, args.batches, args.samples)
+            for key, smp in (("graph", gs), ("sync", ss)):
+                m, lo, hi = boot_ci(smp)
+                fig = r.figures(m)
+                fig.update(ci95_ms=[lo * 1e3, hi * 1e3], samples=len(smp))
+                if key == "graph":
+                    fig["launches_per_replay"] = R
+                rec[key] = fig
+            log("[bench] %-20s graph %.4f ms [%.4f, %.4f]  sync %.4f ms [%.4f, %.4f]"
+                % (r.name, rec["graph"]["ms"], *rec["graph"]["ci95_ms"], rec["sync"]["ms"], *rec["sync"]["ci95_ms"]))
+
+    # ---- dominant kernel roofline (single-kernel rows: one launch = one kernel)
+    single = [(rec, r) for rec, r in zip(out_rows, rows) if not r.wl.fused]
+    dom_rec, dom_row = max(single, key=lambda t: t[0]["step"]["mean_ms"]) if single else (None, None)
+    roof = None
+    if dom_rec is not None:
+        t = dom_rec["step"]["mean_ms"] / 1e3
+        if dom_rec["bound"] == "mfma":
+            achieved = dom_rec["flops"] / t / 1e12
+            roof = dict(bound="mfma", achieved=achieved, peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=achieved / FP32_MFMA_PEAK_TFLOPS)
+        else:
+            achieved = dom_rec["bytes"] / t / 1e9
+            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS)
+        roof.update(traffic=None, kernel=dom_row.algo, row=dom_rec["name"],
+                    avg_launch_ms=dom_rec["step"]["mean_ms"])
+
+    value = geomean([rec["step"]["gbs"] for rec in out_rows])
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "GB/s (geomean over shape rows, device time per launch)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "one pass over the shape rows " + ", ".join(names) +
+                   " (grouped 3x3 cpg4 N1 C8 16x16; depthwise N4 C144 56x56; grouped N32 C256 64x64 g64/128/256; "
+                   "dense N8 C32->64 256x256 5x9; fused N64 C8->32 256x256 3x3 + bias, scale, sigmoid, GN(8))",
+                   "cold_buffer_sets": not args.warm},
+        "geomean": {
+            "step_gbs": value,
+            "step_gflops": geomean([r["step"]["gflops"] for r in out_rows]),
+            "step_roofline_frac": geomean([r["step"]["roofline_frac"] for r in out_rows]),
+        },
+        "roofline": roof,
+        "rows": out_rows,
+    }
+    if not args.no_boundaries:
+        for key in ("graph", "sync"):
+            result["geomean"][key + "_gbs"] = geomean([r[key]["gbs"] for r in out_rows])
+            result["geomean"][key + "_roofline_frac"] = geomean([r[key]["roofline_frac"] for r in out_rows])
+        bw = [r for r in out_rows if r["bound"] in ("hbm", "alu")]
+        if bw:
+            result["geomean"]["graph_roofline_frac_bandwidth_rows"] = geomean([r["graph"]["roofline_frac"] for r in bw])
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

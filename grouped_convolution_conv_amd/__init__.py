@@ -1,0 +1,188 @@
+"""Python binding of libgconv.so, the MI355X FP32 NCHW convolution library.
+
+Argument marshalling only: every function here forwards to the C entry
+point of the same name declared in include/gconv.h, passing device pointers
+taken from torch tensors (or raw integers) and the current HIP stream.
+Every step of the computation runs in the library's HIP kernels; there is
+no CPU or PyTorch fallback, and importing this package fails when the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgconv.so")
+
+GCONV_OK = 0
+GCONV_ERR_INVALID_ARG = 1
+GCONV_ERR_WORKSPACE = 2
+GCONV_ERR_UNSUPPORTED = 3
+GCONV_ERR_LAUNCH = 4
+
+ALGO_AUTO = 0
+ALGO_DIRECT = 1
+ALGO_GROUPED3X3 = 2
+ALGO_IGEMM = 3
+ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DIRECT: "direct", ALGO_GROUPED3X3: "grouped3x3", ALGO_IGEMM: "igemm"}
+
+EXPORTED = (
+    "conv_desc_create", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
+    "conv_desc_get_algo", "conv_fwd", "conv_fused_gn_workspace_size", "conv_fused_gn_fwd",
+    "gconv_status_string", "gconv_last_launch_error",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgconv.so is not built; run `python -m grouped_convolution_conv_amd.build` "
+                      "(or __graft_entry__.build())")
+
+# One HIP runtime per process: torch ships its own libamdhip64 (soname
+# libamdhip64.so.7, loaded under the file name libamdhip64.so).  Importing
+# torch first makes libgconv.so's libamdhip64.so.7 dependency resolve to that
+# already-loaded runtime; loading libgconv.so first would pull in a second
+# runtime from /opt/rocm, and the two do not share devices or streams.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i, _p, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_lib.conv_desc_create.argtypes = [ctypes.POINTER(_p)] + [_i] * 11
+_lib.conv_desc_destroy.argtypes = [_p]
+_lib.conv_desc_get_output_dims.argtypes = [_p, ctypes.POINTER(_i), ctypes.POINTER(_i)]
+_lib.conv_desc_set_algo.argtypes = [_p, _i]
+_lib.conv_desc_get_algo.argtypes = [_p, ctypes.POINTER(_i)]
+_lib.conv_fwd.argtypes = [_p, _p, _p, _p, _p, _p]
+_lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
+_lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
+_lib.gconv_status_string.argtypes = [_i]
+_lib.gconv_status_string.restype = ctypes.c_char_p
+_lib.gconv_last_launch_error.argtypes = []
+_lib.gconv_last_launch_error.restype = ctypes.c_char_p
+for _name in EXPORTED[:-2]:
+    getattr(_lib, _name).restype = _i
+
+
+class GconvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = "%s: %s (status %d)" % (fn, gconv_status_string(status), status)
+        if status == GCONV_ERR_LAUNCH:
+            msg += ": " + gconv_last_launch_error()
+        super().__init__(msg)
+        self.status = status
+
+
+def gconv_last_launch_error() -> str:
+    return _lib.gconv_last_launch_error().decode()
+
+
+def gconv_status_string(status: int) -> str:
+    return _lib.gconv_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != GCONV_OK:
+        raise GconvError(fn, status)
+
+
+class ConvDesc:
+    """Owns a gconv_desc_t; released on close() or garbage collection."""
+
+    def __init__(self, handle: int, geom: tuple):
+        self._h = ctypes.c_void_p(handle)
+        self.geom = geom  # (N, C, H, W, K, R, S, stride, pad, dilation, groups)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            _lib.conv_desc_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def conv_desc_create(N, C, H, W, K, R, S, stride=1, pad=0, dilation=1, groups=1) -> ConvDesc:
+    h = ctypes.c_void_p()
+    _check("conv_desc_create", _lib.conv_desc_create(ctypes.byref(h), N, C, H, W, K, R, S, stride, pad,
+                                                     dilation, groups))
+    return ConvDesc(h.value, (N, C, H, W, K, R, S, stride, pad, dilation, groups))
+
+
+def conv_desc_destroy(desc: ConvDesc) -> None:
+    desc.close()
+
+
+def conv_desc_get_output_dims(desc: ConvDesc):
+    ho, wo = _i(), _i()
+    _check("conv_desc_get_output_dims", _lib.conv_desc_get_output_dims(desc.handle, ctypes.byref(ho),
+                                                                       ctypes.byref(wo)))
+    return ho.value, wo.value
+
+
+def conv_desc_set_algo(desc: ConvDesc, algo: int) -> None:
+    _check("conv_desc_set_algo", _lib.conv_desc_set_algo(desc.handle, algo))
+
+
+def conv_desc_get_algo(desc: ConvDesc) -> int:
+    a = _i()
+    _check("conv_desc_get_algo", _lib.conv_desc_get_algo(desc.handle, ctypes.byref(a)))
+    return a.value
+
+
+def _ptr(t):
+    """Device address of a torch tensor (checked: cuda, float32, contiguous) or a raw int."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if t.dtype != torch.float32:
+        raise ValueError("tensor must be float32, got %s" % t.dtype)
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def conv_fwd(desc: ConvDesc, x, w, bias, y, stream=None) -> None:
+    """y = conv(x, w) [+ bias] on `stream` (default: torch's current stream)."""
+    _check("conv_fwd", _lib.conv_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _stream(stream)))
+
+
+def conv_fused_gn_workspace_size(desc: ConvDesc, gn_groups: int) -> int:
+    n = _sz()
+    _check("conv_fused_gn_workspace_size", _lib.conv_fused_gn_workspace_size(desc.handle, gn_groups,
+                                                                             ctypes.byref(n)))
+    return n.value
+
+
+def conv_fused_gn_fwd(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups: int, eps: float, y,
+                      workspace, workspace_bytes: int = None, stream=None) -> None:
+    """conv -> +bias -> *scale -> sigmoid -> GroupNorm(gn_groups, eps, gamma, beta) into y."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wsp = None if workspace is None else (workspace if isinstance(workspace, int) else workspace.data_ptr())
+    _check("conv_fused_gn_fwd", _lib.conv_fused_gn_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale),
+                                                       _ptr(gamma), _ptr(beta), gn_groups, float(eps), _ptr(y),
+                                                       wsp, workspace_bytes, _stream(stream)))
+
+
+def library():
+    """The loaded ctypes library (for symbol checks)."""
+    return _lib

@@ -1,0 +1,73 @@
+// internal.h -- shared host-side declarations of the gconv library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "gconv.h"
+
+// Descriptor: geometry fixed at creation plus the derived quantities every
+// launcher needs.
+struct gconv_desc {
+    int N, C, H, W, K, R, S;
+    int stride, pad, dil, groups;
+    int Ho, Wo;
+    int cin;   // input channels per group  (C / groups)
+    int cout;  // output channels per group (K / groups)
+    int algo;  // GCONV_ALGO_* requested by the caller (AUTO by default)
+};
+
+namespace gconv {
+
+// hipLaunchKernelGGL reports through the runtime's per-thread last error,
+// which an unrelated earlier call (a stream or event query that found work
+// pending, say) may have left set.  Launchers drop that stale value first so
+// the error they return belongs to their own launch.
+inline void clear_stale_launch_error() { (void)hipGetLastError(); }
+
+// Per-tile GroupNorm statistics written by a fused stage-A kernel and read by
+// the normalize kernel: element count, mean and sum of squared deviations
+// from that mean (the fourth slot is padding).
+struct alignas(16) Partial {
+    float count, mean, m2, pad;
+};
+
+// Epilogue parameters of the fused chain.
+struct FusedEpilogue {
+    const float *bias;   // [K]
+    const float *scale;  // [K]
+    Partial *parts;      // [N][gn_groups][parts_per_group]
+    int gn_groups;
+    int gn_cpg;          // channels per GroupNorm group (K / gn_groups)
+    int parts_per_group;
+};
+
+// ---- applicability tests -------------------------------------------------
+bool grouped3x3_supported(const gconv_desc *d);
+bool igemm_supported(const gconv_desc *d);
+bool igemm_fused_supported(const gconv_desc *d, int gn_groups);
+
+// ---- plain convolution launchers (y = conv(x, w) [+ bias]) ---------------
+hipError_t launch_direct(const gconv_desc *d, const float *x, const float *w,
+                         const float *bias, float *y, hipStream_t st);
+hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w,
+                             const float *bias, float *y, hipStream_t st);
+hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w,
+                        const float *bias, float *y, hipStream_t st);
+
+// ---- fused chain, stage A: conv + bias/scale/sigmoid + per-tile stats ----
+int direct_fused_parts_per_group(const gconv_desc *d, int gn_groups);
+int igemm_fused_parts_per_group(const gconv_desc *d, int gn_groups);
+hipError_t launch_direct_fused(const gconv_desc *d, const float *x, const float *w,
+                               float *y, const FusedEpilogue &ep, hipStream_t st);
+hipError_t launch_igemm_fused(const gconv_desc *d, const float *x, const float *w,
+                              float *y, const FusedEpilogue &ep, hipStream_t st);
+
+// ---- fused chain, stage B: merge statistics, normalize y in place -------
+hipError_t launch_gn_normalize(const gconv_desc *d, float *y, const Partial *parts,
+                               int gn_groups, int parts_per_group, const float *gamma,
+                               const float *beta, float eps, hipStream_t st);
+
+}  // namespace gconv

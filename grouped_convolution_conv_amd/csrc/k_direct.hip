@@ -1,0 +1,135 @@
+// k_direct.hip -- direct convolution for any geometry: one output per lane.
+//
+// This is the always-available path (the "direct mapping" kernel of the
+// GroupConv Atlas page, "CUDA / Mapping / Data reuse": recover the output
+// coordinates from the thread index and support general geometry).  A
+// workgroup covers 256 consecutive pixels of one (n, k) output plane, so
+// the weight reads of a workgroup are uniform and go through the scalar
+// cache.  The fused variant also applies the bias/scale/sigmoid epilogue and
+// writes one GroupNorm partial (count, mean, M2) per workgroup.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace gconv {
+namespace {
+
+constexpr int kBlock = 256;
+
+struct DirectGeom {
+    int C, H, W, K, R, S, stride, pad, dil, cin, cout, Ho, Wo;
+};
+
+__device__ __forceinline__ float direct_point(const float *__restrict__ x,
+                                              const float *__restrict__ w, const DirectGeom &g,
+                                              int n, int k, int oh, int ow) {
+    const int grp = k / g.cout;
+    const float *xb = x + ((size_t)n * g.C + (size_t)grp * g.cin) * g.H * g.W;
+    const float *wk = w + (size_t)k * g.cin * g.R * g.S;
+    const int ih0 = oh * g.stride - g.pad;
+    const int iw0 = ow * g.stride - g.pad;
+    float acc = 0.0f;
+    for (int c = 0; c < g.cin; ++c) {
+        const float *xc = xb + (size_t)c * g.H * g.W;
+        const float *wc = wk + c * g.R * g.S;
+        for (int r = 0; r < g.R; ++r) {
+            const int ih = ih0 + r * g.dil;
+            if (ih < 0 || ih >= g.H) continue;
+            const float *xr = xc + (size_t)ih * g.W;
+            const float *wr = wc + r * g.S;
+            for (int s = 0; s < g.S; ++s) {
+                const int iw = iw0 + s * g.dil;
+                if (iw < 0 || iw >= g.W) continue;
+                acc = fmaf(xr[iw], wr[s], acc);
+            }
+        }
+    }
+    return acc;
+}
+
+__global__ __launch_bounds__(kBlock) void direct_conv_kernel(const float *__restrict__ x,
+                                                             const float *__restrict__ w,
+                                                             const float *__restrict__ bias,
+                                                             float *__restrict__ y, DirectGeom g) {
+    const int plane = g.Ho * g.Wo;
+    const int p = blockIdx.x * kBlock + threadIdx.x;
+    if (p >= plane) return;
+    const int k = blockIdx.y, n = blockIdx.z;
+    const int oh = p / g.Wo, ow = p - oh * g.Wo;
+    float acc = direct_point(x, w, g, n, k, oh, ow);
+    if (bias) acc += bias[k];
+    y[((size_t)n * g.K + k) * plane + p] = acc;
+}
+
+__global__ __launch_bounds__(kBlock) void direct_fused_kernel(const float *__restrict__ x,
+                                                              const float *__restrict__ w,
+                                                              float *__restrict__ y, DirectGeom g,
+                                                              FusedEpilogue ep) {
+    __shared__ float scratch[4];
+    const int plane = g.Ho * g.Wo;
+    const int p = blockIdx.x * kBlock + threadIdx.x;
+    const int k = blockIdx.y, n = blockIdx.z;
+    const bool valid = p < plane;
+    float v = 0.0f;
+    if (valid) {
+        const int oh = p / g.Wo, ow = p - oh * g.Wo;
+        const float acc = direct_point(x, w, g, n, k, oh, ow);
+        v = sigmoidf((acc + ep.bias[k]) * ep.scale[k]);
+        y[((size_t)n * g.K + k) * plane + p] = v;
+    }
+    // two-pass statistics of this block's values
+    const int cnt = min(kBlock, plane - (int)blockIdx.x * kBlock);
+    const float mean = block256_sum(valid ? v : 0.0f, scratch) / (float)cnt;
+    const float d = valid ? v - mean : 0.0f;
+    const float m2 = block256_sum(d * d, scratch);
+    if (threadIdx.x == 0) {
+        const int gg = k / ep.gn_cpg, kl = k - gg * ep.gn_cpg;
+        const size_t idx = ((size_t)n * ep.gn_groups + gg) * ep.parts_per_group +
+                           (size_t)kl * gridDim.x + blockIdx.x;
+        Partial pt;
+        pt.count = (float)cnt;
+        pt.mean = mean;
+        pt.m2 = m2;
+        pt.pad = 0.0f;
+        ep.parts[idx] = pt;
+    }
+}
+
+DirectGeom make_geom(const gconv_desc *d) {
+    DirectGeom g;
+    g.C = d->C; g.H = d->H; g.W = d->W; g.K = d->K; g.R = d->R; g.S = d->S;
+    g.stride = d->stride; g.pad = d->pad; g.dil = d->dil;
+    g.cin = d->cin; g.cout = d->cout; g.Ho = d->Ho; g.Wo = d->Wo;
+    return g;
+}
+
+dim3 direct_grid(const gconv_desc *d) {
+    const int plane = d->Ho * d->Wo;
+    return dim3((unsigned)((plane + kBlock - 1) / kBlock), (unsigned)d->K, (unsigned)d->N);
+}
+
+}  // namespace
+
+int direct_fused_parts_per_group(const gconv_desc *d, int gn_groups) {
+    const int plane = d->Ho * d->Wo;
+    return (d->K / gn_groups) * ((plane + kBlock - 1) / kBlock);
+}
+
+hipError_t launch_direct(const gconv_desc *d, const float *x, const float *w, const float *bias,
+                         float *y, hipStream_t st) {
+    if (d->K > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    clear_stale_launch_error();
+    hipLaunchKernelGGL(direct_conv_kernel, direct_grid(d), dim3(kBlock), 0, st, x, w, bias, y,
+                       make_geom(d));
+    return hipGetLastError();
+}
+
+hipError_t launch_direct_fused(const gconv_desc *d, const float *x, const float *w, float *y,
+                               const FusedEpilogue &ep, hipStream_t st) {
+    if (d->K > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    clear_stale_launch_error();
+    hipLaunchKernelGGL(direct_fused_kernel, direct_grid(d), dim3(kBlock), 0, st, x, w, y,
+                       make_geom(d), ep);
+    return hipGetLastError();
+}
+
+}  // namespace gconv

@@ -1,0 +1,359 @@
+// k_igemm.hip -- FP32 MFMA implicit GEMM for dense and wide-group
+// convolution (stride 1, dilation 1, any padding).
+//
+// The implicit-GEMM view of the POPCORNBENCH traces ("Kimi-K2.6 l2_p21",
+// GEMM framing; "Kimi-K2.6 l1_p62", output-channel blocking): per group,
+//   D[k][p] = sum_q Wt[k][q] * X[q][p],   q = (c, r, s),  p = (oh, ow),
+// with Wt the weights viewed as [K][C/G*R*S] and X gathered on the fly from
+// an LDS input band (no im2col buffer).
+//
+// gfx950 mapping:
+//  - v_mfma_f32_32x32x2f32: A = 32 output channels x 2 reduction slots,
+//    B = 2 reduction slots x 32 pixels along W.  The two reduction slots are
+//    the two 32-lane halves of the wave; each half walks its own half of the
+//    input-channel chunk, so every tap offset (r, s) is a compile-time LDS
+//    immediate for both operands.
+//  - Workgroup = 4 waves; wave w owns NBR output rows x (32*NBC) columns x
+//    (32*MB) output channels, i.e. MB*NBR*NBC accumulator blocks of 16
+//    floats per lane.  The workgroup tile is (4*NBR) x (32*NBC) pixels.
+//  - Input channels are streamed through LDS CC at a time: the input band
+//    [CC][TH+R-1][TW+S-1] and the weights, transposed to [CC][R*S][32*MB]
+//    so that 32 lanes read 32 consecutive output channels.
+//  - Output: lane (half h, column j) holds rows i = 8*(v/4) + 4*h + v%4 of
+//    each 32x32 block; every store instruction writes two runs of 32
+//    consecutive pixels of two channels.
+//  - The fused variant applies (acc + bias) * scale -> sigmoid before the
+//    store and writes, per workgroup and GroupNorm group of 4 channels, the
+//    count, mean and M2 of its values (two passes over the registers).
+#include "dev_common.h"
+#include "internal.h"
+
+namespace gconv {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kNBR = 2;  // output rows per wave
+constexpr int kNBC = 2;  // 32-column blocks per wave row
+constexpr int kTH = 4 * kNBR;
+constexpr int kTW = 32 * kNBC;
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+struct IgParams {
+    int C, H, W, K, Ho, Wo, pad;
+    int cin, cout;
+    int n_kb;          // output-channel blocks of 32*MB per group
+    int n_tw;          // column tiles per image
+    int n_tiles;       // spatial tiles per image
+    int pitch;         // LDS row pitch of the input band (floats)
+};
+
+template <int R, int S, int MB, int CC, bool FUSED>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_kernel(const float *__restrict__ x,
+                                                       const float *__restrict__ w,
+                                                       const float *__restrict__ bias,
+                                                       float *__restrict__ y, IgParams p,
+                                                       FusedEpilogue ep) {
+    constexpr int RS = R * S;
+    constexpr int KW = 32 * MB;
+    constexpr int TIH = kTH + R - 1;
+    constexpr int TIW = kTW + S - 1;
+    constexpr int NB = kNBR * kNBC;
+    constexpr int HALF = CC / 2;
+
+    extern __shared__ float4 lds4[];
+    float *xin = reinterpret_cast<float *>(lds4);   // [CC][TIH][pitch]
+    float *wl = xin + CC * TIH * p.pitch;            // [CC][RS][KW]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, j = lane & 31;
+    const int n = blockIdx.z;
+    const int th = blockIdx.x / p.n_tw, tw = blockIdx.x - th * p.n_tw;
+    const int oh0 = th * kTH, ow0 = tw * kTW;
+    const int g = blockIdx.y / p.n_kb, kb = blockIdx.y - g * p.n_kb;
+    const int kg0 = kb * KW;                 // first output channel within the group
+    const int k0 = g * p.cout + kg0;         // first global output channel
+    const int kvalid = min(KW, p.cout - kg0);
+
+    const size_t HW = (size_t)p.H * p.W;
+    const float *xg = x + ((size_t)n * p.C + (size_t)g * p.cin) * HW;
+    const float *wg = w + (size_t)k0 * p.cin * RS;
+
+    floatx16 acc[MB][NB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][b][v] = 0.0f;
+
+    for (int c0 = 0; c0 < p.cin; c0 += CC) {
+        __syncthreads();  // previous chunk fully consumed
+        // input band of channels c0 .. c0+CC-1, zero outside the image
+        for (int e = tid; e < CC * TIH * TIW; e += kBlock) {
+            const int row = e / TIW;            // cl * TIH + lr
+            const int col = e - row * TIW;
+            const int cl = row / TIH;
+            const int lr = row - cl * TIH;
+            const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
+            float v = 0.0f;
+            if (c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
+                v = xg[(size_t)(c0 + cl) * HW + (size_t)ih * p.W + iw];
+            xin[row * p.pitch + col] = v;
+        }
+        // weights of output channels k0 .. k0+KW-1, channels c0 .. c0+CC-1,
+        // transposed so that the output channel runs fastest
+        for (int e = tid; e < KW * CC * RS; e += kBlock) {
+            const int k = e / (CC * RS);
+            const int rem = e - k * (CC * RS);  // cl * RS + t
+            const int cl = rem / RS;
+            float v = 0.0f;
+            if (k < kvalid && c0 + cl < p.cin) v = wg[(size_t)k * p.cin * RS + (size_t)c0 * RS + rem];
+            wl[rem * KW + k] = v;
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int ci = 0; ci < HALF; ++ci) {
+            const int cl = h * HALF + ci;
+            const float *xb = xin + (cl * TIH + wave * kNBR) * p.pitch + j;
+            const float *wb = wl + cl * RS * KW + j;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    float a[MB], b[NB];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) a[m] = wb[(r * S + s) * KW + m * 32];
+#pragma unroll
+                    for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                        for (int bc = 0; bc < kNBC; ++bc)
+                            b[br * kNBC + bc] = xb[(br + r) * p.pitch + bc * 32 + s];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], b[nb], acc[m][nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue
+    const size_t plane = (size_t)p.Ho * p.Wo;
+    float *yb = y + ((size_t)n * p.K + k0) * plane;
+    if constexpr (!FUSED) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int br = 0; br < kNBR; ++br) {
+                const int oh = oh0 + wave * kNBR + br;
+#pragma unroll
+                for (int bc = 0; bc < kNBC; ++bc) {
+                    const int ow = ow0 + bc * 32 + j;
+                    if (oh >= p.Ho || ow >= p.Wo) continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int k = m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        if (k < kvalid) {
+                            float o = acc[m][br * kNBC + bc][v];
+                            if (bias) o += bias[k0 + k];
+                            yb[(size_t)k * plane + (size_t)oh * p.Wo + ow] = o;
+                        }
+                    }
+                }
+            }
+    } else {
+        // Every output channel of the block is valid here (cout % (32*MB) == 0)
+        // and a GroupNorm group is 4 channels: rows 8q + 4h + (0..3) of a
+        // 32x32 block, i.e. local group lg = 8m + 2q + h.
+        __shared__ float red[4][8 * MB];
+        __shared__ float mean_s[8 * MB];
+        const int rows_ok = min(kTH, p.Ho - oh0), cols_ok = min(kTW, p.Wo - ow0);
+        const float count = 4.0f * (float)(rows_ok * cols_ok);
+        float s1[MB][4];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s1[m][q] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int k = k0 + m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                const float bk = ep.bias[k], sk = ep.scale[k];
+#pragma unroll
+                for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                    for (int bc = 0; bc < kNBC; ++bc) {
+                        const int oh = oh0 + wave * kNBR + br, ow = ow0 + bc * 32 + j;
+                        const bool ok = oh < p.Ho && ow < p.Wo;
+                        const float val = sigmoidf((acc[m][br * kNBC + bc][v] + bk) * sk);
+                        acc[m][br * kNBC + bc][v] = val;
+                        if (ok) {
+                            yb[(size_t)(k - k0) * plane + (size_t)oh * p.Wo + ow] = val;
+                            s1[m][v >> 2] += val;
+                        }
+                    }
+            }
+        }
+        // pass 1: tile means per local group
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float t = half_wave_sum(s1[m][q]);
+                if (j == 0) red[wave][8 * m + 2 * q + h] = t;
+            }
+        __syncthreads();
+        if (tid < 8 * MB) mean_s[tid] = ((red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid])) / count;
+        __syncthreads();
+        // pass 2: squared deviations from the tile mean
+        float s2[MB][4];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float mu = mean_s[8 * m + 2 * q + h];
+                float t = 0.0f;
+#pragma unroll
+                for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                    for (int bc = 0; bc < kNBC; ++bc) {
+                        const int oh = oh0 + wave * kNBR + br, ow = ow0 + bc * 32 + j;
+                        if (oh < p.Ho && ow < p.Wo) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const float dv = acc[m][br * kNBC + bc][4 * q + u] - mu;
+                                t = fmaf(dv, dv, t);
+                            }
+                        }
+                    }
+                s2[m][q] = t;
+            }
+        __syncthreads();  // red[] reused
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float t = half_wave_sum(s2[m][q]);
+                if (j == 0) red[wave][8 * m + 2 * q + h] = t;
+            }
+        __syncthreads();
+        if (tid < 8 * MB) {
+            const int gg = k0 / 4 + tid;  // global GroupNorm group (4 channels each)
+            Partial pt;
+            pt.count = count;
+            pt.mean = mean_s[tid];
+            pt.m2 = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+            pt.pad = 0.0f;
+            ep.parts[((size_t)n * ep.gn_groups + gg) * ep.parts_per_group + blockIdx.x] = pt;
+        }
+    }
+}
+
+// Input-channel chunk for a kernel size: the weights of one chunk stay
+// within about 24 KB for a 64-channel block.
+template <int R, int S>
+constexpr int chunk_for() {
+    return R * S <= 9 ? 8 : (R * S <= 25 ? 4 : 2);
+}
+
+size_t lds_bytes(int R, int S, int MB, int CC, int pitch) {
+    return sizeof(float) * ((size_t)CC * (kTH + R - 1) * pitch + (size_t)CC * R * S * 32 * MB);
+}
+
+template <int R, int S, int MB, bool FUSED>
+hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w, const float *bias,
+                    float *y, const FusedEpilogue &ep, hipStream_t st) {
+    constexpr int CC = chunk_for<R, S>();
+    const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
+    clear_stale_launch_error();
+    hipLaunchKernelGGL((igemm_kernel<R, S, MB, CC, FUSED>), grid, dim3(kBlock), lds, st, x, w, bias,
+                       y, p, ep);
+    return hipGetLastError();
+}
+
+template <int R, int S, bool FUSED>
+hipError_t launch_mb(int MB, const IgParams &p, dim3 grid, const float *x, const float *w,
+                     const float *bias, float *y, const FusedEpilogue &ep, hipStream_t st) {
+    if (MB == 2) return launch_t<R, S, 2, FUSED>(p, grid, x, w, bias, y, ep, st);
+    return launch_t<R, S, 1, FUSED>(p, grid, x, w, bias, y, ep, st);
+}
+
+template <bool FUSED>
+hipError_t launch_rs(const gconv_desc *d, const IgParams &p, int MB, dim3 grid, const float *x,
+                     const float *w, const float *bias, float *y, const FusedEpilogue &ep,
+                     hipStream_t st) {
+    const int rs = d->R * 16 + d->S;
+    switch (rs) {
+        case 1 * 16 + 1: return launch_mb<1, 1, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
+        case 3 * 16 + 3: return launch_mb<3, 3, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
+        case 5 * 16 + 5: return launch_mb<5, 5, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
+        case 5 * 16 + 9: return launch_mb<5, 9, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
+        case 7 * 16 + 7: return launch_mb<7, 7, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+bool rs_instantiated(int R, int S) {
+    return (R == 1 && S == 1) || (R == 3 && S == 3) || (R == 5 && S == 5) || (R == 5 && S == 9) ||
+           (R == 7 && S == 7);
+}
+
+int pick_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
+
+IgParams make_params(const gconv_desc *d, int MB) {
+    IgParams p;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo; p.pad = d->pad;
+    p.cin = d->cin; p.cout = d->cout;
+    p.n_kb = (d->cout + 32 * MB - 1) / (32 * MB);
+    p.n_tw = (d->Wo + kTW - 1) / kTW;
+    p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
+    p.pitch = kTW + d->S - 1;
+    return p;
+}
+
+}  // namespace
+
+bool igemm_supported(const gconv_desc *d) {
+    return d->stride == 1 && d->dil == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
+           d->cout >= 8;
+}
+
+bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
+    // every output channel of every 32*MB block must exist, and a GroupNorm
+    // group must be 4 channels
+    return igemm_supported(d) && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4;
+}
+
+int igemm_fused_parts_per_group(const gconv_desc *d, int) {
+    return make_params(d, pick_mb(d)).n_tiles;
+}
+
+hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, const float *bias,
+                        float *y, hipStream_t st) {
+    if (!igemm_supported(d)) return hipErrorInvalidValue;
+    const int MB = pick_mb(d);
+    const IgParams p = make_params(d, MB);
+    const long long gy = (long long)d->groups * p.n_kb;
+    if (gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
+    FusedEpilogue none{};
+    return launch_rs<false>(d, p, MB, grid, x, w, bias, y, none, st);
+}
+
+hipError_t launch_igemm_fused(const gconv_desc *d, const float *x, const float *w, float *y,
+                              const FusedEpilogue &ep, hipStream_t st) {
+    if (!igemm_fused_supported(d, ep.gn_groups)) return hipErrorInvalidValue;
+    const int MB = pick_mb(d);
+    const IgParams p = make_params(d, MB);
+    const long long gy = (long long)d->groups * p.n_kb;
+    if (gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
+    return launch_rs<true>(d, p, MB, grid, x, w, nullptr, y, ep, st);
+}
+
+}  // namespace gconv

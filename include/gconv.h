@@ -1,0 +1,133 @@
+/*
+ * gconv.h -- C ABI of the MI355X (gfx950) FP32 NCHW convolution library.
+ *
+ * What it computes
+ * ----------------
+ * conv_fwd: the forward pass of 2-D convolution (cross-correlation, no
+ * kernel flip) on contiguous NCHW FP32 tensors:
+ *
+ *   y[n,k,oh,ow] = bias[k] + sum_{c < C/G} sum_{r < R} sum_{s < S}
+ *                  x[n, g*(C/G) + c, oh*stride - pad + r*dil, ow*stride - pad + s*dil]
+ *                  * w[k, c, r, s]          with g = k / (K/G),
+ *
+ * where taps that fall outside the input read zero.  The sum over the input
+ * channels and the window is the direct-convolution definition of the
+ * POPCORNBENCH trace "Kimi-K2.6 l2_p21" (tiled direct conv design); the
+ * weight layout [K][C/G][R][S], the output size
+ * Ho = (H + 2*pad - dil*(R-1) - 1)/stride + 1 (likewise Wo) and the
+ * input coordinate out*stride - pad + tap*dil are those of the POPCORNBENCH
+ * trace "Kimi-K2.6 l1_p62" (dense 5x9 conv, tile and host-wrapper
+ * discussion).  Grouped 3x3 stride-1 pad-1 convolution with 1, 2 or 4
+ * channels per group up to depthwise is the workload of the GroupConv Atlas
+ * page ("Source / Method / Records", first step).  Output channels form G
+ * contiguous groups, each reading its own contiguous block of C/G input
+ * channels.
+ *
+ * conv_fused_gn_fwd: the chain of the "Kimi-K2.6 l2_p21" trace, in module
+ * order (parameter discussion of that trace):
+ *
+ *   t   = (conv(x, w)[n,k,oh,ow] + bias[k]) * scale[k]
+ *   v   = 1 / (1 + exp(-t))
+ *   out = (v - mu[n,gg]) / sqrt(var[n,gg] + eps) * gamma[k] + beta[k]
+ *
+ * where gg = k / (K/gn_groups) is the GroupNorm group of channel k and
+ * mu, var are the mean and the population variance of v over the
+ * (K/gn_groups) x Ho x Wo elements of group gg of sample n.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every tensor argument is a device pointer to contiguous FP32 data
+ *    owned by the caller (x [N][C][H][W], w [K][C/G][R][S], y [N][K][Ho][Wo],
+ *    per-channel vectors [K]).  Pointers must be 4-byte aligned; faster
+ *    kernels are picked when they are 16-byte aligned.  y must not overlap
+ *    any input.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    The compute calls only enqueue kernels on it: they never allocate,
+ *    free, memset or synchronize, so they may be captured into a hipGraph.
+ *    A device fault shows up at the caller's next synchronization.
+ *  - The descriptor is an opaque host object.  Its geometry is fixed at
+ *    creation; the only mutable setting is the algorithm choice.  A
+ *    descriptor may be used from several host threads only if none of them
+ *    changes the algorithm concurrently.
+ *  - Every function returns a status code and never throws across the ABI.
+ */
+#ifndef GCONV_H
+#define GCONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GCONV_OK 0
+#define GCONV_ERR_INVALID_ARG 1 /* null pointer, non-positive size, bad groups, empty output, ... */
+#define GCONV_ERR_WORKSPACE 2   /* workspace missing or smaller than required                  */
+#define GCONV_ERR_UNSUPPORTED 3 /* a forced algorithm does not cover this geometry             */
+#define GCONV_ERR_LAUNCH 4      /* the HIP runtime refused a kernel launch                     */
+
+/* Algorithm choices for conv_desc_set_algo.  AUTO lets the dispatcher pick. */
+#define GCONV_ALGO_AUTO 0
+#define GCONV_ALGO_DIRECT 1     /* one output per lane, any geometry                           */
+#define GCONV_ALGO_GROUPED3X3 2 /* 3x3 stride 1 pad 1 dil 1, <= 4 input channels per group     */
+#define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
+
+typedef struct gconv_desc *gconv_desc_t;
+
+/* Creates a descriptor for x[N][C][H][W] * w[K][C/groups][R][S] with a
+ * symmetric stride, zero padding and dilation.  Requires N,C,H,W,K,R,S >= 1,
+ * stride >= 1, dilation >= 1, pad >= 0, groups >= 1 dividing both C and K,
+ * Ho >= 1 and Wo >= 1, and every tensor below 2^31 elements.  On success
+ * *out owns a host allocation released by conv_desc_destroy; on failure
+ * *out is set to NULL. */
+int conv_desc_create(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S,
+                     int stride, int pad, int dilation, int groups);
+
+/* Releases a descriptor.  NULL is accepted and ignored. */
+int conv_desc_destroy(gconv_desc_t desc);
+
+/* Output height and width of the descriptor's convolution. */
+int conv_desc_get_output_dims(gconv_desc_t desc, int *Ho, int *Wo);
+
+/* Forces an algorithm (GCONV_ALGO_*).  Returns GCONV_ERR_UNSUPPORTED, and
+ * leaves the setting unchanged, when the algorithm cannot run this
+ * geometry. */
+int conv_desc_set_algo(gconv_desc_t desc, int algo);
+
+/* The algorithm conv_fwd and conv_fused_gn_fwd will run (never AUTO). */
+int conv_desc_get_algo(gconv_desc_t desc, int *algo);
+
+/* y = conv(x, w) (+ bias[k] when bias is not NULL).  See the conventions
+ * above. */
+int conv_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
+             float *y, void *stream);
+
+/* Bytes of device workspace conv_fused_gn_fwd needs for gn_groups groups
+ * (gn_groups >= 1 dividing K). */
+int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes);
+
+/* The fused chain above.  bias and scale are required [K] vectors; gamma
+ * and beta are [K] vectors or NULL for 1 and 0; eps > 0.  y receives the
+ * normalized output.  workspace is caller-owned device memory of at least
+ * conv_fused_gn_workspace_size bytes, 16-byte aligned; its contents on
+ * entry do not matter and are overwritten.  Two kernels run back to back
+ * on `stream`: the conv with the elementwise epilogue and per-tile group
+ * statistics, then the merge of those statistics and the normalization of
+ * y in place. */
+int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
+                      const float *scale, const float *gamma, const float *beta, int gn_groups,
+                      float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *gconv_status_string(int status);
+
+/* Text of the HIP runtime error behind the calling thread's most recent
+ * GCONV_ERR_LAUNCH, or "none". */
+const char *gconv_last_launch_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCONV_H */

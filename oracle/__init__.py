@@ -59,7 +59,8 @@ def _load():
 
 
 def default_threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)))
+    """Host threads for the oracle: the CPUs this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def _f32(a):

@@ -1,0 +1,343 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (written into every check below):
+  conv:      |y_gpu - y_oracle| <= 1e-4 * A + 1e-6 at every compared output,
+             A = sum |x * w| over the output's receptive field;
+  GroupNorm: |out_gpu - out_oracle| <= 1e-4 at every compared output;
+  integer-valued inputs: bit-for-bit equality (every partial sum is an
+             exactly representable integer, so any summation order is exact).
+Outputs are pre-filled with NaN so that an element a kernel fails to write
+fails the comparison.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import grouped_convolution_conv_amd as gc
+
+pytestmark = pytest.mark.gpu
+
+CONV_RTOL, CONV_ATOL, GN_ATOL = 1e-4, 1e-6, 1e-4
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _desc(wl):
+    return gc.conv_desc_create(wl.N, wl.C, wl.H, wl.W, wl.K, wl.R, wl.S, wl.stride, wl.pad, wl.dil, wl.groups)
+
+
+def gpu_conv(wl, inp, algo=gc.ALGO_AUTO, bias=None, y_offset=0):
+    d = _desc(wl)
+    gc.conv_desc_set_algo(d, algo)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    x, w, b = _dev(inp["x"]), _dev(inp["w"]), _dev(bias)
+    n_out = wl.N * wl.K * ho * wo
+    ybuf = torch.full((n_out + y_offset,), float("nan"), device="cuda")
+    y = ybuf[y_offset:]
+    gc.conv_fwd(d, x, w, b, y.data_ptr() if y_offset else y)
+    torch.cuda.synchronize()
+    return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
+
+
+def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None):
+    gn_groups = gn_groups or wl.gn_groups
+    d = _desc(wl)
+    gc.conv_desc_set_algo(d, algo)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    ws = torch.empty(max(1, gc.conv_fused_gn_workspace_size(d, gn_groups)), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)  # the kernels must not rely on its contents
+    y = torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda")
+    gc.conv_fused_gn_fwd(d, _dev(inp["x"]), _dev(inp["w"]), _dev(inp["bias"]), _dev(inp["scale"]),
+                         _dev(inp.get("gamma")), _dev(inp.get("beta")), gn_groups, wl.eps, y, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check_conv(y_gpu, y_ref, A, what):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = CONV_RTOL * A + CONV_ATOL
+    ok = err <= bound
+    if not np.all(ok):
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d of %d outputs outside 1e-4*A+1e-6; first at %s: gpu %r oracle %r A %r"
+                             % (what, len(bad), err.size, i, y_gpu[i], y_ref[i], A[i]))
+    return float(np.max(err / bound))
+
+
+def oracle_conv(wl, inp, bias=None):
+    return oracle.conv2d(inp["x"], inp["w"], bias, wl.stride, wl.pad, wl.dil, wl.groups)
+
+
+# Reduced versions of the workloads: the oracle finishes them in seconds, and
+# they still span several tiles and ragged tails.
+W = synth.WORKLOADS
+SMALL = {
+    "c1_grouped_cpg4": W["c1_grouped_cpg4"],
+    "c2_depthwise_144": W["c2_depthwise_144"],
+    "c3a_grouped_g64": W["c3a_grouped_g64"].with_(N=2),
+    "c3b_grouped_g128": W["c3b_grouped_g128"].with_(N=2),
+    "c3c_depthwise_g256": W["c3c_depthwise_g256"].with_(N=2),
+    "c4_dense_5x9": W["c4_dense_5x9"].with_(N=1, H=44, W=75),        # out 40 x 67: 5 x 2 tiles
+    "c5_fused_gn": W["c5_fused_gn"].with_(N=2, H=42, W=70),          # out 40 x 68
+}
+AUTO_ALGO = {"c1_grouped_cpg4": gc.ALGO_GROUPED3X3, "c2_depthwise_144": gc.ALGO_GROUPED3X3,
+             "c3a_grouped_g64": gc.ALGO_GROUPED3X3, "c3b_grouped_g128": gc.ALGO_GROUPED3X3,
+             "c3c_depthwise_g256": gc.ALGO_GROUPED3X3, "c4_dense_5x9": gc.ALGO_IGEMM,
+             "c5_fused_gn": gc.ALGO_IGEMM}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("algo", [gc.ALGO_AUTO, gc.ALGO_DIRECT])
+def test_conv_small_workloads(name, algo):
+    wl = SMALL[name]
+    _say("[parity] conv", name, gc.ALGO_NAMES[algo], wl)
+    inp = synth.make_inputs(wl)
+    y, used = gpu_conv(wl, inp, algo)
+    assert used == (AUTO_ALGO[name] if algo == gc.ALGO_AUTO else algo)
+    y_ref, A = oracle_conv(wl, inp)
+    r = check_conv(y, y_ref, A, name)
+    _say("   max err/bound %.3g" % r)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("algo", [gc.ALGO_AUTO, gc.ALGO_DIRECT])
+def test_conv_integer_inputs_bit_exact(name, algo):
+    wl = SMALL[name].with_(x_dist=("int", -2, 2), w_dist=("int", -2, 2), seed=SMALL[name].seed + 500)
+    _say("[parity] int", name, gc.ALGO_NAMES[algo])
+    inp = synth.make_inputs(wl)
+    y, _ = gpu_conv(wl, inp, algo)
+    y_ref, _ = oracle_conv(wl, inp)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_conv_with_bias(name):
+    wl = SMALL[name]
+    inp = synth.make_inputs(wl)
+    bias = synth.normal((wl.K,), 0.5, wl.seed, 7)
+    _say("[parity] bias", name)
+    for algo in (gc.ALGO_AUTO, gc.ALGO_DIRECT):
+        y, _ = gpu_conv(wl, inp, algo, bias=bias)
+        y_ref, A = oracle_conv(wl, inp, bias)
+        check_conv(y, y_ref, A, name + " bias")
+
+
+def _sample_indices(shape, n_random, seed):
+    """Random flat indices plus every border pixel of a few planes."""
+    N, K, Ho, Wo = shape
+    rng = np.random.default_rng(seed)
+    idx = [rng.integers(0, N * K * Ho * Wo, n_random)]
+    for (n, k) in [(0, 0), (N - 1, K - 1), (N // 2, K // 3)]:
+        base = (n * K + k) * Ho * Wo
+        rows = np.arange(Wo)
+        cols = np.arange(Ho) * Wo
+        idx += [base + rows, base + (Ho - 1) * Wo + rows, base + cols, base + cols + Wo - 1]
+    return np.unique(np.concatenate(idx))
+
+
+@pytest.mark.parametrize("name", synth.ROW_ORDER)
+def test_conv_full_size_sampled(name):
+    """The full workload, in the launch configuration the benchmark times."""
+    wl = W[name]
+    _say("[parity] full-size sampled", name)
+    inp = synth.make_inputs(wl)
+    y, used = gpu_conv(wl, inp)
+    assert used == AUTO_ALGO[name]
+    assert not np.isnan(y).any(), "unwritten outputs"
+    idx = _sample_indices(y.shape, 6000, wl.seed)
+    y_ref, A = oracle.conv2d_points(inp["x"], inp["w"], idx, None, wl.stride, wl.pad, wl.dil, wl.groups)
+    check_conv(y.ravel()[idx], y_ref, A, name + " sampled")
+
+
+# ------------------------------------------------------------------ fused chain
+
+
+def check_gn(out_gpu, out_ref, what):
+    err = np.abs(out_gpu.astype(np.float64) - out_ref)
+    if not np.all(err <= GN_ATOL):
+        i = np.unravel_index(np.nanargmax(np.where(np.isnan(err), np.inf, err)), err.shape)
+        raise AssertionError("%s: max |err| %r > 1e-4 at %s (gpu %r oracle %r)"
+                             % (what, float(np.nanmax(err)) if not np.isnan(err).all() else float("nan"),
+                                i, out_gpu[i], out_ref[i]))
+    return float(err.max())
+
+
+def oracle_fused(wl, inp, gn_groups=None):
+    return oracle.fused_gn(inp["x"], inp["w"], inp["bias"], inp["scale"], inp.get("gamma"), inp.get("beta"),
+                           gn_groups or wl.gn_groups, wl.eps, wl.stride, wl.pad, wl.dil, wl.groups)
+
+
+@pytest.mark.parametrize("algo", [gc.ALGO_AUTO, gc.ALGO_DIRECT])
+def test_fused_small(algo):
+    wl = SMALL["c5_fused_gn"]
+    _say("[parity] fused small", gc.ALGO_NAMES[algo])
+    inp = synth.make_inputs(wl)
+    out = gpu_fused(wl, inp, algo)
+    e = check_gn(out, oracle_fused(wl, inp), "fused c5 small")
+    _say("   max |err| %.3g" % e)
+
+
+@pytest.mark.parametrize("gn_groups", [1, 2, 4, 8, 16, 32])
+def test_fused_group_counts(gn_groups):
+    wl = SMALL["c5_fused_gn"].with_(N=1, H=23, W=37)
+    inp = synth.make_inputs(wl)
+    inp["gamma"] = synth.uniform((wl.K,), 0.5, 1.5, 5, 0)
+    inp["beta"] = synth.uniform((wl.K,), -0.5, 0.5, 5, 1)
+    _say("[parity] fused gn_groups", gn_groups)
+    out = gpu_fused(wl, inp, gn_groups=gn_groups)
+    check_gn(out, oracle_fused(wl, inp, gn_groups), "gn_groups=%d" % gn_groups)
+
+
+def test_fused_other_geometries():
+    # padded, stride 2, wider channel counts: stage A takes the direct kernel
+    # or the MFMA kernel according to the geometry
+    cases = [W["c5_fused_gn"].with_(N=1, H=19, W=21, pad=1),
+             W["c5_fused_gn"].with_(N=1, H=19, W=21, stride=2),
+             W["c5_fused_gn"].with_(N=2, C=16, K=64, H=17, W=33, gn_groups=16),
+             W["c5_fused_gn"].with_(N=1, C=6, K=12, H=9, W=9, groups=3, gn_groups=3)]
+    for wl in cases:
+        _say("[parity] fused geometry", wl)
+        inp = synth.make_inputs(wl)
+        check_gn(gpu_fused(wl, inp), oracle_fused(wl, inp), str(wl))
+
+
+@pytest.mark.parametrize("n", [0, 63])
+def test_fused_full_size_whole_samples(n):
+    """Full c5 in the benchmark's launch configuration; samples n compared whole."""
+    wl = W["c5_fused_gn"]
+    _say("[parity] fused full size, sample", n)
+    inp = synth.make_inputs(wl)
+    out = gpu_fused(wl, inp)
+    sl = dict(inp)
+    sl["x"] = inp["x"][n:n + 1]
+    ref = oracle_fused(wl.with_(N=1), sl)
+    check_gn(out[n:n + 1], ref, "c5 full, sample %d" % n)
+
+
+# ------------------------------------------------------------------ geometry fuzz and edges
+
+
+def _fuzz_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        groups = int(rng.choice([1, 1, 2, 3, 4]))
+        cin = int(rng.choice([1, 2, 3, 4, 5, 8, 9]))
+        cout = int(rng.choice([1, 2, 4, 8, 33, 40]))
+        R, S = int(rng.integers(1, 10)), int(rng.integers(1, 10))
+        st, pad, dil = int(rng.integers(1, 4)), int(rng.integers(0, 3)), int(rng.integers(1, 3))
+        H, W_ = int(rng.integers(1, 40)), int(rng.integers(1, 80))
+        if H + 2 * pad - dil * (R - 1) - 1 < 0 or W_ + 2 * pad - dil * (S - 1) - 1 < 0:
+            continue
+        out.append(synth.Workload("fuzz%d" % len(out), int(rng.integers(1, 3)), groups * cin, H, W_,
+                                  groups * cout, R, S, st, pad, dil, groups, 3000 + len(out),
+                                  ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _fuzz_cases(40, 11), ids=lambda w: w.name)
+def test_conv_geometry_fuzz(wl):
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    for algo in (gc.ALGO_AUTO, gc.ALGO_DIRECT, gc.ALGO_IGEMM, gc.ALGO_GROUPED3X3):
+        d = _desc(wl)
+        try:
+            gc.conv_desc_set_algo(d, algo)
+        except gc.GconvError:
+            continue
+        y, _ = gpu_conv(wl, inp, algo)
+        check_conv(y, y_ref, A, "%s %s" % (wl, gc.ALGO_NAMES[algo]))
+
+
+EDGE = [
+    synth.Workload("one_pixel", 2, 4, 1, 1, 4, 3, 3, 1, 1, 1, 4, 41, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("w5_tail", 1, 8, 7, 5, 8, 3, 3, 1, 1, 1, 2, 42, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("w33_tail", 1, 4, 9, 33, 8, 3, 3, 1, 1, 1, 4, 43, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wide_300", 1, 2, 5, 300, 2, 3, 3, 1, 1, 1, 2, 44, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("cout3", 1, 8, 10, 10, 6, 3, 3, 1, 1, 1, 2, 45, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_cin5_pad2", 2, 5, 13, 70, 40, 5, 5, 1, 2, 1, 1, 47, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_groups2", 1, 16, 11, 35, 128, 7, 7, 1, 3, 1, 2, 49, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_5x9_K130", 1, 6, 12, 40, 130, 5, 9, 1, 1, 1, 1, 50, ("uniform", -1, 1), ("uniform", -1, 1)),
+]
+
+
+@pytest.mark.parametrize("wl", EDGE, ids=lambda w: w.name)
+def test_conv_edge_cases(wl):
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    y, algo = gpu_conv(wl, inp)
+    _say("[parity] edge", wl.name, gc.ALGO_NAMES[algo])
+    check_conv(y, y_ref, A, wl.name)
+    # an output pointer that is only 4-byte aligned takes the scalar stores
+    y1, _ = gpu_conv(wl, inp, y_offset=1)
+    check_conv(y1, y_ref, A, wl.name + " misaligned y")
+
+
+def test_repeatable_bitwise():
+    for name in ("c4_dense_5x9", "c3a_grouped_g64"):
+        wl = SMALL[name]
+        inp = synth.make_inputs(wl)
+        a, _ = gpu_conv(wl, inp)
+        b, _ = gpu_conv(wl, inp)
+        assert np.array_equal(a, b), name
+    wl = SMALL["c5_fused_gn"]
+    inp = synth.make_inputs(wl)
+    assert np.array_equal(gpu_fused(wl, inp), gpu_fused(wl, inp))
+
+
+def test_graph_capture_replays_match_eager():
+    """Both entry points captured in a HIP graph; every replay equals the eager run."""
+    wl = SMALL["c4_dense_5x9"]
+    inp = synth.make_inputs(wl)
+    d = _desc(wl)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    x, w = _dev(inp["x"]), _dev(inp["w"])
+    y_eager = torch.empty((wl.N, wl.K, ho, wo), device="cuda")
+    gc.conv_fwd(d, x, w, None, y_eager)
+
+    wf = SMALL["c5_fused_gn"]
+    fi = synth.make_inputs(wf)
+    df = _desc(wf)
+    hf, wfo = gc.conv_desc_get_output_dims(df)
+    fx, fw, fb, fs = _dev(fi["x"]), _dev(fi["w"]), _dev(fi["bias"]), _dev(fi["scale"])
+    ws = torch.empty(gc.conv_fused_gn_workspace_size(df, wf.gn_groups), dtype=torch.uint8, device="cuda")
+    f_eager = torch.empty((wf.N, wf.K, hf, wfo), device="cuda")
+    gc.conv_fused_gn_fwd(df, fx, fw, fb, fs, None, None, wf.gn_groups, wf.eps, f_eager, ws)
+    torch.cuda.synchronize()
+
+    y_g = torch.zeros_like(y_eager)
+    f_g = torch.zeros_like(f_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            gc.conv_fwd(d, x, w, None, y_g)
+            gc.conv_fused_gn_fwd(df, fx, fw, fb, fs, None, None, wf.gn_groups, wf.eps, f_g, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        y_g.fill_(float("nan"))
+        f_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_g, y_eager), rep
+        assert torch.equal(f_g, f_eager), rep
+        # unrelated eager work between replays
+        y_eager.add_(0.0)
+        torch.cuda.synchronize()
