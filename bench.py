@@ -58,7 +58,32 @@ def parse():
     ap.add_argument("--no-boundaries", action="store_true", help="skip the graph/sync tables")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--warm", action="store_true", help="one buffer set per row (cache-warm)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="run only the plain device-copy calibration (known byte count per launch)")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20  # bytes read (and as many written) by one calibration copy
+
+
+def copy_calibration(torch, reps=20):
+    """Plain device-to-device copy of COPY_BYTES: the practical streaming rate
+    (read + write bytes / time) and the reference launch for scaling HBM
+    traffic counters (its FETCH_SIZE and WRITE_SIZE are each COPY_BYTES)."""
+    n = COPY_BYTES // 4
+    src = torch.empty(n, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / 1e3 / reps
+    return dict(bytes_per_launch=2 * COPY_BYTES, ms=t * 1e3, gbs=2 * COPY_BYTES / t / 1e9)
 
 
 # ------------------------------------------------------------------ work accounting
@@ -243,6 +268,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    copy = copy_calibration(torch)
+    log("[bench] plain copy of %d MiB: %.1f GB/s (read + write)" % (COPY_BYTES >> 20, copy["gbs"]))
+    if args.copy_only:
+        print(json.dumps({"copy_calibration": copy}), flush=True)
+        return
     names = [n for n in synth.ROW_ORDER if not args.rows or n in args.rows.split(",")]
     log("[bench] device:", torch.cuda.get_device_name(0))
     rows = []
@@ -334,6 +364,7 @@ def main():
             "step_roofline_frac": geomean([r["step"]["roofline_frac"] for r in out_rows]),
         },
         "roofline": roof,
+        "hbm_copy_calibration": copy,
         "rows": out_rows,
     }
     if not args.no_boundaries:

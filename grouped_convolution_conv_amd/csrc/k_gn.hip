@@ -16,6 +16,7 @@ namespace gconv {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kUnroll = 4;
 
 struct Moments {
     double n, mean, m2;
@@ -79,13 +80,26 @@ __global__ __launch_bounds__(kBlock) void gn_normalize_kernel(float *__restrict_
         const int per = (nv + nsplit - 1) / nsplit;
         const int beg = part * per, end = min(nv, beg + per);
         float4 *yv = reinterpret_cast<float4 *>(yk);
-        for (int i = beg + tid; i < end; i += kBlock) {
-            float4 v = yv[i];
-            v.x = fmaf(v.x - mean, a, b);
-            v.y = fmaf(v.y - mean, a, b);
-            v.z = fmaf(v.z - mean, a, b);
-            v.w = fmaf(v.w - mean, a, b);
-            yv[i] = v;
+        // kUnroll independent 128-bit loads in flight per lane
+        for (int i0 = beg + tid; i0 < end; i0 += kUnroll * kBlock) {
+            float4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = i0 + u * kBlock;
+                if (i < end) v[u] = yv[i];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = i0 + u * kBlock;
+                if (i < end) {
+                    float4 o;
+                    o.x = fmaf(v[u].x - mean, a, b);
+                    o.y = fmaf(v[u].y - mean, a, b);
+                    o.z = fmaf(v[u].z - mean, a, b);
+                    o.w = fmaf(v[u].w - mean, a, b);
+                    yv[i] = o;
+                }
+            }
         }
     } else {
         const int per = (plane + nsplit - 1) / nsplit;

@@ -32,6 +32,7 @@ namespace gconv {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kBatch = 8;  // global loads in flight per lane while staging
 constexpr int kNBR = 2;  // output rows per wave
 constexpr int kNBC = 2;  // 32-column blocks per wave row
 constexpr int kTH = 4 * kNBR;
@@ -88,29 +89,51 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[m][b][v] = 0.0f;
 
+    // Staging of one channel chunk into LDS.  Each lane issues kBatch
+    // independent global loads before writing any of them, so a chunk costs
+    // a few load round trips rather than one per element.
+    constexpr int XE = CC * TIH * TIW;                  // input elements per chunk
+    constexpr int WE = KW * CC * RS;                    // weight elements per chunk
     for (int c0 = 0; c0 < p.cin; c0 += CC) {
         __syncthreads();  // previous chunk fully consumed
-        // input band of channels c0 .. c0+CC-1, zero outside the image
-        for (int e = tid; e < CC * TIH * TIW; e += kBlock) {
-            const int row = e / TIW;            // cl * TIH + lr
-            const int col = e - row * TIW;
-            const int cl = row / TIH;
-            const int lr = row - cl * TIH;
-            const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
-            float v = 0.0f;
-            if (c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
-                v = xg[(size_t)(c0 + cl) * HW + (size_t)ih * p.W + iw];
-            xin[row * p.pitch + col] = v;
+        for (int base = tid; base < XE; base += kBatch * kBlock) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = base + u * kBlock;
+                const int row = e / TIW, col = e - row * TIW;  // row = cl * TIH + lr
+                const int cl = row / TIH, lr = row - cl * TIH;
+                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
+                v[u] = 0.0f;
+                if (e < XE && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
+                    v[u] = xg[(size_t)(c0 + cl) * HW + (size_t)ih * p.W + iw];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = base + u * kBlock;
+                const int row = e / TIW, col = e - row * TIW;
+                if (e < XE) xin[row * p.pitch + col] = v[u];
+            }
         }
-        // weights of output channels k0 .. k0+KW-1, channels c0 .. c0+CC-1,
+        // weights of output channels k0 .. k0+KW-1 and channels c0 .. c0+CC-1,
         // transposed so that the output channel runs fastest
-        for (int e = tid; e < KW * CC * RS; e += kBlock) {
-            const int k = e / (CC * RS);
-            const int rem = e - k * (CC * RS);  // cl * RS + t
-            const int cl = rem / RS;
-            float v = 0.0f;
-            if (k < kvalid && c0 + cl < p.cin) v = wg[(size_t)k * p.cin * RS + (size_t)c0 * RS + rem];
-            wl[rem * KW + k] = v;
+        for (int base = tid; base < WE; base += kBatch * kBlock) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = base + u * kBlock;
+                const int k = e / (CC * RS), rem = e - k * (CC * RS);  // rem = cl * RS + t
+                const int cl = rem / RS;
+                v[u] = 0.0f;
+                if (e < WE && k < kvalid && c0 + cl < p.cin)
+                    v[u] = wg[(size_t)k * p.cin * RS + (size_t)c0 * RS + rem];
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = base + u * kBlock;
+                const int k = e / (CC * RS), rem = e - k * (CC * RS);
+                if (e < WE) wl[rem * KW + k] = v[u];
+            }
         }
         __syncthreads();
 

@@ -268,6 +268,10 @@ EDGE = [
     synth.Workload("w33_tail", 1, 4, 9, 33, 8, 3, 3, 1, 1, 1, 4, 43, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("wide_300", 1, 2, 5, 300, 2, 3, 3, 1, 1, 1, 2, 44, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("cout3", 1, 8, 10, 10, 6, 3, 3, 1, 1, 1, 2, 45, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("stream_h37_cob2", 2, 8, 37, 64, 16, 3, 3, 1, 1, 1, 2, 51, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("stream_w252_q4", 1, 4, 9, 252, 4, 3, 3, 1, 1, 1, 4, 52, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("stream_w20_cpg2", 3, 6, 11, 20, 6, 3, 3, 1, 1, 1, 3, 53, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("stream_h1", 2, 8, 1, 8, 8, 3, 3, 1, 1, 1, 8, 54, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_cin5_pad2", 2, 5, 13, 70, 40, 5, 5, 1, 2, 1, 1, 47, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
