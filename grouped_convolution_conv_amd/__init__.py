@@ -27,9 +27,14 @@ ALGO_GROUPED3X3 = 2
 ALGO_IGEMM = 3
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DIRECT: "direct", ALGO_GROUPED3X3: "grouped3x3", ALGO_IGEMM: "igemm"}
 
+FUSED_AUTO = 0
+FUSED_STORE = 1
+FUSED_RECOMPUTE = 2
+FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recompute"}
+
 EXPORTED = (
     "conv_desc_create", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
-    "conv_desc_get_algo", "conv_fwd", "conv_fused_gn_workspace_size", "conv_fused_gn_fwd",
+    "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd", "conv_fused_gn_workspace_size", "conv_fused_gn_fwd",
     "gconv_status_string", "gconv_last_launch_error",
 )
 
@@ -51,6 +56,8 @@ _lib.conv_desc_destroy.argtypes = [_p]
 _lib.conv_desc_get_output_dims.argtypes = [_p, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.conv_desc_set_algo.argtypes = [_p, _i]
 _lib.conv_desc_get_algo.argtypes = [_p, ctypes.POINTER(_i)]
+_lib.conv_desc_set_fused_variant.argtypes = [_p, _i]
+_lib.conv_desc_get_fused_variant.argtypes = [_p, _i, ctypes.POINTER(_i)]
 _lib.conv_fwd.argtypes = [_p, _p, _p, _p, _p, _p]
 _lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
 _lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
@@ -133,6 +140,16 @@ def conv_desc_get_algo(desc: ConvDesc) -> int:
     a = _i()
     _check("conv_desc_get_algo", _lib.conv_desc_get_algo(desc.handle, ctypes.byref(a)))
     return a.value
+
+
+def conv_desc_set_fused_variant(desc: ConvDesc, variant: int) -> None:
+    _check("conv_desc_set_fused_variant", _lib.conv_desc_set_fused_variant(desc.handle, variant))
+
+
+def conv_desc_get_fused_variant(desc: ConvDesc, gn_groups: int) -> int:
+    v = _i()
+    _check("conv_desc_get_fused_variant", _lib.conv_desc_get_fused_variant(desc.handle, gn_groups, ctypes.byref(v)))
+    return v.value
 
 
 def _ptr(t):

@@ -42,15 +42,38 @@ bool algo_supported(const gconv_desc *d, int algo) {
     }
 }
 
-// Stage-A flavour for the fused chain: the MFMA kernel when it covers the
-// geometry and the GroupNorm grouping, otherwise the direct kernel.
-bool fused_uses_igemm(const gconv_desc *d, int gn_groups) {
-    return resolve_algo(d) == GCONV_ALGO_IGEMM && gconv::igemm_fused_supported(d, gn_groups);
+// Kernel that runs the conv of the fused chain: the persistent MFMA kernel
+// with LDS-resident weights, the chunked MFMA kernel, or the direct kernel.
+enum StageA { kStageDirect, kStageIgemm, kStageResident };
+
+// The recompute variant measured faster on MI355X for the shapes the
+// resident kernel takes (it trades re-reading and re-writing v for a second
+// MFMA pass).
+constexpr int kDefaultResidentVariant = GCONV_FUSED_RECOMPUTE;
+
+StageA fused_stage_a(const gconv_desc *d, int gn_groups) {
+    if (resolve_algo(d) == GCONV_ALGO_IGEMM) {
+        if (gconv::igemm_res_fused_supported(d, gn_groups)) return kStageResident;
+        if (gconv::igemm_fused_supported(d, gn_groups)) return kStageIgemm;
+    }
+    return kStageDirect;
+}
+
+int resolve_fused_variant(const gconv_desc *d, int gn_groups) {
+    if (d->fused_variant != GCONV_FUSED_AUTO) return d->fused_variant;
+    return fused_stage_a(d, gn_groups) == kStageResident ? kDefaultResidentVariant : GCONV_FUSED_STORE;
 }
 
 int fused_parts_per_group(const gconv_desc *d, int gn_groups) {
-    return fused_uses_igemm(d, gn_groups) ? gconv::igemm_fused_parts_per_group(d, gn_groups)
-                                          : gconv::direct_fused_parts_per_group(d, gn_groups);
+    switch (fused_stage_a(d, gn_groups)) {
+        case kStageResident: return gconv::igemm_res_parts_per_group(d);
+        case kStageIgemm: return gconv::igemm_fused_parts_per_group(d, gn_groups);
+        default: return gconv::direct_fused_parts_per_group(d, gn_groups);
+    }
+}
+
+size_t partials_bytes(const gconv_desc *d, int gn_groups) {
+    return sizeof(gconv::Partial) * (size_t)d->N * (size_t)gn_groups * (size_t)fused_parts_per_group(d, gn_groups);
 }
 
 // HIP error behind the most recent GCONV_ERR_LAUNCH of the calling thread.
@@ -87,6 +110,7 @@ int conv_desc_create(gconv_desc_t *out, int N, int C, int H, int W, int K, int R
     d->stride = stride; d->pad = pad; d->dil = dilation; d->groups = groups;
     d->Ho = Ho; d->Wo = Wo; d->cin = C / groups; d->cout = K / groups;
     d->algo = GCONV_ALGO_AUTO;
+    d->fused_variant = GCONV_FUSED_AUTO;
     *out = d;
     return GCONV_OK;
 }
@@ -117,6 +141,20 @@ int conv_desc_get_algo(gconv_desc_t d, int *algo) {
     return GCONV_OK;
 }
 
+int conv_desc_set_fused_variant(gconv_desc_t d, int variant) {
+    if (!d) return GCONV_ERR_INVALID_ARG;
+    if (variant < GCONV_FUSED_AUTO || variant > GCONV_FUSED_RECOMPUTE) return GCONV_ERR_INVALID_ARG;
+    d->fused_variant = variant;
+    return GCONV_OK;
+}
+
+int conv_desc_get_fused_variant(gconv_desc_t d, int gn_groups, int *variant) {
+    if (!d || !variant) return GCONV_ERR_INVALID_ARG;
+    if (gn_groups < 1 || d->K % gn_groups != 0) return GCONV_ERR_INVALID_ARG;
+    *variant = resolve_fused_variant(d, gn_groups);
+    return GCONV_OK;
+}
+
 int conv_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias, float *y,
              void *stream) {
     if (!d || !x || !w || !y) return GCONV_ERR_INVALID_ARG;
@@ -124,7 +162,9 @@ int conv_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias, 
     hipStream_t st = (hipStream_t)stream;
     switch (resolve_algo(d)) {
         case GCONV_ALGO_GROUPED3X3: return launch_status(gconv::launch_grouped3x3(d, x, w, bias, y, st));
-        case GCONV_ALGO_IGEMM: return launch_status(gconv::launch_igemm(d, x, w, bias, y, st));
+        case GCONV_ALGO_IGEMM:
+            if (gconv::igemm_res_supported(d)) return launch_status(gconv::launch_igemm_res(d, x, w, bias, y, st));
+            return launch_status(gconv::launch_igemm(d, x, w, bias, y, st));
         default: return launch_status(gconv::launch_direct(d, x, w, bias, y, st));
     }
 }
@@ -132,8 +172,10 @@ int conv_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias, 
 int conv_fused_gn_workspace_size(gconv_desc_t d, int gn_groups, size_t *bytes) {
     if (!d || !bytes) return GCONV_ERR_INVALID_ARG;
     if (gn_groups < 1 || d->K % gn_groups != 0) return GCONV_ERR_INVALID_ARG;
-    *bytes = sizeof(gconv::Partial) * (size_t)d->N * (size_t)gn_groups *
-             (size_t)fused_parts_per_group(d, gn_groups);
+    size_t b = partials_bytes(d, gn_groups);
+    if (resolve_fused_variant(d, gn_groups) == GCONV_FUSED_RECOMPUTE)
+        b += (sizeof(float2) * (size_t)d->N * (size_t)gn_groups + 15) & ~(size_t)15;
+    *bytes = b;
     return GCONV_OK;
 }
 
@@ -149,6 +191,9 @@ int conv_fused_gn_fwd(gconv_desc_t d, const float *x, const float *w, const floa
     conv_fused_gn_workspace_size(d, gn_groups, &need);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return GCONV_ERR_WORKSPACE;
     hipStream_t st = (hipStream_t)stream;
+    const StageA stage = fused_stage_a(d, gn_groups);
+    const int variant = resolve_fused_variant(d, gn_groups);
+    if (variant == GCONV_FUSED_RECOMPUTE && stage != kStageResident) return GCONV_ERR_UNSUPPORTED;
     gconv::FusedEpilogue ep;
     ep.bias = bias;
     ep.scale = scale;
@@ -156,9 +201,22 @@ int conv_fused_gn_fwd(gconv_desc_t d, const float *x, const float *w, const floa
     ep.gn_groups = gn_groups;
     ep.gn_cpg = d->K / gn_groups;
     ep.parts_per_group = fused_parts_per_group(d, gn_groups);
-    hipError_t e = fused_uses_igemm(d, gn_groups) ? gconv::launch_igemm_fused(d, x, w, y, ep, st)
-                                                  : gconv::launch_direct_fused(d, x, w, y, ep, st);
-    int rc = launch_status(e);
+    int rc;
+    if (variant == GCONV_FUSED_RECOMPUTE) {
+        float2 *gstat = (float2 *)((char *)workspace + partials_bytes(d, gn_groups));
+        rc = launch_status(gconv::launch_igemm_res_stats(d, x, w, nullptr, false, ep, st));
+        if (rc != GCONV_OK) return rc;
+        rc = launch_status(gconv::launch_gn_merge(d, ep.parts, gn_groups, ep.parts_per_group, eps, gstat, st));
+        if (rc != GCONV_OK) return rc;
+        return launch_status(gconv::launch_igemm_res_normalize(d, x, w, y, ep, gstat, gamma, beta, st));
+    }
+    hipError_t e;
+    switch (stage) {
+        case kStageResident: e = gconv::launch_igemm_res_stats(d, x, w, y, true, ep, st); break;
+        case kStageIgemm: e = gconv::launch_igemm_fused(d, x, w, y, ep, st); break;
+        default: e = gconv::launch_direct_fused(d, x, w, y, ep, st); break;
+    }
+    rc = launch_status(e);
     if (rc != GCONV_OK) return rc;
     return launch_status(gconv::launch_gn_normalize(d, y, ep.parts, gn_groups, ep.parts_per_group,
                                                     gamma, beta, eps, st));

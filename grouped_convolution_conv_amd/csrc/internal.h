@@ -16,7 +16,8 @@ struct gconv_desc {
     int Ho, Wo;
     int cin;   // input channels per group  (C / groups)
     int cout;  // output channels per group (K / groups)
-    int algo;  // GCONV_ALGO_* requested by the caller (AUTO by default)
+    int algo;           // GCONV_ALGO_* requested by the caller (AUTO by default)
+    int fused_variant;  // GCONV_FUSED_* requested by the caller (AUTO by default)
 };
 
 namespace gconv {
@@ -64,6 +65,23 @@ hipError_t launch_direct_fused(const gconv_desc *d, const float *x, const float 
                                float *y, const FusedEpilogue &ep, hipStream_t st);
 hipError_t launch_igemm_fused(const gconv_desc *d, const float *x, const float *w,
                               float *y, const FusedEpilogue &ep, hipStream_t st);
+
+// ---- persistent MFMA kernel with LDS-resident weights (few input channels)
+bool igemm_res_supported(const gconv_desc *d);
+bool igemm_res_fused_supported(const gconv_desc *d, int gn_groups);
+int igemm_res_parts_per_group(const gconv_desc *d);
+hipError_t launch_igemm_res(const gconv_desc *d, const float *x, const float *w, const float *bias,
+                            float *y, hipStream_t st);
+// conv + bias/scale/sigmoid + per-tile statistics; stores v when `store`
+hipError_t launch_igemm_res_stats(const gconv_desc *d, const float *x, const float *w, float *y,
+                                  bool store, const FusedEpilogue &ep, hipStream_t st);
+// merged (mean, rstd) per (n, group) from the partials
+hipError_t launch_gn_merge(const gconv_desc *d, const Partial *parts, int gn_groups,
+                           int parts_per_group, float eps, float2 *gstat, hipStream_t st);
+// conv + bias/scale/sigmoid + normalization with merged statistics, stored to y
+hipError_t launch_igemm_res_normalize(const gconv_desc *d, const float *x, const float *w, float *y,
+                                      const FusedEpilogue &ep, const float2 *gstat,
+                                      const float *gamma, const float *beta, hipStream_t st);
 
 // ---- fused chain, stage B: merge statistics, normalize y in place -------
 hipError_t launch_gn_normalize(const gconv_desc *d, float *y, const Partial *parts,

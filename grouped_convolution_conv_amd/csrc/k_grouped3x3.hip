@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void grouped3x3_stream_kernel(
     // finds them long done instead of stalling on freshly issued ones.
     float outv[CO][Q];
     float *out_dst = nullptr;  // row start of channel k0 for outv; null: nothing pending
-    auto flush = [&]() {
+    auto flush = [&]() __attribute__((always_inline)) {
         if (out_dst) {
 #pragma unroll
             for (int co = 0; co < CO; ++co)
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kBlock) void grouped3x3_stream_kernel(
             out_dst = nullptr;
         }
     };
-    auto unit = [&](int u, const float *cur, float *nxt) {
+    auto unit = [&](int u, const float *cur, float *nxt) __attribute__((always_inline)) {
         wait_async_loads();
         __syncthreads();  // unit u staged in cur; every lane is done with nxt
         flush();

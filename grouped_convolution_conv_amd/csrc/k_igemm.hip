@@ -17,8 +17,8 @@
 //    (32*MB) output channels, i.e. MB*NBR*NBC accumulator blocks of 16
 //    floats per lane.  The workgroup tile is (4*NBR) x (32*NBC) pixels.
 //  - Input channels are streamed through LDS CC at a time: the input band
-//    [CC][TH+R-1][TW+S-1] and the weights, transposed to [CC][R*S][32*MB]
-//    so that 32 lanes read 32 consecutive output channels.
+//    [CC][TH+R-1][TW+S-1] and the weights [32*MB][CC*R*S] (row pitch made
+//    odd so that the 32 lanes reading 32 output channels hit 32 banks).
 //  - Output: lane (half h, column j) holds rows i = 8*(v/4) + 4*h + v%4 of
 //    each 32x32 block; every store instruction writes two runs of 32
 //    consecutive pixels of two channels.
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     extern __shared__ float4 lds4[];
     float *xin = reinterpret_cast<float *>(lds4);   // [CC][TIH][pitch]
-    float *wl = xin + CC * TIH * p.pitch;            // [CC][RS][KW]
+    float *wl = xin + CC * TIH * p.pitch;            // [KW][CC*RS], pitch WP
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -94,6 +94,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // a few load round trips rather than one per element.
     constexpr int XE = CC * TIH * TIW;                  // input elements per chunk
     constexpr int WE = KW * CC * RS;                    // weight elements per chunk
+    // weights stay [k][c][r][s] in LDS with an odd row pitch WP: the fill
+    // writes consecutive floats and the 32 lanes reading 32 consecutive
+    // output channels land on 32 different banks
+    constexpr int WP = (CC * RS) | 1;
     for (int c0 = 0; c0 < p.cin; c0 += CC) {
         __syncthreads();  // previous chunk fully consumed
         for (int base = tid; base < XE; base += kBatch * kBlock) {
@@ -115,8 +119,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 if (e < XE) xin[row * p.pitch + col] = v[u];
             }
         }
-        // weights of output channels k0 .. k0+KW-1 and channels c0 .. c0+CC-1,
-        // transposed so that the output channel runs fastest
+        // weights of output channels k0 .. k0+KW-1 and channels c0 .. c0+CC-1
         for (int base = tid; base < WE; base += kBatch * kBlock) {
             float v[kBatch];
 #pragma unroll
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int u = 0; u < kBatch; ++u) {
                 const int e = base + u * kBlock;
                 const int k = e / (CC * RS), rem = e - k * (CC * RS);
-                if (e < WE) wl[rem * KW + k] = v[u];
+                if (e < WE) wl[k * WP + rem] = v[u];
             }
         }
         __syncthreads();
@@ -141,14 +144,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
             const float *xb = xin + (cl * TIH + wave * kNBR) * p.pitch + j;
-            const float *wb = wl + cl * RS * KW + j;
+            const float *wb = wl + j * WP + cl * RS;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     float a[MB], b[NB];
 #pragma unroll
-                    for (int m = 0; m < MB; ++m) a[m] = wb[(r * S + s) * KW + m * 32];
+                    for (int m = 0; m < MB; ++m) a[m] = wb[m * 32 * WP + r * S + s];
 #pragma unroll
                     for (int br = 0; br < kNBR; ++br)
 #pragma unroll
@@ -285,7 +288,7 @@ constexpr int chunk_for() {
 }
 
 size_t lds_bytes(int R, int S, int MB, int CC, int pitch) {
-    return sizeof(float) * ((size_t)CC * (kTH + R - 1) * pitch + (size_t)CC * R * S * 32 * MB);
+    return sizeof(float) * ((size_t)CC * (kTH + R - 1) * pitch + (size_t)((CC * R * S) | 1) * 32 * MB);
 }
 
 template <int R, int S, int MB, bool FUSED>

@@ -73,6 +73,11 @@ extern "C" {
 #define GCONV_ALGO_GROUPED3X3 2 /* 3x3 stride 1 pad 1 dil 1, <= 4 input channels per group     */
 #define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
 
+/* How conv_fused_gn_fwd organizes its passes (conv_desc_set_fused_variant). */
+#define GCONV_FUSED_AUTO 0
+#define GCONV_FUSED_STORE 1     /* conv+epilogue+stats storing v, then normalize v in place    */
+#define GCONV_FUSED_RECOMPUTE 2 /* conv+epilogue+stats, merge, then conv again + normalize     */
+
 typedef struct gconv_desc *gconv_desc_t;
 
 /* Creates a descriptor for x[N][C][H][W] * w[K][C/groups][R][S] with a
@@ -98,6 +103,18 @@ int conv_desc_set_algo(gconv_desc_t desc, int algo);
 /* The algorithm conv_fwd and conv_fused_gn_fwd will run (never AUTO). */
 int conv_desc_get_algo(gconv_desc_t desc, int *algo);
 
+/* Forces how conv_fused_gn_fwd organizes its passes (GCONV_FUSED_*).
+ * GCONV_FUSED_RECOMPUTE needs the MFMA kernel with LDS-resident weights
+ * (stride 1, dilation 1, 3x3 or 1x1, 4..8 input and 8..64 output channels,
+ * groups 1, 4 channels per GroupNorm group); otherwise it returns
+ * GCONV_ERR_UNSUPPORTED when the fused call is made.  Both variants compute
+ * the same function; they trade HBM traffic (storing and re-reading v) for
+ * a second convolution pass. */
+int conv_desc_set_fused_variant(gconv_desc_t desc, int variant);
+
+/* The variant conv_fused_gn_fwd will run for gn_groups groups (never AUTO). */
+int conv_desc_get_fused_variant(gconv_desc_t desc, int gn_groups, int *variant);
+
 /* y = conv(x, w) (+ bias[k] when bias is not NULL).  See the conventions
  * above. */
 int conv_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
@@ -111,10 +128,12 @@ int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes
  * and beta are [K] vectors or NULL for 1 and 0; eps > 0.  y receives the
  * normalized output.  workspace is caller-owned device memory of at least
  * conv_fused_gn_workspace_size bytes, 16-byte aligned; its contents on
- * entry do not matter and are overwritten.  Two kernels run back to back
- * on `stream`: the conv with the elementwise epilogue and per-tile group
- * statistics, then the merge of those statistics and the normalization of
- * y in place. */
+ * entry do not matter and are overwritten.  Kernels run back to back on
+ * `stream`: GCONV_FUSED_STORE runs the conv with the elementwise epilogue
+ * and per-tile group statistics (storing v in y), then merges the
+ * statistics and normalizes y in place; GCONV_FUSED_RECOMPUTE runs the conv
+ * with the epilogue for the statistics only, merges them, then runs the
+ * conv again and writes the normalized output. */
 int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);

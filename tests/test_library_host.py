@@ -124,11 +124,18 @@ def test_forcing_an_unsupported_algorithm_is_refused():
 def test_fused_workspace_size():
     wl = synth.WORKLOADS["c5_fused_gn"]
     d = _desc(wl)
-    # MFMA stage A: one 16-byte partial per (sample, group, 8x64 tile)
-    tiles = ((254 + 7) // 8) * ((254 + 63) // 64)
-    assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * tiles
+    # resident-weight MFMA stage A: one 16-byte partial per (sample, group,
+    # 8x64 tile, wave of 2 rows); the recompute variant adds (mean, rstd) per
+    # (sample, group)
+    parts = 4 * ((254 + 7) // 8) * ((254 + 63) // 64)
+    assert gc.conv_desc_get_fused_variant(d, 8) == gc.FUSED_RECOMPUTE
+    assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * parts + 8 * 64 * 8
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_STORE)
+    assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * parts
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_AUTO)
     gc.conv_desc_set_algo(d, gc.ALGO_DIRECT)
     # direct stage A: one partial per (sample, channel, 256-pixel block)
+    assert gc.conv_desc_get_fused_variant(d, 8) == gc.FUSED_STORE
     assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 32 * ((254 * 254 + 255) // 256)
     with pytest.raises(gc.GconvError):
         gc.conv_fused_gn_workspace_size(d, 5)
@@ -156,3 +163,22 @@ def test_compute_calls_validate_before_launching():
 
 def test_destroy_accepts_null():
     assert gc.library().conv_desc_destroy(None) == gc.GCONV_OK
+
+
+def test_fused_variant_setting():
+    d = gc.conv_desc_create(2, 8, 20, 20, 32, 3, 3, 1, 0, 1, 1)
+    for v in (gc.FUSED_STORE, gc.FUSED_RECOMPUTE, gc.FUSED_AUTO):
+        gc.conv_desc_set_fused_variant(d, v)
+    with pytest.raises(gc.GconvError):
+        gc.conv_desc_set_fused_variant(d, 3)
+    with pytest.raises(gc.GconvError):
+        gc.conv_desc_get_fused_variant(d, 5)
+    # the recompute variant needs the resident-weight MFMA kernel: with the
+    # direct kernel forced, the fused call refuses before launching
+    gc.conv_desc_set_algo(d, gc.ALGO_DIRECT)
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_RECOMPUTE)
+    fake = 1 << 20
+    ws = gc.conv_fused_gn_workspace_size(d, 8)
+    lib = gc.library()
+    assert lib.conv_fused_gn_fwd(d.handle, fake, fake, fake, fake, None, None, 8, ctypes.c_float(1e-5), fake, fake,
+                                 ws, None) == gc.GCONV_ERR_UNSUPPORTED

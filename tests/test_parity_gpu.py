@@ -51,10 +51,11 @@ def gpu_conv(wl, inp, algo=gc.ALGO_AUTO, bias=None, y_offset=0):
     return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
 
 
-def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None):
+def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO):
     gn_groups = gn_groups or wl.gn_groups
     d = _desc(wl)
     gc.conv_desc_set_algo(d, algo)
+    gc.conv_desc_set_fused_variant(d, variant)
     ho, wo = gc.conv_desc_get_output_dims(d)
     ws = torch.empty(max(1, gc.conv_fused_gn_workspace_size(d, gn_groups)), dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)  # the kernels must not rely on its contents
@@ -180,12 +181,13 @@ def oracle_fused(wl, inp, gn_groups=None):
                            gn_groups or wl.gn_groups, wl.eps, wl.stride, wl.pad, wl.dil, wl.groups)
 
 
-@pytest.mark.parametrize("algo", [gc.ALGO_AUTO, gc.ALGO_DIRECT])
-def test_fused_small(algo):
+@pytest.mark.parametrize("algo,variant", [(gc.ALGO_AUTO, gc.FUSED_RECOMPUTE), (gc.ALGO_AUTO, gc.FUSED_STORE),
+                                           (gc.ALGO_DIRECT, gc.FUSED_AUTO)])
+def test_fused_small(algo, variant):
     wl = SMALL["c5_fused_gn"]
-    _say("[parity] fused small", gc.ALGO_NAMES[algo])
+    _say("[parity] fused small", gc.ALGO_NAMES[algo], gc.FUSED_NAMES[variant])
     inp = synth.make_inputs(wl)
-    out = gpu_fused(wl, inp, algo)
+    out = gpu_fused(wl, inp, algo, variant=variant)
     e = check_gn(out, oracle_fused(wl, inp), "fused c5 small")
     _say("   max |err| %.3g" % e)
 
@@ -202,25 +204,40 @@ def test_fused_group_counts(gn_groups):
 
 
 def test_fused_other_geometries():
-    # padded, stride 2, wider channel counts: stage A takes the direct kernel
-    # or the MFMA kernel according to the geometry
+    # padded, stride 2, wider channel counts: stage A takes the direct kernel,
+    # the chunked MFMA kernel or the resident-weight MFMA kernel (both
+    # variants) according to the geometry
     cases = [W["c5_fused_gn"].with_(N=1, H=19, W=21, pad=1),
              W["c5_fused_gn"].with_(N=1, H=19, W=21, stride=2),
              W["c5_fused_gn"].with_(N=2, C=16, K=64, H=17, W=33, gn_groups=16),
+             W["c5_fused_gn"].with_(N=2, C=8, K=64, H=17, W=70, gn_groups=16),
+             W["c5_fused_gn"].with_(N=2, C=5, K=32, H=21, W=67, pad=1),
+             W["c5_fused_gn"].with_(N=1, C=4, K=32, H=12, W=140, R=1, S=1),
              W["c5_fused_gn"].with_(N=1, C=6, K=12, H=9, W=9, groups=3, gn_groups=3)]
     for wl in cases:
-        _say("[parity] fused geometry", wl)
         inp = synth.make_inputs(wl)
-        check_gn(gpu_fused(wl, inp), oracle_fused(wl, inp), str(wl))
+        ref = oracle_fused(wl, inp)
+        for variant in (gc.FUSED_AUTO, gc.FUSED_STORE, gc.FUSED_RECOMPUTE):
+            d = _desc(wl)
+            gc.conv_desc_set_fused_variant(d, variant)
+            try:
+                gc.conv_desc_get_fused_variant(d, wl.gn_groups)
+                out = gpu_fused(wl, inp, variant=variant)
+            except gc.GconvError as e:
+                assert variant == gc.FUSED_RECOMPUTE and e.status == gc.GCONV_ERR_UNSUPPORTED
+                continue
+            _say("[parity] fused geometry", wl, gc.FUSED_NAMES[variant])
+            check_gn(out, ref, "%s %s" % (wl, gc.FUSED_NAMES[variant]))
 
 
-@pytest.mark.parametrize("n", [0, 63])
-def test_fused_full_size_whole_samples(n):
+@pytest.mark.parametrize("n,variant", [(0, gc.FUSED_AUTO), (63, gc.FUSED_AUTO), (17, gc.FUSED_STORE),
+                                       (40, gc.FUSED_RECOMPUTE)])
+def test_fused_full_size_whole_samples(n, variant):
     """Full c5 in the benchmark's launch configuration; samples n compared whole."""
     wl = W["c5_fused_gn"]
-    _say("[parity] fused full size, sample", n)
+    _say("[parity] fused full size, sample", n, gc.FUSED_NAMES[variant])
     inp = synth.make_inputs(wl)
-    out = gpu_fused(wl, inp)
+    out = gpu_fused(wl, inp, variant=variant)
     sl = dict(inp)
     sl["x"] = inp["x"][n:n + 1]
     ref = oracle_fused(wl.with_(N=1), sl)
@@ -272,6 +289,9 @@ EDGE = [
     synth.Workload("stream_w252_q4", 1, 4, 9, 252, 4, 3, 3, 1, 1, 1, 4, 52, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("stream_w20_cpg2", 3, 6, 11, 20, 6, 3, 3, 1, 1, 1, 3, 53, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("stream_h1", 2, 8, 1, 8, 8, 3, 3, 1, 1, 1, 8, 54, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("res_cin5_pad1", 2, 5, 13, 70, 32, 3, 3, 1, 1, 1, 1, 55, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("res_cin4_k40", 1, 4, 19, 131, 40, 3, 3, 1, 0, 1, 1, 56, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("res_1x1_k64", 2, 8, 9, 66, 64, 1, 1, 1, 0, 1, 1, 57, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_cin5_pad2", 2, 5, 13, 70, 40, 5, 5, 1, 2, 1, 1, 47, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
