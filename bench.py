@@ -10,8 +10,9 @@ rows that fit the 256 MB Infinity Cache).
 Timing boundaries:
   step      K steps launched back to back; HIP events recorded on the launch
             stream around every row give each row's device time per launch.
-  graph     per row, R launches captured in one HIP graph; device events
-            around each replay, 10 batches x 30 samples; time / R.
+  graph     per row, R launches captured in one HIP graph by the library's
+            gconv_time_graph; device events around each replay, 10 batches
+            x 30 samples; time / R.
   sync      per row, host clock around (library call + stream sync),
             10 batches x 30 samples.
 Medians come with a 95% bootstrap interval (10,000 resamples).
@@ -206,33 +207,23 @@ class Row:
 
 
 def graph_boundary(row, torch, batches, samples):
-    """R launches captured in one graph; per-launch device time of each replay."""
+    """R launches captured in one HIP graph by the library's gconv_time_graph;
+    per-launch device time of each replay (device events around the replay)."""
     per = row.acct["bytes"] / (HBM_PEAK_GBS * 1e9) + row.acct["flops"] / 100e12
     R = int(min(500, max(2, math.ceil(1e-3 / max(per, 2e-6)))))
-    g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        row.launch(0, stream=s)          # warm the code objects before capture
-        s.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(R):
-                row.launch(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    for _ in range(3):
-        g.replay()
-    torch.cuda.synchronize()
+    gc = row.gc
+    fused = None
+    if row.wl.fused:
+        v = row.vec
+        fused = dict(scale=v["scale"], gamma=v["gamma"], beta=v["beta"], gn_groups=row.wl.gn_groups,
+                     eps=row.wl.eps, workspace=row.ws)
     out = []
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(samples)]
     for _ in range(batches):
-        for a, b in ev:
-            a.record()
-            g.replay()
-            b.record()
-        torch.cuda.synchronize()
-        out += [a.elapsed_time(b) / 1e3 / R for a, b in ev]
-    del g
+        out += [m / 1e3 for m in gc.gconv_time_graph(row.desc, row.x, row.y, row.w, row.vec["bias"], launches=R,
+                                                    replays=samples, fused=fused, stream=s)]
+    torch.cuda.synchronize()
     return out, R
 
 

@@ -34,7 +34,8 @@ FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recom
 
 EXPORTED = (
     "conv_desc_create", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
-    "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd", "conv_fused_gn_workspace_size", "conv_fused_gn_fwd",
+    "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
+    "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "gconv_time_graph",
     "gconv_status_string", "gconv_last_launch_error",
 )
 
@@ -61,6 +62,8 @@ _lib.conv_desc_get_fused_variant.argtypes = [_p, _i, ctypes.POINTER(_i)]
 _lib.conv_fwd.argtypes = [_p, _p, _p, _p, _p, _p]
 _lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
 _lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
+_lib.gconv_time_graph.argtypes = [_p, _i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _p, _p, _p, _p, _p, _i,
+                                  ctypes.c_float, _p, _sz, _i, _i, ctypes.POINTER(ctypes.c_float), _p]
 _lib.gconv_status_string.argtypes = [_i]
 _lib.gconv_status_string.restype = ctypes.c_char_p
 _lib.gconv_last_launch_error.argtypes = []
@@ -198,6 +201,36 @@ def conv_fused_gn_fwd(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups:
     _check("conv_fused_gn_fwd", _lib.conv_fused_gn_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale),
                                                        _ptr(gamma), _ptr(beta), gn_groups, float(eps), _ptr(y),
                                                        wsp, workspace_bytes, _stream(stream)))
+
+
+def gconv_time_graph(desc: ConvDesc, xs, ys, w, bias=None, launches: int = 1, replays: int = 1, fused=None,
+                     stream=None):
+    """Per-launch milliseconds of `replays` replays of a graph of `launches` calls.
+
+    xs, ys: sequences of input / output tensors (or raw pointers) rotated over
+    the launches.  fused: None for conv_fwd, else a dict with scale, gamma,
+    beta, gn_groups, eps and workspace for conv_fused_gn_fwd.  Returns a
+    list of `replays` floats."""
+    if len(xs) != len(ys) or not xs:
+        raise ValueError("xs and ys must be non-empty sequences of the same length")
+    n = len(xs)
+    xa = (_p * n)(*[_ptr(t) for t in xs])
+    ya = (_p * n)(*[_ptr(t) for t in ys])
+    out = (ctypes.c_float * replays)()
+    if fused is None:
+        args = (0, None, None, None, 0, 0.0, None, 0)
+    else:
+        ws = fused.get("workspace")
+        wsb = fused.get("workspace_bytes")
+        if wsb is None:
+            wsb = ws.numel() * ws.element_size() if ws is not None else 0
+        wsp = None if ws is None else (ws if isinstance(ws, int) else ws.data_ptr())
+        args = (1, _ptr(fused["scale"]), _ptr(fused.get("gamma")), _ptr(fused.get("beta")), int(fused["gn_groups"]),
+                float(fused["eps"]), wsp, wsb)
+    fl, sc, ga, be, gg, eps, wsp, wsb = args
+    _check("gconv_time_graph", _lib.gconv_time_graph(desc.handle, fl, xa, ya, n, _ptr(w), _ptr(bias), sc, ga, be, gg,
+                                                     eps, wsp, wsb, launches, replays, out, _stream(stream)))
+    return list(out)
 
 
 def library():

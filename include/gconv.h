@@ -138,6 +138,28 @@ int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const f
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Timing harness for the graph boundary of the GroupConv Atlas page
+ * ("Method": device events around launches captured in a CUDA graph).
+ * Captures `launches` back-to-back calls into one hipGraph on `stream` and
+ * replays it `replays` times between device events; ms_per_launch (host
+ * array of `replays` floats) receives each replay's elapsed time divided by
+ * `launches`.
+ *  - fused = 0: the calls are conv_fwd(desc, xs[i % nsets], w, bias,
+ *    ys[i % nsets]); scale, gamma, beta, gn_groups, eps and the workspace
+ *    are ignored.
+ *  - fused = 1: the calls are conv_fused_gn_fwd with the same rotation.
+ * xs and ys are host arrays of nsets device pointers (rotating buffer sets
+ * keep the inputs out of the caches between launches).  stream must not be
+ * NULL (the null stream cannot be captured).  One eager call runs first
+ * and its status is returned if it fails, so a bad argument never leaves a
+ * capture open.  Unlike the compute calls this one synchronizes: it
+ * returns after the last replay has finished.  The outputs hold the result
+ * of the last launch of each buffer set. */
+int gconv_time_graph(gconv_desc_t desc, int fused, const float *const *xs, float *const *ys, int nsets,
+                     const float *w, const float *bias, const float *scale, const float *gamma,
+                     const float *beta, int gn_groups, float eps, void *workspace, size_t workspace_bytes,
+                     int launches, int replays, float *ms_per_launch, void *stream);
+
 /* Static text for a status code. */
 const char *gconv_status_string(int status);
 

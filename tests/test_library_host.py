@@ -182,3 +182,28 @@ def test_fused_variant_setting():
     lib = gc.library()
     assert lib.conv_fused_gn_fwd(d.handle, fake, fake, fake, fake, None, None, 8, ctypes.c_float(1e-5), fake, fake,
                                  ws, None) == gc.GCONV_ERR_UNSUPPORTED
+
+
+def test_time_graph_validates_before_any_device_call():
+    lib = gc.library()
+    d = gc.conv_desc_create(1, 4, 8, 8, 4, 3, 3, 1, 1, 1, 2)
+    fake = 1 << 20
+    P = ctypes.c_void_p
+    xs = (P * 1)(fake)
+    ys = (P * 1)(fake)
+    out = (ctypes.c_float * 4)()
+
+    def call(desc=d.handle, fused=0, xa=xs, ya=ys, nsets=1, launches=2, replays=4, o=out, stream=fake):
+        return lib.gconv_time_graph(desc, fused, xa, ya, nsets, fake, None, None, None, None, 0,
+                                    ctypes.c_float(0.0), None, 0, launches, replays, o, stream)
+
+    assert call(stream=None) == gc.GCONV_ERR_INVALID_ARG      # the null stream cannot be captured
+    assert call(desc=None) == gc.GCONV_ERR_INVALID_ARG
+    assert call(nsets=0) == gc.GCONV_ERR_INVALID_ARG
+    assert call(launches=0) == gc.GCONV_ERR_INVALID_ARG
+    assert call(replays=0) == gc.GCONV_ERR_INVALID_ARG
+    assert call(o=None) == gc.GCONV_ERR_INVALID_ARG
+    assert call(fused=2) == gc.GCONV_ERR_INVALID_ARG
+    assert call(xa=(P * 1)(None)) == gc.GCONV_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        gc.gconv_time_graph(d, [fake], [], fake)

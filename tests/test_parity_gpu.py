@@ -365,3 +365,45 @@ def test_graph_capture_replays_match_eager():
         # unrelated eager work between replays
         y_eager.add_(0.0)
         torch.cuda.synchronize()
+
+
+def test_time_graph_helper_outputs_match_eager():
+    """gconv_time_graph: positive per-launch times, and the rotated outputs
+    equal eager calls on the same buffers (conv and fused entry points)."""
+    wl = SMALL["c3a_grouped_g64"]
+    inp = synth.make_inputs(wl)
+    d = _desc(wl)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    w = _dev(inp["w"])
+    xs = [_dev(inp["x"]), _dev(inp["x"] * 0.5 - 0.25)]
+    ys = [torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda") for _ in xs]
+    ref = []
+    for x in xs:
+        r = torch.empty((wl.N, wl.K, ho, wo), device="cuda")
+        gc.conv_fwd(d, x, w, None, r)
+        ref.append(r)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    ms = gc.gconv_time_graph(d, xs, ys, w, None, launches=3, replays=5, stream=s)
+    torch.cuda.synchronize()
+    assert len(ms) == 5 and all(m > 0 for m in ms), ms
+    for a, b in zip(ys, ref):
+        assert torch.equal(a, b)
+
+    wf = SMALL["c5_fused_gn"]
+    fi = synth.make_inputs(wf)
+    df = _desc(wf)
+    hf, wfo = gc.conv_desc_get_output_dims(df)
+    fx, fw, fb, fs = _dev(fi["x"]), _dev(fi["w"]), _dev(fi["bias"]), _dev(fi["scale"])
+    ws = torch.empty(gc.conv_fused_gn_workspace_size(df, wf.gn_groups), dtype=torch.uint8, device="cuda")
+    f_eager = torch.empty((wf.N, wf.K, hf, wfo), device="cuda")
+    gc.conv_fused_gn_fwd(df, fx, fw, fb, fs, None, None, wf.gn_groups, wf.eps, f_eager, ws)
+    torch.cuda.synchronize()
+    f_g = torch.full_like(f_eager, float("nan"))
+    ms = gc.gconv_time_graph(df, [fx], [f_g], fw, fb, launches=2, replays=3, stream=s,
+                             fused=dict(scale=fs, gamma=None, beta=None, gn_groups=wf.gn_groups, eps=wf.eps,
+                                        workspace=ws))
+    torch.cuda.synchronize()
+    assert len(ms) == 3 and all(m > 0 for m in ms), ms
+    assert torch.equal(f_g, f_eager)
