@@ -15,8 +15,8 @@
 //    so interior columns land 16-byte aligned (128-bit LDS writes) and a
 //    lane's window of Q+2 inputs is read as b32 + Q/4 x b128 + b32.
 //  - Each lane computes Q adjacent outputs along W for every output channel
-//    of the block (the Atlas page's fourth kernel computes four adjacent
-//    outputs per thread; here Q is 4 or 8 and the lane also covers up to four
+//    of the block (the Atlas page's fourth kernel gives each thread four
+//    neighbouring outputs; here Q is 4 or 8 and the lane also covers up to four
 //    output channels): per input channel and kernel row, Q+2 LDS reads feed
 //    CO*3*Q FMAs.  The block's weights sit in LDS and are read as broadcasts.
 //  - Results leave as 128-bit stores; the W tail is masked.
