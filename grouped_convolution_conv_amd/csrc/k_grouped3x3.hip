@@ -1,25 +1,25 @@
 // k_grouped3x3.hip -- grouped / depthwise 3x3, stride 1, pad 1, dilation 1,
 // with 1, 2 or 4 input channels per group (the workload of the GroupConv
-// Atlas page).
+// Atlas page).  VALU arithmetic, HBM-bound.
 //
-// Design for gfx950 (VALU, HBM-bound):
-//  - One workgroup (256 lanes = 4 wave64) owns one (n, group, block of up
-//    to 4 output channels, band of BH rows x TW columns).  It stages the
-//    band's input rows for the group's channels, with a one-pixel zero halo,
-//    in LDS, so every input byte comes from HBM once per output-channel
-//    block (the cooperative shared halo of the Atlas page's third kernel).
-//  - The staging issues its global loads in batches of kBatch independent
-//    128-bit loads per lane before writing any of them to LDS, so a lane
-//    keeps several loads in flight instead of waiting on each one.
-//  - LDS row layout: [3 pad][left halo][TW interior columns][right halo][pad]
-//    so interior columns land 16-byte aligned (128-bit LDS writes) and a
-//    lane's window of Q+2 inputs is read as b32 + Q/4 x b128 + b32.
-//  - Each lane computes Q adjacent outputs along W for every output channel
-//    of the block (the Atlas page's fourth kernel gives each thread four
-//    neighbouring outputs; here Q is 4 or 8 and the lane also covers up to four
-//    output channels): per input channel and kernel row, Q+2 LDS reads feed
-//    CO*3*Q FMAs.  The block's weights sit in LDS and are read as broadcasts.
-//  - Results leave as 128-bit stores; the W tail is masked.
+// Two kernels:
+//  - grouped3x3_rows_kernel (W a multiple of 4, W <= 256, 16-byte aligned
+//    tensors): register streaming with no LDS and no barriers.  A lane owns
+//    RB rows x 4 columns of one (n, group, block of up to 4 output channels)
+//    plane, reads its 4-column piece of every input row it needs with one
+//    16-byte load, and takes the columns to its left and right from the
+//    neighbouring lanes.  This is the Atlas page's fourth kernel (several
+//    neighbouring outputs per thread, sharing the overlapping input windows)
+//    turned 2-D and widened over output channels, with the page's shared
+//    halo tile left to the L2: on gfx950 the occupancy that no LDS
+//    allocation buys is worth more than the reuse an LDS tile would add.
+//  - grouped3x3_kernel (any other W or alignment): one workgroup stages a
+//    band of input rows with a one-pixel zero halo in LDS (the cooperative
+//    halo tile of the Atlas page's third kernel) using batches of
+//    independent 128-bit loads, then each lane computes Q = 4 or 8
+//    neighbouring outputs along W for up to 4 output channels, reading its
+//    window of Q+2 inputs per row as b32 + Q/4 x b128 + b32 and the weights
+//    as LDS broadcasts.  The W tail is masked.
 #include "dev_common.h"
 #include "internal.h"
 
@@ -29,6 +29,14 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kBatch = 8;   // global loads in flight per lane during staging
 constexpr int kLead = 4;    // LDS index of interior column 0
+constexpr bool kUseMfma4 = false;
+// buffer resource descriptor word 3 for raw (untyped, unswizzled) 32-bit
+// access on gfx9-family GPUs, and a byte offset no plane reaches (reads 0)
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kOutOfPlane = 0x7fffffff;
+constexpr int kMfmaRB = 8;
+constexpr int kSmallWaves = 256;    // below this many waves at 2 rows per lane, use 1
+constexpr int kLargeWaves = 8192;   // depthwise with at least this many waves at 4 rows per lane uses 4
 
 struct G3Params {
     int C, H, W, K;
@@ -193,264 +201,321 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Streaming variant for full-row bands (W % 4 == 0, W <= 256, 16-byte aligned
-// tensors): a persistent grid walks the units (n, group, channel block, band)
-// and double-buffers them in LDS.  A band of one input channel is a single
-// contiguous run of global memory, copied straight into LDS with
-// global_load_lds_dwordx4 (lane l of a wave writes 16 bytes at M0 + 16*l),
-// so the next unit's loads are in flight, without using registers, while the
-// current unit is computed.  Rows above and below the image are zero-filled
-// with LDS stores; the left/right zero padding is applied when a lane reads
-// its window.  The weights of a unit are uniform over the workgroup and come
-// through the scalar cache.
+// Register variant (W % 4 == 0, W <= 256, 16-byte aligned tensors): no LDS
+// and no barriers.  Each wave owns a set of whole image rows of one
+// (n, group, channel block) plane; a lane owns RB rows x 4 columns of the
+// plane for the CO output channels of the block.  It reads its 4-column
+// piece of each of the RB+2 input rows it needs straight from global memory
+// into registers (one 16-byte load per row and input channel, coalesced
+// along the row), takes the column to its left and right from the
+// neighbouring lanes with cross-lane moves, and accumulates every 3x3 tap
+// it touches.  The halo rows that neighbouring lanes and waves share come
+// from the L2, so HBM sees each input byte about once.  With no LDS the
+// occupancy is set by registers alone and every wave streams on its own.
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
-struct G3Stream {
+struct G3Rows {
     int C, H, W, K, G;
     int cout, n_cob;
-    int BH, n_rb;      // band height and bands per plane
-    int units;         // N * G * n_cob * n_rb
-    int buf_floats;    // floats of one staged band (CI * (BH + 2) * W)
+    int cg;       // 4-column groups per row (W / 4)
+    int rpw;      // lane strips (of RB rows) per wave: 64 / cg
+    int strips;   // strips per plane: ceil(H / RB)
+    int wpp;      // waves per plane: ceil(strips / rpw)
+    int waves;    // N * G * n_cob * wpp
 };
 
-__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-template <int CI, int CO>
-__device__ __forceinline__ void stream_stage(const float *__restrict__ x, const float *__restrict__ w,
-                                             const G3Stream &p, int u, float *buf) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rb = u % p.n_rb;
-    int t = u / p.n_rb;
-    const int cob = t % p.n_cob;
-    t /= p.n_cob;
+template <int CI, int CO, int RB>
+__global__ __launch_bounds__(kBlock) void grouped3x3_rows_kernel(const float *__restrict__ x,
+                                                                 const float *__restrict__ w,
+                                                                 const float *__restrict__ bias,
+                                                                 float *__restrict__ y, G3Rows p) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
+    if (wv >= p.waves) return;  // whole waves only
+    const int plane = wv / p.wpp, wip = wv - plane * p.wpp;
+    const int cob = plane % p.n_cob;
+    const int t = plane / p.n_cob;
     const int g = t % p.G, n = t / p.G;
-    const int oh0 = rb * p.BH;
-    const int rows = p.BH + 2;
-    const int ih_lo = max(oh0 - 1, 0), ih_hi = min(oh0 + p.BH + 1, p.H);
-    const int lr_lo = ih_lo - (oh0 - 1);                  // first staged row that exists
-    const int n16 = (ih_hi - ih_lo) * p.W / 4;            // 16-byte pieces per channel
+    const int sl = lane / p.cg, cgi = lane - sl * p.cg;
+    const int strip = wip * p.rpw + sl;
+    const bool active = sl < p.rpw && strip < p.strips;
+    const int r0 = strip * RB, c0 = cgi * 4;
+    const bool has_left = cgi > 0, has_right = cgi < p.cg - 1;
     const size_t HW = (size_t)p.H * p.W;
-    const float *xg = x + ((size_t)n * p.C + (size_t)g * CI) * HW + (size_t)ih_lo * p.W;
-    // rows outside the image read zero: staged rows [0, lr_lo) and
-    // [lr_hi, rows) of every channel
-    const int lr_hi = lr_lo + (ih_hi - ih_lo);
-    const int nz = lr_lo + (rows - lr_hi);                 // zero rows per channel
-    if (nz > 0) {
-        const int w4 = p.W >> 2;
-        for (int e = tid; e < CI * nz * w4; e += kBlock) {
-            const int zr = e / w4, c4 = (e - zr * w4) << 2;
-            const int ci = zr / nz, k = zr - ci * nz;
-            const int lr = k < lr_lo ? k : lr_hi + (k - lr_lo);
-            *reinterpret_cast<float4 *>(buf + (ci * rows + lr) * p.W + c4) = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    // the rows that exist, one contiguous run of global memory per channel,
-    // straight into LDS (after the zero rows: an LDS store issued after the
-    // DMA would make the compiler wait for the DMA)
-#pragma unroll
-    for (int ci = 0; ci < CI; ++ci) {
-        float *dst = buf + (ci * rows + lr_lo) * p.W;
-        const float *src = xg + ci * HW;
-        for (int q = wave; q * 64 < n16; q += 4) {
-            const int e = q * 64 + lane;
-            if (e < n16)
-                __builtin_amdgcn_global_load_lds((glb_void_t *)(src + 4 * e), (lds_void_t *)(dst + q * 256), 16, 0, 0);
-        }
-    }
-}
+    const float *xg = x + ((size_t)n * p.C + (size_t)g * CI) * HW + c0;
+    const int k0 = g * p.cout + cob * CO;
 
-// One unit's compute from band buffer `buf`: every lane's CI*3 windows feed
-// CO*CI*9*Q FMAs; the results stay in `outv` and are stored by the caller
-// after the next barrier (see the kernel below).
-template <int CI, int CO, int Q>
-__device__ __forceinline__ void stream_compute(const float *buf, const float *__restrict__ w,
-                                               const float *__restrict__ bias, const G3Stream &p,
-                                               int k0, int lr, int jq, float (&outv)[CO][Q]) {
-    const int rows = p.BH + 2;
+    float acc[CO][RB][4];
 #pragma unroll
     for (int co = 0; co < CO; ++co) {
         const float b = bias ? bias[k0 + co] : 0.0f;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) outv[co][q] = b;
+        for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[co][rr][q] = b;
     }
-#pragma unroll 1
-    for (int ci = 0; ci < CI; ++ci) {
+    // Input channels are processed in pairs with two row buffers: the rows
+    // of channel ci+1 are loaded before the FMAs of channel ci and the rows
+    // of ci+2 before those of ci+1, so every channel's loads are in flight
+    // during the previous channel's arithmetic.
+    float4 ra[RB + 2], rb[RB + 2];
+    // Rows are read through a buffer resource spanning one input-channel
+    // plane: rows above or below the image and idle lanes get an offset
+    // outside the plane, for which the hardware returns zero.  The loads are
+    // unconditional, so the code has no branches around them and the
+    // compiler waits for exactly the loads it needs (a partial vmcnt).
+    const int plane_bytes = (int)(HW * sizeof(float));
+    auto load_rows = [&](float4 (&dst)[RB + 2], int ci) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(xg - c0 + (size_t)ci * HW), (short)0, plane_bytes, kBufferWord3);
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            const int base = (ci * rows + lr + r) * p.W + jq;
-            float win[Q + 2];
-            const float left = buf[jq > 0 ? base - 1 : base];
-            const float right = buf[jq + Q < p.W ? base + Q : base];
-            win[0] = jq > 0 ? left : 0.0f;
-            win[Q + 1] = jq + Q < p.W ? right : 0.0f;
+        for (int i = 0; i < RB + 2; ++i) {
+            const int ih = r0 - 1 + i;
+            const int off = active ? (ih * p.W + c0) * (int)sizeof(float) : kOutOfPlane;
+            dst[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        }
+    };
+    auto accumulate = [&](const float4 (&rows)[RB + 2], int ci) __attribute__((always_inline)) {
+        const float *wc = w + ((size_t)k0 * CI + ci) * 9;
 #pragma unroll
-            for (int q = 0; q < Q; q += 4) {
-                const float4 v = *reinterpret_cast<const float4 *>(buf + base + q);
-                win[q + 1] = v.x; win[q + 2] = v.y; win[q + 3] = v.z; win[q + 4] = v.w;
-            }
+        for (int i = 0; i < RB + 2; ++i) {
+            float win[6];
+            const float l = __shfl_up(rows[i].w, 1, 64);
+            const float r = __shfl_down(rows[i].x, 1, 64);
+            win[0] = has_left ? l : 0.0f;
+            win[1] = rows[i].x; win[2] = rows[i].y; win[3] = rows[i].z; win[4] = rows[i].w;
+            win[5] = has_right ? r : 0.0f;
 #pragma unroll
-            for (int co = 0; co < CO; ++co) {
-                // readfirstlane keeps the weight offset uniform (scalar loads,
-                // which never wait on the band DMA) and opaque, so the loads
-                // of different channels are not merged into one long batch
-                const int off = __builtin_amdgcn_readfirstlane(((k0 + co) * CI + ci) * 9 + r * 3);
-                const float *wg = w + off;
+            for (int kr = 0; kr < 3; ++kr) {
+                const int rr = i - kr;  // output row fed by input row i through kernel row kr
+                if (rr < 0 || rr >= RB) continue;
 #pragma unroll
-                for (int s = 0; s < 3; ++s) {
-                    const float wv = wg[s];
+                for (int co = 0; co < CO; ++co) {
+                    const float *wk = wc + (size_t)co * CI * 9 + kr * 3;
 #pragma unroll
-                    for (int q = 0; q < Q; ++q) outv[co][q] = fmaf(win[q + s], wv, outv[co][q]);
+                    for (int s = 0; s < 3; ++s) {
+                        const float wv_s = wk[s];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[co][rr][q] = fmaf(win[q + s], wv_s, acc[co][rr][q]);
+                    }
                 }
             }
         }
+    };
+    load_rows(ra, 0);
+#pragma unroll 1
+    for (int ci = 0; ci < CI; ci += 2) {
+        if (ci + 1 < CI) load_rows(rb, ci + 1);
+        accumulate(ra, ci);
+        if (ci + 1 < CI) {
+            if (ci + 2 < CI) load_rows(ra, ci + 2);
+            accumulate(rb, ci + 1);
+        }
     }
+    if (!active) return;
+    float *yb = y + ((size_t)n * p.K + k0) * HW + c0;
+#pragma unroll
+    for (int co = 0; co < CO; ++co)
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+            const int oh = r0 + rr;
+            if (oh < p.H)
+                *reinterpret_cast<float4 *>(yb + (size_t)co * HW + (size_t)oh * p.W) =
+                    make_float4(acc[co][rr][0], acc[co][rr][1], acc[co][rr][2], acc[co][rr][3]);
+        }
 }
 
-// Static LDS double buffer: two distinct LDS objects, so the compiler can
-// tell that reads of one buffer never alias the DMA into the other and does
-// not wait for the DMA before them.  CAP floats per buffer (a size class
-// chosen on the host).
-template <int CI, int CO, int Q, int CAP>
-__global__ __launch_bounds__(kBlock) void grouped3x3_stream_kernel(
-    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
-    float *__restrict__ y, G3Stream p) {
-    __shared__ float4 bufA4[CAP / 4];
-    __shared__ float4 bufB4[CAP / 4];
-    float *bufA = reinterpret_cast<float *>(bufA4);
-    float *bufB = reinterpret_cast<float *>(bufB4);
-    const int tid = threadIdx.x;
-    const int tasks_per_row = p.W / Q;
-    const int lr = tid / tasks_per_row;                 // this lane's output row in the band
-    const int jq = (tid - lr * tasks_per_row) * Q;      // and its first column
+// Matrix-core variant for groups of exactly 4 output channels (any W, any
+// alignment).  v_mfma_f32_4x4x1f32 computes 16 independent 4x4 outer
+// products per instruction: for block b (lanes 4b..4b+3), D_b[i][j] +=
+// A[lane 4b+i] * B[lane 4b+j], with D_b[i][j] in register i of lane 4b+j.
+// Lane l owns output column c0 + l of a row band: its A operand is the
+// weight of output channel k0 + l%4 at the current tap, its B operand is the
+// input under that tap, so register i of lane l accumulates output channel
+// k0 + i at column c0 + l.  Each instruction is one tap (input channel, r,
+// s) for 64 pixels x 4 output channels, with no zero padding in the
+// operands: the group's 4 output channels fill the 4 rows of every block.
+// A wave loads one value per lane of each input row it needs (coalesced
+// along the row) and takes the s = 0 and s = 2 taps from the neighbouring
+// lanes with DPP wave shifts; the lanes at the two ends of a 64-column chunk
+// load their outer neighbour themselves when the image continues there.
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct G3Mfma {
+    int C, H, W, K, G;
+    int cin;
+    int n_cc;     // 64-column chunks per row
+    int n_rb;     // row bands of RB rows
+    int waves;    // N * G * n_rb * n_cc
+};
+
+// DPP wave_shr:1 / wave_shl:1: lane l receives lane l-1 / l+1; the lane
+// with no source (0 / 63) receives `edge`.
+__device__ __forceinline__ float wave_shr1(float v, float edge) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, edge),
+                                                                 __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_shl1(float v, float edge) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, edge),
+                                                                 __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, false));
+}
+
+template <int CI, int RB>
+__global__ __launch_bounds__(kBlock) void grouped3x3_mfma_kernel(const float *__restrict__ x,
+                                                                 const float *__restrict__ w,
+                                                                 const float *__restrict__ bias,
+                                                                 float *__restrict__ y, G3Mfma p) {
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
+    if (wv >= p.waves) return;  // whole waves only
+    const int cc = wv % p.n_cc;
+    int t = wv / p.n_cc;
+    const int rb = t % p.n_rb;
+    t /= p.n_rb;
+    const int g = t % p.G, n = t / p.G;
+    const int c0 = cc * 64, ow = c0 + lane;
+    const int oh0 = rb * RB;
+    const bool col_ok = ow < p.W;
+    const bool need_l = c0 > 0, need_r = c0 + 64 < p.W;  // wave-uniform
     const size_t HW = (size_t)p.H * p.W;
+    const float *xg = x + ((size_t)n * p.C + (size_t)g * CI) * HW;
+    const int k0 = g * 4;
 
-    // Per unit: wait for its band, store the previous unit's outputs, start
-    // the next unit's DMA, compute.  The vector-memory counter covers stores
-    // as well as loads and retires them in order, so stores issued before
-    // the next DMA are older than it: the wait at the top of the next unit
-    // finds them long done instead of stalling on freshly issued ones.
-    float outv[CO][Q];
-    float *out_dst = nullptr;  // row start of channel k0 for outv; null: nothing pending
-    auto flush = [&]() __attribute__((always_inline)) {
-        if (out_dst) {
+    // A operands: the weights of output channel k0 + lane%4, all taps
+    float wr[CI * 9];
+    const float *wl = w + (size_t)(k0 + (lane & 3)) * CI * 9;
 #pragma unroll
-            for (int co = 0; co < CO; ++co)
+    for (int q = 0; q < CI * 9; ++q) wr[q] = wl[q];
+
+    floatx4 acc[RB];
 #pragma unroll
-                for (int q = 0; q < Q; q += 4)
-                    *reinterpret_cast<float4 *>(out_dst + co * HW + q) =
-                        make_float4(outv[co][q], outv[co][q + 1], outv[co][q + 2], outv[co][q + 3]);
-            out_dst = nullptr;
+    for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rr][i] = bias ? bias[k0 + i] : 0.0f;
+
+    float rows[RB + 2], next[RB + 2];
+    auto load_rows = [&](float (&dst)[RB + 2], int ci) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RB + 2; ++i) {
+            const int ih = oh0 - 1 + i;
+            dst[i] = (col_ok && ih >= 0 && ih < p.H) ? xg[(size_t)ci * HW + (size_t)ih * p.W + ow] : 0.0f;
         }
     };
-    auto unit = [&](int u, const float *cur, float *nxt) __attribute__((always_inline)) {
-        wait_async_loads();
-        __syncthreads();  // unit u staged in cur; every lane is done with nxt
-        flush();
-        const int un = u + (int)gridDim.x;
-        if (un < p.units) stream_stage<CI, CO>(x, w, p, un, nxt);
-        const int rb = u % p.n_rb;
-        int t = u / p.n_rb;
-        const int cob = t % p.n_cob;
-        t /= p.n_cob;
-        const int g = t % p.G, n = t / p.G;
-        const int oh = rb * p.BH + lr;
-        if (lr < p.BH && oh < p.H) {
-            const int k0 = g * p.cout + cob * CO;
-            stream_compute<CI, CO, Q>(cur, w, bias, p, k0, lr, jq, outv);
-            out_dst = y + ((size_t)n * p.K + k0) * HW + (size_t)oh * p.W + jq;
+    load_rows(rows, 0);
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+        if (ci + 1 < CI) load_rows(next, ci + 1);
+#pragma unroll
+        for (int i = 0; i < RB + 2; ++i) {
+            const int ih = oh0 - 1 + i;
+            const bool row_ok = ih >= 0 && ih < p.H;
+            const float *xr = xg + (size_t)ci * HW + (size_t)ih * p.W;
+            float el = 0.0f, er = 0.0f;
+            if (need_l && lane == 0 && row_ok) el = xr[c0 - 1];
+            if (need_r && lane == 63 && row_ok) er = xr[c0 + 64];
+            const float xm = wave_shr1(rows[i], el);  // column ow - 1 (tap s = 0)
+            const float xp = wave_shl1(rows[i], er);  // column ow + 1 (tap s = 2)
+#pragma unroll
+            for (int kr = 0; kr < 3; ++kr) {
+                const int rr = i - kr;  // output row fed by input row i through kernel row kr
+                if (rr < 0 || rr >= RB) continue;
+                const float *wt = wr + (ci * 3 + kr) * 3;
+                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[0], xm, acc[rr], 0, 0, 0);
+                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[1], rows[i], acc[rr], 0, 0, 0);
+                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[2], xp, acc[rr], 0, 0, 0);
+            }
         }
-    };
-    int u = blockIdx.x;
-    if (u < p.units) stream_stage<CI, CO>(x, w, p, u, bufA);
-    while (u < p.units) {
-        unit(u, bufA, bufB);
-        u += gridDim.x;
-        if (u >= p.units) break;
-        unit(u, bufB, bufA);
-        u += gridDim.x;
+        if (ci + 1 < CI) {
+#pragma unroll
+            for (int i = 0; i < RB + 2; ++i) rows[i] = next[i];
+        }
     }
-    flush();
+    if (!col_ok) return;
+    float *yb = y + ((size_t)n * p.K + k0) * HW + ow;
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+        const int oh = oh0 + rr;
+        if (oh < p.H) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yb[(size_t)i * HW + (size_t)oh * p.W] = acc[rr][i];
+        }
+    }
 }
 
-template <int CI, int CO, int Q, int CAP>
-hipError_t launch_stream_t(const G3Stream &p, const float *x, const float *w, const float *bias,
-                           float *y, hipStream_t st) {
-    auto kern = grouped3x3_stream_kernel<CI, CO, Q, CAP>;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    const long long want = (long long)cus * per_cu;
-    const int grid = (int)(p.units < want ? p.units : want);
+template <int CI, int RB>
+hipError_t launch_mfma_t(const G3Mfma &p, const float *x, const float *w, const float *bias, float *y,
+                         hipStream_t st) {
+    const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    hipLaunchKernelGGL((grouped3x3_mfma_kernel<CI, RB>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
     return hipGetLastError();
 }
 
-// buffer size classes (floats per band buffer)
-constexpr int kCapS = 2304, kCapM = 4608, kCapL = 9216;
-
-template <int CI, int CO, int Q>
-hipError_t launch_stream_cap(int cap, const G3Stream &p, const float *x, const float *w,
-                             const float *bias, float *y, hipStream_t st) {
-    if (cap == kCapS) return launch_stream_t<CI, CO, Q, kCapS>(p, x, w, bias, y, st);
-    if (cap == kCapM) return launch_stream_t<CI, CO, Q, kCapM>(p, x, w, bias, y, st);
-    return launch_stream_t<CI, CO, Q, kCapL>(p, x, w, bias, y, st);
+bool mfma_plan(const gconv_desc *d, int RB, G3Mfma *p) {
+    if (d->cout != 4) return false;
+    p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K; p->G = d->groups;
+    p->cin = d->cin;
+    p->n_cc = (d->W + 63) / 64;
+    p->n_rb = (d->H + RB - 1) / RB;
+    const long long waves = (long long)d->N * d->groups * p->n_rb * p->n_cc;
+    if (waves > 0x7fffffffLL - 64) return false;
+    p->waves = (int)waves;
+    return true;
 }
 
-template <int CI, int Q>
-hipError_t launch_stream_co(int CO, int cap, const G3Stream &p, const float *x, const float *w,
-                            const float *bias, float *y, hipStream_t st) {
-    switch (CO) {
-        case 4: return launch_stream_cap<CI, 4, Q>(cap, p, x, w, bias, y, st);
-        case 2: return launch_stream_cap<CI, 2, Q>(cap, p, x, w, bias, y, st);
-        default: return launch_stream_cap<CI, 1, Q>(cap, p, x, w, bias, y, st);
+template <int RB>
+hipError_t launch_mfma(const G3Mfma &p, const float *x, const float *w, const float *bias, float *y,
+                       hipStream_t st) {
+    if (p.cin == 4) return launch_mfma_t<4, RB>(p, x, w, bias, y, st);
+    if (p.cin == 2) return launch_mfma_t<2, RB>(p, x, w, bias, y, st);
+    return launch_mfma_t<1, RB>(p, x, w, bias, y, st);
+}
+
+template <int CI, int CO, int RB>
+hipError_t launch_rows_t(const G3Rows &p, const float *x, const float *w, const float *bias, float *y,
+                         hipStream_t st) {
+    const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
+    clear_stale_launch_error();
+    hipLaunchKernelGGL((grouped3x3_rows_kernel<CI, CO, RB>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    return hipGetLastError();
+}
+
+template <int RB>
+hipError_t launch_rows(int CI, int CO, const G3Rows &p, const float *x, const float *w, const float *bias,
+                       float *y, hipStream_t st) {
+    if (CI == 4) {
+        if (CO == 4) return launch_rows_t<4, 4, RB>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_rows_t<4, 2, RB>(p, x, w, bias, y, st);
+        return launch_rows_t<4, 1, RB>(p, x, w, bias, y, st);
     }
-}
-
-template <int Q>
-hipError_t launch_stream_ci(int CI, int CO, int cap, const G3Stream &p, const float *x,
-                            const float *w, const float *bias, float *y, hipStream_t st) {
-    switch (CI) {
-        case 4:
-            if constexpr (Q == 8) return hipErrorInvalidValue;  // never planned: Q = 4 for 4-channel groups
-            else return launch_stream_co<4, Q>(CO, cap, p, x, w, bias, y, st);
-        case 2: return launch_stream_co<2, Q>(CO, cap, p, x, w, bias, y, st);
-        default: return launch_stream_co<1, Q>(CO, cap, p, x, w, bias, y, st);
+    if (CI == 2) {
+        if (CO == 4) return launch_rows_t<2, 4, RB>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_rows_t<2, 2, RB>(p, x, w, bias, y, st);
+        return launch_rows_t<2, 1, RB>(p, x, w, bias, y, st);
     }
+    if (CO == 4) return launch_rows_t<1, 4, RB>(p, x, w, bias, y, st);
+    if (CO == 2) return launch_rows_t<1, 2, RB>(p, x, w, bias, y, st);
+    return launch_rows_t<1, 1, RB>(p, x, w, bias, y, st);
 }
 
-// The streaming variant's geometry, or false when it does not apply.
-bool stream_plan(const gconv_desc *d, const float *x, const float *y, int *Qout, G3Stream *p, int *cap) {
+// The register variant's geometry for RB rows per lane, or false.
+bool rows_plan(const gconv_desc *d, const float *x, const float *y, int RB, G3Rows *p) {
     if (d->W % 4 != 0 || d->W > 256) return false;
+    // byte offsets within one plane, including one row before and after it,
+    // must fit a signed 32-bit buffer offset
+    if ((long long)(d->H + 2) * d->W * (long long)sizeof(float) >= 0x7fffffffLL) return false;
     if (((uintptr_t)x | (uintptr_t)y) & 15u) return false;
-    // Q = 8 halves the LDS reads per output, but a lane then holds 3*CI
-    // windows of 10 inputs; 4-channel groups take Q = 4 (fewer registers,
-    // half-height bands, four workgroups per CU).
-    const int Q = (d->W % 8 == 0 && d->cin < 4) ? 8 : 4;
-    const int tpr = d->W / Q;
-    if (tpr > 64) return false;
     const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
-    int bh = kBlock / tpr;
-    if (bh > d->H) bh = d->H;
-    const int n_rb = (d->H + bh - 1) / bh;
     p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K; p->G = d->groups;
     p->cout = d->cout;
     p->n_cob = d->cout / CO;
-    p->BH = (d->H + n_rb - 1) / n_rb;
-    p->n_rb = n_rb;
-    const long long units = (long long)d->N * d->groups * p->n_cob * n_rb;
-    if (units > 0x7fffffffLL) return false;
-    p->units = (int)units;
-    p->buf_floats = d->cin * (p->BH + 2) * d->W;
-    if (p->buf_floats <= kCapS) *cap = kCapS;
-    else if (p->buf_floats <= kCapM) *cap = kCapM;
-    else if (p->buf_floats <= kCapL) *cap = kCapL;
-    else return false;
-    *Qout = Q;
+    p->cg = d->W / 4;
+    p->rpw = 64 / p->cg;
+    p->strips = (d->H + RB - 1) / RB;
+    p->wpp = (p->strips + p->rpw - 1) / p->rpw;
+    const long long waves = (long long)d->N * d->groups * p->n_cob * p->wpp;
+    if (waves > 0x7fffffffLL - 64) return false;
+    p->waves = (int)waves;
     return true;
 }
 
@@ -492,13 +557,23 @@ bool grouped3x3_supported(const gconv_desc *d) {
 hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w, const float *bias,
                              float *y, hipStream_t st) {
     if (!grouped3x3_supported(d)) return hipErrorInvalidValue;
+    if (kUseMfma4) {
+        G3Mfma mp;
+        if (mfma_plan(d, kMfmaRB, &mp)) return launch_mfma<kMfmaRB>(mp, x, w, bias, y, st);
+    }
     {
-        G3Stream sp;
-        int cap = 0, sq = 0;
-        if (stream_plan(d, x, y, &sq, &sp, &cap)) {
-            const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
-            if (sq == 8) return launch_stream_ci<8>(d->cin, CO, cap, sp, x, w, bias, y, st);
-            return launch_stream_ci<4>(d->cin, CO, cap, sp, x, w, bias, y, st);
+        // rows per lane: 2 in general; 4 for large depthwise problems (less
+        // halo traffic through the L2, and registers to spare); 1 when the
+        // problem is so small that the critical path of one wave dominates
+        G3Rows rp;
+        const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
+        if (rows_plan(d, x, y, 2, &rp)) {
+            if (rp.waves < kSmallWaves && rows_plan(d, x, y, 1, &rp))
+                return launch_rows<1>(d->cin, CO, rp, x, w, bias, y, st);
+            if (d->cin == 1 && rows_plan(d, x, y, 4, &rp) && rp.waves >= kLargeWaves)
+                return launch_rows<4>(d->cin, CO, rp, x, w, bias, y, st);
+            rows_plan(d, x, y, 2, &rp);
+            return launch_rows<2>(d->cin, CO, rp, x, w, bias, y, st);
         }
     }
     const int Q = d->W >= 32 ? 8 : 4;

@@ -285,10 +285,16 @@ EDGE = [
     synth.Workload("w33_tail", 1, 4, 9, 33, 8, 3, 3, 1, 1, 1, 4, 43, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("wide_300", 1, 2, 5, 300, 2, 3, 3, 1, 1, 1, 2, 44, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("cout3", 1, 8, 10, 10, 6, 3, 3, 1, 1, 1, 2, 45, ("uniform", -1, 1), ("uniform", -1, 1)),
-    synth.Workload("stream_h37_cob2", 2, 8, 37, 64, 16, 3, 3, 1, 1, 1, 2, 51, ("uniform", -1, 1), ("uniform", -1, 1)),
-    synth.Workload("stream_w252_q4", 1, 4, 9, 252, 4, 3, 3, 1, 1, 1, 4, 52, ("uniform", -1, 1), ("uniform", -1, 1)),
-    synth.Workload("stream_w20_cpg2", 3, 6, 11, 20, 6, 3, 3, 1, 1, 1, 3, 53, ("uniform", -1, 1), ("uniform", -1, 1)),
-    synth.Workload("stream_h1", 2, 8, 1, 8, 8, 3, 3, 1, 1, 1, 8, 54, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_h37_cob2", 2, 8, 37, 64, 16, 3, 3, 1, 1, 1, 2, 51, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_w252", 1, 4, 9, 252, 4, 3, 3, 1, 1, 1, 4, 52, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_w20_cpg2", 3, 6, 11, 20, 6, 3, 3, 1, 1, 1, 3, 53, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_h1", 2, 8, 1, 8, 8, 3, 3, 1, 1, 1, 8, 54, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # depthwise with enough waves for 4 rows per lane, H not a multiple of 4
+    synth.Workload("rows_rb4_h30", 64, 128, 30, 16, 128, 3, 3, 1, 1, 1, 128, 58, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # a whole 256-column row per wave, one lane strip per wave
+    synth.Workload("rows_w256_cpg4", 1, 8, 5, 256, 8, 3, 3, 1, 1, 1, 2, 59, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # tiny: one row per lane
+    synth.Workload("rows_rb1_w4", 1, 2, 3, 4, 2, 3, 3, 1, 1, 1, 1, 60, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("res_cin5_pad1", 2, 5, 13, 70, 32, 3, 3, 1, 1, 1, 1, 55, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("res_cin4_k40", 1, 4, 19, 131, 40, 3, 3, 1, 0, 1, 1, 56, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("res_1x1_k64", 2, 8, 9, 66, 64, 1, 1, 1, 0, 1, 1, 57, ("uniform", -1, 1), ("uniform", -1, 1)),
