@@ -29,7 +29,6 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kBatch = 8;   // global loads in flight per lane during staging
 constexpr int kLead = 4;    // LDS index of interior column 0
-constexpr bool kUseMfma4 = false;
 // buffer resource descriptor word 3 for raw (untyped, unswizzled) 32-bit
 // access on gfx9-family GPUs, and a byte offset no plane reaches (reads 0)
 constexpr int kBufferWord3 = 0x00020000;
@@ -324,153 +323,6 @@ __global__ __launch_bounds__(kBlock) void grouped3x3_rows_kernel(const float *__
         }
 }
 
-// Matrix-core variant for groups of exactly 4 output channels (any W, any
-// alignment).  v_mfma_f32_4x4x1f32 computes 16 independent 4x4 outer
-// products per instruction: for block b (lanes 4b..4b+3), D_b[i][j] +=
-// A[lane 4b+i] * B[lane 4b+j], with D_b[i][j] in register i of lane 4b+j.
-// Lane l owns output column c0 + l of a row band: its A operand is the
-// weight of output channel k0 + l%4 at the current tap, its B operand is the
-// input under that tap, so register i of lane l accumulates output channel
-// k0 + i at column c0 + l.  Each instruction is one tap (input channel, r,
-// s) for 64 pixels x 4 output channels, with no zero padding in the
-// operands: the group's 4 output channels fill the 4 rows of every block.
-// A wave loads one value per lane of each input row it needs (coalesced
-// along the row) and takes the s = 0 and s = 2 taps from the neighbouring
-// lanes with DPP wave shifts; the lanes at the two ends of a 64-column chunk
-// load their outer neighbour themselves when the image continues there.
-
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-struct G3Mfma {
-    int C, H, W, K, G;
-    int cin;
-    int n_cc;     // 64-column chunks per row
-    int n_rb;     // row bands of RB rows
-    int waves;    // N * G * n_rb * n_cc
-};
-
-// DPP wave_shr:1 / wave_shl:1: lane l receives lane l-1 / l+1; the lane
-// with no source (0 / 63) receives `edge`.
-__device__ __forceinline__ float wave_shr1(float v, float edge) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, edge),
-                                                                 __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float wave_shl1(float v, float edge) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, edge),
-                                                                 __builtin_bit_cast(int, v), 0x130, 0xf, 0xf, false));
-}
-
-template <int CI, int RB>
-__global__ __launch_bounds__(kBlock) void grouped3x3_mfma_kernel(const float *__restrict__ x,
-                                                                 const float *__restrict__ w,
-                                                                 const float *__restrict__ bias,
-                                                                 float *__restrict__ y, G3Mfma p) {
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
-    if (wv >= p.waves) return;  // whole waves only
-    const int cc = wv % p.n_cc;
-    int t = wv / p.n_cc;
-    const int rb = t % p.n_rb;
-    t /= p.n_rb;
-    const int g = t % p.G, n = t / p.G;
-    const int c0 = cc * 64, ow = c0 + lane;
-    const int oh0 = rb * RB;
-    const bool col_ok = ow < p.W;
-    const bool need_l = c0 > 0, need_r = c0 + 64 < p.W;  // wave-uniform
-    const size_t HW = (size_t)p.H * p.W;
-    const float *xg = x + ((size_t)n * p.C + (size_t)g * CI) * HW;
-    const int k0 = g * 4;
-
-    // A operands: the weights of output channel k0 + lane%4, all taps
-    float wr[CI * 9];
-    const float *wl = w + (size_t)(k0 + (lane & 3)) * CI * 9;
-#pragma unroll
-    for (int q = 0; q < CI * 9; ++q) wr[q] = wl[q];
-
-    floatx4 acc[RB];
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rr][i] = bias ? bias[k0 + i] : 0.0f;
-
-    float rows[RB + 2], next[RB + 2];
-    auto load_rows = [&](float (&dst)[RB + 2], int ci) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < RB + 2; ++i) {
-            const int ih = oh0 - 1 + i;
-            dst[i] = (col_ok && ih >= 0 && ih < p.H) ? xg[(size_t)ci * HW + (size_t)ih * p.W + ow] : 0.0f;
-        }
-    };
-    load_rows(rows, 0);
-#pragma unroll
-    for (int ci = 0; ci < CI; ++ci) {
-        if (ci + 1 < CI) load_rows(next, ci + 1);
-#pragma unroll
-        for (int i = 0; i < RB + 2; ++i) {
-            const int ih = oh0 - 1 + i;
-            const bool row_ok = ih >= 0 && ih < p.H;
-            const float *xr = xg + (size_t)ci * HW + (size_t)ih * p.W;
-            float el = 0.0f, er = 0.0f;
-            if (need_l && lane == 0 && row_ok) el = xr[c0 - 1];
-            if (need_r && lane == 63 && row_ok) er = xr[c0 + 64];
-            const float xm = wave_shr1(rows[i], el);  // column ow - 1 (tap s = 0)
-            const float xp = wave_shl1(rows[i], er);  // column ow + 1 (tap s = 2)
-#pragma unroll
-            for (int kr = 0; kr < 3; ++kr) {
-                const int rr = i - kr;  // output row fed by input row i through kernel row kr
-                if (rr < 0 || rr >= RB) continue;
-                const float *wt = wr + (ci * 3 + kr) * 3;
-                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[0], xm, acc[rr], 0, 0, 0);
-                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[1], rows[i], acc[rr], 0, 0, 0);
-                acc[rr] = __builtin_amdgcn_mfma_f32_4x4x1f32(wt[2], xp, acc[rr], 0, 0, 0);
-            }
-        }
-        if (ci + 1 < CI) {
-#pragma unroll
-            for (int i = 0; i < RB + 2; ++i) rows[i] = next[i];
-        }
-    }
-    if (!col_ok) return;
-    float *yb = y + ((size_t)n * p.K + k0) * HW + ow;
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-        const int oh = oh0 + rr;
-        if (oh < p.H) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) yb[(size_t)i * HW + (size_t)oh * p.W] = acc[rr][i];
-        }
-    }
-}
-
-template <int CI, int RB>
-hipError_t launch_mfma_t(const G3Mfma &p, const float *x, const float *w, const float *bias, float *y,
-                         hipStream_t st) {
-    const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
-    clear_stale_launch_error();
-    hipLaunchKernelGGL((grouped3x3_mfma_kernel<CI, RB>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
-    return hipGetLastError();
-}
-
-bool mfma_plan(const gconv_desc *d, int RB, G3Mfma *p) {
-    if (d->cout != 4) return false;
-    p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K; p->G = d->groups;
-    p->cin = d->cin;
-    p->n_cc = (d->W + 63) / 64;
-    p->n_rb = (d->H + RB - 1) / RB;
-    const long long waves = (long long)d->N * d->groups * p->n_rb * p->n_cc;
-    if (waves > 0x7fffffffLL - 64) return false;
-    p->waves = (int)waves;
-    return true;
-}
-
-template <int RB>
-hipError_t launch_mfma(const G3Mfma &p, const float *x, const float *w, const float *bias, float *y,
-                       hipStream_t st) {
-    if (p.cin == 4) return launch_mfma_t<4, RB>(p, x, w, bias, y, st);
-    if (p.cin == 2) return launch_mfma_t<2, RB>(p, x, w, bias, y, st);
-    return launch_mfma_t<1, RB>(p, x, w, bias, y, st);
-}
-
 template <int CI, int CO, int RB>
 hipError_t launch_rows_t(const G3Rows &p, const float *x, const float *w, const float *bias, float *y,
                          hipStream_t st) {
@@ -557,10 +409,6 @@ bool grouped3x3_supported(const gconv_desc *d) {
 hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w, const float *bias,
                              float *y, hipStream_t st) {
     if (!grouped3x3_supported(d)) return hipErrorInvalidValue;
-    if (kUseMfma4) {
-        G3Mfma mp;
-        if (mfma_plan(d, kMfmaRB, &mp)) return launch_mfma<kMfmaRB>(mp, x, w, bias, y, st);
-    }
     {
         // rows per lane: 2 in general; 4 for large depthwise problems (less
         // halo traffic through the L2, and registers to spare); 1 when the
