@@ -33,7 +33,6 @@ constexpr int kLead = 4;    // LDS index of interior column 0
 // access on gfx9-family GPUs, and a byte offset no plane reaches (reads 0)
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfPlane = 0x7fffffff;
-constexpr int kMfmaRB = 8;
 constexpr int kSmallWaves = 256;    // below this many waves at 2 rows per lane, use 1
 constexpr int kLargeWaves = 8192;   // depthwise with at least this many waves at 4 rows per lane uses 4
 
