@@ -11,21 +11,27 @@
 //    pitch so 32 lanes reading 32 output channels hit 32 banks) and then
 //    walks output tiles (n, 8 rows, 64 columns) in a grid-stride loop;
 //  - a tile's input band [CP][8+R-1][64+S-1] (rows padded to whole 16-byte
-//    pieces) is prefetched into registers two tiles ahead (one 16-byte load
-//    per piece when W and the padding are multiples of 4, else four 4-byte
-//    loads) and written to one of two LDS band buffers after the current
-//    tile's MFMAs, so the global loads of tile u+2 are in flight during the
-//    epilogue of tile u and the MFMAs of tile u+1;
+//    pieces) is prefetched into registers two tiles ahead and written to one
+//    of two LDS band buffers after the current tile's MFMAs, so the global
+//    loads of tile u+2 are in flight during the epilogue of tile u and the
+//    MFMAs of tile u+1;
+//  - every global access goes through a buffer resource, and an element
+//    outside the image (padding, tile overhang, idle lanes) gets an offset
+//    beyond the resource's range: the hardware reads it as zero and drops a
+//    store to it.  The code has no branches around memory instructions, so
+//    the compiler waits for exactly the loads a step needs (a partial
+//    vmcnt) instead of for every outstanding load and store;
 //  - the barriers between tiles order LDS only, so no wave waits for its own
 //    output stores before starting the next tile.
 // Epilogue modes:
-//  kPlain      y = acc (+ bias)
-//  kStats      v = sigmoid((acc + bias) * scale), optional store of v, and
-//              per wave (two rows of the tile) the (count, mean, M2) of each
-//              GroupNorm group of 4 channels, two passes over the registers
-//              and no cross-wave reduction (no barrier in the epilogue)
-//  kNormalize  v as above, then out = (v - mean) * rstd * gamma + beta with
-//              the group statistics already merged, stored to y
+//  kPlain       y = acc (+ bias)
+//  kStats       v = sigmoid((acc + bias) * scale) and, per wave (two rows of
+//               the tile), the (count, mean, M2) of each GroupNorm group of 4
+//               channels, two passes over the registers, no cross-wave
+//               reduction (no barrier in the epilogue)
+//  kStatsStore  kStats, and v is stored to y
+//  kNormalize   v as above, then out = (v - mean) * rstd * gamma + beta with
+//               the group statistics already merged, stored to y
 #include "dev_common.h"
 #include "internal.h"
 
@@ -38,70 +44,90 @@ constexpr int kNBC = 2;  // 32-column blocks per wave row
 constexpr int kTH = 4 * kNBR;
 constexpr int kTW = 32 * kNBC;
 
-constexpr int kPlain = 0, kStats = 1, kNormalize = 2;
+constexpr int kPlain = 0, kStats = 1, kNormalize = 2, kStatsStore = 3;
+constexpr int kResWaves = 3;  // waves per SIMD the register budget is sized for
+
+// buffer resource descriptor word 3 for raw (untyped, unswizzled) 32-bit
+// access on gfx9-family GPUs, and a byte offset beyond every range used here
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kOutOfRange = 0x7fffffff;
+constexpr int kStoreOutOfRange = 0x40000000;  // with a scalar offset below 1 GB added
+constexpr float kLog2e = 1.44269504088896340736f;
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct ResParams {
     int C, H, W, K, Ho, Wo, pad;
     int cin, cout;
     int n_tw, n_tiles, units;   // tiles per image row band, per image, in total
-    int store;                  // kStats: also store v
-    int vec;                    // W, pad multiples of 4 and x 16-byte aligned: 16-byte DMA pieces
+    int x_bytes;                // bytes of one input image (C * H * W floats)
+    int y_bytes;                // bytes of one output image (K * Ho * Wo floats)
+    int parts_bytes;            // bytes of one image's GroupNorm partials
 };
 
 struct ResEpilogue {
-    const float *bias;      // kPlain: nullable conv bias; kStats/kNormalize: required
-    const float *scale;     // kStats/kNormalize
-    Partial *parts;         // kStats: [N][gn_groups][n_tiles * 4 waves]
+    const float *bias;      // kPlain: nullable conv bias; other modes: required
+    const float *scale;     // all modes but kPlain
+    Partial *parts;         // kStats*: [N][gn_groups][n_tiles * 4 waves]
     const float2 *gstat;    // kNormalize: (mean, rstd) per (n, gn group)
     const float *gamma;     // kNormalize, nullable
     const float *beta;      // kNormalize, nullable
     int gn_groups;
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
+}
+
 // Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
-// wait for the wave's outstanding global stores.
+// wait for the wave's outstanding global loads and stores.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int R, int S, int MB, int CP, int MODE>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 3 : 2))) void igemm_res_kernel(const float *__restrict__ x,
+template <int R, int S, int MB, int CP, int MODE, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 ? kResWaves : 2))) void igemm_res_kernel(const float *__restrict__ x,
                                                            const float *__restrict__ w,
                                                            float *__restrict__ y, ResParams p,
                                                            ResEpilogue ep) {
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
-    constexpr int TIH = kTH + R - 1;
+    constexpr int NROW = kNBR + R - 1;        // band rows one wave reads
+    constexpr int TIH = kTH + R - 1;          // band rows of a workgroup tile
     constexpr int TIW = kTW + S - 1;
     constexpr int PITCH = (TIW + 3) & ~3;     // LDS row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
-    constexpr int XE = CP * TIH * PITCH;      // band elements
-    constexpr int XE4 = XE / 4;
-    constexpr int NSLOT4 = (XE4 + kBlock - 1) / kBlock;
+    constexpr int XE4 = CP * TIH * P4;        // 16-byte pieces of a tile's band
+    constexpr int NSLOT = (XE4 + kBlock - 1) / kBlock;
     constexpr int WP = (CP * RS) | 1;         // weight row pitch (odd)
     constexpr int NB = kNBR * kNBC;
     constexpr int HALF = CP / 2;
+    constexpr int NWAVE = kBlock / 64;
+    constexpr int NGS = 16 * MB;              // kNormalize: floats of (mean, rstd) per image
+    constexpr bool kStatsMode = MODE == kStats || MODE == kStatsStore;
 
     __shared__ float wl[KW * WP];
     // per-channel constants, staged once: LDS reads in the epilogue count on
     // lgkmcnt, whereas per-lane global loads would count on vmcnt and make
-    // the epilogue wait for the next tile's DMA
+    // the epilogue wait for the next tile's loads
     __shared__ float2 chan_bs[KW];   // (bias, scale); kPlain: (bias or 0, unused)
     __shared__ float2 chan_gb[KW];   // kNormalize: (gamma or 1, beta or 0)
-    __shared__ float4 bufA4[XE4 + 1];
-    __shared__ float4 bufB4[XE4 + 1];
-    float *bufA = reinterpret_cast<float *>(bufA4);
-    float *bufB = reinterpret_cast<float *>(bufB4);
+    // two band buffers (the tile being multiplied and the next one) and,
+    // for kNormalize, the tiles' group statistics; distinct LDS objects, so
+    // the compiler never makes reads of one wait for writes to the other
+    __shared__ float4 bufA4[XE4];
+    __shared__ float4 bufB4[XE4];
+    __shared__ float gsA[NGS];
+    __shared__ float gsB[NGS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, j = lane & 31;
-    const size_t HW = (size_t)p.H * p.W;
-    const size_t plane = (size_t)p.Ho * p.Wo;
+    const int HW = p.H * p.W;
+    const int plane = p.Ho * p.Wo;
 
     // ---- weights, once: w[k][c][r][s] for k < cout, c < cin, zero elsewhere
     for (int e = tid; e < KW * CP * RS; e += kBlock) {
@@ -111,7 +137,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         if (k < p.cout && c < p.cin) v = w[((size_t)k * p.cin + c) * RS + (q - c * RS)];
         wl[k * WP + q] = v;
     }
-
     for (int k = tid; k < KW; k += kBlock) {
         float b = 0.0f, sc = 1.0f, ga = 1.0f, be = 0.0f;
         if (k < p.cout) {
@@ -122,26 +147,41 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                 if (ep.beta) be = ep.beta[k];
             }
         }
-        chan_bs[k] = make_float2(b, sc);
+        // fused modes: sigmoid((acc + b) * sc) = 1 / (1 + 2^(acc * sA + sB))
+        // with sA = -sc * log2(e), sB = -b * sc * log2(e): one FMA feeds
+        // the exponential
+        if constexpr (MODE == kPlain)
+            chan_bs[k] = make_float2(b, sc);
+        else
+            chan_bs[k] = make_float2(-sc * kLog2e, -b * sc * kLog2e);
         chan_gb[k] = make_float2(ga, be);
     }
+    // The grid walks workgroup tiles (n, kTH output rows, kTW columns); wave
+    // w computes rows kNBR*w .. kNBR*w + kNBR-1 of its tile.
+    const int G = gridDim.x;
+    int u = blockIdx.x;
 
-    // ---- band prefetch through registers: pf holds this lane's pieces of a
-    //      tile's band (16-byte pieces when p.vec, else 4-byte elements),
-    //      zero outside the image; commit() writes them to an LDS buffer
-    float4 pf[NSLOT4];
-    auto load = [&](int u) __attribute__((always_inline)) {
-        const int t = u % p.n_tiles, n = u / p.n_tiles;
+    // ---- band prefetch through registers: pf holds this lane's 16-byte
+    //      pieces of a tile's band, zero outside the image
+    float4 pf[NSLOT];
+    float gpf = 0.0f;
+    auto load = [&](int v) __attribute__((always_inline)) {
+        const int t = v % p.n_tiles, n = v / p.n_tiles;
         const int th = t / p.n_tw, tw = t - th * p.n_tw;
         const int ih0 = th * kTH - p.pad, iw0 = tw * kTW - p.pad;
-        const float *xb = x + (size_t)n * p.C * HW;
+        const __amdgpu_buffer_rsrc_t rs = rsrc(x + (size_t)n * p.C * HW, p.x_bytes);
+        if constexpr (MODE == kNormalize) {
+            const __amdgpu_buffer_rsrc_t gr = rsrc(ep.gstat + (size_t)n * ep.gn_groups, NGS * (int)sizeof(float));
+            gpf = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                gr, tid < NGS ? tid * (int)sizeof(float) : kOutOfRange, 0, 0));
+        }
         // an opaque copy of the thread id: the per-slot offsets are the same
         // for every tile, and hoisting them out of the tile loop would keep
         // them live across the MFMA loop
-        int tid_o = threadIdx.x;
+        int tid_o = tid;
         asm volatile("" : "+v"(tid_o));
 #pragma unroll
-        for (int i = 0; i < NSLOT4; ++i) {
+        for (int i = 0; i < NSLOT; ++i) {
             // piece f = (cl*TIH + lr)*P4 + c4: input columns iw0 + 4*c4 .. +3
             // of row ih0 + lr, channel cl
             const int f = i * kBlock + tid_o;
@@ -149,33 +189,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             const int lr = rem / P4, c4 = rem - lr * P4;
             const int ih = ih0 + lr, iw = iw0 + 4 * c4;
             const bool row_ok = f < XE4 && cl < p.cin && ih >= 0 && ih < p.H;
-            const float *src = xb + (size_t)cl * HW + (size_t)ih * p.W + iw;
-            if (p.vec) {
+            const int rowb = (cl * HW + ih * p.W) * (int)sizeof(float);
+            if constexpr (VEC) {
                 // W and iw0 multiples of 4: the piece is wholly in or out
-                pf[i] = (row_ok && iw >= 0 && iw < p.W) ? *reinterpret_cast<const float4 *>(src)
-                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                const int off = (row_ok && iw >= 0 && iw < p.W) ? rowb + iw * (int)sizeof(float) : kOutOfRange;
+                pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
             } else {
-                pf[i].x = (row_ok && iw + 0 >= 0 && iw + 0 < p.W) ? src[0] : 0.0f;
-                pf[i].y = (row_ok && iw + 1 >= 0 && iw + 1 < p.W) ? src[1] : 0.0f;
-                pf[i].z = (row_ok && iw + 2 >= 0 && iw + 2 < p.W) ? src[2] : 0.0f;
-                pf[i].w = (row_ok && iw + 3 >= 0 && iw + 3 < p.W) ? src[3] : 0.0f;
+                float e4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int off = (row_ok && iw + e >= 0 && iw + e < p.W) ? rowb + (iw + e) * (int)sizeof(float)
+                                                                            : kOutOfRange;
+                    e4[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                }
+                pf[i] = make_float4(e4[0], e4[1], e4[2], e4[3]);
             }
         }
     };
-    auto commit = [&](float *buf) __attribute__((always_inline)) {
+    auto commit = [&](float4 *buf4, float *gsb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NSLOT4; ++i) {
+        for (int i = 0; i < NSLOT; ++i) {
             const int f = i * kBlock + tid;
-            if (f < XE4) reinterpret_cast<float4 *>(buf)[f] = pf[i];
+            if (f < XE4) buf4[f] = pf[i];
+        }
+        if constexpr (MODE == kNormalize) {
+            if (tid < NGS) gsb[tid] = gpf;
         }
     };
 
-    auto compute = [&](int u, const float *buf, auto &&between) __attribute__((always_inline)) {
-        const int t = u % p.n_tiles, n = u / p.n_tiles;
-        const int th = t / p.n_tw, tw = t - th * p.n_tw;
-        const int oh0 = th * kTH, ow0 = tw * kTW;
-
-        floatx16 acc[MB][NB];
+    // ---- MFMAs of the tile whose band is in LDS
+    floatx16 acc[MB][NB];
+    auto mfma_tile = [&](const float4 *buf4) __attribute__((always_inline)) {
+        const float *band = reinterpret_cast<const float *>(buf4);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -184,174 +229,187 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                 for (int v = 0; v < 16; ++v) acc[m][b][v] = 0.0f;
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
+            // operands of one input channel (per half): the weights of the
+            // lane's output channel at every tap, and the NROW band rows x
+            // kNBC column blocks x S shifts of the lane's input column
+            float A[MB][RS];
+            float B[NROW][kNBC][S];
             const int cl = h * HALF + ci;
-            const float *xq = buf + (cl * TIH + wave * kNBR) * PITCH + j;
+            const float *xq = band + (cl * TIH + wave * kNBR) * PITCH + j;
             const float *wq = wl + j * WP + cl * RS;
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int q = 0; q < RS; ++q) A[m][q] = wq[m * 32 * WP + q];
+#pragma unroll
+            for (int row = 0; row < NROW; ++row)
+#pragma unroll
+                for (int bc = 0; bc < kNBC; ++bc)
+#pragma unroll
+                    for (int s = 0; s < S; ++s) B[row][bc][s] = xq[row * PITCH + bc * 32 + s];
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int s = 0; s < S; ++s) {
-                    float a[MB], b[NB];
-#pragma unroll
-                    for (int m = 0; m < MB; ++m) a[m] = wq[m * 32 * WP + r * S + s];
-#pragma unroll
-                    for (int br = 0; br < kNBR; ++br)
-#pragma unroll
-                        for (int bc = 0; bc < kNBC; ++bc) b[br * kNBC + bc] = xq[(br + r) * PITCH + bc * 32 + s];
+                for (int s = 0; s < S; ++s)
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb)
-                            acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], b[nb], acc[m][nb], 0, 0, 0);
-                }
-        }
-
-        between();  // next tiles' data movement, after this tile's LDS reads
-        float *yb = y + (size_t)n * p.K * plane;
-        if constexpr (MODE == kPlain) {
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int br = 0; br < kNBR; ++br) {
-                    const int oh = oh0 + wave * kNBR + br;
-#pragma unroll
-                    for (int bc = 0; bc < kNBC; ++bc) {
-                        const int ow = ow0 + bc * 32 + j;
-                        if (oh >= p.Ho || ow >= p.Wo) continue;
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int k = m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                            if (k < p.cout) yb[(size_t)k * plane + (size_t)oh * p.Wo + ow] = acc[m][br * kNBC + bc][v] + chan_bs[k].x;
-                        }
-                    }
-                }
-        } else {
-            // local GroupNorm group of accumulator v in block m: rows
-            // 8q + 4h + (0..3) -> lg = 8m + 2q + h (4 channels per group)
-            float gm[MB][4], ga[MB][4];  // kNormalize: mean and rstd of the lane's groups
-            if constexpr (MODE == kNormalize) {
-                // uniform addresses: scalar loads for both halves, then a select
-                const float2 *gs = ep.gstat + (size_t)n * ep.gn_groups;
-#pragma unroll
-                for (int m = 0; m < MB; ++m)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float2 s0 = gs[8 * m + 2 * q], s1v = gs[8 * m + 2 * q + 1];
-                        // readfirstlane pins the loaded values as uniform, so
-                        // the select is not turned into a per-lane load
-                        const float m0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s0.x)));
-                        const float r0 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s0.y)));
-                        const float m1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s1v.x)));
-                        const float r1 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s1v.y)));
-                        gm[m][q] = h ? m1 : m0;
-                        ga[m][q] = h ? r1 : r0;
-                    }
-            }
-            float s1[MB][4];
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) s1[m][q] = 0.0f;
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int k = m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    const float2 bs = chan_bs[k];
-                    const float bk = bs.x, sk = bs.y;
-                    float gk = 1.0f, ck = 0.0f;
-                    if constexpr (MODE == kNormalize) {
-                        const float2 gb = chan_gb[k];
-                        gk = ga[m][v >> 2] * gb.x;
-                        ck = gb.y;
-                    }
-#pragma unroll
-                    for (int br = 0; br < kNBR; ++br)
-#pragma unroll
-                        for (int bc = 0; bc < kNBC; ++bc) {
-                            const int oh = oh0 + wave * kNBR + br, ow = ow0 + bc * 32 + j;
-                            const bool ok = oh < p.Ho && ow < p.Wo;
-                            const float val = sigmoidf((acc[m][br * kNBC + bc][v] + bk) * sk);
-                            float *dst = yb + (size_t)k * plane + (size_t)oh * p.Wo + ow;
-                            if constexpr (MODE == kStats) {
-                                acc[m][br * kNBC + bc][v] = val;
-                                if (ok) {
-                                    if (p.store) *dst = val;
-                                    s1[m][v >> 2] += val;
-                                }
-                            } else {
-                                if (ok) *dst = fmaf(val - gm[m][v >> 2], gk, ck);
-                            }
-                        }
-                }
-            if constexpr (MODE == kStats) {
-                // statistics of this wave's part of the tile (its kNBR rows),
-                // two passes over the registers, no cross-wave reduction: one
-                // partial per (tile, wave, group)
-                const int rows_ok = max(0, min(kNBR, p.Ho - (oh0 + wave * kNBR)));
-                const int cols_ok = min(kTW, p.Wo - ow0);
-                const float count = 4.0f * (float)(rows_ok * cols_ok);
-                const float inv = count > 0.0f ? 1.0f / count : 0.0f;
-#pragma unroll
-                for (int m = 0; m < MB; ++m)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float mu = half_wave_sum(s1[m][q]) * inv;
-                        float tq = 0.0f;
-#pragma unroll
                         for (int br = 0; br < kNBR; ++br)
 #pragma unroll
-                            for (int bc = 0; bc < kNBC; ++bc) {
-                                const int oh = oh0 + wave * kNBR + br, ow = ow0 + bc * 32 + j;
-                                if (oh < p.Ho && ow < p.Wo) {
-#pragma unroll
-                                    for (int uu = 0; uu < 4; ++uu) {
-                                        const float dv = acc[m][br * kNBC + bc][4 * q + uu] - mu;
-                                        tq = fmaf(dv, dv, tq);
-                                    }
-                                }
-                            }
-                        const float m2 = half_wave_sum(tq);
-                        if (j == 0) {
-                            Partial pt;
-                            pt.count = count;
-                            pt.mean = mu;
-                            pt.m2 = m2;
-                            pt.pad = 0.0f;
-                            ep.parts[((size_t)n * ep.gn_groups + 8 * m + 2 * q + h) * (4 * p.n_tiles) + t * 4 + wave] = pt;
-                        }
-                    }
-            }
+                            for (int bc = 0; bc < kNBC; ++bc)
+                                acc[m][br * kNBC + bc] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                    A[m][r * S + s], B[br + r][bc][s], acc[m][br * kNBC + bc], 0, 0, 0);
         }
     };
 
-    // Tile loop: barrier (LDS only) -> MFMAs of tile u -> commit tile u+G
-    // (loaded one iteration earlier) to the other buffer -> load tile u+2G
-    // into registers -> epilogue of tile u.  The loads have an epilogue and a
-    // whole MFMA phase to land; the barriers fence LDS only, so no wave ever
-    // waits for its output stores.  Two static buffers keep the LDS objects
-    // of the reads and the writes of an iteration distinct.
-    int u = blockIdx.x;
-    const int G = gridDim.x;
-    if (u < p.units) {
-        load(u);
-        commit(bufA);
-        if (u + G < p.units) load(u + G);
-    }
-    while (u < p.units) {
+    // ---- epilogue of tile v from acc
+    auto epilogue = [&](int v, const float2 (&gst)[MB][4]) __attribute__((always_inline)) {
+        const int t = v % p.n_tiles, n = v / p.n_tiles;
+        const int th = t / p.n_tw, tw = t - th * p.n_tw;
+        const int oh0 = th * kTH + wave * kNBR, ow0 = tw * kTW;
+        const __amdgpu_buffer_rsrc_t ys = rsrc(y + (size_t)n * p.K * plane, p.y_bytes);
+        // byte offset of (channel 0, row oh, column ow) for this lane's
+        // pixels, or -1 where the pixel is outside the output
+        int pix[NB];
+#pragma unroll
+        for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+            for (int bc = 0; bc < kNBC; ++bc) {
+                const int oh = oh0 + br, ow = ow0 + bc * 32 + j;
+                pix[br * kNBC + bc] = (oh < p.Ho && ow < p.Wo) ? (oh * p.Wo + ow) * (int)sizeof(float) : -1;
+            }
+        auto store = [&](int nb, int k, float val) __attribute__((always_inline)) {
+            const int off = pix[nb] >= 0 && k < p.cout ? pix[nb] + k * plane * (int)sizeof(float) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, val), ys, off, 0, 0);
+        };
+        // fused modes (every accumulator row is a real channel): the lane's
+        // part of the address (pixel, and 4h channels) goes in the vector
+        // offset once per tile, the register's channel m*32 + 8(v/4) + v%4
+        // in the scalar offset, so a store costs no VALU work.  Outside the
+        // output the vector offset alone is beyond the range (y images are
+        // below 1 GB, so adding the scalar offset cannot wrap).
+        int vofs[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            vofs[nb] = pix[nb] >= 0 ? pix[nb] + 4 * h * plane * (int)sizeof(float) : kStoreOutOfRange;
+        auto store_fast = [&](int nb, int m, int vv, float val) __attribute__((always_inline)) {
+            const int so = (m * 32 + 8 * (vv >> 2) + (vv & 3)) * plane * (int)sizeof(float);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, val), ys, vofs[nb], so, 0);
+        };
+        // accumulator register v of block m holds channel m*32 + 8(v/4) +
+        // 4h + v%4, local GroupNorm group lg = 8m + 2(v/4) + h (4 channels
+        // per group)
+        float s1[MB][4];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s1[m][q] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const int k = m * 32 + 8 * (vv >> 2) + 4 * h + (vv & 3);
+                const float2 bs = chan_bs[k];
+                if constexpr (MODE == kPlain) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) store(nb, k, acc[m][nb][vv] + bs.x);
+                } else {
+                    // kNormalize: out = v * gk + ck with gk = rstd * gamma,
+                    // ck = beta - mean * gk
+                    float gk = 1.0f, ck = 0.0f;
+                    if constexpr (MODE == kNormalize) {
+                        const float2 gb = chan_gb[k];
+                        gk = gst[m][vv >> 2].y * gb.x;
+                        ck = fmaf(-gst[m][vv >> 2].x, gk, gb.y);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const float e2 = __builtin_amdgcn_exp2f(fmaf(acc[m][nb][vv], bs.x, bs.y));
+                        const float val = __builtin_amdgcn_rcpf(1.0f + e2);
+                        if constexpr (kStatsMode) {
+                            acc[m][nb][vv] = val;
+                            if constexpr (MODE == kStatsStore) store_fast(nb, m, vv, val);
+                            s1[m][vv >> 2] += pix[nb] >= 0 ? val : 0.0f;
+                        } else {
+                            store_fast(nb, m, vv, fmaf(val, gk, ck));
+                        }
+                    }
+                }
+            }
+        if constexpr (kStatsMode) {
+            // statistics of the wave's kNBR rows of the tile, two passes over
+            // the registers, no cross-wave reduction: one partial per (tile,
+            // wave, group)
+            const int rows_ok = max(0, min(kNBR, p.Ho - oh0));
+            const int cols_ok = min(kTW, p.Wo - ow0);
+            const float count = 4.0f * (float)(rows_ok * cols_ok);
+            const float inv = count > 0.0f ? 1.0f / count : 0.0f;
+            const __amdgpu_buffer_rsrc_t ps = rsrc(ep.parts + (size_t)n * ep.gn_groups * (NWAVE * p.n_tiles),
+                                                   p.parts_bytes);
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float mu = half_wave_sum(s1[m][q]) * inv;
+                    float tq = 0.0f;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                        for (int uu = 0; uu < 4; ++uu) {
+                            const float dv = pix[nb] >= 0 ? acc[m][nb][4 * q + uu] - mu : 0.0f;
+                            tq = fmaf(dv, dv, tq);
+                        }
+                    }
+                    const float m2 = half_wave_sum(tq);
+                    const int idx = (8 * m + 2 * q + h) * (NWAVE * p.n_tiles) + t * NWAVE + wave;
+                    const u32x4 pt = {__builtin_bit_cast(unsigned int, count), __builtin_bit_cast(unsigned int, mu),
+                                      __builtin_bit_cast(unsigned int, m2), 0u};
+                    __builtin_amdgcn_raw_buffer_store_b128(pt, ps, j == 0 ? idx * (int)sizeof(Partial) : kOutOfRange,
+                                                           0, 0);
+                }
+        }
+    };
+
+    auto read_gstat = [&](const float *gsb, float2 (&gst)[MB][4]) __attribute__((always_inline)) {
+        if constexpr (MODE == kNormalize) {
+            const float2 *gs = reinterpret_cast<const float2 *>(gsb);
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) gst[m][q] = gs[8 * m + 2 * q + h];
+        }
+    };
+
+    // ---- tile loop: barrier (LDS only) -> MFMAs of tile u from one buffer
+    //      -> (kNormalize) its group statistics to registers -> commit tile
+    //      u+G (loaded one iteration earlier) into the other buffer -> start
+    //      loading tile u+2G -> epilogue of tile u.  The loads have an
+    //      epilogue and a whole MFMA phase to land; the barriers order LDS
+    //      only, so no wave ever waits for its output stores.  Past the last
+    //      tile the indices are clamped and the work is redundant, which
+    //      keeps the code free of branches around the loads.
+    if (u >= p.units) return;
+    float2 gst[MB][4];
+    load(u);
+    commit(bufA4, gsA);
+    load(min(u + G, p.units - 1));
+    while (true) {
         lds_barrier();
-        compute(u, bufA, [&]() __attribute__((always_inline)) {
-            if (u + G < p.units) commit(bufB);
-            if (u + 2 * G < p.units) load(u + 2 * G);
-        });
+        mfma_tile(bufA4);
+        read_gstat(gsA, gst);
+        commit(bufB4, gsB);
+        load(min(u + 2 * G, p.units - 1));
+        epilogue(u, gst);
         u += G;
         if (u >= p.units) break;
         lds_barrier();
-        compute(u, bufB, [&]() __attribute__((always_inline)) {
-            if (u + G < p.units) commit(bufA);
-            if (u + 2 * G < p.units) load(u + 2 * G);
-        });
+        mfma_tile(bufB4);
+        read_gstat(gsB, gst);
+        commit(bufA4, gsA);
+        load(min(u + 2 * G, p.units - 1));
+        epilogue(u, gst);
         u += G;
+        if (u >= p.units) break;
     }
 }
 
@@ -405,35 +463,41 @@ constexpr int kMaxResLds = 64 * 1024;  // keep at least two workgroups per CU
 
 template <int R, int S, int MB, int CP>
 constexpr int res_lds_bytes() {
-    return 4 * (32 * MB * ((CP * R * S) | 1) + 2 * (CP * (kTH + R - 1) * ((kTW + S - 1 + 3) & ~3) + 4));
+    return 4 * (32 * MB * ((CP * R * S) | 1) + 2 * (CP * (kTH + R - 1) * ((kTW + S - 1 + 3) & ~3) + 16 * MB)) +
+           2 * 8 * 32 * MB;
 }
 
-ResParams make_params(const gconv_desc *d) {
+// one GroupNorm partial per (tile of kTH rows x kTW columns, wave, group)
+int res_parts_per_group(const gconv_desc *d) {
+    const int n_tw = (d->Wo + kTW - 1) / kTW;
+    return (kBlock / 64) * n_tw * ((d->Ho + kTH - 1) / kTH);
+}
+
+ResParams make_params(const gconv_desc *d, int gn_groups) {
     ResParams p;
     p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo; p.pad = d->pad;
     p.cin = d->cin; p.cout = d->cout;
     p.n_tw = (d->Wo + kTW - 1) / kTW;
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.units = d->N * p.n_tiles;
-    p.store = 1;
-    p.vec = 0;
+    p.x_bytes = (int)((size_t)d->C * d->H * d->W * sizeof(float));
+    p.y_bytes = (int)((size_t)d->K * d->Ho * d->Wo * sizeof(float));
+    p.parts_bytes = (int)((size_t)gn_groups * res_parts_per_group(d) * sizeof(Partial));
     return p;
 }
 
-ResParams make_params(const gconv_desc *d, const float *x) {
-    ResParams p = make_params(d);
-    p.vec = (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
-    return p;
+bool res_vec(const gconv_desc *d, const float *x) {
+    return (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
 }
 
 int res_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
 int res_cp(const gconv_desc *d) { return d->cin <= 4 ? 4 : 8; }
 
-template <int R, int S, int MB, int CP, int MODE>
+template <int R, int S, int MB, int CP, int MODE, bool VEC>
 hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y, const ResEpilogue &ep,
                     hipStream_t st) {
     static_assert(res_lds_bytes<R, S, MB, CP>() <= kMaxResLds, "LDS budget");
-    auto kern = igemm_res_kernel<R, S, MB, CP, MODE>;
+    auto kern = igemm_res_kernel<R, S, MB, CP, MODE, VEC>;
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -447,52 +511,71 @@ hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y
     return hipGetLastError();
 }
 
+template <int MODE, bool VEC>
+hipError_t launch_mode_v(const gconv_desc *d, const ResParams &p, const float *x, const float *w, float *y,
+                         const ResEpilogue &ep, hipStream_t st) {
+    const int mb = res_mb(d), cp = res_cp(d);
+    if (d->R == 3 && d->S == 3) {
+        if (mb == 1)
+            return cp == 4 ? launch_t<3, 3, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
+                           : launch_t<3, 3, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
+        return cp == 4 ? launch_t<3, 3, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
+                       : launch_t<3, 3, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
+    }
+    if (d->R == 1 && d->S == 1) {
+        if (mb == 1)
+            return cp == 4 ? launch_t<1, 1, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
+                           : launch_t<1, 1, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
+        return cp == 4 ? launch_t<1, 1, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
+                       : launch_t<1, 1, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int MODE>
 hipError_t launch_mode(const gconv_desc *d, const ResParams &p, const float *x, const float *w, float *y,
                        const ResEpilogue &ep, hipStream_t st) {
-    const int mb = res_mb(d), cp = res_cp(d);
-    if (d->R == 3 && d->S == 3) {
-        if (mb == 1) return cp == 4 ? launch_t<3, 3, 1, 4, MODE>(p, x, w, y, ep, st) : launch_t<3, 3, 1, 8, MODE>(p, x, w, y, ep, st);
-        return cp == 4 ? launch_t<3, 3, 2, 4, MODE>(p, x, w, y, ep, st) : launch_t<3, 3, 2, 8, MODE>(p, x, w, y, ep, st);
-    }
-    if (d->R == 1 && d->S == 1) {
-        if (mb == 1) return cp == 4 ? launch_t<1, 1, 1, 4, MODE>(p, x, w, y, ep, st) : launch_t<1, 1, 1, 8, MODE>(p, x, w, y, ep, st);
-        return cp == 4 ? launch_t<1, 1, 2, 4, MODE>(p, x, w, y, ep, st) : launch_t<1, 1, 2, 8, MODE>(p, x, w, y, ep, st);
-    }
-    return hipErrorInvalidValue;
+    return res_vec(d, x) ? launch_mode_v<MODE, true>(d, p, x, w, y, ep, st)
+                         : launch_mode_v<MODE, false>(d, p, x, w, y, ep, st);
 }
 
 }  // namespace
 
 bool igemm_res_supported(const gconv_desc *d) {
+    // buffer offsets are signed 32-bit: one image of x and of y (and the
+    // partials of one image) must stay below 2 GB
+    const long long lim = 0x7fffffffLL - 64;
     return d->groups == 1 && d->stride == 1 && d->dil == 1 && d->cin >= 4 && d->cin <= 8 &&
-           d->cout >= 8 && d->cout <= 64 && ((d->R == 3 && d->S == 3) || (d->R == 1 && d->S == 1));
+           d->cout >= 8 && d->cout <= 64 && ((d->R == 3 && d->S == 3) || (d->R == 1 && d->S == 1)) &&
+           (long long)d->C * d->H * d->W * 4 < lim && (long long)d->K * d->Ho * d->Wo * 4 < lim;
 }
 
 bool igemm_res_fused_supported(const gconv_desc *d, int gn_groups) {
-    return igemm_res_supported(d) && d->cout % (32 * res_mb(d)) == 0 && d->K / gn_groups == 4;
+    return igemm_res_supported(d) && d->cout % (32 * res_mb(d)) == 0 && d->K / gn_groups == 4 &&
+           (long long)d->K * d->Ho * d->Wo * (long long)sizeof(float) < kStoreOutOfRange &&
+           (long long)gn_groups * res_parts_per_group(d) * (long long)sizeof(Partial) < 0x7fffffffLL - 64;
 }
 
-int igemm_res_parts_per_group(const gconv_desc *d) { return 4 * make_params(d).n_tiles; }
+int igemm_res_parts_per_group(const gconv_desc *d) { return res_parts_per_group(d); }
 
 hipError_t launch_igemm_res(const gconv_desc *d, const float *x, const float *w, const float *bias, float *y,
                             hipStream_t st) {
     if (!igemm_res_supported(d)) return hipErrorInvalidValue;
     ResEpilogue ep{};
     ep.bias = bias;
-    return launch_mode<kPlain>(d, make_params(d, x), x, w, y, ep, st);
+    return launch_mode<kPlain>(d, make_params(d, 1), x, w, y, ep, st);
 }
 
 hipError_t launch_igemm_res_stats(const gconv_desc *d, const float *x, const float *w, float *y, bool store,
                                   const FusedEpilogue &fe, hipStream_t st) {
     if (!igemm_res_fused_supported(d, fe.gn_groups)) return hipErrorInvalidValue;
-    ResParams p = make_params(d, x);
-    p.store = store ? 1 : 0;
+    const ResParams p = make_params(d, fe.gn_groups);
     ResEpilogue ep{};
     ep.bias = fe.bias;
     ep.scale = fe.scale;
     ep.parts = fe.parts;
     ep.gn_groups = fe.gn_groups;
+    if (store) return launch_mode<kStatsStore>(d, p, x, w, y, ep, st);
     return launch_mode<kStats>(d, p, x, w, y, ep, st);
 }
 
@@ -516,7 +599,7 @@ hipError_t launch_igemm_res_normalize(const gconv_desc *d, const float *x, const
     ep.gamma = gamma;
     ep.beta = beta;
     ep.gn_groups = fe.gn_groups;
-    return launch_mode<kNormalize>(d, make_params(d, x), x, w, y, ep, st);
+    return launch_mode<kNormalize>(d, make_params(d, fe.gn_groups), x, w, y, ep, st);
 }
 
 }  // namespace gconv
