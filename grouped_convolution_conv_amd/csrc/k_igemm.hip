@@ -47,6 +47,7 @@ struct IgParams {
     int n_tw;          // column tiles per image
     int n_tiles;       // spatial tiles per image
     int pitch;         // LDS row pitch of the input band (floats)
+    int vec;           // W, pad multiples of 4 and x 16-byte aligned: 16-byte band loads
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -280,6 +281,206 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant for the plain convolution (no fused epilogue).  Same
+// MFMA mapping and tile as igemm_kernel; what changes is the staging of the
+// channel chunks, which otherwise leaves the matrix pipe idle for about a
+// quarter of the time:
+//  - two LDS buffers per operand (input band, weights), statically
+//    allocated so the compiler sees that reads of one never alias writes
+//    to the other;
+//  - chunk c+2 is loaded into registers while chunk c is multiplied, and
+//    written to the free buffer right after chunk c's MFMAs; one LDS-only
+//    barrier per chunk separates the writes from the next chunk's reads;
+//  - every global load goes through a buffer resource with out-of-range
+//    offsets for padding and missing channels (the hardware returns zero),
+//    so the loads carry no branches and the compiler waits for exactly the
+//    loads each commit needs.
+
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access, gfx9 family
+constexpr int kOutOfRange = 0x7fffffff;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
+}
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for the wave's outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int R, int S, int MB, int CC, bool VEC>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_pipe_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ y, IgParams p) {
+    constexpr int RS = R * S;
+    constexpr int KW = 32 * MB;
+    constexpr int TIH = kTH + R - 1;
+    constexpr int TIW = kTW + S - 1;
+    constexpr int PITCH = (TIW + 3) & ~3;    // band row pitch: whole 16-byte pieces
+    constexpr int P4 = PITCH / 4;
+    constexpr int XE4 = CC * TIH * P4;       // 16-byte pieces of a chunk's band
+    constexpr int NSX = (XE4 + kBlock - 1) / kBlock;
+    constexpr int WE = KW * CC * RS;         // weight elements of a chunk
+    constexpr int NSW = (WE + kBlock - 1) / kBlock;
+    constexpr int WP = (CC * RS) | 1;        // weight row pitch (odd: conflict-free reads)
+    constexpr int NB = kNBR * kNBC;
+    constexpr int HALF = CC / 2;
+
+    __shared__ float4 xA4[XE4];
+    __shared__ float4 xB4[XE4];
+    __shared__ float wA[KW * WP];
+    __shared__ float wB[KW * WP];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, j = lane & 31;
+    const int n = blockIdx.z;
+    const int th = blockIdx.x / p.n_tw, tw = blockIdx.x - th * p.n_tw;
+    const int oh0 = th * kTH, ow0 = tw * kTW;
+    const int g = blockIdx.y / p.n_kb, kb = blockIdx.y - g * p.n_kb;
+    const int kg0 = kb * KW;                 // first output channel within the group
+    const int k0 = g * p.cout + kg0;         // first global output channel
+    const int kvalid = min(KW, p.cout - kg0);
+    const int HW = p.H * p.W;
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + ((size_t)n * p.C + (size_t)g * p.cin) * HW,
+                                                p.cin * HW * (int)sizeof(float));
+    const __amdgpu_buffer_rsrc_t ws = make_rsrc(w + (size_t)k0 * p.cin * RS, kvalid * p.cin * RS * (int)sizeof(float));
+    const int nchunks = (p.cin + CC - 1) / CC;
+
+    float4 px[NSX];
+    float pw[NSW];
+    auto load = [&](int c) __attribute__((always_inline)) {
+        const int c0 = c * CC;
+        int tid_o = tid;  // opaque: keep the per-slot index math out of the MFMA loop
+        asm volatile("" : "+v"(tid_o));
+#pragma unroll
+        for (int i = 0; i < NSX; ++i) {
+            const int f = i * kBlock + tid_o;
+            const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
+            const int lr = rem / P4, c4 = rem - lr * P4;
+            const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + 4 * c4;
+            const bool row_ok = f < XE4 && c0 + cl < p.cin && ih >= 0 && ih < p.H;
+            const int rowb = ((c0 + cl) * HW + ih * p.W) * (int)sizeof(float);
+            if constexpr (VEC) {
+                const int off = (row_ok && iw >= 0 && iw < p.W) ? rowb + iw * (int)sizeof(float) : kOutOfRange;
+                px[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
+            } else {
+                float e4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int off = (row_ok && iw + e >= 0 && iw + e < p.W) ? rowb + (iw + e) * (int)sizeof(float)
+                                                                            : kOutOfRange;
+                    e4[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs, off, 0, 0));
+                }
+                px[i] = make_float4(e4[0], e4[1], e4[2], e4[3]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NSW; ++i) {
+            // element f = k*(CC*RS) + cl*RS + t of the chunk's weights
+            const int f = i * kBlock + tid_o;
+            const int k = f / (CC * RS), rem = f - k * (CC * RS);
+            const int cl = rem / RS;
+            const bool ok = f < WE && k < kvalid && c0 + cl < p.cin;
+            const int off = ok ? (k * p.cin * RS + c0 * RS + rem) * (int)sizeof(float) : kOutOfRange;
+            pw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off, 0, 0));
+        }
+    };
+    auto commit = [&](float4 *xb4, float *wb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NSX; ++i) {
+            const int f = i * kBlock + tid;
+            if (f < XE4) xb4[f] = px[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NSW; ++i) {
+            const int f = i * kBlock + tid;
+            const int k = f / (CC * RS), rem = f - k * (CC * RS);
+            if (f < WE) wb[k * WP + rem] = pw[i];
+        }
+    };
+
+    floatx16 acc[MB][NB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[m][b][v] = 0.0f;
+    auto mfma_chunk = [&](const float4 *xb4, const float *wb) __attribute__((always_inline)) {
+        const float *xin = reinterpret_cast<const float *>(xb4);
+#pragma unroll
+        for (int ci = 0; ci < HALF; ++ci) {
+            const int cl = h * HALF + ci;
+            const float *xq = xin + (cl * TIH + wave * kNBR) * PITCH + j;
+            const float *wq = wb + j * WP + cl * RS;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    float a[MB], b[NB];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) a[m] = wq[m * 32 * WP + r * S + s];
+#pragma unroll
+                    for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                        for (int bc = 0; bc < kNBC; ++bc) b[br * kNBC + bc] = xq[(br + r) * PITCH + bc * 32 + s];
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], b[nb], acc[m][nb], 0, 0, 0);
+                }
+        }
+    };
+
+    // chunk c: barrier -> MFMAs from buffer c%2 -> commit chunk c+1 (loaded
+    // one chunk earlier) into the other buffer -> start loading chunk c+2.
+    // Past the last chunk the index is clamped and the work is redundant.
+    load(0);
+    commit(xA4, wA);
+    load(min(1, nchunks - 1));
+    for (int c = 0; c < nchunks; c += 2) {
+        lds_barrier();
+        mfma_chunk(xA4, wA);
+        commit(xB4, wB);
+        load(min(c + 2, nchunks - 1));
+        if (c + 1 >= nchunks) break;
+        lds_barrier();
+        mfma_chunk(xB4, wB);
+        commit(xA4, wA);
+        load(min(c + 3, nchunks - 1));
+    }
+
+    // ---- epilogue
+    const size_t plane = (size_t)p.Ho * p.Wo;
+    float *yb = y + ((size_t)n * p.K + k0) * plane;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int br = 0; br < kNBR; ++br) {
+            const int oh = oh0 + wave * kNBR + br;
+#pragma unroll
+            for (int bc = 0; bc < kNBC; ++bc) {
+                const int ow = ow0 + bc * 32 + j;
+                if (oh >= p.Ho || ow >= p.Wo) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (k < kvalid) {
+                        float o = acc[m][br * kNBC + bc][v];
+                        if (bias) o += bias[k0 + k];
+                        yb[(size_t)k * plane + (size_t)oh * p.Wo + ow] = o;
+                    }
+                }
+            }
+        }
+}
+
 // Input-channel chunk for a kernel size: the weights of one chunk stay
 // within about 24 KB for a 64-channel block.
 template <int R, int S>
@@ -295,17 +496,28 @@ template <int R, int S, int MB, bool FUSED>
 hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w, const float *bias,
                     float *y, const FusedEpilogue &ep, hipStream_t st) {
     constexpr int CC = chunk_for<R, S>();
-    const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
-    clear_stale_launch_error();
-    hipLaunchKernelGGL((igemm_kernel<R, S, MB, CC, FUSED>), grid, dim3(kBlock), lds, st, x, w, bias,
-                       y, p, ep);
-    return hipGetLastError();
+    if constexpr (!FUSED) {
+        clear_stale_launch_error();
+        if (p.vec)
+            hipLaunchKernelGGL((igemm_pipe_kernel<R, S, MB, CC, true>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+        else
+            hipLaunchKernelGGL((igemm_pipe_kernel<R, S, MB, CC, false>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+        return hipGetLastError();
+    } else {
+        const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
+        clear_stale_launch_error();
+        hipLaunchKernelGGL((igemm_kernel<R, S, MB, CC, FUSED>), grid, dim3(kBlock), lds, st, x, w, bias,
+                           y, p, ep);
+        return hipGetLastError();
+    }
 }
 
 template <int R, int S, bool FUSED>
 hipError_t launch_mb(int MB, const IgParams &p, dim3 grid, const float *x, const float *w,
                      const float *bias, float *y, const FusedEpilogue &ep, hipStream_t st) {
-    if (MB == 2) return launch_t<R, S, 2, FUSED>(p, grid, x, w, bias, y, ep, st);
+    if constexpr (FUSED) {
+        if (MB == 2) return launch_t<R, S, 2, FUSED>(p, grid, x, w, bias, y, ep, st);
+    }
     return launch_t<R, S, 1, FUSED>(p, grid, x, w, bias, y, ep, st);
 }
 
@@ -339,14 +551,17 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.n_tw = (d->Wo + kTW - 1) / kTW;
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.pitch = kTW + d->S - 1;
+    p.vec = 0;
     return p;
 }
 
 }  // namespace
 
 bool igemm_supported(const gconv_desc *d) {
+    // buffer offsets are signed 32-bit: one group's input channels of one
+    // image must stay below 2 GB
     return d->stride == 1 && d->dil == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
-           d->cout >= 8;
+           d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
 
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
@@ -362,8 +577,13 @@ int igemm_fused_parts_per_group(const gconv_desc *d, int) {
 hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, const float *bias,
                         float *y, hipStream_t st) {
     if (!igemm_supported(d)) return hipErrorInvalidValue;
-    const int MB = pick_mb(d);
-    const IgParams p = make_params(d, MB);
+    // the pipelined kernel holds a second chunk in registers: one 32-channel
+    // block per workgroup keeps it within the register budget of two waves
+    // per SIMD (two blocks would spill), at the cost of reading each input
+    // band once per block
+    const int MB = 1;
+    IgParams p = make_params(d, MB);
+    p.vec = (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_kb;
     if (gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
