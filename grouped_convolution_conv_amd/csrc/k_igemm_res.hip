@@ -32,6 +32,8 @@
 //  kStatsStore  kStats, and v is stored to y
 //  kNormalize   v as above, then out = (v - mean) * rstd * gamma + beta with
 //               the group statistics already merged, stored to y
+#include <atomic>
+
 #include "dev_common.h"
 #include "internal.h"
 
@@ -460,6 +462,7 @@ __global__ __launch_bounds__(kBlock) void gn_merge_kernel(const Partial *__restr
 // ---- host side
 
 constexpr int kMaxResLds = 64 * 1024;  // keep at least two workgroups per CU
+constexpr int kMaxDevices = 64;
 
 template <int R, int S, int MB, int CP>
 constexpr int res_lds_bytes() {
@@ -498,13 +501,22 @@ hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y
                     hipStream_t st) {
     static_assert(res_lds_bytes<R, S, MB, CP>() <= kMaxResLds, "LDS budget");
     auto kern = igemm_res_kernel<R, S, MB, CP, MODE, VEC>;
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipErrorInvalidDevice;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0) != hipSuccess || per_cu < 1)
-        per_cu = 1;
-    const long long want = (long long)cus * per_cu;
+    // resident workgroups per device for this kernel: queried once per
+    // device and kept (the query costs host time on every launch otherwise)
+    static std::atomic<int> capacity[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return hipErrorInvalidDevice;
+    int cap = dev < kMaxDevices ? capacity[dev].load(std::memory_order_relaxed) : 0;
+    if (cap == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kBlock, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        cap = cus * per_cu;
+        if (dev < kMaxDevices) capacity[dev].store(cap, std::memory_order_relaxed);
+    }
+    const long long want = cap;
     const int grid = (int)(p.units < want ? p.units : want);
     clear_stale_launch_error();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, st, x, w, y, p, ep);
