@@ -282,22 +282,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined variant for the plain convolution (no fused epilogue).  Same
-// MFMA mapping and tile as igemm_kernel; what changes is the staging of the
-// channel chunks, which otherwise leaves the matrix pipe idle for about a
+// Pipelined kernel for the plain convolution (no fused epilogue).  Same MFMA
+// mapping and tile as igemm_kernel; what changes is the staging of the
+// channel chunks, which there leaves the matrix pipe idle for about a
 // quarter of the time:
 //  - two LDS buffers per operand (input band, weights), statically
-//    allocated so the compiler sees that reads of one never alias writes
-//    to the other;
-//  - chunk c+2 is loaded into registers while chunk c is multiplied, and
-//    written to the free buffer right after chunk c's MFMAs; one LDS-only
-//    barrier per chunk separates the writes from the next chunk's reads;
-//  - every global load goes through a buffer resource with out-of-range
-//    offsets for padding and missing channels (the hardware returns zero),
-//    so the loads carry no branches and the compiler waits for exactly the
-//    loads each commit needs.
+//    allocated so the compiler sees that reads of one never alias the DMA
+//    into the other;
+//  - chunk c+1 goes from global memory straight into the free buffer (buffer
+//    loads with the LDS bit: lane l of a wave writes its 4 or 16 bytes at the
+//    instruction's LDS base + l*size, and an out-of-range offset, used for
+//    padding and missing channels, writes zero) while chunk c is multiplied;
+//    one wait and one LDS-only barrier per chunk;
+//  - no registers hold the next chunk and no VALU work copies it into LDS;
+//  - weights sit in LDS as [tap][output channel], so the 32 lanes reading 32
+//    output channels of one tap read 32 consecutive words.
 
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access, gfx9 family
+// output-channel blocks per workgroup of the plain kernel: with two, the
+// MFMA loop's operands spill at two waves per SIMD (measured slower)
+constexpr int kPlainMB = 1;
 constexpr int kOutOfRange = 0x7fffffff;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
@@ -312,8 +316,10 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 template <int R, int S, int MB, int CC, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_pipe_kernel(
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
     constexpr int RS = R * S;
@@ -323,17 +329,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int PITCH = (TIW + 3) & ~3;    // band row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CC * TIH * P4;       // 16-byte pieces of a chunk's band
-    constexpr int NSX = (XE4 + kBlock - 1) / kBlock;
-    constexpr int WE = KW * CC * RS;         // weight elements of a chunk
-    constexpr int NSW = (WE + kBlock - 1) / kBlock;
-    constexpr int WP = (CC * RS) | 1;        // weight row pitch (odd: conflict-free reads)
+    constexpr int XI = (XE4 + 63) / 64;      // band DMA instructions (16-byte pieces)
+    constexpr int XE = XE4 * 4;
+    constexpr int XI1 = (XE + 63) / 64;      // band DMA instructions (4-byte elements)
+    constexpr int WE = CC * RS * KW;         // weight words of a chunk, [q][KW]
+    constexpr int WI = (WE + 63) / 64;       // weight DMA instructions
     constexpr int NB = kNBR * kNBC;
     constexpr int HALF = CC / 2;
+    constexpr int NWAVE = kBlock / 64;
 
-    __shared__ float4 xA4[XE4];
-    __shared__ float4 xB4[XE4];
-    __shared__ float wA[KW * WP];
-    __shared__ float wB[KW * WP];
+    // buffers padded to whole DMA instructions (idle lanes write zeros there)
+    __shared__ float4 xA4[XI * 64];
+    __shared__ float4 xB4[XI * 64];
+    __shared__ float wA[WI * 64];
+    __shared__ float wB[WI * 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -342,8 +351,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int th = blockIdx.x / p.n_tw, tw = blockIdx.x - th * p.n_tw;
     const int oh0 = th * kTH, ow0 = tw * kTW;
     const int g = blockIdx.y / p.n_kb, kb = blockIdx.y - g * p.n_kb;
-    const int kg0 = kb * KW;                 // first output channel within the group
-    const int k0 = g * p.cout + kg0;         // first global output channel
+    const int kg0 = kb * KW;
+    const int k0 = g * p.cout + kg0;
     const int kvalid = min(KW, p.cout - kg0);
     const int HW = p.H * p.W;
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + ((size_t)n * p.C + (size_t)g * p.cin) * HW,
@@ -351,56 +360,38 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const __amdgpu_buffer_rsrc_t ws = make_rsrc(w + (size_t)k0 * p.cin * RS, kvalid * p.cin * RS * (int)sizeof(float));
     const int nchunks = (p.cin + CC - 1) / CC;
 
-    float4 px[NSX];
-    float pw[NSW];
-    auto load = [&](int c) __attribute__((always_inline)) {
+    // DMA of chunk c into (xb4, wb): wave w issues instructions w, w+4, ...
+    auto dma = [&](int c, float4 *xb4, float *wb) __attribute__((always_inline)) {
         const int c0 = c * CC;
-        int tid_o = tid;  // opaque: keep the per-slot index math out of the MFMA loop
-        asm volatile("" : "+v"(tid_o));
-#pragma unroll
-        for (int i = 0; i < NSX; ++i) {
-            const int f = i * kBlock + tid_o;
-            const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
-            const int lr = rem / P4, c4 = rem - lr * P4;
-            const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + 4 * c4;
-            const bool row_ok = f < XE4 && c0 + cl < p.cin && ih >= 0 && ih < p.H;
-            const int rowb = ((c0 + cl) * HW + ih * p.W) * (int)sizeof(float);
-            if constexpr (VEC) {
-                const int off = (row_ok && iw >= 0 && iw < p.W) ? rowb + iw * (int)sizeof(float) : kOutOfRange;
-                px[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
-            } else {
-                float e4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int off = (row_ok && iw + e >= 0 && iw + e < p.W) ? rowb + (iw + e) * (int)sizeof(float)
-                                                                            : kOutOfRange;
-                    e4[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs, off, 0, 0));
-                }
-                px[i] = make_float4(e4[0], e4[1], e4[2], e4[3]);
+        if constexpr (VEC) {
+            for (int ii = wave; ii < XI; ii += NWAVE) {
+                const int f = ii * 64 + lane;
+                const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
+                const int lr = rem / P4, c4 = rem - lr * P4;
+                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + 4 * c4;
+                const bool ok = f < XE4 && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+                const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb4 + ii * 64), 16, off, 0, 0, 0);
+            }
+        } else {
+            float *xb = reinterpret_cast<float *>(xb4);
+            for (int ii = wave; ii < XI1; ii += NWAVE) {
+                const int e = ii * 64 + lane;
+                const int row = e / PITCH, col = e - row * PITCH;  // row = cl * TIH + lr
+                const int cl = row / TIH, lr = row - cl * TIH;
+                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
+                const bool ok = e < XE && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+                const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64), 4, off, 0, 0, 0);
             }
         }
-#pragma unroll
-        for (int i = 0; i < NSW; ++i) {
-            // element f = k*(CC*RS) + cl*RS + t of the chunk's weights
-            const int f = i * kBlock + tid_o;
-            const int k = f / (CC * RS), rem = f - k * (CC * RS);
-            const int cl = rem / RS;
-            const bool ok = f < WE && k < kvalid && c0 + cl < p.cin;
-            const int off = ok ? (k * p.cin * RS + c0 * RS + rem) * (int)sizeof(float) : kOutOfRange;
-            pw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ws, off, 0, 0));
-        }
-    };
-    auto commit = [&](float4 *xb4, float *wb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NSX; ++i) {
-            const int f = i * kBlock + tid;
-            if (f < XE4) xb4[f] = px[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NSW; ++i) {
-            const int f = i * kBlock + tid;
-            const int k = f / (CC * RS), rem = f - k * (CC * RS);
-            if (f < WE) wb[k * WP + rem] = pw[i];
+        for (int ii = wave; ii < WI; ii += NWAVE) {
+            const int e = ii * 64 + lane;            // e = q * KW + k
+            const int q = e / KW, k = e - q * KW;    // q = cl * RS + t
+            const int cl = q / RS;
+            const bool ok = e < WE && k < kvalid && c0 + cl < p.cin;
+            const int off = ok ? (k * p.cin * RS + c0 * RS + q) * (int)sizeof(float) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, off, 0, 0, 0);
         }
     };
 
@@ -417,14 +408,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
             const float *xq = xin + (cl * TIH + wave * kNBR) * PITCH + j;
-            const float *wq = wb + j * WP + cl * RS;
-#pragma unroll
+            const float *wq = wb + cl * RS * KW + j;
+            // kernel rows one at a time: unrolling them all lets the compiler
+            // hoist every row's LDS reads and spill with two output blocks
+#pragma unroll 1
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
                     float a[MB], b[NB];
 #pragma unroll
-                    for (int m = 0; m < MB; ++m) a[m] = wq[m * 32 * WP + r * S + s];
+                    for (int m = 0; m < MB; ++m) a[m] = wq[(r * S + s) * KW + m * 32];
 #pragma unroll
                     for (int br = 0; br < kNBR; ++br)
 #pragma unroll
@@ -438,22 +431,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
 
-    // chunk c: barrier -> MFMAs from buffer c%2 -> commit chunk c+1 (loaded
-    // one chunk earlier) into the other buffer -> start loading chunk c+2.
-    // Past the last chunk the index is clamped and the work is redundant.
-    load(0);
-    commit(xA4, wA);
-    load(min(1, nchunks - 1));
+    // chunk c: wait for this wave's DMA of chunk c, barrier (every wave's
+    // DMA has landed and every wave is done with chunk c-1's buffer) ->
+    // DMA chunk c+1 into that buffer -> MFMAs of chunk c.
+    dma(0, xA4, wA);
     for (int c = 0; c < nchunks; c += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
+        if (c + 1 < nchunks) dma(c + 1, xB4, wB);
         mfma_chunk(xA4, wA);
-        commit(xB4, wB);
-        load(min(c + 2, nchunks - 1));
         if (c + 1 >= nchunks) break;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
+        if (c + 2 < nchunks) dma(c + 2, xA4, wA);
         mfma_chunk(xB4, wB);
-        commit(xA4, wA);
-        load(min(c + 3, nchunks - 1));
     }
 
     // ---- epilogue
@@ -499,9 +490,9 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
     if constexpr (!FUSED) {
         clear_stale_launch_error();
         if (p.vec)
-            hipLaunchKernelGGL((igemm_pipe_kernel<R, S, MB, CC, true>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
         else
-            hipLaunchKernelGGL((igemm_pipe_kernel<R, S, MB, CC, false>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
         return hipGetLastError();
     } else {
         const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
@@ -515,7 +506,7 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
 template <int R, int S, bool FUSED>
 hipError_t launch_mb(int MB, const IgParams &p, dim3 grid, const float *x, const float *w,
                      const float *bias, float *y, const FusedEpilogue &ep, hipStream_t st) {
-    if constexpr (FUSED) {
+    if constexpr (FUSED || kPlainMB == 2) {
         if (MB == 2) return launch_t<R, S, 2, FUSED>(p, grid, x, w, bias, y, ep, st);
     }
     return launch_t<R, S, 1, FUSED>(p, grid, x, w, bias, y, ep, st);
@@ -577,11 +568,9 @@ int igemm_fused_parts_per_group(const gconv_desc *d, int) {
 hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, const float *bias,
                         float *y, hipStream_t st) {
     if (!igemm_supported(d)) return hipErrorInvalidValue;
-    // the pipelined kernel holds a second chunk in registers: one 32-channel
-    // block per workgroup keeps it within the register budget of two waves
-    // per SIMD (two blocks would spill), at the cost of reading each input
-    // band once per block
-    const int MB = 1;
+    // one 32-channel block per workgroup (kPlainMB): each input band is
+    // read once per block, in exchange for no register spills
+    const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
     p.vec = (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_kb;
