@@ -54,6 +54,12 @@ def _load():
         lib.oracle_conv2d_points.restype = i
         lib.oracle_fused_gn.argtypes = [i] * 11 + [p] * 6 + [i, d, p, p, i]
         lib.oracle_fused_gn.restype = i
+        lib.oracle_conv2d_2d.argtypes = [i] * 14 + [p, p, p, p, p, i]
+        lib.oracle_conv2d_2d.restype = i
+        lib.oracle_conv2d_points_2d.argtypes = [i] * 14 + [p, p, p, ctypes.c_int64, p, p, p, i]
+        lib.oracle_conv2d_points_2d.restype = i
+        lib.oracle_fused_gn_2d.argtypes = [i] * 14 + [p] * 6 + [i, d, p, p, i]
+        lib.oracle_fused_gn_2d.restype = i
         _lib = lib
     return _lib
 
@@ -78,6 +84,20 @@ def out_dim(n: int, k: int, stride: int, pad: int, dil: int) -> int:
     return _load().oracle_out_dim(n, k, stride, pad, dil)
 
 
+def _pair(v):
+    """An int for both axes or an (h, w) pair."""
+    if isinstance(v, (tuple, list)):
+        if len(v) != 2:
+            raise ValueError("expected an int or an (h, w) pair, got %r" % (v,))
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+def _axes(stride, pad, dil):
+    (sh, sw), (ph, pw), (dh, dw) = _pair(stride), _pair(pad), _pair(dil)
+    return sh, sw, ph, pw, dh, dw
+
+
 def _geom(x, w, groups):
     N, C, H, W = x.shape
     K, cin, R, S = w.shape
@@ -87,15 +107,17 @@ def _geom(x, w, groups):
 
 
 def conv2d(x, w, bias=None, stride=1, pad=0, dil=1, groups=1, threads=None, want_bound=True):
-    """Returns (y, A): y the float64 conv output, A = sum |x*w| per output."""
+    """Returns (y, A): y the float64 conv output, A = sum |x*w| per output.
+    stride, pad and dil are ints or (h, w) pairs."""
     x, w, bias = _f32(x), _f32(w), _f32(bias)
     N, C, H, W, K, R, S = _geom(x, w, groups)
-    Ho, Wo = out_dim(H, R, stride, pad, dil), out_dim(W, S, stride, pad, dil)
+    sh, sw, ph, pw, dh, dw = _axes(stride, pad, dil)
+    Ho, Wo = out_dim(H, R, sh, ph, dh), out_dim(W, S, sw, pw, dw)
     y = np.empty((N, K, Ho, Wo), dtype=np.float64)
     A = np.empty_like(y) if want_bound else None
-    rc = _load().oracle_conv2d(N, C, H, W, K, R, S, stride, pad, dil, groups,
-                               _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(A),
-                               threads or default_threads())
+    rc = _load().oracle_conv2d_2d(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups,
+                                  _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _ptr(A),
+                                  threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_conv2d rejected the geometry (rc=%d)" % rc)
     return y, A
@@ -105,12 +127,13 @@ def conv2d_points(x, w, idx, bias=None, stride=1, pad=0, dil=1, groups=1, thread
     """Conv output and bound at flat NCHW output indices `idx` (int64)."""
     x, w, bias = _f32(x), _f32(w), _f32(bias)
     N, C, H, W, K, R, S = _geom(x, w, groups)
+    sh, sw, ph, pw, dh, dw = _axes(stride, pad, dil)
     idx = np.ascontiguousarray(idx, dtype=np.int64)
     y = np.empty(idx.shape, dtype=np.float64)
     A = np.empty_like(y)
-    rc = _load().oracle_conv2d_points(N, C, H, W, K, R, S, stride, pad, dil, groups,
-                                      _ptr(x), _ptr(w), _ptr(bias), idx.size, _ptr(idx),
-                                      _ptr(y), _ptr(A), threads or default_threads())
+    rc = _load().oracle_conv2d_points_2d(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups,
+                                         _ptr(x), _ptr(w), _ptr(bias), idx.size, _ptr(idx),
+                                         _ptr(y), _ptr(A), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_conv2d_points rejected the input (rc=%d)" % rc)
     return y, A
@@ -122,13 +145,14 @@ def fused_gn(x, w, bias, scale, gamma, beta, gn_groups, eps=1e-5, stride=1, pad=
     x, w = _f32(x), _f32(w)
     bias, scale, gamma, beta = _f32(bias), _f32(scale), _f32(gamma), _f32(beta)
     N, C, H, W, K, R, S = _geom(x, w, groups)
-    Ho, Wo = out_dim(H, R, stride, pad, dil), out_dim(W, S, stride, pad, dil)
+    sh, sw, ph, pw, dh, dw = _axes(stride, pad, dil)
+    Ho, Wo = out_dim(H, R, sh, ph, dh), out_dim(W, S, sw, pw, dw)
     out = np.empty((N, K, Ho, Wo), dtype=np.float64)
     v = np.empty_like(out) if want_v else None
-    rc = _load().oracle_fused_gn(N, C, H, W, K, R, S, stride, pad, dil, groups,
-                                 _ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(gamma),
-                                 _ptr(beta), gn_groups, float(eps), _ptr(v), _ptr(out),
-                                 threads or default_threads())
+    rc = _load().oracle_fused_gn_2d(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups,
+                                    _ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(gamma),
+                                    _ptr(beta), gn_groups, float(eps), _ptr(v), _ptr(out),
+                                    threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_fused_gn rejected the input (rc=%d)" % rc)
     return (out, v) if want_v else out

@@ -53,20 +53,20 @@ int oracle_out_dim(int in, int k, int stride, int pad, int dil)
 }
 
 static int geometry_ok(int N, int C, int H, int W, int K, int R, int S,
-                       int stride, int pad, int dil, int groups)
+                       int sh, int sw, int ph, int pw, int dh, int dw, int groups)
 {
     if (N < 1 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1) return 0;
-    if (stride < 1 || dil < 1 || pad < 0 || groups < 1) return 0;
+    if (sh < 1 || sw < 1 || dh < 1 || dw < 1 || ph < 0 || pw < 0 || groups < 1) return 0;
     if (C % groups != 0 || K % groups != 0) return 0;
-    if (oracle_out_dim(H, R, stride, pad, dil) < 1) return 0;
-    if (oracle_out_dim(W, S, stride, pad, dil) < 1) return 0;
+    if (oracle_out_dim(H, R, sh, ph, dh) < 1) return 0;
+    if (oracle_out_dim(W, S, sw, pw, dw) < 1) return 0;
     return 1;
 }
 
 /* One output element of the convolution, y[n,k,oh,ow], and its bound
  * A = sum |x * w| over the same receptive field (plus |bias[k]|). */
 static void conv_one(int C, int H, int W, int K, int R, int S,
-                     int stride, int pad, int dil, int groups,
+                     int sh, int sw, int ph, int pw, int dh, int dw, int groups,
                      const float *x, const float *w, const float *bias,
                      int n, int k, int oh, int ow, double *yv, double *av)
 {
@@ -77,10 +77,10 @@ static void conv_one(int C, int H, int W, int K, int R, int S,
     for (int c = 0; c < cin; ++c) {
         const int ic = g * cin + c;
         for (int r = 0; r < R; ++r) {
-            const int ih = oh * stride - pad + r * dil;
+            const int ih = oh * sh - ph + r * dh;
             if (ih < 0 || ih >= H) continue;            /* zero padding */
             for (int s = 0; s < S; ++s) {
-                const int iw = ow * stride - pad + s * dil;
+                const int iw = ow * sw - pw + s * dw;
                 if (iw < 0 || iw >= W) continue;        /* zero padding */
                 const double xv =
                     (double)x[(((int64_t)n * C + ic) * H + ih) * W + iw];
@@ -100,16 +100,17 @@ static void conv_one(int C, int H, int W, int K, int R, int S,
 }
 
 /* Full convolution: y[N][K][Ho][Wo] (double), optional bound absb of the
- * same shape.  bias may be NULL. */
-int oracle_conv2d(int N, int C, int H, int W, int K, int R, int S,
-                  int stride, int pad, int dil, int groups,
-                  const float *x, const float *w, const float *bias,
-                  double *y, double *absb, int nthreads)
+ * same shape.  bias may be NULL.  Stride, padding and dilation are given
+ * per axis (h: along H and R, w: along W and S). */
+int oracle_conv2d_2d(int N, int C, int H, int W, int K, int R, int S,
+                     int sh, int sw, int ph, int pw, int dh, int dw, int groups,
+                     const float *x, const float *w, const float *bias,
+                     double *y, double *absb, int nthreads)
 {
-    if (!geometry_ok(N, C, H, W, K, R, S, stride, pad, dil, groups)) return ORACLE_BAD;
+    if (!geometry_ok(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups)) return ORACLE_BAD;
     if (!x || !w || !y) return ORACLE_BAD;
-    const int Ho = oracle_out_dim(H, R, stride, pad, dil);
-    const int Wo = oracle_out_dim(W, S, stride, pad, dil);
+    const int Ho = oracle_out_dim(H, R, sh, ph, dh);
+    const int Wo = oracle_out_dim(W, S, sw, pw, dw);
     if (nthreads < 1) nthreads = 1;
     const int64_t planes = (int64_t)N * K;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
@@ -118,25 +119,35 @@ int oracle_conv2d(int N, int C, int H, int W, int K, int R, int S,
         for (int oh = 0; oh < Ho; ++oh)
             for (int ow = 0; ow < Wo; ++ow) {
                 const int64_t o = ((p * Ho) + oh) * Wo + ow;
-                conv_one(C, H, W, K, R, S, stride, pad, dil, groups, x, w, bias,
+                conv_one(C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups, x, w, bias,
                          n, k, oh, ow, &y[o], absb ? &absb[o] : NULL);
             }
     }
     return ORACLE_OK;
 }
 
+/* The same with one stride, padding and dilation for both axes. */
+int oracle_conv2d(int N, int C, int H, int W, int K, int R, int S,
+                  int stride, int pad, int dil, int groups,
+                  const float *x, const float *w, const float *bias,
+                  double *y, double *absb, int nthreads)
+{
+    return oracle_conv2d_2d(N, C, H, W, K, R, S, stride, stride, pad, pad, dil, dil, groups,
+                            x, w, bias, y, absb, nthreads);
+}
+
 /* The same definition evaluated only at the given flat NCHW output indices
  * (for sampled checks of outputs too large to compute whole). */
-int oracle_conv2d_points(int N, int C, int H, int W, int K, int R, int S,
-                         int stride, int pad, int dil, int groups,
-                         const float *x, const float *w, const float *bias,
-                         int64_t npts, const int64_t *idx,
-                         double *y, double *absb, int nthreads)
+int oracle_conv2d_points_2d(int N, int C, int H, int W, int K, int R, int S,
+                            int sh, int sw, int ph, int pw, int dh, int dw, int groups,
+                            const float *x, const float *w, const float *bias,
+                            int64_t npts, const int64_t *idx,
+                            double *y, double *absb, int nthreads)
 {
-    if (!geometry_ok(N, C, H, W, K, R, S, stride, pad, dil, groups)) return ORACLE_BAD;
+    if (!geometry_ok(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups)) return ORACLE_BAD;
     if (!x || !w || !y || (npts > 0 && !idx)) return ORACLE_BAD;
-    const int Ho = oracle_out_dim(H, R, stride, pad, dil);
-    const int Wo = oracle_out_dim(W, S, stride, pad, dil);
+    const int Ho = oracle_out_dim(H, R, sh, ph, dh);
+    const int Wo = oracle_out_dim(W, S, sw, pw, dw);
     const int64_t total = (int64_t)N * K * Ho * Wo;
     for (int64_t i = 0; i < npts; ++i)
         if (idx[i] < 0 || idx[i] >= total) return ORACLE_BAD;
@@ -148,10 +159,20 @@ int oracle_conv2d_points(int N, int C, int H, int W, int K, int R, int S,
         const int oh = (int)(t % Ho); t /= Ho;
         const int k = (int)(t % K);
         const int n = (int)(t / K);
-        conv_one(C, H, W, K, R, S, stride, pad, dil, groups, x, w, bias,
+        conv_one(C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups, x, w, bias,
                  n, k, oh, ow, &y[i], absb ? &absb[i] : NULL);
     }
     return ORACLE_OK;
+}
+
+int oracle_conv2d_points(int N, int C, int H, int W, int K, int R, int S,
+                         int stride, int pad, int dil, int groups,
+                         const float *x, const float *w, const float *bias,
+                         int64_t npts, const int64_t *idx,
+                         double *y, double *absb, int nthreads)
+{
+    return oracle_conv2d_points_2d(N, C, H, W, K, R, S, stride, stride, pad, pad, dil, dil, groups,
+                                   x, w, bias, npts, idx, y, absb, nthreads);
 }
 
 /* Fused chain of the l2_p21 trace, per sample n:
@@ -162,18 +183,18 @@ int oracle_conv2d_points(int N, int C, int H, int W, int K, int R, int S,
  *       var = mean((v - mu)^2)              (second pass, population)
  *       out = (v - mu) / sqrt(var + eps) * gamma[k] + beta[k]
  * v_out (may be NULL) receives v; out receives the normalized result. */
-int oracle_fused_gn(int N, int C, int H, int W, int K, int R, int S,
-                    int stride, int pad, int dil, int groups,
-                    const float *x, const float *w, const float *bias,
-                    const float *scale, const float *gamma, const float *beta,
-                    int gn_groups, double eps,
-                    double *v_out, double *out, int nthreads)
+int oracle_fused_gn_2d(int N, int C, int H, int W, int K, int R, int S,
+                       int sh, int sw, int ph, int pw, int dh, int dw, int groups,
+                       const float *x, const float *w, const float *bias,
+                       const float *scale, const float *gamma, const float *beta,
+                       int gn_groups, double eps,
+                       double *v_out, double *out, int nthreads)
 {
-    if (!geometry_ok(N, C, H, W, K, R, S, stride, pad, dil, groups)) return ORACLE_BAD;
+    if (!geometry_ok(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups)) return ORACLE_BAD;
     if (!x || !w || !bias || !scale || !out) return ORACLE_BAD;
     if (gn_groups < 1 || K % gn_groups != 0 || !(eps > 0.0)) return ORACLE_BAD;
-    const int Ho = oracle_out_dim(H, R, stride, pad, dil);
-    const int Wo = oracle_out_dim(W, S, stride, pad, dil);
+    const int Ho = oracle_out_dim(H, R, sh, ph, dh);
+    const int Wo = oracle_out_dim(W, S, sw, pw, dw);
     const int64_t plane = (int64_t)Ho * Wo;
     const int cpg = K / gn_groups;
     if (nthreads < 1) nthreads = 1;
@@ -188,7 +209,7 @@ int oracle_fused_gn(int N, int C, int H, int W, int K, int R, int S,
             for (int oh = 0; oh < Ho; ++oh)
                 for (int ow = 0; ow < Wo; ++ow) {
                     double yv;
-                    conv_one(C, H, W, K, R, S, stride, pad, dil, groups, x, w,
+                    conv_one(C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, groups, x, w,
                              NULL, n, k, oh, ow, &yv, NULL);
                     const double t = (yv + (double)bias[k]) * (double)scale[k];
                     v[(int64_t)k * plane + (int64_t)oh * Wo + ow] = 1.0 / (1.0 + exp(-t));
@@ -220,4 +241,15 @@ int oracle_fused_gn(int N, int C, int H, int W, int K, int R, int S,
     }
     free(v);
     return ORACLE_OK;
+}
+
+int oracle_fused_gn(int N, int C, int H, int W, int K, int R, int S,
+                    int stride, int pad, int dil, int groups,
+                    const float *x, const float *w, const float *bias,
+                    const float *scale, const float *gamma, const float *beta,
+                    int gn_groups, double eps,
+                    double *v_out, double *out, int nthreads)
+{
+    return oracle_fused_gn_2d(N, C, H, W, K, R, S, stride, stride, pad, pad, dil, dil, groups,
+                              x, w, bias, scale, gamma, beta, gn_groups, eps, v_out, out, nthreads);
 }

@@ -339,3 +339,102 @@ def test_workload_recipes_are_deterministic():
     assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["w"], b["w"])
     assert a["x"].dtype == np.float32 and a["x"].min() >= -1 and a["x"].max() <= 1
     assert np.abs(a["w"]).max() <= 1 / 6
+
+
+# ---- per-axis stride, padding and dilation (the (h, w) form of the oracle)
+
+def _random_axis_geometries(count, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        groups = int(rng.integers(1, 4))
+        cin, cout = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        R, S = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+        sh, sw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        ph, pw = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        dh, dw = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        H, W = int(rng.integers(1, 14)), int(rng.integers(1, 14))
+        if H + 2 * ph - dh * (R - 1) - 1 < 0 or W + 2 * pw - dw * (S - 1) - 1 < 0:
+            continue
+        if (sh, ph, dh) == (sw, pw, dw):
+            continue  # keep only geometries that differ between the axes
+        out.append((2, groups * cin, H, W, groups * cout, R, S, (sh, sw), (ph, pw), (dh, dw), groups))
+    return out
+
+
+@pytest.mark.parametrize("geom", _random_axis_geometries(24, 7))
+def test_per_axis_matches_torch_conv2d_float64(geom):
+    N, C, H, W, K, R, S, stride, pad, dil, groups = geom
+    x = _rand((N, C, H, W), 81)
+    w = _rand((K, C // groups, R, S), 81, 1)
+    b = _rand((K,), 81, 2)
+    y, A = oracle.conv2d(x, w, b, stride, pad, dil, groups)
+    np.testing.assert_allclose(y, _torch_conv(x, w, b, stride, pad, dil, groups), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(A, _torch_conv(np.abs(x), np.abs(w), np.abs(b), stride, pad, dil, groups),
+                               rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("geom", _random_axis_geometries(12, 8))
+def test_per_axis_transposition(geom):
+    """Swapping the image axes swaps the roles of (h, w) parameters and
+    transposes the output: conv(x, w; s, p, d)^T == conv(x^T, w^T; s', p', d')."""
+    N, C, H, W, K, R, S, stride, pad, dil, groups = geom
+    x = _rand((N, C, H, W), 82)
+    w = _rand((K, C // groups, R, S), 82, 1)
+    y, _ = oracle.conv2d(x, w, None, stride, pad, dil, groups)
+    yt, _ = oracle.conv2d(np.swapaxes(x, 2, 3), np.swapaxes(w, 2, 3), None, stride[::-1], pad[::-1], dil[::-1],
+                          groups)
+    # the transposed problem sums the same products in another order
+    np.testing.assert_allclose(np.swapaxes(yt, 2, 3), y, rtol=1e-12, atol=1e-13)
+
+
+def _scatter_conv_axes(x, w, stride, pad, dil, groups):
+    """Scatter form with per-axis parameters: each input pixel adds its
+    products into the outputs whose windows cover it."""
+    (sh, sw), (ph, pw), (dh, dw) = stride, pad, dil
+    N, C, H, W = x.shape
+    K, cin, R, S = w.shape
+    cout = K // groups
+    Ho = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+    Wo = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+    y = np.zeros((N, K, Ho, Wo))
+    for n in range(N):
+        for ic in range(C):
+            g = ic // cin
+            for ih in range(H):
+                for iw in range(W):
+                    for r in range(R):
+                        num_h = ih + ph - r * dh
+                        if num_h % sh or not (0 <= num_h // sh < Ho):
+                            continue
+                        for s in range(S):
+                            num_w = iw + pw - s * dw
+                            if num_w % sw or not (0 <= num_w // sw < Wo):
+                                continue
+                            for kl in range(cout):
+                                k = g * cout + kl
+                                y[n, k, num_h // sh, num_w // sw] += x[n, ic, ih, iw] * w[k, ic - g * cin, r, s]
+    return y
+
+
+@pytest.mark.parametrize("geom", [(1, 2, 7, 6, 2, 3, 3, (2, 1), (1, 0), (1, 2), 1),
+                                  (2, 4, 6, 9, 4, 2, 3, (1, 3), (0, 2), (2, 1), 2),
+                                  (1, 3, 8, 5, 3, 3, 2, (3, 2), (2, 1), (1, 1), 3)])
+def test_per_axis_scatter_bruteforce_exact_on_integers(geom):
+    N, C, H, W, K, R, S, stride, pad, dil, groups = geom
+    x = synth.integers((N, C, H, W), -2, 2, 63, 0)
+    w = synth.integers((K, C // groups, R, S), -2, 2, 63, 1)
+    y, _ = oracle.conv2d(x, w, None, stride, pad, dil, groups)
+    assert np.array_equal(y, _scatter_conv_axes(x, w, stride, pad, dil, groups))
+
+
+def test_per_axis_symmetric_equals_scalar_form():
+    x = _rand((2, 4, 11, 13), 84)
+    w = _rand((6, 2, 3, 5), 84, 1)
+    a, _ = oracle.conv2d(x, w, None, 2, 1, 2, 2)
+    b, _ = oracle.conv2d(x, w, None, (2, 2), (1, 1), (2, 2), 2)
+    assert np.array_equal(a, b)
+    f1 = oracle.fused_gn(x, w, _rand((6,), 84, 2), _rand((6,), 84, 3), None, None, 3, 1e-5, 1, 1, 1, 2)
+    f2 = oracle.fused_gn(x, w, _rand((6,), 84, 2), _rand((6,), 84, 3), None, None, 3, 1e-5, (1, 1), (1, 1),
+                         (1, 1), 2)
+    assert np.array_equal(f1, f2)
