@@ -33,7 +33,7 @@ FUSED_RECOMPUTE = 2
 FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recompute"}
 
 EXPORTED = (
-    "conv_desc_create", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
+    "conv_desc_create", "conv_desc_create_2d", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
     "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
     "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "gconv_time_graph",
     "gconv_status_string", "gconv_last_launch_error",
@@ -53,6 +53,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 _i, _p, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _lib.conv_desc_create.argtypes = [ctypes.POINTER(_p)] + [_i] * 11
+_lib.conv_desc_create_2d.argtypes = [ctypes.POINTER(_p)] + [_i] * 14
 _lib.conv_desc_destroy.argtypes = [_p]
 _lib.conv_desc_get_output_dims.argtypes = [_p, ctypes.POINTER(_i), ctypes.POINTER(_i)]
 _lib.conv_desc_set_algo.argtypes = [_p, _i]
@@ -122,6 +123,15 @@ def conv_desc_create(N, C, H, W, K, R, S, stride=1, pad=0, dilation=1, groups=1)
     _check("conv_desc_create", _lib.conv_desc_create(ctypes.byref(h), N, C, H, W, K, R, S, stride, pad,
                                                      dilation, groups))
     return ConvDesc(h.value, (N, C, H, W, K, R, S, stride, pad, dilation, groups))
+
+
+def conv_desc_create_2d(N, C, H, W, K, R, S, stride=(1, 1), pad=(0, 0), dilation=(1, 1), groups=1) -> ConvDesc:
+    """Descriptor with per-axis stride, padding and dilation, each an (h, w) pair."""
+    (sh, sw), (ph, pw), (dh, dw) = stride, pad, dilation
+    h = ctypes.c_void_p()
+    _check("conv_desc_create_2d", _lib.conv_desc_create_2d(ctypes.byref(h), N, C, H, W, K, R, S, sh, sw, ph, pw,
+                                                           dh, dw, groups))
+    return ConvDesc(h.value, (N, C, H, W, K, R, S, (sh, sw), (ph, pw), (dh, dw), groups))
 
 
 def conv_desc_destroy(desc: ConvDesc) -> None:

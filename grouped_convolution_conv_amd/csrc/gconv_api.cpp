@@ -89,30 +89,42 @@ int launch_status(hipError_t e) {
 
 extern "C" {
 
-int conv_desc_create(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S,
-                     int stride, int pad, int dilation, int groups) {
+int conv_desc_create_2d(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S, int stride_h,
+                        int stride_w, int pad_h, int pad_w, int dil_h, int dil_w, int groups) {
     if (!out) return GCONV_ERR_INVALID_ARG;
     *out = nullptr;
     if (N < 1 || C < 1 || H < 1 || W < 1 || K < 1 || R < 1 || S < 1) return GCONV_ERR_INVALID_ARG;
-    if (stride < 1 || dilation < 1 || pad < 0 || groups < 1) return GCONV_ERR_INVALID_ARG;
+    if (stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1 || pad_h < 0 || pad_w < 0 || groups < 1)
+        return GCONV_ERR_INVALID_ARG;
     if (C % groups != 0 || K % groups != 0) return GCONV_ERR_INVALID_ARG;
-    const int Ho = out_dim(H, R, stride, pad, dilation);
-    const int Wo = out_dim(W, S, stride, pad, dilation);
+    const int Ho = out_dim(H, R, stride_h, pad_h, dil_h);
+    const int Wo = out_dim(W, S, stride_w, pad_w, dil_w);
     if (Ho < 1 || Wo < 1) return GCONV_ERR_INVALID_ARG;
     if (!fits_int32(N, C, H, W) || !fits_int32(N, K, Ho, Wo) || !fits_int32(K, C / groups, R, S))
         return GCONV_ERR_INVALID_ARG;
     // padded extents used by the tiled kernels must stay in int range too
-    if ((long long)H + 2LL * pad > INT_MAX / 2 || (long long)W + 2LL * pad > INT_MAX / 2)
+    if ((long long)H + 2LL * pad_h > INT_MAX / 2 || (long long)W + 2LL * pad_w > INT_MAX / 2)
         return GCONV_ERR_INVALID_ARG;
     gconv_desc *d = new (std::nothrow) gconv_desc;
     if (!d) return GCONV_ERR_INVALID_ARG;
     d->N = N; d->C = C; d->H = H; d->W = W; d->K = K; d->R = R; d->S = S;
-    d->stride = stride; d->pad = pad; d->dil = dilation; d->groups = groups;
+    d->stride_h = stride_h; d->stride_w = stride_w;
+    d->pad_h = pad_h; d->pad_w = pad_w;
+    d->dil_h = dil_h; d->dil_w = dil_w;
+    d->stride = stride_h == stride_w ? stride_h : -1;
+    d->pad = pad_h == pad_w ? pad_h : -1;
+    d->dil = dil_h == dil_w ? dil_h : -1;
+    d->groups = groups;
     d->Ho = Ho; d->Wo = Wo; d->cin = C / groups; d->cout = K / groups;
     d->algo = GCONV_ALGO_AUTO;
     d->fused_variant = GCONV_FUSED_AUTO;
     *out = d;
     return GCONV_OK;
+}
+
+int conv_desc_create(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S,
+                     int stride, int pad, int dilation, int groups) {
+    return conv_desc_create_2d(out, N, C, H, W, K, R, S, stride, stride, pad, pad, dilation, dilation, groups);
 }
 
 int conv_desc_destroy(gconv_desc_t desc) {

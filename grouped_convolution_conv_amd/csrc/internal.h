@@ -12,7 +12,13 @@
 // launcher needs.
 struct gconv_desc {
     int N, C, H, W, K, R, S;
-    int stride, pad, dil, groups;
+    // per-axis geometry (h: along H and R, w: along W and S)
+    int stride_h, stride_w, pad_h, pad_w, dil_h, dil_w;
+    // the common value when both axes agree, else -1: the fast paths, which
+    // take one value for both axes, test these and so refuse asymmetric
+    // geometry (the direct kernel takes the per-axis fields)
+    int stride, pad, dil;
+    int groups;
     int Ho, Wo;
     int cin;   // input channels per group  (C / groups)
     int cout;  // output channels per group (K / groups)

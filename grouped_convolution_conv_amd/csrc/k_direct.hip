@@ -16,7 +16,7 @@ namespace {
 constexpr int kBlock = 256;
 
 struct DirectGeom {
-    int C, H, W, K, R, S, stride, pad, dil, cin, cout, Ho, Wo;
+    int C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, cin, cout, Ho, Wo;
 };
 
 __device__ __forceinline__ float direct_point(const float *__restrict__ x,
@@ -25,19 +25,19 @@ __device__ __forceinline__ float direct_point(const float *__restrict__ x,
     const int grp = k / g.cout;
     const float *xb = x + ((size_t)n * g.C + (size_t)grp * g.cin) * g.H * g.W;
     const float *wk = w + (size_t)k * g.cin * g.R * g.S;
-    const int ih0 = oh * g.stride - g.pad;
-    const int iw0 = ow * g.stride - g.pad;
+    const int ih0 = oh * g.sh - g.ph;
+    const int iw0 = ow * g.sw - g.pw;
     float acc = 0.0f;
     for (int c = 0; c < g.cin; ++c) {
         const float *xc = xb + (size_t)c * g.H * g.W;
         const float *wc = wk + c * g.R * g.S;
         for (int r = 0; r < g.R; ++r) {
-            const int ih = ih0 + r * g.dil;
+            const int ih = ih0 + r * g.dh;
             if (ih < 0 || ih >= g.H) continue;
             const float *xr = xc + (size_t)ih * g.W;
             const float *wr = wc + r * g.S;
             for (int s = 0; s < g.S; ++s) {
-                const int iw = iw0 + s * g.dil;
+                const int iw = iw0 + s * g.dw;
                 if (iw < 0 || iw >= g.W) continue;
                 acc = fmaf(xr[iw], wr[s], acc);
             }
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kBlock) void direct_fused_kernel(const float *__res
 DirectGeom make_geom(const gconv_desc *d) {
     DirectGeom g;
     g.C = d->C; g.H = d->H; g.W = d->W; g.K = d->K; g.R = d->R; g.S = d->S;
-    g.stride = d->stride; g.pad = d->pad; g.dil = d->dil;
+    g.sh = d->stride_h; g.sw = d->stride_w; g.ph = d->pad_h; g.pw = d->pad_w; g.dh = d->dil_h; g.dw = d->dil_w;
     g.cin = d->cin; g.cout = d->cout; g.Ho = d->Ho; g.Wo = d->Wo;
     return g;
 }

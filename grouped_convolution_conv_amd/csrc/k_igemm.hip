@@ -41,7 +41,8 @@ constexpr int kTW = 32 * kNBC;
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 struct IgParams {
-    int C, H, W, K, Ho, Wo, pad;
+    int C, H, W, K, Ho, Wo;
+    int pad_h, pad_w;  // zero padding above/below and left/right
     int cin, cout;
     int n_kb;          // output-channel blocks of 32*MB per group
     int n_tw;          // column tiles per image
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int e = base + u * kBlock;
                 const int row = e / TIW, col = e - row * TIW;  // row = cl * TIH + lr
                 const int cl = row / TIH, lr = row - cl * TIH;
-                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
+                const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + col;
                 v[u] = 0.0f;
                 if (e < XE && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W)
                     v[u] = xg[(size_t)(c0 + cl) * HW + (size_t)ih * p.W + iw];
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int f = ii * 64 + lane;
                 const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
                 const int lr = rem / P4, c4 = rem - lr * P4;
-                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + 4 * c4;
+                const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + 4 * c4;
                 const bool ok = f < XE4 && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
                 const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb4 + ii * 64), 16, off, 0, 0, 0);
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int e = ii * 64 + lane;
                 const int row = e / PITCH, col = e - row * PITCH;  // row = cl * TIH + lr
                 const int cl = row / TIH, lr = row - cl * TIH;
-                const int ih = oh0 - p.pad + lr, iw = ow0 - p.pad + col;
+                const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + col;
                 const bool ok = e < XE && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
                 const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64), 4, off, 0, 0, 0);
@@ -536,7 +537,8 @@ int pick_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
 
 IgParams make_params(const gconv_desc *d, int MB) {
     IgParams p;
-    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo; p.pad = d->pad;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo;
+    p.pad_h = d->pad_h; p.pad_w = d->pad_w;
     p.cin = d->cin; p.cout = d->cout;
     p.n_kb = (d->cout + 32 * MB - 1) / (32 * MB);
     p.n_tw = (d->Wo + kTW - 1) / kTW;
@@ -551,7 +553,7 @@ IgParams make_params(const gconv_desc *d, int MB) {
 bool igemm_supported(const gconv_desc *d) {
     // buffer offsets are signed 32-bit: one group's input channels of one
     // image must stay below 2 GB
-    return d->stride == 1 && d->dil == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
+    return d->stride_h == 1 && d->stride_w == 1 && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
            d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
 
@@ -572,7 +574,7 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     // read once per block, in exchange for no register spills
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
-    p.vec = (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    p.vec = (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_kb;
     if (gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);

@@ -60,7 +60,8 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct ResParams {
-    int C, H, W, K, Ho, Wo, pad;
+    int C, H, W, K, Ho, Wo;
+    int pad_h, pad_w;  // zero padding above/below and left/right
     int cin, cout;
     int n_tw, n_tiles, units;   // tiles per image row band, per image, in total
     int x_bytes;                // bytes of one input image (C * H * W floats)
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     auto load = [&](int v) __attribute__((always_inline)) {
         const int t = v % p.n_tiles, n = v / p.n_tiles;
         const int th = t / p.n_tw, tw = t - th * p.n_tw;
-        const int ih0 = th * kTH - p.pad, iw0 = tw * kTW - p.pad;
+        const int ih0 = th * kTH - p.pad_h, iw0 = tw * kTW - p.pad_w;
         const __amdgpu_buffer_rsrc_t rs = rsrc(x + (size_t)n * p.C * HW, p.x_bytes);
         if constexpr (MODE == kNormalize) {
             const __amdgpu_buffer_rsrc_t gr = rsrc(ep.gstat + (size_t)n * ep.gn_groups, NGS * (int)sizeof(float));
@@ -478,7 +479,8 @@ int res_parts_per_group(const gconv_desc *d) {
 
 ResParams make_params(const gconv_desc *d, int gn_groups) {
     ResParams p;
-    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo; p.pad = d->pad;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo;
+    p.pad_h = d->pad_h; p.pad_w = d->pad_w;
     p.cin = d->cin; p.cout = d->cout;
     p.n_tw = (d->Wo + kTW - 1) / kTW;
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
@@ -490,7 +492,7 @@ ResParams make_params(const gconv_desc *d, int gn_groups) {
 }
 
 bool res_vec(const gconv_desc *d, const float *x) {
-    return (d->W % 4 == 0) && (d->pad % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    return (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
 }
 
 int res_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
@@ -557,7 +559,7 @@ bool igemm_res_supported(const gconv_desc *d) {
     // buffer offsets are signed 32-bit: one image of x and of y (and the
     // partials of one image) must stay below 2 GB
     const long long lim = 0x7fffffffLL - 64;
-    return d->groups == 1 && d->stride == 1 && d->dil == 1 && d->cin >= 4 && d->cin <= 8 &&
+    return d->groups == 1 && d->stride_h == 1 && d->stride_w == 1 && d->dil_h == 1 && d->dil_w == 1 && d->cin >= 4 && d->cin <= 8 &&
            d->cout >= 8 && d->cout <= 64 && ((d->R == 3 && d->S == 3) || (d->R == 1 && d->S == 1)) &&
            (long long)d->C * d->H * d->W * 4 < lim && (long long)d->K * d->Ho * d->Wo * 4 < lim;
 }

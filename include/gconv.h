@@ -89,6 +89,20 @@ typedef struct gconv_desc *gconv_desc_t;
 int conv_desc_create(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S,
                      int stride, int pad, int dilation, int groups);
 
+/* The same with stride, zero padding and dilation given per axis (h along
+ * H and R, w along W and S), as in the per-axis conv2d host wrapper of the
+ * POPCORNBENCH trace "Kimi-K2.6 l1_p62" (host-wrapper discussion):
+ *   Ho = (H + 2*pad_h - dil_h*(R-1) - 1)/stride_h + 1, likewise Wo,
+ *   input row oh*stride_h - pad_h + r*dil_h, column ow*stride_w - pad_w + s*dil_w.
+ * The fast paths take unit stride and dilation on both axes (the implicit
+ * GEMM kernels accept different paddings per axis; the grouped 3x3 kernels
+ * need pad 1 on both); any other geometry runs on the direct kernel.
+ * conv_desc_create(..., stride, pad, dil, ...) is this call with equal
+ * values on both axes. */
+int conv_desc_create_2d(gconv_desc_t *out, int N, int C, int H, int W, int K, int R, int S,
+                        int stride_h, int stride_w, int pad_h, int pad_w, int dil_h, int dil_w,
+                        int groups);
+
 /* Releases a descriptor.  NULL is accepted and ignored. */
 int conv_desc_destroy(gconv_desc_t desc);
 

@@ -207,3 +207,43 @@ def test_time_graph_validates_before_any_device_call():
     assert call(xa=(P * 1)(None)) == gc.GCONV_ERR_INVALID_ARG
     with pytest.raises(ValueError):
         gc.gconv_time_graph(d, [fake], [], fake)
+
+
+def test_per_axis_descriptor_dims_and_dispatch():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        H, W = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        R, S = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        sh, sw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        ph, pw = int(rng.integers(0, 4)), int(rng.integers(0, 4))
+        dh, dw = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        ho, wo = oracle.out_dim(H, R, sh, ph, dh), oracle.out_dim(W, S, sw, pw, dw)
+        if ho < 1 or wo < 1:
+            with pytest.raises(gc.GconvError):
+                gc.conv_desc_create_2d(1, 2, H, W, 2, R, S, (sh, sw), (ph, pw), (dh, dw), 1)
+            continue
+        d = gc.conv_desc_create_2d(1, 2, H, W, 2, R, S, (sh, sw), (ph, pw), (dh, dw), 1)
+        assert gc.conv_desc_get_output_dims(d) == (ho, wo)
+    # asymmetric stride or dilation: only the direct kernel
+    d = gc.conv_desc_create_2d(2, 8, 20, 20, 8, 3, 3, (1, 2), (1, 1), (1, 1), 2)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_DIRECT
+    with pytest.raises(gc.GconvError):
+        gc.conv_desc_set_algo(d, gc.ALGO_GROUPED3X3)
+    # asymmetric padding, unit stride and dilation: the implicit GEMM takes it
+    d = gc.conv_desc_create_2d(2, 16, 20, 20, 32, 5, 5, (1, 1), (0, 2), (1, 1), 1)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_IGEMM
+    # grouped 3x3 needs pad 1 on both axes
+    d = gc.conv_desc_create_2d(2, 8, 20, 20, 8, 3, 3, (1, 1), (1, 0), (1, 1), 4)
+    assert gc.conv_desc_get_algo(d) != gc.ALGO_GROUPED3X3
+    # the symmetric call is the per-axis call with equal values
+    a = gc.conv_desc_create(2, 8, 20, 20, 8, 3, 3, 2, 1, 2, 4)
+    b = gc.conv_desc_create_2d(2, 8, 20, 20, 8, 3, 3, (2, 2), (1, 1), (2, 2), 4)
+    assert gc.conv_desc_get_output_dims(a) == gc.conv_desc_get_output_dims(b)
+    assert gc.conv_desc_get_algo(a) == gc.conv_desc_get_algo(b)
+
+
+def test_per_axis_descriptor_rejects_bad_values():
+    for args in [((0, 1), (0, 0), (1, 1)), ((1, 1), (-1, 0), (1, 1)), ((1, 1), (0, 0), (1, 0))]:
+        with pytest.raises(gc.GconvError) as ei:
+            gc.conv_desc_create_2d(1, 4, 8, 8, 4, 3, 3, *args, 1)
+        assert ei.value.status == gc.GCONV_ERR_INVALID_ARG
