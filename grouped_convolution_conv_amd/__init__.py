@@ -25,7 +25,9 @@ ALGO_AUTO = 0
 ALGO_DIRECT = 1
 ALGO_GROUPED3X3 = 2
 ALGO_IGEMM = 3
-ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DIRECT: "direct", ALGO_GROUPED3X3: "grouped3x3", ALGO_IGEMM: "igemm"}
+ALGO_DEPTHWISE = 4
+ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DIRECT: "direct", ALGO_GROUPED3X3: "grouped3x3", ALGO_IGEMM: "igemm",
+              ALGO_DEPTHWISE: "depthwise"}
 
 FUSED_AUTO = 0
 FUSED_STORE = 1

@@ -28,6 +28,7 @@ bool fits_int32(long long a, long long b, long long c, long long d) {
 int resolve_algo(const gconv_desc *d) {
     if (d->algo != GCONV_ALGO_AUTO) return d->algo;
     if (gconv::grouped3x3_supported(d)) return GCONV_ALGO_GROUPED3X3;
+    if (gconv::depthwise_supported(d)) return GCONV_ALGO_DEPTHWISE;
     if (gconv::igemm_supported(d)) return GCONV_ALGO_IGEMM;
     return GCONV_ALGO_DIRECT;
 }
@@ -38,6 +39,7 @@ bool algo_supported(const gconv_desc *d, int algo) {
         case GCONV_ALGO_DIRECT: return true;
         case GCONV_ALGO_GROUPED3X3: return gconv::grouped3x3_supported(d);
         case GCONV_ALGO_IGEMM: return gconv::igemm_supported(d);
+        case GCONV_ALGO_DEPTHWISE: return gconv::depthwise_supported(d);
         default: return false;
     }
 }
@@ -141,7 +143,7 @@ int conv_desc_get_output_dims(gconv_desc_t d, int *Ho, int *Wo) {
 
 int conv_desc_set_algo(gconv_desc_t d, int algo) {
     if (!d) return GCONV_ERR_INVALID_ARG;
-    if (algo < GCONV_ALGO_AUTO || algo > GCONV_ALGO_IGEMM) return GCONV_ERR_INVALID_ARG;
+    if (algo < GCONV_ALGO_AUTO || algo > GCONV_ALGO_DEPTHWISE) return GCONV_ERR_INVALID_ARG;
     if (!algo_supported(d, algo)) return GCONV_ERR_UNSUPPORTED;
     d->algo = algo;
     return GCONV_OK;
@@ -174,6 +176,7 @@ int conv_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias, 
     hipStream_t st = (hipStream_t)stream;
     switch (resolve_algo(d)) {
         case GCONV_ALGO_GROUPED3X3: return launch_status(gconv::launch_grouped3x3(d, x, w, bias, y, st));
+        case GCONV_ALGO_DEPTHWISE: return launch_status(gconv::launch_depthwise(d, x, w, bias, y, st));
         case GCONV_ALGO_IGEMM:
             if (gconv::igemm_res_supported(d)) return launch_status(gconv::launch_igemm_res(d, x, w, bias, y, st));
             return launch_status(gconv::launch_igemm(d, x, w, bias, y, st));

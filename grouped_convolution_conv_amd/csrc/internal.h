@@ -54,6 +54,7 @@ struct FusedEpilogue {
 // ---- applicability tests -------------------------------------------------
 bool grouped3x3_supported(const gconv_desc *d);
 bool igemm_supported(const gconv_desc *d);
+bool depthwise_supported(const gconv_desc *d);
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups);
 
 // ---- plain convolution launchers (y = conv(x, w) [+ bias]) ---------------
@@ -63,6 +64,8 @@ hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w
                              const float *bias, float *y, hipStream_t st);
 hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w,
                         const float *bias, float *y, hipStream_t st);
+hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
+                            const float *bias, float *y, hipStream_t st);
 
 // ---- fused chain, stage A: conv + bias/scale/sigmoid + per-tile stats ----
 int direct_fused_parts_per_group(const gconv_desc *d, int gn_groups);

@@ -1,0 +1,173 @@
+// k_depthwise.hip -- depthwise K x K convolution, zero padding K/2, dilation 1:
+// K = 5 or 7 at stride 1, and K = 3 at stride 2.  The GroupConv Atlas
+// project page's direct kernel (k0, "Direct mapping") takes any geometry;
+// its k3 card computes four adjacent outputs per thread.  This kernel is the
+// four-outputs-per-lane form for these depthwise geometries.  VALU
+// arithmetic, HBM-bound for K = 3 and 5.
+//
+// The same register-streaming design as grouped3x3_rows_kernel, for one
+// channel per group and one output channel per group:
+//  - a wave owns whole output rows of one (n, channel) plane; a lane owns
+//    RB output rows x 4 output columns;
+//  - per input row it needs, a lane reads its own ST*4 input columns (one or
+//    two 16-byte buffer loads, zero outside the image) and takes the K/2
+//    columns to its left and the columns past its right edge from the
+//    neighbouring lanes with cross-lane moves;
+//  - no LDS, no barriers; rows shared by neighbouring lanes and waves come
+//    from the L2.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace gconv {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access, gfx9 family
+constexpr int kOutOfPlane = 0x7fffffff;
+constexpr int kRB = 2;                     // output rows per lane
+
+struct DwParams {
+    int C, H, W, Ho, Wo;
+    int cg;       // 4-column output groups per row (Wo / 4)
+    int rpw;      // lane strips (of kRB output rows) per wave: 64 / cg
+    int strips;   // strips per plane: ceil(Ho / kRB)
+    int wpp;      // waves per plane: ceil(strips / rpw)
+    int waves;    // N * C * wpp
+};
+
+template <int KS, int ST>
+__global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__restrict__ x,
+                                                                const float *__restrict__ w,
+                                                                const float *__restrict__ bias,
+                                                                float *__restrict__ y, DwParams p) {
+    constexpr int PAD = KS / 2;
+    constexpr int NIR = ST * (kRB - 1) + KS;   // input rows a lane reads
+    constexpr int OWN = 4 * ST;                // input columns a lane loads itself
+    constexpr int RIGHT = KS - PAD - ST;       // columns needed past the lane's own ones
+    constexpr int WL = PAD + OWN + RIGHT;      // window: input columns ST*oc - PAD ...
+    static_assert(PAD <= OWN && RIGHT >= 0 && RIGHT <= OWN, "neighbour exchange reaches one lane");
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
+    if (wv >= p.waves) return;  // whole waves only
+    const int plane = wv / p.wpp, wip = wv - plane * p.wpp;  // plane = n * C + c
+    const int c = plane % p.C;
+    const int sl = lane / p.cg, cgi = lane - sl * p.cg;
+    const int strip = wip * p.rpw + sl;
+    const bool active = sl < p.rpw && strip < p.strips;
+    const int oh0 = strip * kRB, oc0 = cgi * 4;
+    const int ih0 = ST * oh0 - PAD, ic0 = ST * oc0;
+    const bool has_left = cgi > 0, has_right = cgi < p.cg - 1;
+    const int HW = p.H * p.W;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + (size_t)plane * HW), (short)0, HW * (int)sizeof(float), kBufferWord3);
+
+    float wk[KS * KS];
+#pragma unroll
+    for (int t = 0; t < KS * KS; ++t) wk[t] = w[(size_t)c * KS * KS + t];
+    const float b = bias ? bias[c] : 0.0f;
+
+    float acc[kRB][4];
+#pragma unroll
+    for (int rr = 0; rr < kRB; ++rr)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[rr][q] = b;
+
+    // the lane's own columns of every input row it needs: buffer loads with
+    // out-of-range offsets (rows above/below the image, idle lanes) reading 0
+    float own[NIR][OWN];
+#pragma unroll
+    for (int i = 0; i < NIR; ++i) {
+        const int ih = ih0 + i;
+        const int rowb = (ih * p.W + ic0) * (int)sizeof(float);
+#pragma unroll
+        for (int v = 0; v < ST; ++v) {
+            const int off = active && ih >= 0 && ih < p.H ? rowb + 16 * v : kOutOfPlane;
+            const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            own[i][4 * v + 0] = f.x; own[i][4 * v + 1] = f.y; own[i][4 * v + 2] = f.z; own[i][4 * v + 3] = f.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NIR; ++i) {
+        float win[WL];
+#pragma unroll
+        for (int t = 0; t < PAD; ++t) {  // columns ic0 - PAD + t: the left lane's last ones
+            const float v = __shfl_up(own[i][OWN - PAD + t], 1, 64);
+            win[t] = has_left ? v : 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < OWN; ++t) win[PAD + t] = own[i][t];
+#pragma unroll
+        for (int t = 0; t < RIGHT; ++t) {  // columns ic0 + OWN + t: the right lane's first ones
+            const float v = __shfl_down(own[i][t], 1, 64);
+            win[PAD + OWN + t] = has_right ? v : 0.0f;
+        }
+#pragma unroll
+        for (int kr = 0; kr < KS; ++kr) {
+            // input row i feeds output row rr through kernel row kr when i = ST*rr + kr
+            if ((i - kr) % ST != 0) continue;
+            const int rr = (i - kr) / ST;
+            if (i < kr || rr >= kRB) continue;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[rr][q] = fmaf(win[ST * q + s], wk[kr * KS + s], acc[rr][q]);
+        }
+    }
+    if (!active) return;
+    float *yb = y + (size_t)plane * p.Ho * p.Wo + oc0;
+#pragma unroll
+    for (int rr = 0; rr < kRB; ++rr) {
+        const int oh = oh0 + rr;
+        if (oh < p.Ho)
+            *reinterpret_cast<float4 *>(yb + (size_t)oh * p.Wo) =
+                make_float4(acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]);
+    }
+}
+
+template <int KS, int ST>
+hipError_t launch_t(const DwParams &p, const float *x, const float *w, const float *bias, float *y,
+                    hipStream_t st) {
+    const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
+    clear_stale_launch_error();
+    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool depthwise_supported(const gconv_desc *d) {
+    if (d->cin != 1 || d->cout != 1 || d->R != d->S || d->dil_h != 1 || d->dil_w != 1) return false;
+    const int ks = d->R;
+    if (d->pad_h != ks / 2 || d->pad_w != ks / 2 || d->stride_h != d->stride_w) return false;
+    const int st = d->stride_h;
+    if (!((ks == 5 && st == 1) || (ks == 7 && st == 1) || (ks == 3 && st == 2))) return false;
+    // whole 4-column output groups, one lane's own input columns in whole
+    // 16-byte pieces, a row within one wave, buffer offsets in 32 bits
+    if (d->Wo < 4 || d->Wo % 4 != 0 || d->Wo / 4 > 64 || d->Ho < 1) return false;
+    if (st == 2 && d->W != 2 * d->Wo) return false;
+    if (st == 1 && d->W != d->Wo) return false;
+    return (long long)(d->H + 16) * d->W * 4 < 0x7fffffffLL;
+}
+
+hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w, const float *bias, float *y,
+                            hipStream_t st) {
+    if (!depthwise_supported(d)) return hipErrorInvalidValue;
+    // 16-byte row pieces need 16-byte aligned planes; other pointers take the
+    // direct kernel, which computes the same outputs
+    if ((((uintptr_t)x) | ((uintptr_t)y)) & 15u) return launch_direct(d, x, w, bias, y, st);
+    DwParams p;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.Ho = d->Ho; p.Wo = d->Wo;
+    p.cg = d->Wo / 4;
+    p.rpw = 64 / p.cg;
+    p.strips = (d->Ho + kRB - 1) / kRB;
+    p.wpp = (p.strips + p.rpw - 1) / p.rpw;
+    const long long waves = (long long)d->N * d->C * p.wpp;
+    if (waves > 0x7fffffffLL - 64) return hipErrorInvalidConfiguration;
+    p.waves = (int)waves;
+    if (d->R == 5) return launch_t<5, 1>(p, x, w, bias, y, st);
+    if (d->R == 7) return launch_t<7, 1>(p, x, w, bias, y, st);
+    return launch_t<3, 2>(p, x, w, bias, y, st);
+}
+
+}  // namespace gconv

@@ -1,0 +1,137 @@
+"""GPU parity of the depthwise kernel (5x5 and 7x7 at stride 1, 3x3 at
+stride 2, padding R // 2) through the C ABI against the CPU oracle.
+
+Same bars as the other parity tests: |y_gpu - y_oracle| <= 1e-4 * A + 1e-6
+with A = sum |x * w| over the receptive field; bit-for-bit equality for
+integer-valued inputs.  Outputs are pre-filled with NaN.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import synth
+import grouped_convolution_conv_amd as gc
+
+pytestmark = pytest.mark.gpu
+
+CONV_RTOL, CONV_ATOL = 1e-4, 1e-6
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _dw(name, N, C, H, W, R, stride, seed):
+    return synth.Workload(name, N, C, H, W, C, R, R, stride, R // 2, 1, C, seed,
+                          ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0))
+
+
+# Small cases: the oracle computes every output.  They cover one 4-column
+# group per row (a wave holds 64 row strips), a full 256-column output row
+# per wave (one strip per wave), row counts that leave part of the last
+# strip and part of the last wave idle, a single input row, and output rows
+# whose lanes do not fill a wave.
+SMALL = [
+    _dw("dw5_h13_w20", 2, 6, 13, 20, 5, 1, 201),
+    _dw("dw5_h1_w8", 3, 4, 1, 8, 5, 1, 202),
+    _dw("dw5_h14_w28_planes", 8, 64, 14, 28, 5, 1, 203),
+    _dw("dw7_h9_w256", 1, 3, 9, 256, 7, 1, 204),
+    _dw("dw7_h3_w4", 2, 4, 3, 4, 7, 1, 205),
+    _dw("dw7_h31_w60", 2, 5, 31, 60, 7, 1, 206),
+    _dw("dw3s2_h7_w8", 2, 5, 7, 8, 3, 2, 207),
+    _dw("dw3s2_h33_w512", 1, 2, 33, 512, 3, 2, 208),
+    _dw("dw3s2_h2_w16", 4, 3, 2, 16, 3, 2, 209),
+    _dw("dw3s2_h30_w56_planes", 4, 48, 30, 56, 3, 2, 210),
+]
+
+# The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
+# networks at batch 16: compared on sampled outputs (random ones plus every
+# border pixel of a few planes).
+FULL = [
+    _dw("dw3s2_mobilenet_144x112", 16, 144, 112, 112, 3, 2, 211),
+    _dw("dw5_efficientnet_240x28", 16, 240, 28, 28, 5, 1, 212),
+    _dw("dw7_convnext_96x56", 16, 96, 56, 56, 7, 1, 213),
+]
+
+
+def _dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run(wl, inp, bias=None, algo=gc.ALGO_AUTO, y_offset=0):
+    d = gc.conv_desc_create(wl.N, wl.C, wl.H, wl.W, wl.K, wl.R, wl.S, wl.stride, wl.pad, wl.dil, wl.groups)
+    gc.conv_desc_set_algo(d, algo)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    n_out = wl.N * wl.K * ho * wo
+    ybuf = torch.full((n_out + y_offset,), float("nan"), device="cuda")
+    y = ybuf[y_offset:]
+    gc.conv_fwd(d, _dev(inp["x"]), _dev(inp["w"]), _dev(bias), y.data_ptr() if y_offset else y)
+    torch.cuda.synchronize()
+    return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
+
+
+def _check(y_gpu, y_ref, A, what):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    bound = CONV_RTOL * A + CONV_ATOL
+    ok = err <= bound
+    if not np.all(ok):
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d of %d outputs outside 1e-4*A+1e-6; first at %s: gpu %r oracle %r"
+                             % (what, len(bad), err.size, i, y_gpu[i], y_ref[i]))
+    return float(np.max(err / bound))
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_depthwise_small(wl):
+    inp = synth.make_inputs(wl)
+    bias = synth.normal((wl.K,), 0.5, wl.seed, 7)
+    for b in (None, bias):
+        _say("[parity] depthwise", wl.name, "bias" if b is not None else "")
+        y_ref, A = oracle.conv2d(inp["x"], inp["w"], b, wl.stride, wl.pad, wl.dil, wl.groups)
+        y, used = _run(wl, inp, b)
+        assert used == gc.ALGO_DEPTHWISE
+        _check(y, y_ref, A, wl.name)
+        # a 4-byte aligned output takes the direct kernel; same outputs
+        y1, _ = _run(wl, inp, b, y_offset=1)
+        _check(y1, y_ref, A, wl.name + " misaligned y")
+
+
+@pytest.mark.parametrize("wl", SMALL[::3], ids=lambda w: w.name)
+def test_depthwise_integer_inputs_bit_exact(wl):
+    wl = wl.with_(x_dist=("int", -3, 3), w_dist=("int", -2, 2), seed=wl.seed + 500)
+    _say("[parity] depthwise int", wl.name)
+    inp = synth.make_inputs(wl)
+    y, used = _run(wl, inp)
+    assert used == gc.ALGO_DEPTHWISE
+    y_ref, _ = oracle.conv2d(inp["x"], inp["w"], None, wl.stride, wl.pad, wl.dil, wl.groups)
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def _sample_indices(shape, n_random, seed):
+    N, K, Ho, Wo = shape
+    rng = np.random.default_rng(seed)
+    idx = [rng.integers(0, N * K * Ho * Wo, n_random)]
+    for (n, k) in [(0, 0), (N - 1, K - 1), (N // 2, K // 3)]:
+        base = (n * K + k) * Ho * Wo
+        cols = np.arange(Wo)
+        rows = np.arange(Ho) * Wo
+        idx += [base + cols, base + (Ho - 1) * Wo + cols, base + rows, base + rows + Wo - 1]
+    return np.unique(np.concatenate(idx))
+
+
+@pytest.mark.parametrize("wl", FULL, ids=lambda w: w.name)
+def test_depthwise_full_size_sampled(wl):
+    _say("[parity] depthwise full-size sampled", wl.name)
+    inp = synth.make_inputs(wl)
+    bias = synth.normal((wl.K,), 0.5, wl.seed, 7)
+    y, used = _run(wl, inp, bias)
+    assert used == gc.ALGO_DEPTHWISE
+    assert not np.isnan(y).any(), "unwritten outputs"
+    idx = _sample_indices(y.shape, 6000, wl.seed)
+    y_ref, A = oracle.conv2d_points(inp["x"], inp["w"], idx, bias, wl.stride, wl.pad, wl.dil, wl.groups)
+    _check(y.ravel()[idx], y_ref, A, wl.name + " sampled")

@@ -247,3 +247,33 @@ def test_per_axis_descriptor_rejects_bad_values():
         with pytest.raises(gc.GconvError) as ei:
             gc.conv_desc_create_2d(1, 4, 8, 8, 4, 3, 3, *args, 1)
         assert ei.value.status == gc.GCONV_ERR_INVALID_ARG
+
+
+def test_depthwise_dispatch():
+    # (C, H, W, R, stride, pad): depthwise 5x5 / 7x7 stride 1 and 3x3 stride 2,
+    # padding R // 2, output width a multiple of 4 up to 256
+    taken = [(16, 20, 20, 5, 1, 2), (16, 9, 256, 7, 1, 3), (8, 7, 8, 3, 2, 1), (8, 33, 512, 3, 2, 1)]
+    for C, H, W, R, st, pad in taken:
+        d = gc.conv_desc_create(2, C, H, W, C, R, R, st, pad, 1, C)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, H, W, R, st, pad)
+        gc.conv_desc_set_algo(d, gc.ALGO_DIRECT)
+        gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
+    refused = [
+        (2, 16, 20, 20, 16, 5, 5, 1, 1, 1, 16),    # padding other than R // 2
+        (2, 16, 20, 22, 16, 5, 5, 1, 2, 1, 16),    # output width not a multiple of 4
+        (2, 16, 20, 520, 16, 5, 5, 1, 2, 1, 16),   # output row wider than one wave
+        (2, 16, 20, 21, 16, 3, 3, 2, 1, 1, 16),    # stride 2 with an odd input width
+        (2, 16, 20, 20, 16, 5, 5, 2, 2, 1, 16),    # 5x5 at stride 2
+        (2, 16, 20, 20, 16, 5, 5, 1, 4, 2, 16),    # dilation 2
+        (2, 16, 20, 20, 32, 5, 5, 1, 2, 1, 16),    # two output channels per group
+        (2, 16, 20, 20, 8, 5, 5, 1, 2, 1, 8),      # two input channels per group
+    ]
+    for geom in refused:
+        d = gc.conv_desc_create(*geom)
+        assert gc.conv_desc_get_algo(d) != gc.ALGO_DEPTHWISE, geom
+        with pytest.raises(gc.GconvError) as ei:
+            gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
+        assert ei.value.status == gc.GCONV_ERR_UNSUPPORTED
+    # per-axis: unequal padding is refused
+    d = gc.conv_desc_create_2d(2, 16, 20, 20, 16, 5, 5, (1, 1), (2, 1), (1, 1), 16)
+    assert gc.conv_desc_get_algo(d) != gc.ALGO_DEPTHWISE

@@ -269,7 +269,7 @@ def _fuzz_cases(n, seed):
 def test_conv_geometry_fuzz(wl):
     inp = synth.make_inputs(wl)
     y_ref, A = oracle_conv(wl, inp)
-    for algo in (gc.ALGO_AUTO, gc.ALGO_DIRECT, gc.ALGO_IGEMM, gc.ALGO_GROUPED3X3):
+    for algo in (gc.ALGO_AUTO, gc.ALGO_DIRECT, gc.ALGO_IGEMM, gc.ALGO_GROUPED3X3, gc.ALGO_DEPTHWISE):
         d = _desc(wl)
         try:
             gc.conv_desc_set_algo(d, algo)
