@@ -113,6 +113,7 @@ KERNEL_SOURCES = {
     "igemm": ["k_igemm.hip"],
     "grouped3x3": ["k_grouped3x3.hip"],
     "direct": ["k_direct.hip"],
+    "depthwise": ["k_depthwise.hip"],
 }
 
 
@@ -323,6 +324,26 @@ def cpu_baseline(rows):
 # ------------------------------------------------------------------ main
 
 
+def workload_text(names, known):
+    if names == [n for n in known if n in names] and all(n in ROW_TEXT for n in names):
+        return "one pass over the shape rows " + ", ".join(names) + " (" + "; ".join(ROW_TEXT[n] for n in names) + ")"
+    return "one pass over the shape rows " + "; ".join(
+        "%s: N%d C%d->%d %dx%d %dx%d stride %d pad %d dil %d groups %d" % (
+            n, known[n].N, known[n].C, known[n].K, known[n].H, known[n].W, known[n].R, known[n].S,
+            known[n].stride, known[n].pad, known[n].dil, known[n].groups) for n in names)
+
+
+ROW_TEXT = {
+    "c1_grouped_cpg4": "grouped 3x3 cpg4 N1 C8 16x16",
+    "c2_depthwise_144": "depthwise N4 C144 56x56",
+    "c3a_grouped_g64": "grouped N32 C256 64x64 g64",
+    "c3b_grouped_g128": "grouped N32 C256 64x64 g128",
+    "c3c_depthwise_g256": "grouped N32 C256 64x64 g256",
+    "c4_dense_5x9": "dense N8 C32->64 256x256 5x9",
+    "c5_fused_gn": "fused N64 C8->32 256x256 3x3 + bias, scale, sigmoid, GN(8)",
+}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -344,11 +365,19 @@ def main():
     if args.copy_only:
         print(json.dumps({"copy_calibration": copy}), flush=True)
         return
-    names = [n for n in synth.ROW_ORDER if not args.rows or n in args.rows.split(",")]
+    known = dict(synth.WORKLOADS, **synth.EXTRA_WORKLOADS)
+    if args.rows:
+        names = args.rows.split(",")
+        unknown = [n for n in names if n not in known]
+        if unknown:
+            print("bench.py: unknown rows %s (known: %s)" % (unknown, ", ".join(known)), file=sys.stderr)
+            sys.exit(2)
+    else:
+        names = list(synth.ROW_ORDER)
     log("[bench] device:", torch.cuda.get_device_name(0))
     rows = []
     for n in names:
-        rows.append(Row(n, synth.WORKLOADS[n], gc, torch, args.warm))
+        rows.append(Row(n, known[n], gc, torch, args.warm))
         log("[bench] row %-20s algo=%-10s sets=%d bytes=%d flops=%d" % (n, rows[-1].algo, rows[-1].nsets,
                                                                       rows[-1].acct["bytes"], rows[-1].acct["flops"]))
     torch.cuda.synchronize()
@@ -430,10 +459,7 @@ def main():
         "unit": "GB/s (geomean over shape rows, device time per launch)",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "one pass over the shape rows " + ", ".join(names) +
-                   " (grouped 3x3 cpg4 N1 C8 16x16; depthwise N4 C144 56x56; grouped N32 C256 64x64 g64/128/256; "
-                   "dense N8 C32->64 256x256 5x9; fused N64 C8->32 256x256 3x3 + bias, scale, sigmoid, GN(8))",
-                   "cold_buffer_sets": not args.warm},
+        "config": {"workload": workload_text(names, known), "cold_buffer_sets": not args.warm},
         "geomean": {
             "step_gbs": value,
             "step_gflops": geomean([r["step"]["gflops"] for r in out_rows]),

@@ -129,3 +129,15 @@ WORKLOADS = {
 }
 
 ROW_ORDER = list(WORKLOADS)
+
+# Depthwise layers (padding R // 2, batch 16) of MobileNet-, EfficientNet- and
+# ConvNeXt-style networks: the general-geometry shapes measured beside the
+# five workloads (not part of the benchmark step).
+EXTRA_WORKLOADS = {
+    "dw3s2_mobilenet_144x112": Workload("dw3s2_mobilenet_144x112", 16, 144, 112, 112, 144, 3, 3, 2, 1, 1, 144,
+                                        211, ("uniform", -1.0, 1.0), _u(1 / 3)),
+    "dw5_efficientnet_240x28": Workload("dw5_efficientnet_240x28", 16, 240, 28, 28, 240, 5, 5, 1, 2, 1, 240,
+                                        212, ("uniform", -1.0, 1.0), _u(1 / 5)),
+    "dw7_convnext_96x56": Workload("dw7_convnext_96x56", 16, 96, 56, 56, 96, 7, 7, 1, 3, 1, 96,
+                                   213, ("uniform", -1.0, 1.0), _u(1 / 7)),
+}

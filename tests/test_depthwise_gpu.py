@@ -49,13 +49,10 @@ SMALL = [
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
-# networks at batch 16: compared on sampled outputs (random ones plus every
-# border pixel of a few planes).
-FULL = [
-    _dw("dw3s2_mobilenet_144x112", 16, 144, 112, 112, 3, 2, 211),
-    _dw("dw5_efficientnet_240x28", 16, 240, 28, 28, 5, 1, 212),
-    _dw("dw7_convnext_96x56", 16, 96, 56, 56, 7, 1, 213),
-]
+# networks at batch 16 (the shapes the benchmark can time beside the five
+# workloads): compared on sampled outputs (random ones plus every border pixel
+# of a few planes).
+FULL = list(synth.EXTRA_WORKLOADS.values())
 
 
 def _dev(a):
