@@ -1,5 +1,6 @@
-// k_depthwise.hip -- depthwise K x K convolution, zero padding K/2, dilation 1:
-// K = 5 or 7 at stride 1, and K = 3 at stride 2.  The GroupConv Atlas
+// k_depthwise.hip -- depthwise K x K convolution with zero padding
+// dilation * (K/2) ("same" padding): K = 5 or 7 at stride 1, K = 3 or 5 at
+// stride 2, and K = 3 at dilation 2 (stride 1).  The GroupConv Atlas
 // project page's direct kernel (k0, "Direct mapping") takes any geometry;
 // its k3 card computes four adjacent outputs per thread.  This kernel is the
 // four-outputs-per-lane form for these depthwise geometries.  VALU
@@ -10,7 +11,7 @@
 //  - a wave owns whole output rows of one (n, channel) plane; a lane owns
 //    RB output rows x 4 output columns;
 //  - per input row it needs, a lane reads its own ST*4 input columns (one or
-//    two 16-byte buffer loads, zero outside the image) and takes the K/2
+//    two 16-byte buffer loads, zero outside the image) and takes the padding
 //    columns to its left and the columns past its right edge from the
 //    neighbouring lanes with cross-lane moves;
 //  - no LDS, no barriers; rows shared by neighbouring lanes and waves come
@@ -35,16 +36,17 @@ struct DwParams {
     int waves;    // N * C * wpp
 };
 
-template <int KS, int ST>
+template <int KS, int ST, int DL>
 __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__restrict__ x,
                                                                 const float *__restrict__ w,
                                                                 const float *__restrict__ bias,
                                                                 float *__restrict__ y, DwParams p) {
-    constexpr int PAD = KS / 2;
-    constexpr int NIR = ST * (kRB - 1) + KS;   // input rows a lane reads
-    constexpr int OWN = 4 * ST;                // input columns a lane loads itself
-    constexpr int RIGHT = KS - PAD - ST;       // columns needed past the lane's own ones
-    constexpr int WL = PAD + OWN + RIGHT;      // window: input columns ST*oc - PAD ...
+    constexpr int PAD = DL * (KS / 2);
+    constexpr int SPAN = DL * (KS - 1) + 1;          // input rows (columns) one output sees
+    constexpr int NIR = ST * (kRB - 1) + SPAN;       // input rows a lane reads
+    constexpr int OWN = 4 * ST;                      // input columns a lane loads itself
+    constexpr int RIGHT = SPAN - PAD - ST;           // columns needed past the lane's own ones
+    constexpr int WL = PAD + OWN + RIGHT;            // window: input columns ST*oc0 - PAD ...
     static_assert(PAD <= OWN && RIGHT >= 0 && RIGHT <= OWN, "neighbour exchange reaches one lane");
 
     const int lane = threadIdx.x & 63;
@@ -104,14 +106,15 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
         }
 #pragma unroll
         for (int kr = 0; kr < KS; ++kr) {
-            // input row i feeds output row rr through kernel row kr when i = ST*rr + kr
-            if ((i - kr) % ST != 0) continue;
-            const int rr = (i - kr) / ST;
-            if (i < kr || rr >= kRB) continue;
+            // input row i feeds output row rr through kernel row kr when
+            // i = ST*rr + DL*kr
+            const int di = i - DL * kr;
+            if (di < 0 || di % ST != 0 || di / ST >= kRB) continue;
+            const int rr = di / ST;
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[rr][q] = fmaf(win[ST * q + s], wk[kr * KS + s], acc[rr][q]);
+                for (int q = 0; q < 4; ++q) acc[rr][q] = fmaf(win[ST * q + DL * s], wk[kr * KS + s], acc[rr][q]);
         }
     }
     if (!active) return;
@@ -125,23 +128,37 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
     }
 }
 
-template <int KS, int ST>
+template <int KS, int ST, int DL>
 hipError_t launch_t(const DwParams &p, const float *x, const float *w, const float *bias, float *y,
                     hipStream_t st) {
     const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
-    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
+namespace {
+
+// The instantiated (K, stride, dilation) triples: 0 if none.
+int variant_of(int ks, int st, int dl) {
+    if (ks == 5 && st == 1 && dl == 1) return 1;
+    if (ks == 7 && st == 1 && dl == 1) return 2;
+    if (ks == 3 && st == 2 && dl == 1) return 3;
+    if (ks == 5 && st == 2 && dl == 1) return 4;
+    if (ks == 3 && st == 1 && dl == 2) return 5;
+    return 0;
+}
+
+}  // namespace
+
 bool depthwise_supported(const gconv_desc *d) {
-    if (d->cin != 1 || d->cout != 1 || d->R != d->S || d->dil_h != 1 || d->dil_w != 1) return false;
-    const int ks = d->R;
-    if (d->pad_h != ks / 2 || d->pad_w != ks / 2 || d->stride_h != d->stride_w) return false;
-    const int st = d->stride_h;
-    if (!((ks == 5 && st == 1) || (ks == 7 && st == 1) || (ks == 3 && st == 2))) return false;
+    if (d->cin != 1 || d->cout != 1 || d->R != d->S) return false;
+    if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;
+    const int ks = d->R, st = d->stride_h, dl = d->dil_h;
+    if (d->pad_h != dl * (ks / 2) || d->pad_w != dl * (ks / 2)) return false;
+    if (!variant_of(ks, st, dl)) return false;
     // whole 4-column output groups, one lane's own input columns in whole
     // 16-byte pieces, a row within one wave, buffer offsets in 32 bits
     if (d->Wo < 4 || d->Wo % 4 != 0 || d->Wo / 4 > 64 || d->Ho < 1) return false;
@@ -165,9 +182,13 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
     const long long waves = (long long)d->N * d->C * p.wpp;
     if (waves > 0x7fffffffLL - 64) return hipErrorInvalidConfiguration;
     p.waves = (int)waves;
-    if (d->R == 5) return launch_t<5, 1>(p, x, w, bias, y, st);
-    if (d->R == 7) return launch_t<7, 1>(p, x, w, bias, y, st);
-    return launch_t<3, 2>(p, x, w, bias, y, st);
+    switch (variant_of(d->R, d->stride_h, d->dil_h)) {
+        case 1: return launch_t<5, 1, 1>(p, x, w, bias, y, st);
+        case 2: return launch_t<7, 1, 1>(p, x, w, bias, y, st);
+        case 3: return launch_t<3, 2, 1>(p, x, w, bias, y, st);
+        case 4: return launch_t<5, 2, 1>(p, x, w, bias, y, st);
+        default: return launch_t<3, 1, 2>(p, x, w, bias, y, st);
+    }
 }
 
 }  // namespace gconv

@@ -72,7 +72,8 @@ extern "C" {
 #define GCONV_ALGO_DIRECT 1     /* one output per lane, any geometry                           */
 #define GCONV_ALGO_GROUPED3X3 2 /* 3x3 stride 1 pad 1 dil 1, <= 4 input channels per group     */
 #define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
-#define GCONV_ALGO_DEPTHWISE 4  /* depthwise 5x5/7x7 stride 1 or 3x3 stride 2, padding K/2     */
+#define GCONV_ALGO_DEPTHWISE 4  /* depthwise KxK, padding dil*(K/2): (K, stride, dil) = (5,1,1),
+                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2)                          */
 
 /* How conv_fused_gn_fwd organizes its passes (conv_desc_set_fused_variant). */
 #define GCONV_FUSED_AUTO 0

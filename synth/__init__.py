@@ -130,9 +130,10 @@ WORKLOADS = {
 
 ROW_ORDER = list(WORKLOADS)
 
-# Depthwise layers (padding R // 2, batch 16) of MobileNet-, EfficientNet- and
-# ConvNeXt-style networks: the general-geometry shapes measured beside the
-# five workloads (not part of the benchmark step).
+# Depthwise layers ("same" padding dil * (R // 2), batch 16) of MobileNet-,
+# EfficientNet-, ConvNeXt- and atrous (dilated) networks: the
+# general-geometry shapes measured beside the five workloads (not part of
+# the benchmark step).
 EXTRA_WORKLOADS = {
     "dw3s2_mobilenet_144x112": Workload("dw3s2_mobilenet_144x112", 16, 144, 112, 112, 144, 3, 3, 2, 1, 1, 144,
                                         211, ("uniform", -1.0, 1.0), _u(1 / 3)),
@@ -140,4 +141,8 @@ EXTRA_WORKLOADS = {
                                         212, ("uniform", -1.0, 1.0), _u(1 / 5)),
     "dw7_convnext_96x56": Workload("dw7_convnext_96x56", 16, 96, 56, 56, 96, 7, 7, 1, 3, 1, 96,
                                    213, ("uniform", -1.0, 1.0), _u(1 / 7)),
+    "dw5s2_efficientnet_144x56": Workload("dw5s2_efficientnet_144x56", 16, 144, 56, 56, 144, 5, 5, 2, 2, 1, 144,
+                                          214, ("uniform", -1.0, 1.0), _u(1 / 5)),
+    "dw3d2_atrous_576x32": Workload("dw3d2_atrous_576x32", 16, 576, 32, 32, 576, 3, 3, 1, 2, 2, 576,
+                                    215, ("uniform", -1.0, 1.0), _u(1 / 3)),
 }

@@ -1,5 +1,6 @@
-"""GPU parity of the depthwise kernel (5x5 and 7x7 at stride 1, 3x3 at
-stride 2, padding R // 2) through the C ABI against the CPU oracle.
+"""GPU parity of the depthwise kernel (5x5 and 7x7 at stride 1, 3x3 and 5x5
+at stride 2, 3x3 at dilation 2; padding dil * (R // 2)) through the C ABI
+against the CPU oracle.
 
 Same bars as the other parity tests: |y_gpu - y_oracle| <= 1e-4 * A + 1e-6
 with A = sum |x * w| over the receptive field; bit-for-bit equality for
@@ -25,8 +26,8 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _dw(name, N, C, H, W, R, stride, seed):
-    return synth.Workload(name, N, C, H, W, C, R, R, stride, R // 2, 1, C, seed,
+def _dw(name, N, C, H, W, R, stride, seed, dil=1):
+    return synth.Workload(name, N, C, H, W, C, R, R, stride, dil * (R // 2), dil, C, seed,
                           ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0))
 
 
@@ -46,6 +47,12 @@ SMALL = [
     _dw("dw3s2_h33_w512", 1, 2, 33, 512, 3, 2, 208),
     _dw("dw3s2_h2_w16", 4, 3, 2, 16, 3, 2, 209),
     _dw("dw3s2_h30_w56_planes", 4, 48, 30, 56, 3, 2, 210),
+    _dw("dw5s2_h9_w8", 2, 5, 9, 8, 5, 2, 216),
+    _dw("dw5s2_h27_w512", 1, 3, 27, 512, 5, 2, 217),
+    _dw("dw5s2_h2_w24_planes", 8, 40, 2, 24, 5, 2, 218),
+    _dw("dw3d2_h11_w12", 2, 5, 11, 12, 3, 1, 219, dil=2),
+    _dw("dw3d2_h3_w256", 1, 3, 3, 256, 3, 1, 220, dil=2),
+    _dw("dw3d2_h17_w4_planes", 8, 36, 17, 4, 3, 1, 221, dil=2),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style

@@ -250,11 +250,13 @@ def test_per_axis_descriptor_rejects_bad_values():
 
 
 def test_depthwise_dispatch():
-    # (C, H, W, R, stride, pad): depthwise 5x5 / 7x7 stride 1 and 3x3 stride 2,
-    # padding R // 2, output width a multiple of 4 up to 256
-    taken = [(16, 20, 20, 5, 1, 2), (16, 9, 256, 7, 1, 3), (8, 7, 8, 3, 2, 1), (8, 33, 512, 3, 2, 1)]
-    for C, H, W, R, st, pad in taken:
-        d = gc.conv_desc_create(2, C, H, W, C, R, R, st, pad, 1, C)
+    # (C, H, W, R, stride, pad, dil): depthwise 5x5 / 7x7 stride 1, 3x3 / 5x5
+    # stride 2, 3x3 dilation 2, padding dil * (R // 2), output width a
+    # multiple of 4 up to 256
+    taken = [(16, 20, 20, 5, 1, 2, 1), (16, 9, 256, 7, 1, 3, 1), (8, 7, 8, 3, 2, 1, 1), (8, 33, 512, 3, 2, 1, 1),
+             (8, 9, 8, 5, 2, 2, 1), (8, 30, 512, 5, 2, 2, 1), (8, 11, 12, 3, 1, 2, 2), (8, 5, 256, 3, 1, 2, 2)]
+    for C, H, W, R, st, pad, dil in taken:
+        d = gc.conv_desc_create(2, C, H, W, C, R, R, st, pad, dil, C)
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, H, W, R, st, pad)
         gc.conv_desc_set_algo(d, gc.ALGO_DIRECT)
         gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
@@ -263,8 +265,11 @@ def test_depthwise_dispatch():
         (2, 16, 20, 22, 16, 5, 5, 1, 2, 1, 16),    # output width not a multiple of 4
         (2, 16, 20, 520, 16, 5, 5, 1, 2, 1, 16),   # output row wider than one wave
         (2, 16, 20, 21, 16, 3, 3, 2, 1, 1, 16),    # stride 2 with an odd input width
-        (2, 16, 20, 20, 16, 5, 5, 2, 2, 1, 16),    # 5x5 at stride 2
-        (2, 16, 20, 20, 16, 5, 5, 1, 4, 2, 16),    # dilation 2
+        (2, 16, 20, 20, 16, 7, 7, 2, 3, 1, 16),    # 7x7 at stride 2
+        (2, 16, 20, 20, 16, 5, 5, 1, 4, 2, 16),    # 5x5 at dilation 2
+        (2, 16, 20, 20, 16, 3, 3, 2, 2, 2, 16),    # 3x3 at stride 2 and dilation 2
+        (2, 16, 20, 20, 16, 3, 3, 1, 1, 2, 16),    # dilation 2 with padding 1
+        (2, 16, 21, 21, 16, 5, 5, 2, 2, 1, 16),    # 5x5 stride 2 with an odd input width
         (2, 16, 20, 20, 32, 5, 5, 1, 2, 1, 16),    # two output channels per group
         (2, 16, 20, 20, 8, 5, 5, 1, 2, 1, 8),      # two input channels per group
     ]
@@ -274,6 +279,7 @@ def test_depthwise_dispatch():
         with pytest.raises(gc.GconvError) as ei:
             gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
         assert ei.value.status == gc.GCONV_ERR_UNSUPPORTED
-    # per-axis: unequal padding is refused
-    d = gc.conv_desc_create_2d(2, 16, 20, 20, 16, 5, 5, (1, 1), (2, 1), (1, 1), 16)
-    assert gc.conv_desc_get_algo(d) != gc.ALGO_DEPTHWISE
+    # per-axis: unequal padding, stride or dilation is refused
+    for st, pad, dil in [((1, 1), (2, 1), (1, 1)), ((2, 1), (2, 2), (1, 1)), ((1, 1), (2, 2), (1, 2))]:
+        d = gc.conv_desc_create_2d(2, 16, 20, 20, 16, 5, 5, st, pad, dil, 16)
+        assert gc.conv_desc_get_algo(d) != gc.ALGO_DEPTHWISE
