@@ -316,9 +316,28 @@ def cpu_baseline(rows):
             % (r.name, n, reps, dt, per_row[r.name]["gbs"], per_row[r.name]["gflops"]))
     return dict(value=geomean([v["gbs"] for v in per_row.values()]),
                 unit="GB/s (geomean of rows, oracle fp64 on the host)", cores=threads, kind="oracle",
+                cpu_model=cpu_model(),
                 sample="each row on its first n images (repeated when the whole batch is short): " +
                        ", ".join("%s n=%d x%d" % (k, v["samples_n"], v["repeats"]) for k, v in per_row.items()),
                 seconds=total, rows=per_row)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measured_floor_s(acct, wl, peaks):
+    """Floor time against what this GPU sustains: the measured copy rate and
+    the measured FP32 MFMA (dense rows) or FMA (grouped rows) peak."""
+    peak = peaks["fp32_mfma_tflops"] if wl.groups == 1 else peaks["fp32_fma_tflops"]
+    return max(acct["bytes"] / (peaks["hbm_copy_gbs"] * 1e9), acct["flops"] / (peak * 1e12))
 
 
 # ------------------------------------------------------------------ main
@@ -362,6 +381,10 @@ def main():
     torch.cuda.set_device(0)
     copy = copy_calibration(torch)
     log("[bench] plain copy of %d MiB: %.1f GB/s (read + write)" % (COPY_BYTES >> 20, copy["gbs"]))
+    sink = torch.zeros(4, device="cuda")
+    mfma_meas, fma_meas = gc.gconv_probe_peaks(sink)
+    peaks = dict(fp32_mfma_tflops=mfma_meas, fp32_fma_tflops=fma_meas, hbm_copy_gbs=copy["gbs"])
+    log("[bench] measured peaks: FP32 MFMA %.1f TFLOP/s, FP32 FMA %.1f TFLOP/s" % (mfma_meas, fma_meas))
     if args.copy_only:
         print(json.dumps({"copy_calibration": copy}), flush=True)
         return
@@ -416,6 +439,7 @@ def main():
                    floor_us=r.acct["floor_s"] * 1e6, buffer_sets=r.nsets)
         rec["step"] = r.figures(med)
         rec["step"]["mean_ms"] = float(np.mean(step_times[r.name])) * 1e3
+        rec["floor_us_measured_peaks"] = measured_floor_s(r.acct, r.wl, peaks) * 1e6
         out_rows.append(rec)
         log("[bench] %-20s step  %.4f ms  %8.1f GB/s  %8.1f GFLOP/s  frac %.3f"
             % (r.name, rec["step"]["ms"], rec["step"]["gbs"], rec["step"]["gflops"], rec["step"]["roofline_frac"]))
@@ -434,6 +458,11 @@ def main():
             log("[bench] %-20s graph %.4f ms [%.4f, %.4f]  sync %.4f ms [%.4f, %.4f]"
                 % (r.name, rec["graph"]["ms"], *rec["graph"]["ci95_ms"], rec["sync"]["ms"], *rec["sync"]["ci95_ms"]))
 
+    for rec in out_rows:
+        for key in ("step", "graph", "sync"):
+            if key in rec:
+                rec[key]["roofline_frac_measured_peaks"] = rec["floor_us_measured_peaks"] / (rec[key]["ms"] * 1e3)
+
     # ---- dominant kernel roofline (single-kernel rows: one launch = one kernel)
     single = [(rec, r) for rec, r in zip(out_rows, rows) if not r.wl.fused]
     dom_rec, dom_row = max(single, key=lambda t: t[0]["step"]["mean_ms"]) if single else (None, None)
@@ -443,10 +472,12 @@ def main():
         if dom_rec["bound"] == "mfma":
             achieved = dom_rec["flops"] / t / 1e12
             roof = dict(bound="mfma", achieved=achieved, peak=FP32_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=achieved / FP32_MFMA_PEAK_TFLOPS)
+                        frac=achieved / FP32_MFMA_PEAK_TFLOPS, measured_peak=peaks["fp32_mfma_tflops"],
+                        frac_of_measured_peak=achieved / peaks["fp32_mfma_tflops"])
         else:
             achieved = dom_rec["bytes"] / t / 1e9
-            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS)
+            roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
+                        measured_peak=peaks["hbm_copy_gbs"], frac_of_measured_peak=achieved / peaks["hbm_copy_gbs"])
         roof.update(traffic=measured_traffic(dom_row.algo, dom_rec["name"]), traffic_unit="bytes per launch",
                     algorithmic_bytes=dom_rec["bytes"], algorithmic_flops=dom_rec["flops"],
                     kernel=dom_row.algo, row=dom_rec["name"],
@@ -467,6 +498,7 @@ def main():
         },
         "roofline": roof,
         "hbm_copy_calibration": copy,
+        "measured_peaks": peaks,
         "rows": out_rows,
     }
     if not args.no_boundaries:
@@ -478,6 +510,9 @@ def main():
             result["geomean"]["graph_roofline_frac_bandwidth_rows"] = geomean([r["graph"]["roofline_frac"] for r in bw])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(rows)
+        for rec in out_rows:
+            c = result["cpu_baseline"]["rows"][rec["name"]]
+            c["gpu_step_speedup"] = rec["step"]["gbs"] / c["gbs"]
     print(json.dumps(result), flush=True)
 
 

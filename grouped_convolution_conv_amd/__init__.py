@@ -37,7 +37,7 @@ FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recom
 EXPORTED = (
     "conv_desc_create", "conv_desc_create_2d", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
     "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
-    "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "gconv_time_graph",
+    "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "gconv_time_graph", "gconv_probe_peaks",
     "gconv_status_string", "gconv_last_launch_error",
 )
 
@@ -67,6 +67,7 @@ _lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
 _lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
 _lib.gconv_time_graph.argtypes = [_p, _i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _p, _p, _p, _p, _p, _i,
                                   ctypes.c_float, _p, _sz, _i, _i, ctypes.POINTER(ctypes.c_float), _p]
+_lib.gconv_probe_peaks.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _p, _p]
 _lib.gconv_status_string.argtypes = [_i]
 _lib.gconv_status_string.restype = ctypes.c_char_p
 _lib.gconv_last_launch_error.argtypes = []
@@ -243,6 +244,14 @@ def gconv_time_graph(desc: ConvDesc, xs, ys, w, bias=None, launches: int = 1, re
     _check("gconv_time_graph", _lib.gconv_time_graph(desc.handle, fl, xa, ya, n, _ptr(w), _ptr(bias), sc, ga, be, gg,
                                                      eps, wsp, wsb, launches, replays, out, _stream(stream)))
     return list(out)
+
+
+def gconv_probe_peaks(sink, stream=None):
+    """Measured (FP32 MFMA, non-packed FP32 FMA) peaks of the current GPU in
+    TFLOP/s.  sink: a device tensor (or raw pointer) of at least 4 bytes."""
+    m, f = ctypes.c_float(), ctypes.c_float()
+    _check("gconv_probe_peaks", _lib.gconv_probe_peaks(ctypes.byref(m), ctypes.byref(f), _ptr(sink), _stream(stream)))
+    return float(m.value), float(f.value)
 
 
 def library():

@@ -60,7 +60,9 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             msg = "\n".join("%s:\n%s" % (s, t) for s, t in failed)
             raise RuntimeError("hipcc failed:\n" + msg)
         tmp_lib = LIB + ".tmp%d" % os.getpid()
-        link = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp_lib] + objs
+        # every symbol resolved at link time: a kernel whose host launch stub
+        # is missing fails the build, not the first load
+        link = [HIPCC, "-shared", "-fPIC", "-Wl,--no-undefined", "--offload-arch=" + ARCH, "-o", tmp_lib] + objs
         subprocess.run(link, check=True)
         os.replace(tmp_lib, LIB)
     return LIB

@@ -93,3 +93,97 @@ extern "C" int gconv_time_graph(gconv_desc_t desc, int fused, const float *const
     }
     return GCONV_OK;
 }
+
+// ---------------------------------------------------------------------------
+// Measured compute peaks.  Fractions of the published peaks say how far a
+// kernel is from the datasheet; fractions of what the chip sustains under
+// load (clocks drop under a full MFMA load) say how far it is from what is
+// reachable.  Two register-only probes, each one timed launch after one
+// warm-up launch on every CU: chains of v_mfma_f32_32x32x2f32 (four
+// independent accumulators per wave) and chains of non-packed FP32 FMAs
+// (eight independent per lane).  No memory is touched but one store that
+// only a value the arithmetic cannot produce would trigger, which keeps the
+// loops from being optimized away.
+
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+constexpr int kProbeBlock = 256;
+constexpr int kMfmaChains = 4;
+constexpr int kFmaChains = 8;
+constexpr float kNever = -3.0e38f;  // below anything the probes compute
+
+__global__ __launch_bounds__(kProbeBlock) void mfma_peak_kernel(float *sink, int iters) {
+    floatx16 acc[kMfmaChains];
+    for (int i = 0; i < kMfmaChains; ++i)
+        for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+    const float a = 1.0f + (float)threadIdx.x * 1e-7f, b = 0.5f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kMfmaChains; ++i) acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i], 0, 0, 0);
+    }
+    float s = 0.0f;
+    for (int i = 0; i < kMfmaChains; ++i)
+        for (int v = 0; v < 16; ++v) s += acc[i][v];
+    if (s == kNever) sink[0] = s;
+}
+
+__global__ __launch_bounds__(kProbeBlock) void fma_peak_kernel(float *sink, int iters) {
+    float v[kFmaChains];
+    for (int i = 0; i < kFmaChains; ++i) v[i] = (float)threadIdx.x * 1e-3f + (float)i;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kFmaChains; ++i) v[i] = fmaf(v[i], 0.999f, 0.001f);
+    }
+    float s = 0.0f;
+    for (int i = 0; i < kFmaChains; ++i) s += v[i];
+    if (s == kNever) sink[0] = s;
+}
+
+struct EventPair {
+    hipEvent_t a = nullptr, b = nullptr;
+    ~EventPair() {
+        if (a) (void)hipEventDestroy(a);
+        if (b) (void)hipEventDestroy(b);
+    }
+};
+
+// Milliseconds of one launch of `kern` (after one warm-up launch).
+template <typename K>
+int time_probe(K kern, int blocks, float *sink, int iters, hipStream_t st, float *ms) {
+    EventPair ev;
+    if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return GCONV_ERR_LAUNCH;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kProbeBlock), 0, st, sink, iters);
+    if (hipEventRecord(ev.a, st) != hipSuccess) return GCONV_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kProbeBlock), 0, st, sink, iters);
+    if (hipEventRecord(ev.b, st) != hipSuccess) return GCONV_ERR_LAUNCH;
+    if (hipGetLastError() != hipSuccess) return GCONV_ERR_LAUNCH;
+    if (hipEventSynchronize(ev.b) != hipSuccess) return GCONV_ERR_LAUNCH;
+    if (hipEventElapsedTime(ms, ev.a, ev.b) != hipSuccess || !(*ms > 0.0f)) return GCONV_ERR_LAUNCH;
+    return GCONV_OK;
+}
+
+}  // namespace
+
+extern "C" int gconv_probe_peaks(float *mfma_tflops, float *fma_tflops, float *sink, void *stream) {
+    if (!mfma_tflops || !fma_tflops || !sink) return GCONV_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return GCONV_ERR_LAUNCH;
+    const int blocks = 4 * cus;  // four workgroups (16 waves) per CU
+    // about 2 ms per probe at the published peaks
+    const int mfma_iters = 4096, fma_iters = 32768;
+    float ms = 0.0f;
+    int rc = time_probe(mfma_peak_kernel, blocks, sink, mfma_iters, st, &ms);
+    if (rc != GCONV_OK) return rc;
+    const double mfma_flops = (double)blocks * (kProbeBlock / 64) * mfma_iters * kMfmaChains * (32.0 * 32.0 * 2.0 * 2.0);
+    *mfma_tflops = (float)(mfma_flops / (ms * 1e-3) / 1e12);
+    rc = time_probe(fma_peak_kernel, blocks, sink, fma_iters, st, &ms);
+    if (rc != GCONV_OK) return rc;
+    const double fma_flops = (double)blocks * kProbeBlock * fma_iters * kFmaChains * 2.0;
+    *fma_tflops = (float)(fma_flops / (ms * 1e-3) / 1e12);
+    return GCONV_OK;
+}

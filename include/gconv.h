@@ -176,6 +176,17 @@ int gconv_time_graph(gconv_desc_t desc, int fused, const float *const *xs, float
                      const float *beta, int gn_groups, float eps, void *workspace, size_t workspace_bytes,
                      int launches, int replays, float *ms_per_launch, void *stream);
 
+/* Measured compute peaks of the current device, for roofline fractions
+ * against what the chip sustains rather than its datasheet: *mfma_tflops
+ * from back-to-back FP32 MFMA (v_mfma_f32_32x32x2f32) chains, *fma_tflops
+ * from non-packed FP32 FMA chains, each one timed launch (after a warm-up
+ * launch) over four workgroups per CU on `stream` (a hipStream_t; NULL is the
+ * default stream).  sink: a caller-owned device buffer of at least 4 bytes that
+ * the probes never write in practice (it keeps their arithmetic alive).
+ * Synchronizes on the stream.  Returns GCONV_ERR_INVALID_ARG for a null
+ * argument, GCONV_ERR_LAUNCH if the runtime refuses a call. */
+int gconv_probe_peaks(float *mfma_tflops, float *fma_tflops, float *sink, void *stream);
+
 /* Static text for a status code. */
 const char *gconv_status_string(int status);
 

@@ -283,3 +283,12 @@ def test_depthwise_dispatch():
     for st, pad, dil in [((1, 1), (2, 1), (1, 1)), ((2, 1), (2, 2), (1, 1)), ((1, 1), (2, 2), (1, 2))]:
         d = gc.conv_desc_create_2d(2, 16, 20, 20, 16, 5, 5, st, pad, dil, 16)
         assert gc.conv_desc_get_algo(d) != gc.ALGO_DEPTHWISE
+
+
+def test_probe_peaks_validates_before_any_device_call():
+    lib = ctypes.CDLL(gc.LIB_PATH)
+    lib.gconv_probe_peaks.argtypes = [ctypes.c_void_p] * 4
+    f = ctypes.c_float()
+    assert lib.gconv_probe_peaks(None, ctypes.byref(f), ctypes.c_void_p(16), None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_peaks(ctypes.byref(f), None, ctypes.c_void_p(16), None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_peaks(ctypes.byref(f), ctypes.byref(f), None, None) == gc.GCONV_ERR_INVALID_ARG

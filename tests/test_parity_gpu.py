@@ -465,3 +465,16 @@ def test_per_axis_fused_matches_oracle():
         torch.cuda.synchronize()
         err = np.abs(y.cpu().numpy() - ref).max()
         assert err <= GN_ATOL, (variant, err)
+
+
+def test_probe_peaks_are_plausible():
+    """The measured FP32 MFMA and FMA peaks are positive and below the
+    datasheet's 157.3 TFLOP/s (FP32 matrix, and FP32 vector with packed
+    instructions: the ceiling for any FP32 vector code) with a little margin.
+    Non-packed FMA chains measure above half of it on gfx950."""
+    sink = torch.zeros(4, device="cuda")
+    mfma, fma = gc.gconv_probe_peaks(sink)
+    _say("[parity] measured peaks: MFMA %.1f TFLOP/s, FMA %.1f TFLOP/s" % (mfma, fma))
+    assert 20.0 < mfma < 170.0, mfma
+    assert 10.0 < fma < 165.0, fma
+    assert float(sink[0]) == 0.0
