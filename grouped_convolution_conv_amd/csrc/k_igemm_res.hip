@@ -33,6 +33,7 @@
 //  kNormalize   v as above, then out = (v - mean) * rstd * gamma + beta with
 //               the group statistics already merged, stored to y
 #include <atomic>
+#include <type_traits>
 
 #include "dev_common.h"
 #include "internal.h"
@@ -168,6 +169,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     //      pieces of a tile's band, zero outside the image
     float4 pf[NSLOT];
     float gpf = 0.0f;
+    // Tiles whose band lies wholly inside the image (VEC): a piece's offset
+    // is a per-lane part (channel, band row, column), the same for every
+    // tile and computed once here, plus the tile's corner, which is uniform
+    // and goes in the instruction's scalar offset.  Pieces past the band or
+    // past the input channels get an offset beyond every range.
+    int lane_off[NSLOT];
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i) {
+        const int f = i * kBlock + tid;
+        const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
+        const int lr = rem / P4, c4 = rem - lr * P4;
+        lane_off[i] = f < XE4 && cl < p.cin ? (cl * HW + lr * p.W + 4 * c4) * (int)sizeof(float) : kOutOfRange;
+    }
     auto load = [&](int v) __attribute__((always_inline)) {
         const int t = v % p.n_tiles, n = v / p.n_tiles;
         const int th = t / p.n_tw, tw = t - th * p.n_tw;
@@ -177,6 +191,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             const __amdgpu_buffer_rsrc_t gr = rsrc(ep.gstat + (size_t)n * ep.gn_groups, NGS * (int)sizeof(float));
             gpf = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                 gr, tid < NGS ? tid * (int)sizeof(float) : kOutOfRange, 0, 0));
+        }
+        if constexpr (VEC) {
+            if (ih0 >= 0 && ih0 + TIH <= p.H && iw0 >= 0 && iw0 + 4 * P4 <= p.W) {
+                const int corner = (ih0 * p.W + iw0) * (int)sizeof(float);
+#pragma unroll
+                for (int i = 0; i < NSLOT; ++i) {
+                    const int lo = lane_off[i];
+                    pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, corner, 0));
+                }
+                return;
+            }
         }
         // an opaque copy of the thread id: the per-slot offsets are the same
         // for every tile, and hoisting them out of the tile loop would keep
@@ -302,11 +327,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         // accumulator register v of block m holds channel m*32 + 8(v/4) +
         // 4h + v%4, local GroupNorm group lg = 8m + 2(v/4) + h (4 channels
         // per group)
-        float s1[MB][4];
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s1[m][q] = 0.0f;
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -332,7 +352,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                         if constexpr (kStatsMode) {
                             acc[m][nb][vv] = val;
                             if constexpr (MODE == kStatsStore) store_fast(nb, m, vv, val);
-                            s1[m][vv >> 2] += pix[nb] >= 0 ? val : 0.0f;
                         } else {
                             store_fast(nb, m, vv, fmaf(val, gk, ck));
                         }
@@ -349,27 +368,46 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             const float inv = count > 0.0f ? 1.0f / count : 0.0f;
             const __amdgpu_buffer_rsrc_t ps = rsrc(ep.parts + (size_t)n * ep.gn_groups * (NWAVE * p.n_tiles),
                                                    p.parts_bytes);
+            // both passes skip the pixel masks when the wave's rows lie wholly
+            // inside the output (most tiles), which the masks would otherwise
+            // cost once per output and pass
+            auto stats = [&](auto masked) __attribute__((always_inline)) {
+                constexpr bool kMask = decltype(masked)::value;
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+                for (int m = 0; m < MB; ++m)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float mu = half_wave_sum(s1[m][q]) * inv;
-                    float tq = 0.0f;
+                    for (int q = 0; q < 4; ++q) {
+                        float sq = 0.0f;
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
+                        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                        for (int uu = 0; uu < 4; ++uu) {
-                            const float dv = pix[nb] >= 0 ? acc[m][nb][4 * q + uu] - mu : 0.0f;
-                            tq = fmaf(dv, dv, tq);
+                            for (int uu = 0; uu < 4; ++uu) {
+                                const float v = acc[m][nb][4 * q + uu];
+                                sq += kMask ? (pix[nb] >= 0 ? v : 0.0f) : v;
+                            }
+                        const float mu = half_wave_sum(sq) * inv;
+                        float tq = 0.0f;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                            for (int uu = 0; uu < 4; ++uu) {
+                                const float d = acc[m][nb][4 * q + uu] - mu;
+                                const float dv = kMask ? (pix[nb] >= 0 ? d : 0.0f) : d;
+                                tq = fmaf(dv, dv, tq);
+                            }
                         }
+                        const float m2 = half_wave_sum(tq);
+                        const int idx = (8 * m + 2 * q + h) * (NWAVE * p.n_tiles) + t * NWAVE + wave;
+                        const u32x4 pt = {__builtin_bit_cast(unsigned int, count), __builtin_bit_cast(unsigned int, mu),
+                                          __builtin_bit_cast(unsigned int, m2), 0u};
+                        __builtin_amdgcn_raw_buffer_store_b128(pt, ps, j == 0 ? idx * (int)sizeof(Partial) : kOutOfRange,
+                                                               0, 0);
                     }
-                    const float m2 = half_wave_sum(tq);
-                    const int idx = (8 * m + 2 * q + h) * (NWAVE * p.n_tiles) + t * NWAVE + wave;
-                    const u32x4 pt = {__builtin_bit_cast(unsigned int, count), __builtin_bit_cast(unsigned int, mu),
-                                      __builtin_bit_cast(unsigned int, m2), 0u};
-                    __builtin_amdgcn_raw_buffer_store_b128(pt, ps, j == 0 ? idx * (int)sizeof(Partial) : kOutOfRange,
-                                                           0, 0);
-                }
+            };
+            if (oh0 + kNBR <= p.Ho && ow0 + kTW <= p.Wo)
+                stats(std::false_type{});
+            else
+                stats(std::true_type{});
         }
     };
 
