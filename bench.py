@@ -61,6 +61,12 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="one buffer set per row (cache-warm)")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only the plain device-copy calibration (known byte count per launch)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the 80-shape grouped 3x3 grid instead of the shape rows: the dispatcher's "
+                         "choice against the direct kernel and PyTorch's conv2d, paired batches")
+    ap.add_argument("--sweep-shapes", default="", help="comma-separated subset of the grid (default: all 80)")
+    ap.add_argument("--sweep-out", default="", help="write the per-shape sweep records to this JSON file")
+    ap.add_argument("--sweep-no-torch", action="store_true", help="leave PyTorch's conv2d out of the sweep")
     return ap.parse_args()
 
 
@@ -340,6 +346,264 @@ def measured_floor_s(acct, wl, peaks):
     return max(acct["bytes"] / (peaks["hbm_copy_gbs"] * 1e9), acct["flops"] / (peak * 1e12))
 
 
+# ------------------------------------------------------------------ shape sweep
+
+PRACTICAL = 1.05   # a ratio counts only when its whole 95% interval clears 5%
+
+
+def paired_ratio(base_batches, cand_batches, n_boot=10000, seed=0):
+    """base / candidate latency from paired batches (the GroupConv Atlas's
+    "ten paired batches, 95% bootstrap intervals, 5% practical threshold").
+
+    Each batch gives the ratio of the two medians; the point estimate is the
+    geometric mean over batches and the interval comes from resampling the
+    batches.  A shape is a "win" for the candidate when the whole interval lies
+    above 1.05, a "loss" when it lies below 1/1.05, and a "tie" otherwise."""
+    lr = np.log([np.median(b) / np.median(c) for b, c in zip(base_batches, cand_batches)])
+    rng = np.random.default_rng(seed)
+    means = lr[rng.integers(0, lr.size, size=(n_boot, lr.size))].mean(axis=1)
+    lo, hi = float(np.exp(np.percentile(means, 2.5))), float(np.exp(np.percentile(means, 97.5)))
+    cls = "win" if lo > PRACTICAL else ("loss" if hi < 1.0 / PRACTICAL else "tie")
+    return dict(ratio=float(np.exp(lr.mean())), ci95=[lo, hi], cls=cls)
+
+
+def _launches_for(seconds_per_launch, target=0.5e-3):
+    return int(min(400, max(2, math.ceil(target / max(seconds_per_launch, 1e-6)))))
+
+
+class LibCandidate:
+    """One library descriptor (AUTO or a forced algorithm) on fixed buffers."""
+
+    def __init__(self, gc, torch, wl, x, w, algo):
+        self.gc, self.torch = gc, torch
+        self.d = gc.conv_desc_create(wl.N, wl.C, wl.H, wl.W, wl.K, wl.R, wl.S, wl.stride, wl.pad, wl.dil, wl.groups)
+        gc.conv_desc_set_algo(self.d, algo)
+        self.algo = gc.ALGO_NAMES[gc.conv_desc_get_algo(self.d)]
+        ho, wo = gc.conv_desc_get_output_dims(self.d)
+        self.x, self.w = x, w
+        self.y = torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda")
+        self.px, self.pw, self.py = x.data_ptr(), w.data_ptr(), self.y.data_ptr()
+        self.side = torch.cuda.Stream()
+        self.sh = torch.cuda.current_stream().cuda_stream
+
+    def launch(self):
+        self.gc.conv_fwd(self.d, self.px, self.pw, None, self.py, stream=self.sh)
+
+    def output(self):
+        return self.y
+
+    def graph(self, R, n):
+        self.side.wait_stream(self.torch.cuda.current_stream())
+        ms = self.gc.gconv_time_graph(self.d, [self.x], [self.y], self.w, None, launches=R, replays=n,
+                                      stream=self.side)
+        self.torch.cuda.current_stream().wait_stream(self.side)
+        return [m / 1e3 for m in ms]
+
+
+class TorchCandidate:
+    """PyTorch's conv2d on ROCm (MIOpen): another system, timed as context."""
+
+    algo = "torch"
+
+    def __init__(self, torch, wl, x, w):
+        import torch.nn.functional as F
+        self.torch, self.groups = torch, wl.groups
+        self.fn = lambda: F.conv2d(x, w, None, wl.stride, wl.pad, wl.dil, wl.groups)
+        self.g, self.gR, self.graph_error = None, 0, None
+
+    def launch(self):
+        self.fn()
+
+    def output(self):
+        return self.fn()
+
+    def graph(self, R, n):
+        torch = self.torch
+        if self.graph_error is not None:
+            return None
+        if self.g is None or self.gR != R:
+            try:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for _ in range(R):
+                        self.fn()
+                self.g, self.gR = g, R
+            except RuntimeError as e:  # capture not supported for this call
+                self.graph_error = str(e).splitlines()[0]
+                torch.cuda.synchronize()
+                return None
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            a.record()
+            self.g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) / 1e3 / R for a, b in ev]
+
+
+def _event_time(torch, launch, reps=10):
+    for _ in range(3):
+        launch()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        launch()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3 / reps
+
+
+def _sync_samples(torch, launch, n):
+    out = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        launch()
+        torch.cuda.synchronize()
+        out.append(time.perf_counter() - t0)
+    return out
+
+
+def sweep_shape(wl, gc, torch, args):
+    import synth
+    inp = synth.make_inputs(wl)
+    x = torch.from_numpy(inp["x"]).cuda()
+    w = torch.from_numpy(inp["w"]).cuda()
+    cands = {"auto": LibCandidate(gc, torch, wl, x, w, gc.ALGO_AUTO),
+             "direct": LibCandidate(gc, torch, wl, x, w, gc.ALGO_DIRECT)}
+    if not args.sweep_no_torch:
+        cands["torch"] = TorchCandidate(torch, wl, x, w)
+    ho, wo = gc.conv_desc_get_output_dims(cands["auto"].d)
+    acct = row_accounting(wl, ho, wo)
+    rec = dict(name=wl.name, N=wl.N, C=wl.C, H=wl.H, W=wl.W, K=wl.K, groups=wl.groups, cpg=wl.C // wl.groups,
+               algo=cands["auto"].algo, bytes=acct["bytes"], flops=acct["flops"], floor_us=acct["floor_s"] * 1e6)
+
+    # verify before timing: every candidate's full output against PyTorch's
+    # FP32 conv2d, with the bar 1e-4 * sum|x*w| + 1e-6 (sum|x*w| from the same
+    # conv of |x| and |w|); the oracle check of the grid is a GPU test
+    import torch.nn.functional as F
+    ref = F.conv2d(x, w, None, wl.stride, wl.pad, wl.dil, wl.groups)
+    A = F.conv2d(x.abs(), w.abs(), None, wl.stride, wl.pad, wl.dil, wl.groups)
+    bound = 1e-4 * A + 1e-6
+    rec["check"] = {}
+    for k, c in cands.items():
+        c.launch()
+        torch.cuda.synchronize()
+        y = c.output()
+        ok = k == "torch" or bool(((y - ref).abs() <= bound).all().item())
+        rec["check"][k] = ("pass" if ok else "FAIL") if k != "torch" else "reference"
+    del ref, A
+
+    # per-candidate launch count for graph replays of ~0.5 ms
+    est = {k: _event_time(torch, c.launch) for k, c in cands.items()}
+    Rs = {k: _launches_for(t) for k, t in est.items()}
+    boundaries = {"graph": {k: [] for k in cands}, "sync": {k: [] for k in cands}}
+    keys = list(cands)
+    for b in range(args.batches):
+        order = keys[b % len(keys):] + keys[:b % len(keys)]
+        for k in order:
+            g = cands[k].graph(Rs[k], args.samples)
+            if g is not None:
+                boundaries["graph"][k].append(g)
+        for k in order:
+            boundaries["sync"][k].append(_sync_samples(torch, cands[k].launch, args.samples))
+    rec["launches_per_replay"] = Rs
+    for bname, per in boundaries.items():
+        out = {}
+        for k, batches in per.items():
+            if len(batches) != args.batches:
+                out[k] = None
+                continue
+            flat = [v for bt in batches for v in bt]
+            m, lo, hi = boot_ci(flat, n_boot=2000)
+            out[k] = dict(us=m * 1e6, ci95_us=[lo * 1e6, hi * 1e6])
+            if k == "auto":
+                out[k].update(gbs=acct["bytes"] / m / 1e9, gflops=acct["flops"] / m / 1e9,
+                              roofline_frac=acct["floor_s"] / m)
+        for base in keys:
+            if base == "auto" or out.get(base) is None or out.get("auto") is None:
+                continue
+            out[base + "_over_auto"] = paired_ratio(per[base], per["auto"])
+        rec[bname] = out
+    if "torch" in cands and cands["torch"].graph_error:
+        rec["torch_graph_error"] = cands["torch"].graph_error
+    del cands, x, w
+    return rec
+
+
+def sweep(args):
+    import torch
+    import synth
+    import grouped_convolution_conv_amd as gc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    # "tuned PyTorch": MIOpen searches for its fastest solution per shape on
+    # the first call (outside every timed region); FP32 arithmetic only
+    torch.backends.cudnn.benchmark = True
+    torch.backends.cudnn.allow_tf32 = False
+    names = args.sweep_shapes.split(",") if args.sweep_shapes else list(synth.ATLAS_GRID)
+    unknown = [n for n in names if n not in synth.ATLAS_GRID]
+    if unknown:
+        print("bench.py: unknown grid shapes %s" % unknown, file=sys.stderr)
+        sys.exit(2)
+    log("[sweep] device:", torch.cuda.get_device_name(0), " shapes:", len(names))
+    t0 = time.perf_counter()
+    records = []
+    for i, n in enumerate(names):
+        rec = sweep_shape(synth.ATLAS_GRID[n], gc, torch, args)
+        records.append(rec)
+        g = rec["graph"]
+        parts = ["%-26s %-10s auto %8.2f us" % (n, rec["algo"], g["auto"]["us"])]
+        for base in ("direct", "torch"):
+            r = g.get(base + "_over_auto")
+            if r:
+                parts.append("%s/auto %6.2fx %-4s" % (base, r["ratio"], r["cls"]))
+        s = rec["sync"]
+        parts.append("| sync auto %7.2f us" % s["auto"]["us"])
+        if s.get("torch_over_auto"):
+            parts.append("torch/auto %5.2fx %s" % (s["torch_over_auto"]["ratio"], s["torch_over_auto"]["cls"]))
+        parts.append("check %s" % ",".join("%s:%s" % kv for kv in rec["check"].items()))
+        log("[sweep %2d/%d] " % (i + 1, len(names)) + "  ".join(parts))
+        torch.cuda.empty_cache()
+    summary = {}
+    for bname in ("graph", "sync"):
+        summary[bname] = {}
+        for base in ("direct", "torch"):
+            rs = [r[bname].get(base + "_over_auto") for r in records]
+            rs = [r for r in rs if r]
+            if not rs:
+                continue
+            summary[bname][base + "_over_auto"] = dict(
+                geomean=geomean([r["ratio"] for r in rs]), shapes=len(rs),
+                win=sum(r["cls"] == "win" for r in rs), tie=sum(r["cls"] == "tie" for r in rs),
+                loss=sum(r["cls"] == "loss" for r in rs))
+        summary[bname]["auto_gbs_geomean"] = geomean([r[bname]["auto"]["gbs"] for r in records])
+        summary[bname]["auto_roofline_frac_geomean"] = geomean([r[bname]["auto"]["roofline_frac"] for r in records])
+    by_cpg = {}
+    for r in records:
+        by_cpg.setdefault(r["cpg"], []).append(r)
+    summary["graph_by_cpg"] = {
+        str(c): dict(shapes=len(rs), algo=sorted(set(r["algo"] for r in rs)),
+                     direct_over_auto=geomean([r["graph"]["direct_over_auto"]["ratio"] for r in rs]),
+                     torch_over_auto=geomean([r["graph"]["torch_over_auto"]["ratio"] for r in rs
+                                              if r["graph"].get("torch_over_auto")]),
+                     auto_roofline_frac=geomean([r["graph"]["auto"]["roofline_frac"] for r in rs]))
+        for c, rs in sorted(by_cpg.items())}
+    out = dict(metric="grouped 3x3 shape sweep: baseline latency / dispatcher latency (above 1 favours the library), "
+                      "geomean over shapes, paired batches with 95% bootstrap intervals and a 5% practical threshold",
+               shapes=len(records), batches=args.batches, samples=args.samples,
+               checks_failed=[r["name"] for r in records if "FAIL" in r["check"].values()],
+               summary=summary, torch_settings=dict(cudnn_benchmark=True, allow_tf32=False),
+               seconds=time.perf_counter() - t0)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump(dict(out, records=records), f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -370,6 +634,10 @@ def main():
         print("bench.py: this library runs on one GPU; multi-GPU runs are not part of this build "
               "(got --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args)
+        return
 
     import torch
     import synth

@@ -1,6 +1,7 @@
 // k_grouped3x3.hip -- grouped / depthwise 3x3, stride 1, pad 1, dilation 1,
 // with 1, 2 or 4 input channels per group (the workload of the GroupConv
-// Atlas page).  VALU arithmetic, HBM-bound.
+// Atlas page), and 8 or 16 on the register kernel.  VALU arithmetic,
+// HBM-bound up to 4 channels per group, FMA-bound beyond.
 //
 // Two kernels:
 //  - grouped3x3_rows_kernel (W a multiple of 4, W <= 256, 16-byte aligned
@@ -35,6 +36,9 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfPlane = 0x7fffffff;
 constexpr int kSmallWaves = 256;    // below this many waves at 2 rows per lane, use 1
 constexpr int kLargeWaves = 8192;   // depthwise with at least this many waves at 4 rows per lane uses 4
+constexpr int kWideWaves = 1536;    // 8 or 16 channels per group: halve the output channels per lane below this
+constexpr int kWideBlocks = 1024;   // the same for the LDS band kernel's workgroups
+constexpr size_t kWideBandLds = 64 * 1024;  // largest LDS band a wide group may stage
 
 struct G3Params {
     int C, H, W, K;
@@ -334,6 +338,19 @@ hipError_t launch_rows_t(const G3Rows &p, const float *x, const float *w, const 
 template <int RB>
 hipError_t launch_rows(int CI, int CO, const G3Rows &p, const float *x, const float *w, const float *bias,
                        float *y, hipStream_t st) {
+    if constexpr (RB <= 2) {
+        // 8 or 16 channels per group: blocks of 8 (or 4) output channels
+        if (CI == 16) {
+            if (CO == 4) return launch_rows_t<16, 4, RB>(p, x, w, bias, y, st);
+            if (CO == 2) return launch_rows_t<16, 2, RB>(p, x, w, bias, y, st);
+            return launch_rows_t<16, 1, RB>(p, x, w, bias, y, st);
+        }
+        if (CI == 8) {
+            if (CO == 4) return launch_rows_t<8, 4, RB>(p, x, w, bias, y, st);
+            if (CO == 2) return launch_rows_t<8, 2, RB>(p, x, w, bias, y, st);
+            return launch_rows_t<8, 1, RB>(p, x, w, bias, y, st);
+        }
+    }
     if (CI == 4) {
         if (CO == 4) return launch_rows_t<4, 4, RB>(p, x, w, bias, y, st);
         if (CO == 2) return launch_rows_t<4, 2, RB>(p, x, w, bias, y, st);
@@ -349,14 +366,54 @@ hipError_t launch_rows(int CI, int CO, const G3Rows &p, const float *x, const fl
     return launch_rows_t<1, 1, RB>(p, x, w, bias, y, st);
 }
 
+// Output channels per lane: up to 4 (the most that divides the group's).
+int rows_co(const gconv_desc *d) { return d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1); }
+
+// The LDS band kernel's geometry for CO output channels per workgroup: Q
+// outputs per lane along W, the band (BH rows x TW columns), the number of
+// bands (*gx) and the dynamic LDS bytes (staged rows with halo + weights).
+size_t band_plan(const gconv_desc *d, int CO, G3Params *p, int *Q, long long *gx) {
+    *Q = d->W >= 32 ? 8 : 4;
+    p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K;
+    p->cout = d->cout;
+    p->n_cob = d->cout / CO;
+    // band width: the whole row when it fits 32 lanes, else 32*Q columns
+    const int wq = (d->W + *Q - 1) / *Q;
+    const int tasks_per_row = wq < 32 ? wq : 32;
+    p->TW = tasks_per_row * *Q;
+    p->n_cb = (d->W + p->TW - 1) / p->TW;
+    // band height: fill 256 lanes, then even out the bands over H
+    int bh = kBlock / tasks_per_row;
+    if (bh > d->H) bh = d->H;
+    const int n_rb = (d->H + bh - 1) / bh;
+    p->BH = (d->H + n_rb - 1) / n_rb;
+    p->pitch = (p->TW + kLead + 1 + 3) & ~3;
+    p->vec_load = p->vec_store = 0;
+    *gx = (long long)n_rb * p->n_cb;
+    return sizeof(float) * ((size_t)d->cin * (p->BH + 2) * p->pitch + (size_t)CO * d->cin * 9);
+}
+
+// Wide groups: 8 or 16 input channels per group and up to 16 output
+// channels (a multiple of 4).  They run on the register kernel when W allows
+// it, else on the LDS band kernel when its band fits kWideBandLds; the
+// register kernel's alignment limit is checked at launch.
+bool wide_geometry(const gconv_desc *d) {
+    if (!((d->cin == 8 || d->cin == 16) && d->groups > 1 && d->cout % 4 == 0 && d->cout <= 16)) return false;
+    if (d->W % 4 == 0 && d->W <= 256 && (long long)(d->H + 2) * d->W * (long long)sizeof(float) < 0x7fffffffLL)
+        return true;
+    G3Params p;
+    int Q;
+    long long gx;
+    return band_plan(d, 4, &p, &Q, &gx) <= kWideBandLds;
+}
+
 // The register variant's geometry for RB rows per lane, or false.
-bool rows_plan(const gconv_desc *d, const float *x, const float *y, int RB, G3Rows *p) {
+bool rows_plan(const gconv_desc *d, const float *x, const float *y, int RB, int CO, G3Rows *p) {
     if (d->W % 4 != 0 || d->W > 256) return false;
     // byte offsets within one plane, including one row before and after it,
     // must fit a signed 32-bit buffer offset
     if ((long long)(d->H + 2) * d->W * (long long)sizeof(float) >= 0x7fffffffLL) return false;
     if (((uintptr_t)x | (uintptr_t)y) & 15u) return false;
-    const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
     p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K; p->G = d->groups;
     p->cout = d->cout;
     p->n_cob = d->cout / CO;
@@ -392,6 +449,8 @@ template <int Q>
 hipError_t launch_ci(int CI, int CO, const G3Params &p, dim3 grid, size_t lds, const float *x,
                      const float *w, const float *bias, float *y, hipStream_t st) {
     switch (CI) {
+        case 16: return launch_co<16, Q>(CO, p, grid, lds, x, w, bias, y, st);
+        case 8: return launch_co<8, Q>(CO, p, grid, lds, x, w, bias, y, st);
         case 4: return launch_co<4, Q>(CO, p, grid, lds, x, w, bias, y, st);
         case 2: return launch_co<2, Q>(CO, p, grid, lds, x, w, bias, y, st);
         default: return launch_co<1, Q>(CO, p, grid, lds, x, w, bias, y, st);
@@ -402,7 +461,7 @@ hipError_t launch_ci(int CI, int CO, const G3Params &p, dim3 grid, size_t lds, c
 
 bool grouped3x3_supported(const gconv_desc *d) {
     return d->R == 3 && d->S == 3 && d->stride == 1 && d->pad == 1 && d->dil == 1 &&
-           (d->cin == 1 || d->cin == 2 || d->cin == 4);
+           (d->cin == 1 || d->cin == 2 || d->cin == 4 || wide_geometry(d));
 }
 
 hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w, const float *bias,
@@ -413,39 +472,49 @@ hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w
         // halo traffic through the L2, and registers to spare); 1 when the
         // problem is so small that the critical path of one wave dominates
         G3Rows rp;
-        const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
-        if (rows_plan(d, x, y, 2, &rp)) {
-            if (rp.waves < kSmallWaves && rows_plan(d, x, y, 1, &rp))
+        int CO = rows_co(d);
+        if (d->cin > 4) {
+            // wide groups: a lane runs 9 * cin FMAs per output it owns, so on
+            // small problems one wave's chain of channels sets the time;
+            // fewer output channels per lane then buy more waves
+            while (CO > 1) {
+                if (!rows_plan(d, x, y, 2, CO, &rp)) break;
+                if (rp.waves < kSmallWaves) rows_plan(d, x, y, 1, CO, &rp);
+                if (rp.waves >= kWideWaves) break;
+                CO /= 2;
+            }
+        }
+        if (rows_plan(d, x, y, 2, CO, &rp)) {
+            if (rp.waves < kSmallWaves && rows_plan(d, x, y, 1, CO, &rp))
                 return launch_rows<1>(d->cin, CO, rp, x, w, bias, y, st);
-            if (d->cin == 1 && rows_plan(d, x, y, 4, &rp) && rp.waves >= kLargeWaves)
+            if (d->cin == 1 && rows_plan(d, x, y, 4, CO, &rp) && rp.waves >= kLargeWaves)
                 return launch_rows<4>(d->cin, CO, rp, x, w, bias, y, st);
-            rows_plan(d, x, y, 2, &rp);
+            rows_plan(d, x, y, 2, CO, &rp);
             return launch_rows<2>(d->cin, CO, rp, x, w, bias, y, st);
         }
     }
-    const int Q = d->W >= 32 ? 8 : 4;
-    const int CO = d->cout % 4 == 0 ? 4 : (d->cout % 2 == 0 ? 2 : 1);
+    int CO = rows_co(d);
     G3Params p;
-    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K;
-    p.cout = d->cout;
-    p.n_cob = d->cout / CO;
-    // band width: the whole row when it fits 32 lanes, else 32*Q columns
-    const int wq = (d->W + Q - 1) / Q;
-    const int tasks_per_row = wq < 32 ? wq : 32;
-    p.TW = tasks_per_row * Q;
-    p.n_cb = (d->W + p.TW - 1) / p.TW;
-    // band height: fill 256 lanes, then even out the bands over H
-    int bh = kBlock / tasks_per_row;
-    if (bh > d->H) bh = d->H;
-    const int n_rb = (d->H + bh - 1) / bh;
-    p.BH = (d->H + n_rb - 1) / n_rb;
-    p.pitch = (p.TW + kLead + 1 + 3) & ~3;
+    int Q;
+    long long gx = 0;
+    size_t lds = band_plan(d, CO, &p, &Q, &gx);
+    if (d->cin > 4) {
+        if (lds > kWideBandLds) {
+            // wide groups on a band that does not fit (wide rows that are
+            // not 16-byte aligned): the implicit GEMM or the direct kernel
+            if (igemm_supported(d)) return launch_igemm(d, x, w, bias, y, st);
+            return launch_direct(d, x, w, bias, y, st);
+        }
+        // fewer output channels per workgroup buy more workgroups
+        while (CO > 1 && gx * d->groups * (d->cout / CO) * d->N < kWideBlocks) {
+            CO /= 2;
+            lds = band_plan(d, CO, &p, &Q, &gx);
+        }
+    }
     p.vec_load = (d->W % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     p.vec_store = (d->W % 4 == 0) && (((uintptr_t)y & 15u) == 0);
-    const long long gx = (long long)n_rb * p.n_cb;
     const long long gy = (long long)d->groups * p.n_cob;
     if (gx > 0x7fffffffLL || gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
-    const size_t lds = sizeof(float) * ((size_t)d->cin * (p.BH + 2) * p.pitch + (size_t)CO * d->cin * 9);
     dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)d->N);
     if (Q == 8) return launch_ci<8>(d->cin, CO, p, grid, lds, x, w, bias, y, st);
     return launch_ci<4>(d->cin, CO, p, grid, lds, x, w, bias, y, st);

@@ -146,3 +146,29 @@ EXTRA_WORKLOADS = {
     "dw3d2_atrous_576x32": Workload("dw3d2_atrous_576x32", 16, 576, 32, 32, 576, 3, 3, 1, 2, 2, 576,
                                     215, ("uniform", -1.0, 1.0), _u(1 / 3)),
 }
+
+# Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the
+# fixed experiment of the GroupConv Atlas): 80 shapes standing in for the
+# Atlas's own 80-shape list, which is not published.  Batch {1, 8} x
+# channels {64, 256} x square images {14, 28, 56, 112} x channels per group
+# {1, 2, 4, 8, 16}; C = K, x ~ U[-1, 1], w ~ U[+-1/sqrt(9 * cpg)], seed
+# 3000 + position in the grid.
+ATLAS_BATCH = (1, 8)
+ATLAS_CHANNELS = (64, 256)
+ATLAS_SIZES = (14, 28, 56, 112)
+ATLAS_CPG = (1, 2, 4, 8, 16)
+
+
+def _atlas_grid():
+    grid = {}
+    for n in ATLAS_BATCH:
+        for c in ATLAS_CHANNELS:
+            for hw in ATLAS_SIZES:
+                for cpg in ATLAS_CPG:
+                    name = "g3_n%d_c%d_%dx%d_cpg%d" % (n, c, hw, hw, cpg)
+                    grid[name] = Workload(name, n, c, hw, hw, c, 3, 3, 1, 1, 1, c // cpg, 3000 + len(grid),
+                                          ("uniform", -1.0, 1.0), _u(1 / math.sqrt(9 * cpg)))
+    return grid
+
+
+ATLAS_GRID = _atlas_grid()

@@ -107,6 +107,27 @@ def test_dispatch_of_the_workloads(name):
     assert gc.conv_desc_get_algo(d) == EXPECTED_ALGO[name]
 
 
+def test_dispatch_of_wide_groups():
+    # 8 or 16 channels per group, up to 16 output channels per group, W a
+    # multiple of 4 up to 256: the register kernel
+    for (C, G, K, W) in ((256, 32, 256, 56), (256, 16, 256, 112), (64, 8, 32, 28), (32, 2, 24, 64)):
+        d = gc.conv_desc_create(2, C, 20, W, K, 3, 3, 1, 1, 1, G)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3, (C, G, K, W)
+    # W not a multiple of 4: the LDS band kernel, while its band fits 64 KB
+    d = gc.conv_desc_create(2, 64, 20, 14, 64, 3, 3, 1, 1, 1, 4)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3
+    # wider than 256 with a band over 64 KB: the implicit GEMM
+    d = gc.conv_desc_create(2, 64, 20, 260, 64, 3, 3, 1, 1, 1, 8)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_IGEMM
+    with pytest.raises(gc.GconvError):
+        gc.conv_desc_set_algo(d, gc.ALGO_GROUPED3X3)
+    # dense (groups = 1) and wide output groups stay on the matrix cores
+    assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 8, 20, 32, 32, 3, 3, 1, 1, 1, 1)) == gc.ALGO_IGEMM
+    assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 64, 20, 32, 256, 3, 3, 1, 1, 1, 8)) == gc.ALGO_IGEMM
+    # 32 channels per group is not a register-kernel width
+    assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 64, 20, 32, 64, 3, 3, 1, 1, 1, 2)) == gc.ALGO_IGEMM
+
+
 def test_forcing_an_unsupported_algorithm_is_refused():
     d = gc.conv_desc_create(2, 32, 20, 20, 64, 5, 9, 1, 0, 1, 1)
     with pytest.raises(gc.GconvError) as ei:

@@ -298,6 +298,21 @@ EDGE = [
     synth.Workload("res_cin5_pad1", 2, 5, 13, 70, 32, 3, 3, 1, 1, 1, 1, 55, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("res_cin4_k40", 1, 4, 19, 131, 40, 3, 3, 1, 0, 1, 1, 56, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("res_1x1_k64", 2, 8, 9, 66, 64, 1, 1, 1, 0, 1, 1, 57, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # wide groups on the register kernel: 8 and 16 input channels per group,
+    # blocks of 4, 2 or 1 output channels, one or two rows per lane, ragged H;
+    # the misaligned-y pass takes the implicit GEMM or the direct kernel
+    synth.Workload("rows_cpg8_cob8", 2, 32, 13, 36, 32, 3, 3, 1, 1, 1, 4, 61, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_cpg16_h9", 3, 64, 9, 20, 64, 3, 3, 1, 1, 1, 4, 62, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_cpg8_cout4", 1, 16, 11, 8, 8, 3, 3, 1, 1, 1, 2, 63, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_cpg16_cout12", 2, 32, 7, 64, 24, 3, 3, 1, 1, 1, 2, 64, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_cpg8_w256_rb2", 8, 64, 37, 256, 64, 3, 3, 1, 1, 1, 8, 65, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # wide groups with W not a multiple of 4: the LDS band kernel (and wider
+    # than 256 with a band over 64 KB: the implicit GEMM)
+    synth.Workload("band_cpg16_w14", 2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 4, 67, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("band_cpg8_w30", 8, 256, 9, 30, 256, 3, 3, 1, 1, 1, 32, 68, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wide_w260_igemm", 1, 32, 6, 260, 32, 3, 3, 1, 1, 1, 4, 69, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # enough waves for 2 output channels per lane, not for 4
+    synth.Workload("rows_cpg16_co2", 4, 64, 37, 256, 64, 3, 3, 1, 1, 1, 4, 66, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_cin5_pad2", 2, 5, 13, 70, 40, 5, 5, 1, 2, 1, 1, 47, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
@@ -316,6 +331,26 @@ def test_conv_edge_cases(wl):
     # an output pointer that is only 4-byte aligned takes the scalar stores
     y1, _ = gpu_conv(wl, inp, y_offset=1)
     check_conv(y1, y_ref, A, wl.name + " misaligned y")
+
+
+WIDE = [wl for wl in EDGE if wl.name.startswith(("rows_cpg", "band_cpg"))]
+
+
+@pytest.mark.parametrize("wl", WIDE, ids=lambda w: w.name)
+def test_wide_groups_register_kernel(wl):
+    """8 and 16 channels per group on the register kernel: integer inputs
+    bit-exact, and a bias."""
+    assert gc.conv_desc_get_algo(_desc(wl)) == gc.ALGO_GROUPED3X3
+    wi = wl.with_(x_dist=("int", -2, 2), w_dist=("int", -2, 2), seed=wl.seed + 500)
+    inp = synth.make_inputs(wi)
+    y, _ = gpu_conv(wi, inp)
+    y_ref, _ = oracle_conv(wi, inp)
+    assert np.array_equal(y.astype(np.float64), y_ref), wl.name
+    inp = synth.make_inputs(wl)
+    bias = synth.normal((wl.K,), 0.5, wl.seed, 7)
+    y, _ = gpu_conv(wl, inp, bias=bias)
+    y_ref, A = oracle_conv(wl, inp, bias)
+    check_conv(y, y_ref, A, wl.name + " bias")
 
 
 def test_repeatable_bitwise():
