@@ -52,7 +52,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rows", default="", help="comma-separated subset of rows (default: all)")
     ap.add_argument("--batches", type=int, default=10)
     ap.add_argument("--samples", type=int, default=30)

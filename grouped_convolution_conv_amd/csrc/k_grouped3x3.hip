@@ -233,9 +233,14 @@ __global__ __launch_bounds__(kBlock) void grouped3x3_rows_kernel(const float *__
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
     if (wv >= p.waves) return;  // whole waves only
-    const int plane = wv / p.wpp, wip = wv - plane * p.wpp;
-    const int cob = plane % p.n_cob;
-    const int t = plane / p.n_cob;
+    // wave -> (n, group, wave in plane, channel block), channel block
+    // fastest: the blocks that read the same input rows are neighbouring
+    // waves of one workgroup, so they run together on one XCD and share its
+    // L2 instead of each fetching the rows from memory
+    const int cob = wv % p.n_cob;
+    const int t0 = wv / p.n_cob;
+    const int wip = t0 % p.wpp;
+    const int t = t0 / p.wpp;
     const int g = t % p.G, n = t / p.G;
     const int sl = lane / p.cg, cgi = lane - sl * p.cg;
     const int strip = wip * p.rpw + sl;

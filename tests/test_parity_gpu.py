@@ -231,7 +231,7 @@ def test_fused_other_geometries():
 
 
 @pytest.mark.parametrize("n,variant", [(0, gc.FUSED_AUTO), (63, gc.FUSED_AUTO), (17, gc.FUSED_STORE),
-                                       (40, gc.FUSED_RECOMPUTE)])
+                                       (15, gc.FUSED_STORE), (63, gc.FUSED_STORE), (40, gc.FUSED_RECOMPUTE)])
 def test_fused_full_size_whole_samples(n, variant):
     """Full c5 in the benchmark's launch configuration; samples n compared whole."""
     wl = W["c5_fused_gn"]
@@ -242,6 +242,22 @@ def test_fused_full_size_whole_samples(n, variant):
     sl["x"] = inp["x"][n:n + 1]
     ref = oracle_fused(wl.with_(N=1), sl)
     check_gn(out[n:n + 1], ref, "c5 full, sample %d" % n)
+
+
+def test_fused_store_batch_slices_direct_stage():
+    """The store variant runs over slices of the batch (v of a slice sized
+    for the last-level cache): 66 images of 32 x 128 x 128 outputs make a
+    slice of 64 and one of 2.  The direct kernel runs stage A here; the
+    images at both slice edges are compared whole."""
+    wl = W["c5_fused_gn"].with_(N=66, H=130, W=130)
+    inp = synth.make_inputs(wl)
+    _say("[parity] fused store slices, direct stage A")
+    out = gpu_fused(wl, inp, algo=gc.ALGO_DIRECT, variant=gc.FUSED_STORE)
+    for n in (0, 63, 64, 65):
+        sl = dict(inp)
+        sl["x"] = inp["x"][n:n + 1]
+        ref = oracle_fused(wl.with_(N=1), sl)
+        check_gn(out[n:n + 1], ref, "store slices, sample %d" % n)
 
 
 # ------------------------------------------------------------------ geometry fuzz and edges
