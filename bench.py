@@ -67,6 +67,10 @@ def parse():
     ap.add_argument("--sweep-shapes", default="", help="comma-separated subset of the grid (default: all 80)")
     ap.add_argument("--sweep-out", default="", help="write the per-shape sweep records to this JSON file")
     ap.add_argument("--sweep-no-torch", action="store_true", help="leave PyTorch's conv2d out of the sweep")
+    ap.add_argument("--block", action="store_true",
+                    help="block-substitution probe: an inverted-residual block (MobileNetV2 features[3] shape) "
+                         "timed as is and with its depthwise conv replaced by the library's, paired batches")
+    ap.add_argument("--block-batch", default="1,4", help="comma-separated batch sizes for --block")
     return ap.parse_args()
 
 
@@ -604,6 +608,127 @@ def sweep(args):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------ block substitution probe
+
+
+def _inverted_residual(torch, seed):
+    """The MobileNetV2 inverted-residual block at features[3]'s shape (24
+    channels in and out, expansion 6, stride 1, 56x56): 1x1 conv 24->144, BN,
+    ReLU6, 3x3 depthwise conv 144 (pad 1), BN, ReLU6, 1x1 conv 144->24, BN,
+    plus the input.  Random weights and BN statistics, inference mode."""
+    nn = torch.nn
+    g = torch.Generator().manual_seed(seed)
+
+    def bn(c):
+        m = nn.BatchNorm2d(c)
+        with torch.no_grad():
+            m.weight.copy_(0.5 + torch.rand(c, generator=g))
+            m.bias.copy_(0.1 * torch.randn(c, generator=g))
+            m.running_mean.copy_(0.1 * torch.randn(c, generator=g))
+            m.running_var.copy_(0.5 + torch.rand(c, generator=g))
+        return m
+
+    def conv(cin, cout, k, groups=1):
+        m = nn.Conv2d(cin, cout, k, 1, k // 2, groups=groups, bias=False)
+        bound = 1.0 / math.sqrt(cin // groups * k * k)
+        with torch.no_grad():
+            m.weight.copy_((2 * torch.rand(m.weight.shape, generator=g) - 1) * bound)
+        return m
+
+    expand = nn.Sequential(conv(24, 144, 1), bn(144), nn.ReLU6())
+    dw = conv(144, 144, 3, groups=144)
+    rest = nn.Sequential(bn(144), nn.ReLU6(), conv(144, 24, 1), bn(24))
+    return [m.cuda().eval() for m in (expand, dw, rest)]
+
+
+def block_probe(args):
+    import torch
+    import grouped_convolution_conv_amd as gc
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    torch.backends.cudnn.benchmark = True
+    torch.backends.cudnn.allow_tf32 = False
+    expand, dw, rest = _inverted_residual(torch, 1234)
+    w_dw = dw.weight.detach().contiguous()
+    out = dict(metric="block substitution: original block latency / block with the library's depthwise conv "
+                      "(above 1 favours the library), paired batches, 95% bootstrap intervals, 5% practical threshold",
+               block="inverted residual 24->144->24, 3x3 depthwise 144, 56x56, BN + ReLU6, residual; random weights",
+               batches=args.batches, samples=args.samples, results=[])
+    for n in [int(v) for v in args.block_batch.split(",")]:
+        x = torch.randn(n, 24, 56, 56, device="cuda")
+        d = gc.conv_desc_create(n, 144, 56, 56, 144, 3, 3, 1, 1, 1, 144)
+        y_buf = torch.empty(n, 144, 56, 56, device="cuda")
+
+        def original():
+            return x + rest(dw(expand(x)))
+
+        def substituted():
+            # the expansion's output is a fresh contiguous tensor: the
+            # library reads it in place, on torch's current stream
+            gc.conv_fwd(d, expand(x), w_dw, None, y_buf)
+            return x + rest(y_buf)
+
+        with torch.no_grad():
+            # verify: the depthwise conv at the block's own activations, and the block output
+            h = expand(x).contiguous()
+            ref = dw(h)
+            gc.conv_fwd(d, h, w_dw, None, y_buf)
+            A = torch.nn.functional.conv2d(h.abs(), w_dw.abs(), None, 1, 1, 1, 144)
+            conv_ok = bool(((y_buf - ref).abs() <= 1e-4 * A + 1e-6).all().item())
+            a, b = original(), substituted()
+            torch.cuda.synchronize()
+            block_err = float((a - b).abs().max().item())
+            cands = {"original": original, "substituted": substituted}
+            graphs, graph_error = {}, None
+            for k, f in cands.items():
+                for _ in range(3):
+                    f()
+                torch.cuda.synchronize()
+                try:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        f()
+                    graphs[k] = g
+                except RuntimeError as e:  # a call in the block that capture does not support
+                    graph_error = str(e).splitlines()[0]
+                    torch.cuda.synchronize()
+                    break
+            torch.cuda.synchronize()
+            per = {b: {k: [] for k in cands} for b in (("sync",) if graph_error else ("graph", "sync"))}
+            keys = list(cands)
+            for bt in range(args.batches):
+                order = keys[bt % 2:] + keys[:bt % 2]
+                for k in (order if not graph_error else []):
+                    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                          for _ in range(args.samples)]
+                    for e0, e1 in ev:
+                        e0.record()
+                        graphs[k].replay()
+                        e1.record()
+                    torch.cuda.synchronize()
+                    per["graph"][k].append([e0.elapsed_time(e1) / 1e3 for e0, e1 in ev])
+                for k in order:
+                    per["sync"][k].append(_sync_samples(torch, cands[k], args.samples))
+        rec = dict(N=n, conv_check="pass" if conv_ok else "FAIL", block_max_abs_diff=block_err)
+        if graph_error:
+            rec["graph_error"] = graph_error
+        for bname, pk in per.items():
+            r = paired_ratio(pk["original"], pk["substituted"])
+            r.update({k + "_us": float(np.median([v for bt in pk[k] for v in bt])) * 1e6 for k in keys})
+            rec[bname] = r
+            log("[block] N=%d %-5s original %.2f us  substituted %.2f us  ratio %.3fx [%.3f, %.3f] %s"
+                % (n, bname, r["original_us"], r["substituted_us"], r["ratio"], r["ci95"][0], r["ci95"][1], r["cls"]))
+        out["results"].append(rec)
+        log("[block] N=%d  conv %s  block max|diff| %.2e%s" % (n, rec["conv_check"], block_err,
+                                                             ("  graph: " + graph_error) if graph_error else ""))
+        del graphs
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 
 
@@ -637,6 +762,9 @@ def main():
 
     if args.sweep:
         sweep(args)
+        return
+    if args.block:
+        block_probe(args)
         return
 
     import torch
