@@ -7,9 +7,11 @@
 // arithmetic, HBM-bound for K = 3 and 5.
 //
 // The same register-streaming design as grouped3x3_rows_kernel, for one
-// channel per group and one output channel per group:
-//  - a wave owns whole output rows of one (n, channel) plane; a lane owns
-//    RB output rows x 4 output columns;
+// input channel per group (depthwise) or groups of 2 or 4 input channels,
+// with CO output channels per lane:
+//  - a wave owns whole output rows of one (n, group, block of CO output
+//    channels) plane; a lane owns RB output rows x 4 output columns of each
+//    of the CO channels, and walks the group's input channels one by one;
 //  - per input row it needs, a lane reads its own ST*4 input columns (one or
 //    two 16-byte buffer loads, zero outside the image) and takes the padding
 //    columns to its left and the columns past its right edge from the
@@ -28,15 +30,18 @@ constexpr int kOutOfPlane = 0x7fffffff;
 constexpr int kRB = 2;                     // output rows per lane
 
 struct DwParams {
-    int C, H, W, Ho, Wo;
+    int C, H, W, Ho, Wo, K;
+    int G;        // groups
+    int cout;     // output channels per group
+    int n_cob;    // blocks of CO output channels per group
     int cg;       // 4-column output groups per row (Wo / 4)
     int rpw;      // lane strips (of kRB output rows) per wave: 64 / cg
     int strips;   // strips per plane: ceil(Ho / kRB)
     int wpp;      // waves per plane: ceil(strips / rpw)
-    int waves;    // N * C * wpp
+    int waves;    // N * G * n_cob * wpp
 };
 
-template <int KS, int ST, int DL>
+template <int KS, int ST, int DL, int CI, int CO>
 __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__restrict__ x,
                                                                 const float *__restrict__ w,
                                                                 const float *__restrict__ bias,
@@ -52,8 +57,14 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
     if (wv >= p.waves) return;  // whole waves only
-    const int plane = wv / p.wpp, wip = wv - plane * p.wpp;  // plane = n * C + c
-    const int c = plane % p.C;
+    // wave -> (n, group, wave in plane, output-channel block), block fastest:
+    // blocks that read the same input rows are neighbouring waves
+    const int cob = wv % p.n_cob;
+    const int t0 = wv / p.n_cob;
+    const int wip = t0 % p.wpp;
+    const int t1 = t0 / p.wpp;
+    const int g = t1 % p.G, n = t1 / p.G;
+    const int k0 = g * p.cout + cob * CO;
     const int sl = lane / p.cg, cgi = lane - sl * p.cg;
     const int strip = wip * p.rpw + sl;
     const bool active = sl < p.rpw && strip < p.strips;
@@ -61,80 +72,114 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
     const int ih0 = ST * oh0 - PAD, ic0 = ST * oc0;
     const bool has_left = cgi > 0, has_right = cgi < p.cg - 1;
     const int HW = p.H * p.W;
+    // one resource over the group's CI input planes
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(x + (size_t)plane * HW), (short)0, HW * (int)sizeof(float), kBufferWord3);
+        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * CI) * HW), (short)0, CI * HW * (int)sizeof(float),
+        kBufferWord3);
 
-    float wk[KS * KS];
+    float acc[CO][kRB][4];
 #pragma unroll
-    for (int t = 0; t < KS * KS; ++t) wk[t] = w[(size_t)c * KS * KS + t];
-    const float b = bias ? bias[c] : 0.0f;
-
-    float acc[kRB][4];
+    for (int co = 0; co < CO; ++co) {
+        const float b = bias ? bias[k0 + co] : 0.0f;
 #pragma unroll
-    for (int rr = 0; rr < kRB; ++rr)
+        for (int rr = 0; rr < kRB; ++rr)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[rr][q] = b;
-
-    // the lane's own columns of every input row it needs: buffer loads with
-    // out-of-range offsets (rows above/below the image, idle lanes) reading 0
-    float own[NIR][OWN];
-#pragma unroll
-    for (int i = 0; i < NIR; ++i) {
-        const int ih = ih0 + i;
-        const int rowb = (ih * p.W + ic0) * (int)sizeof(float);
-#pragma unroll
-        for (int v = 0; v < ST; ++v) {
-            const int off = active && ih >= 0 && ih < p.H ? rowb + 16 * v : kOutOfPlane;
-            const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-            own[i][4 * v + 0] = f.x; own[i][4 * v + 1] = f.y; own[i][4 * v + 2] = f.z; own[i][4 * v + 3] = f.w;
-        }
+            for (int q = 0; q < 4; ++q) acc[co][rr][q] = b;
     }
+
+#pragma unroll 1
+    for (int ci = 0; ci < CI; ++ci) {
+        // weights of the block's output channels for input channel ci
+        // (wave-uniform: scalar loads)
+        float wk[CO][KS * KS];
 #pragma unroll
-    for (int i = 0; i < NIR; ++i) {
-        float win[WL];
+        for (int co = 0; co < CO; ++co)
 #pragma unroll
-        for (int t = 0; t < PAD; ++t) {  // columns ic0 - PAD + t: the left lane's last ones
-            const float v = __shfl_up(own[i][OWN - PAD + t], 1, 64);
-            win[t] = has_left ? v : 0.0f;
+            for (int t = 0; t < KS * KS; ++t) wk[co][t] = w[((size_t)(k0 + co) * CI + ci) * KS * KS + t];
+
+        // the lane's own columns of every input row it needs: buffer loads
+        // with out-of-range offsets (rows above/below the image, idle lanes)
+        // reading 0
+        float own[NIR][OWN];
+#pragma unroll
+        for (int i = 0; i < NIR; ++i) {
+            const int ih = ih0 + i;
+            const int rowb = ((ci * p.H + ih) * p.W + ic0) * (int)sizeof(float);
+#pragma unroll
+            for (int v = 0; v < ST; ++v) {
+                const int off = active && ih >= 0 && ih < p.H ? rowb + 16 * v : kOutOfPlane;
+                const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                own[i][4 * v + 0] = f.x; own[i][4 * v + 1] = f.y; own[i][4 * v + 2] = f.z; own[i][4 * v + 3] = f.w;
+            }
         }
 #pragma unroll
-        for (int t = 0; t < OWN; ++t) win[PAD + t] = own[i][t];
+        for (int i = 0; i < NIR; ++i) {
+            float win[WL];
 #pragma unroll
-        for (int t = 0; t < RIGHT; ++t) {  // columns ic0 + OWN + t: the right lane's first ones
-            const float v = __shfl_down(own[i][t], 1, 64);
-            win[PAD + OWN + t] = has_right ? v : 0.0f;
-        }
+            for (int t = 0; t < PAD; ++t) {  // columns ic0 - PAD + t: the left lane's last ones
+                const float v = __shfl_up(own[i][OWN - PAD + t], 1, 64);
+                win[t] = has_left ? v : 0.0f;
+            }
 #pragma unroll
-        for (int kr = 0; kr < KS; ++kr) {
-            // input row i feeds output row rr through kernel row kr when
-            // i = ST*rr + DL*kr
-            const int di = i - DL * kr;
-            if (di < 0 || di % ST != 0 || di / ST >= kRB) continue;
-            const int rr = di / ST;
+            for (int t = 0; t < OWN; ++t) win[PAD + t] = own[i][t];
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+            for (int t = 0; t < RIGHT; ++t) {  // columns ic0 + OWN + t: the right lane's first ones
+                const float v = __shfl_down(own[i][t], 1, 64);
+                win[PAD + OWN + t] = has_right ? v : 0.0f;
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[rr][q] = fmaf(win[ST * q + DL * s], wk[kr * KS + s], acc[rr][q]);
+            for (int kr = 0; kr < KS; ++kr) {
+                // input row i feeds output row rr through kernel row kr when
+                // i = ST*rr + DL*kr
+                const int di = i - DL * kr;
+                if (di < 0 || di % ST != 0 || di / ST >= kRB) continue;
+                const int rr = di / ST;
+#pragma unroll
+                for (int co = 0; co < CO; ++co)
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc[co][rr][q] = fmaf(win[ST * q + DL * s], wk[co][kr * KS + s], acc[co][rr][q]);
+            }
         }
     }
     if (!active) return;
-    float *yb = y + (size_t)plane * p.Ho * p.Wo + oc0;
+    const size_t plane_out = (size_t)p.Ho * p.Wo;
+    float *yb = y + ((size_t)n * p.K + k0) * plane_out + oc0;
 #pragma unroll
-    for (int rr = 0; rr < kRB; ++rr) {
-        const int oh = oh0 + rr;
-        if (oh < p.Ho)
-            *reinterpret_cast<float4 *>(yb + (size_t)oh * p.Wo) =
-                make_float4(acc[rr][0], acc[rr][1], acc[rr][2], acc[rr][3]);
-    }
+    for (int co = 0; co < CO; ++co)
+#pragma unroll
+        for (int rr = 0; rr < kRB; ++rr) {
+            const int oh = oh0 + rr;
+            if (oh < p.Ho)
+                *reinterpret_cast<float4 *>(yb + co * plane_out + (size_t)oh * p.Wo) =
+                    make_float4(acc[co][rr][0], acc[co][rr][1], acc[co][rr][2], acc[co][rr][3]);
+        }
 }
 
-template <int KS, int ST, int DL>
+template <int KS, int ST, int DL, int CI, int CO>
 hipError_t launch_t(const DwParams &p, const float *x, const float *w, const float *bias, float *y,
                     hipStream_t st) {
     const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
-    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO>), dim3(grid), dim3(kBlock), 0, st, x, w, bias,
+                       y, p);
     return hipGetLastError();
+}
+
+// channels per group (CI) and output channels per lane (CO) for one geometry
+template <int KS, int ST, int DL>
+hipError_t launch_geom(int CI, int CO, const DwParams &p, const float *x, const float *w, const float *bias,
+                       float *y, hipStream_t st) {
+    if (CI == 1) return launch_t<KS, ST, DL, 1, 1>(p, x, w, bias, y, st);
+    if (CI == 2) {
+        if (CO == 2) return launch_t<KS, ST, DL, 2, 2>(p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 2, 1>(p, x, w, bias, y, st);
+    }
+    if (CO == 4) return launch_t<KS, ST, DL, 4, 4>(p, x, w, bias, y, st);
+    if (CO == 2) return launch_t<KS, ST, DL, 4, 2>(p, x, w, bias, y, st);
+    return launch_t<KS, ST, DL, 4, 1>(p, x, w, bias, y, st);
 }
 
 }  // namespace
@@ -153,8 +198,19 @@ int variant_of(int ks, int st, int dl) {
 
 }  // namespace
 
+// Output channels per lane: the channels per group, up to 4 (1 for depthwise).
+int dw_co(const gconv_desc *d) {
+    if (d->cin == 1) return 1;
+    const int lim = d->cin;  // 2 or 4: as many output channels per lane as inputs
+    return d->cout % lim == 0 ? lim : (d->cout % 2 == 0 ? 2 : 1);
+}
+
 bool depthwise_supported(const gconv_desc *d) {
-    if (d->cin != 1 || d->cout != 1 || d->R != d->S) return false;
+    // depthwise (one input and one output channel per group), or groups of 2
+    // or 4 input channels (any output channels per group)
+    const bool dw = d->cin == 1 && d->cout == 1;
+    const bool small_groups = (d->cin == 2 || d->cin == 4) && d->groups > 1;
+    if (!(dw || small_groups) || d->R != d->S) return false;
     if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;
     const int ks = d->R, st = d->stride_h, dl = d->dil_h;
     if (d->pad_h != dl * (ks / 2) || d->pad_w != dl * (ks / 2)) return false;
@@ -164,7 +220,7 @@ bool depthwise_supported(const gconv_desc *d) {
     if (d->Wo < 4 || d->Wo % 4 != 0 || d->Wo / 4 > 64 || d->Ho < 1) return false;
     if (st == 2 && d->W != 2 * d->Wo) return false;
     if (st == 1 && d->W != d->Wo) return false;
-    return (long long)(d->H + 16) * d->W * 4 < 0x7fffffffLL;
+    return (long long)d->cin * (d->H + 16) * d->W * 4 < 0x7fffffffLL;
 }
 
 hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w, const float *bias, float *y,
@@ -173,21 +229,25 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
     // 16-byte row pieces need 16-byte aligned planes; other pointers take the
     // direct kernel, which computes the same outputs
     if ((((uintptr_t)x) | ((uintptr_t)y)) & 15u) return launch_direct(d, x, w, bias, y, st);
+    const int CO = dw_co(d);
     DwParams p;
-    p.C = d->C; p.H = d->H; p.W = d->W; p.Ho = d->Ho; p.Wo = d->Wo;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.Ho = d->Ho; p.Wo = d->Wo; p.K = d->K;
+    p.G = d->groups;
+    p.cout = d->cout;
+    p.n_cob = d->cout / CO;
     p.cg = d->Wo / 4;
     p.rpw = 64 / p.cg;
     p.strips = (d->Ho + kRB - 1) / kRB;
     p.wpp = (p.strips + p.rpw - 1) / p.rpw;
-    const long long waves = (long long)d->N * d->C * p.wpp;
+    const long long waves = (long long)d->N * d->groups * p.n_cob * p.wpp;
     if (waves > 0x7fffffffLL - 64) return hipErrorInvalidConfiguration;
     p.waves = (int)waves;
     switch (variant_of(d->R, d->stride_h, d->dil_h)) {
-        case 1: return launch_t<5, 1, 1>(p, x, w, bias, y, st);
-        case 2: return launch_t<7, 1, 1>(p, x, w, bias, y, st);
-        case 3: return launch_t<3, 2, 1>(p, x, w, bias, y, st);
-        case 4: return launch_t<5, 2, 1>(p, x, w, bias, y, st);
-        default: return launch_t<3, 1, 2>(p, x, w, bias, y, st);
+        case 1: return launch_geom<5, 1, 1>(d->cin, CO, p, x, w, bias, y, st);
+        case 2: return launch_geom<7, 1, 1>(d->cin, CO, p, x, w, bias, y, st);
+        case 3: return launch_geom<3, 2, 1>(d->cin, CO, p, x, w, bias, y, st);
+        case 4: return launch_geom<5, 2, 1>(d->cin, CO, p, x, w, bias, y, st);
+        default: return launch_geom<3, 1, 2>(d->cin, CO, p, x, w, bias, y, st);
     }
 }
 

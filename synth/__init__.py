@@ -131,9 +131,9 @@ WORKLOADS = {
 ROW_ORDER = list(WORKLOADS)
 
 # Depthwise layers ("same" padding dil * (R // 2), batch 16) of MobileNet-,
-# EfficientNet-, ConvNeXt- and atrous (dilated) networks: the
-# general-geometry shapes measured beside the five workloads (not part of
-# the benchmark step).
+# EfficientNet-, ConvNeXt- and atrous (dilated) networks, and a grouped
+# stride-2 layer: the general-geometry shapes measured beside the five
+# workloads (not part of the benchmark step).
 EXTRA_WORKLOADS = {
     "dw3s2_mobilenet_144x112": Workload("dw3s2_mobilenet_144x112", 16, 144, 112, 112, 144, 3, 3, 2, 1, 1, 144,
                                         211, ("uniform", -1.0, 1.0), _u(1 / 3)),
@@ -145,6 +145,10 @@ EXTRA_WORKLOADS = {
                                           214, ("uniform", -1.0, 1.0), _u(1 / 5)),
     "dw3d2_atrous_576x32": Workload("dw3d2_atrous_576x32", 16, 576, 32, 32, 576, 3, 3, 1, 2, 2, 576,
                                     215, ("uniform", -1.0, 1.0), _u(1 / 3)),
+    # grouped 3x3 at stride 2 with 4 channels per group (a downsampling
+    # grouped layer)
+    "g3s2_cpg4_256x56": Workload("g3s2_cpg4_256x56", 16, 256, 56, 56, 256, 3, 3, 2, 1, 1, 64,
+                                 216, ("uniform", -1.0, 1.0), _u(1 / 6)),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

@@ -31,6 +31,11 @@ def _dw(name, N, C, H, W, R, stride, seed, dil=1):
                           ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0))
 
 
+def _grp(name, N, C, H, W, K, R, stride, G, seed, dil=1):
+    return synth.Workload(name, N, C, H, W, K, R, R, stride, dil * (R // 2), dil, G, seed,
+                          ("uniform", -1.0, 1.0), ("uniform", -1.0, 1.0))
+
+
 # Small cases: the oracle computes every output.  They cover one 4-column
 # group per row (a wave holds 64 row strips), a full 256-column output row
 # per wave (one strip per wave), row counts that leave part of the last
@@ -53,6 +58,15 @@ SMALL = [
     _dw("dw3d2_h11_w12", 2, 5, 11, 12, 3, 1, 219, dil=2),
     _dw("dw3d2_h3_w256", 1, 3, 3, 256, 3, 1, 220, dil=2),
     _dw("dw3d2_h17_w4_planes", 8, 36, 17, 4, 3, 1, 221, dil=2),
+    # groups of 2 or 4 input channels: 4, 2 or 1 output channels per lane,
+    # several blocks per group, ragged rows, a whole 256-column row per wave
+    _grp("grp3s2_cpg4", 2, 16, 14, 16, 16, 3, 2, 4, 222),
+    _grp("grp3s2_cpg2_cout3", 2, 8, 9, 24, 12, 3, 2, 4, 223),
+    _grp("grp5_cpg4_cout8", 1, 8, 11, 20, 16, 5, 1, 2, 224),
+    _grp("grp7_cpg2", 2, 4, 9, 12, 4, 7, 1, 2, 225),
+    _grp("grp3d2_cpg4", 2, 8, 13, 16, 8, 3, 1, 2, 226, dil=2),
+    _grp("grp5s2_cpg2_cout4", 1, 4, 10, 40, 8, 5, 2, 2, 227),
+    _grp("grp3s2_cpg4_w512", 1, 8, 9, 512, 8, 3, 2, 2, 228),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
