@@ -49,6 +49,8 @@ struct IgParams {
     int n_tiles;       // spatial tiles per image
     int pitch;         // LDS row pitch of the input band (floats)
     int vec;           // W, pad multiples of 4 and x 16-byte aligned: 16-byte band loads
+    int G;             // groups
+    int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -348,10 +350,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, j = lane & 31;
-    const int n = blockIdx.z;
-    const int th = blockIdx.x / p.n_tw, tw = blockIdx.x - th * p.n_tw;
+    // Workgroup -> work item, XCD-aware.  The hardware deals consecutive
+    // workgroup ids to the 8 XCDs in turn, so XCD i receives ids i, i + 8,
+    // i + 16, ...  Each XCD is given a contiguous run of work items instead,
+    // ordered (n, group, tile row, tile column, channel block) with the
+    // channel block fastest: the blocks of one tile, and the tiles whose
+    // bands share halo rows, then run on one XCD close in time and its L2
+    // serves the rows they have in common.
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int per = p.n_wg >> 3, rem = p.n_wg & 7;
+    const int item = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int kb = item % p.n_kb;
+    const int t1 = item / p.n_kb;
+    const int tile = t1 % p.n_tiles;
+    const int t2 = t1 / p.n_tiles;
+    const int g = t2 % p.G, n = t2 / p.G;
+    const int th = tile / p.n_tw, tw = tile - th * p.n_tw;
     const int oh0 = th * kTH, ow0 = tw * kTW;
-    const int g = blockIdx.y / p.n_kb, kb = blockIdx.y - g * p.n_kb;
     const int kg0 = kb * KW;
     const int k0 = g * p.cout + kg0;
     const int kvalid = min(KW, p.cout - kg0);
@@ -537,11 +553,14 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
                     float *y, const FusedEpilogue &ep, hipStream_t st) {
     constexpr int CC = chunk_for<R, S>();
     if constexpr (!FUSED) {
+        // one-dimensional grid of p.n_wg workgroups (the kernel maps ids to
+        // work items itself)
+        const dim3 g1((unsigned)p.n_wg);
         clear_stale_launch_error();
         if (p.vec)
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
         else
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false>), grid, dim3(kBlock), 0, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
         return hipGetLastError();
     } else {
         const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
@@ -593,6 +612,8 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.pitch = kTW + d->S - 1;
     p.vec = 0;
+    p.G = d->groups;
+    p.n_wg = 0;
     return p;
 }
 
@@ -624,7 +645,9 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     IgParams p = make_params(d, MB);
     p.vec = (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_kb;
-    if (gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    const long long n_wg = gy * p.n_tiles * d->N;
+    if (gy > 65535 || d->N > 65535 || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    p.n_wg = (int)n_wg;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
     FusedEpilogue none{};
     return launch_rs<false>(d, p, MB, grid, x, w, bias, y, none, st);
