@@ -57,6 +57,12 @@ bool igemm_supported(const gconv_desc *d);
 bool depthwise_supported(const gconv_desc *d);
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups);
 
+// grouped 3x3 with 16 input and 16 output channels per group on the FP32
+// matrix cores (taken inside launch_grouped3x3 when it applies)
+bool grouped16_mfma_applies(const gconv_desc *d);
+hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const float *w,
+                                 const float *bias, float *y, hipStream_t st);
+
 // ---- plain convolution launchers (y = conv(x, w) [+ bias]) ---------------
 hipError_t launch_direct(const gconv_desc *d, const float *x, const float *w,
                          const float *bias, float *y, hipStream_t st);

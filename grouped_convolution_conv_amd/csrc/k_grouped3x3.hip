@@ -466,12 +466,15 @@ hipError_t launch_ci(int CI, int CO, const G3Params &p, dim3 grid, size_t lds, c
 
 bool grouped3x3_supported(const gconv_desc *d) {
     return d->R == 3 && d->S == 3 && d->stride == 1 && d->pad == 1 && d->dil == 1 &&
-           (d->cin == 1 || d->cin == 2 || d->cin == 4 || wide_geometry(d));
+           (d->cin == 1 || d->cin == 2 || d->cin == 4 || wide_geometry(d) || grouped16_mfma_applies(d));
 }
 
 hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w, const float *bias,
                              float *y, hipStream_t st) {
     if (!grouped3x3_supported(d)) return hipErrorInvalidValue;
+    // 16 input and 16 output channels per group with enough waves: the FP32
+    // matrix cores (k_grouped_mfma.hip)
+    if (grouped16_mfma_applies(d)) return launch_grouped16_mfma(d, x, w, bias, y, st);
     {
         // rows per lane: 2 in general; 4 for large depthwise problems (less
         // halo traffic through the L2, and registers to spare); 1 when the

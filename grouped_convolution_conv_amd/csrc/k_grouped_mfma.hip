@@ -1,0 +1,222 @@
+// k_grouped_mfma.hip -- grouped 3x3 convolution (stride 1, padding 1,
+// dilation 1) with 16 input and 16 output channels per group on the FP32
+// matrix cores.
+//
+// The grouped convolution of the GroupConv Atlas page, at the width where
+// its per-group sum (16 channels x 9 taps = 144 products per output) makes
+// the vector-FMA kernels bound by their arithmetic: on gfx950 the non-packed
+// FP32 VALU runs at half the FP32 matrix rate.  Per group the convolution is
+// a small GEMM, D[k][p] = sum_q W[k][q] X[q][p], with k the group's 16 output
+// channels, p output pixels and q = (input channel, tap); it maps onto
+// v_mfma_f32_16x16x4f32 exactly (M = 16 output channels, N = 16 pixels along
+// a row, K = 4 input channels at one tap), so no MFMA row is idle.
+//
+// Data movement follows the register kernel of k_grouped3x3.hip: no LDS, no
+// barriers.  A wave owns RB = 2 output rows x NB blocks of 16 columns of one
+// (image, group).  Its 36 A operands (the group's weights, lane = (output
+// channel, input channel within a quad)) are loaded once.  Its B operands
+// are read straight from the input with buffer loads: lane (kq, j) of a load
+// reads channel 4q + kq, column (block start + j + s - 1) of one input row,
+// one load per (row, block, shift s).  The per-lane part of every offset
+// (channel within the quad, column) is computed once; the row and the
+// channel quad go in the instruction's scalar offset, so a load costs no
+// vector instruction.  Columns outside the image get an offset beyond the
+// buffer (the hardware returns zero: the padding), and a row outside the
+// image gets a scalar offset beyond it.  The next quad's loads are issued
+// before the current quad's 72 MFMAs.  The 3 loads of an input row (one per
+// shift) hit the L1; the halo rows shared by neighbouring waves come from
+// the L2.
+#include "dev_common.h"
+#include "internal.h"
+
+namespace gconv {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kBufferWord3 = 0x00020000;     // raw 32-bit buffer access, gfx9 family
+constexpr int kOutOfRange = 0x7fffffff;      // a per-lane offset beyond every range
+constexpr int kRowOutOfRange = 0x40000000;   // a scalar offset beyond every range (images < 1 GB)
+constexpr int kRB = 2;                       // output rows per wave
+// grid sizes (waves) where this kernel runs; outside them the VALU register
+// kernel of k_grouped3x3.hip measured as fast or faster.  At N8 C256 G16:
+// 28x28 (1792 waves) 13.9 us against 15.3, 112x112 at N1 (1792) 20.5 against
+// 24.2, 56x56 (3584) 41.0 against 41.1, 112x112 (14336) 129 against 125.
+// Both kernels stream B through the vector memory path; this one issues a
+// dword load per (row, block, shift), and at the largest size the texture
+// address units (about half busy) and the load latency, not the matrix
+// cores (about half busy), set its time.
+constexpr int kMfmaMinWaves = 1536;
+constexpr int kMfmaMaxWaves = 8192;
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct GmParams {
+    int C, H, W, K, G;
+    int n_seg;    // column segments (NB blocks of 16) per row
+    int n_rp;     // row pairs per image
+    int units;    // waves: N * G * n_rp * n_seg
+};
+
+template <int NB>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void grouped16_mfma_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ y, GmParams p) {
+    const int lane = threadIdx.x & 63;
+    const int unit = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
+    if (unit >= p.units) return;  // whole waves only
+    // wave -> (image, group, row pair, column segment), segment fastest
+    const int seg = unit % p.n_seg;
+    int t = unit / p.n_seg;
+    const int rp = t % p.n_rp;
+    t /= p.n_rp;
+    const int g = t % p.G, n = t / p.G;
+    const int oh0 = kRB * rp, ow0 = 16 * NB * seg;
+    const int j = lane & 15, kq = lane >> 4;
+    const int HW = p.H * p.W;
+
+    // A operands: lane (row j, k = kq) of the quad-q, tap-t MFMA holds the
+    // weight of output channel g*16 + j for input channel 4q + kq
+    float A[4][9];
+    {
+        const float *wl = w + ((size_t)(g * 16 + j) * 16 + kq) * 9;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int tp = 0; tp < 9; ++tp) A[q][tp] = wl[q * 36 + tp];
+    }
+
+    // the group's 16 input planes
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * 16) * HW), (short)0, 16 * HW * (int)sizeof(float),
+        kBufferWord3);
+    // per-lane offsets of (block b, shift s): channel kq of the quad, column
+    // ow0 + 16b + j + s - 1; beyond the buffer outside the image
+    int co[NB][3];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const int iw = ow0 + 16 * b + j + s - 1;
+            co[b][s] = (iw >= 0 && iw < p.W) ? (kq * HW + iw) * (int)sizeof(float) : kOutOfRange;
+        }
+    // scalar part of a load: channel quad q, input row oh0 - 1 + i
+    auto soff = [&](int q, int i) __attribute__((always_inline)) {
+        const int ih = oh0 - 1 + i;
+        return (ih >= 0 && ih < p.H) ? (4 * q * HW + ih * p.W) * (int)sizeof(float) : kRowOutOfRange;
+    };
+
+    // accumulators start at the bias: register v of block b holds output
+    // channel g*16 + 4kq + v at column ow0 + 16b + j
+    floatx4 acc[kRB][NB];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float bv = bias ? bias[g * 16 + 4 * kq + v] : 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < kRB; ++rr)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[rr][b][v] = bv;
+    }
+
+    constexpr int NIR = kRB + 2;  // input rows
+    float B0[NIR][NB][3], B1[NIR][NB][3];
+    auto load = [&](float (&B)[NIR][NB][3], int q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NIR; ++i) {
+            const int so = soff(q, i);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int s = 0; s < 3; ++s)
+                    B[i][b][s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(xs, co[b][s], so, 0));
+        }
+    };
+    auto mma = [&](const float (&B)[NIR][NB][3], int q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+#pragma unroll
+                for (int rr = 0; rr < kRB; ++rr)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[rr][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[q][r * 3 + s], B[rr + r][b][s],
+                                                                          acc[rr][b], 0, 0, 0);
+    };
+    load(B0, 0);
+    load(B1, 1);
+    mma(B0, 0);
+    load(B0, 2);
+    mma(B1, 1);
+    load(B1, 3);
+    mma(B0, 2);
+    mma(B1, 3);
+
+    // stores: the pixel in the per-lane offset (beyond the range outside
+    // the output), the register's channel in the scalar offset
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+        y + ((size_t)n * p.K + (size_t)g * 16) * HW, (short)0, 16 * HW * (int)sizeof(float), kBufferWord3);
+#pragma unroll
+    for (int rr = 0; rr < kRB; ++rr) {
+        const int oh = oh0 + rr;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int ow = ow0 + 16 * b + j;
+            const int vo = (oh < p.H && ow < p.W) ? ((4 * kq) * HW + oh * p.W + ow) * (int)sizeof(float)
+                                                  : kRowOutOfRange;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                // copy the element out first: a bit cast applied to the
+                // vector element expression itself reads element 0
+                const float val = acc[rr][b][v];
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, val), ys, vo,
+                                                      v * HW * (int)sizeof(float), 0);
+            }
+        }
+    }
+}
+
+template <int NB>
+hipError_t launch_nb(const GmParams &p, const float *x, const float *w, const float *bias, float *y,
+                     hipStream_t st) {
+    const int grid = (p.units + kBlock / 64 - 1) / (kBlock / 64);
+    clear_stale_launch_error();
+    hipLaunchKernelGGL((grouped16_mfma_kernel<NB>), dim3(grid), dim3(kBlock), 0, st, x, w, bias, y, p);
+    return hipGetLastError();
+}
+
+// blocks of 16 columns per wave: 4, or fewer when the row is narrow
+int pick_nb(int W) { return W > 32 ? 4 : (W > 16 ? 2 : 1); }
+
+bool plan(const gconv_desc *d, int NB, GmParams *p) {
+    p->C = d->C; p->H = d->H; p->W = d->W; p->K = d->K; p->G = d->groups;
+    p->n_seg = (d->W + 16 * NB - 1) / (16 * NB);
+    p->n_rp = (d->H + kRB - 1) / kRB;
+    const long long units = (long long)d->N * d->groups * p->n_rp * p->n_seg;
+    if (units > 0x7fffffffLL - 64) return false;
+    p->units = (int)units;
+    return true;
+}
+
+}  // namespace
+
+bool grouped16_mfma_applies(const gconv_desc *d) {
+    if (!(d->R == 3 && d->S == 3 && d->stride == 1 && d->pad == 1 && d->dil == 1 && d->cin == 16 &&
+          d->cout == 16 && d->groups > 1))
+        return false;
+    // 32-bit buffer offsets: a group's 16 planes stay below 1 GB
+    if ((long long)16 * d->H * d->W * (long long)sizeof(float) >= kRowOutOfRange) return false;
+    GmParams p;
+    return plan(d, pick_nb(d->W), &p) && p.units >= kMfmaMinWaves && p.units < kMfmaMaxWaves;
+}
+
+hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const float *w, const float *bias,
+                                 float *y, hipStream_t st) {
+    const int NB = pick_nb(d->W);
+    GmParams p;
+    if (!plan(d, NB, &p)) return hipErrorInvalidConfiguration;
+    if (NB == 4) return launch_nb<4>(p, x, w, bias, y, st);
+    if (NB == 2) return launch_nb<2>(p, x, w, bias, y, st);
+    return launch_nb<1>(p, x, w, bias, y, st);
+}
+
+}  // namespace gconv

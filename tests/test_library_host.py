@@ -121,6 +121,12 @@ def test_dispatch_of_wide_groups():
     assert gc.conv_desc_get_algo(d) == gc.ALGO_IGEMM
     with pytest.raises(gc.GconvError):
         gc.conv_desc_set_algo(d, gc.ALGO_GROUPED3X3)
+    # 16 in / 16 out per group at any width (the matrix-core kernel takes
+    # it when the grid has enough waves, and is chosen inside GROUPED3X3)
+    d = gc.conv_desc_create(4, 128, 97, 40, 128, 3, 3, 1, 1, 1, 8)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3
+    d = gc.conv_desc_create(2, 64, 200, 150, 64, 3, 3, 1, 1, 1, 4)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3
     # dense (groups = 1) and wide output groups stay on the matrix cores
     assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 8, 20, 32, 32, 3, 3, 1, 1, 1, 1)) == gc.ALGO_IGEMM
     assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 64, 20, 32, 256, 3, 3, 1, 1, 1, 8)) == gc.ALGO_IGEMM

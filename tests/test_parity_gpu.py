@@ -327,6 +327,13 @@ EDGE = [
     synth.Workload("band_cpg16_w14", 2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 4, 67, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("band_cpg8_w30", 8, 256, 9, 30, 256, 3, 3, 1, 1, 1, 32, 68, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("wide_w260_igemm", 1, 32, 6, 260, 32, 3, 3, 1, 1, 1, 4, 69, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # 16 input and 16 output channels per group with enough waves: the FP32
+    # matrix-core kernel (blocks of 16 columns: 4, 2 or 1 per wave; ragged
+    # rows, partial blocks, three column segments)
+    synth.Workload("mfma16_h97_w40", 4, 128, 97, 40, 128, 3, 3, 1, 1, 1, 8, 70, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("mfma16_h193_w20", 2, 128, 193, 20, 128, 3, 3, 1, 1, 1, 8, 71, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("mfma16_h100_w9", 4, 128, 100, 9, 128, 3, 3, 1, 1, 1, 8, 72, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("mfma16_h200_w150", 2, 64, 200, 150, 64, 3, 3, 1, 1, 1, 4, 73, ("uniform", -1, 1), ("uniform", -1, 1)),
     # enough waves for 2 output channels per lane, not for 4
     synth.Workload("rows_cpg16_co2", 4, 64, 37, 256, 64, 3, 3, 1, 1, 1, 4, 66, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
@@ -349,7 +356,7 @@ def test_conv_edge_cases(wl):
     check_conv(y1, y_ref, A, wl.name + " misaligned y")
 
 
-WIDE = [wl for wl in EDGE if wl.name.startswith(("rows_cpg", "band_cpg"))]
+WIDE = [wl for wl in EDGE if wl.name.startswith(("rows_cpg", "band_cpg", "mfma16"))]
 
 
 @pytest.mark.parametrize("wl", WIDE, ids=lambda w: w.name)
