@@ -11,8 +11,19 @@
 // v_mfma_f32_16x16x4f32 exactly (M = 16 output channels, N = 16 pixels along
 // a row, K = 4 input channels at one tap), so no MFMA row is idle.
 //
-// Data movement follows the register kernel of k_grouped3x3.hip: no LDS, no
-// barriers.  A wave owns RB = 2 output rows x NB blocks of 16 columns of one
+// Two kernels.  grouped16_mfma_lds_kernel (W a multiple of 4, x 16-byte
+// aligned) stages a workgroup's band in LDS with 128-bit loads and reads
+// every B operand from LDS.  grouped16_mfma_kernel (any other W or
+// alignment) reads B straight from memory, described next.  Measured on the
+// 16 cpg-16 shapes of the grouped 3x3 grid, the two beat the VALU register
+// kernel everywhere but one tie (N8 C256 112x112: 91 us against 126;
+// N8 C256 14x14: 6.5 against 18.9); the direct-load form alone was slower
+// than the VALU kernel at N8 C256 112x112 (129 against 125 us): its dword
+// load per B operand keeps the texture address units and the load latency,
+// not the matrix cores, in charge.
+//
+// grouped16_mfma_kernel's data movement follows the register kernel of
+// k_grouped3x3.hip: no LDS, no barriers.  A wave owns RB = 2 output rows x NB blocks of 16 columns of one
 // (image, group).  Its 36 A operands (the group's weights, lane = (output
 // channel, input channel within a quad)) are loaded once.  Its B operands
 // are read straight from the input with buffer loads: lane (kq, j) of a load
@@ -37,16 +48,7 @@ constexpr int kBufferWord3 = 0x00020000;     // raw 32-bit buffer access, gfx9 f
 constexpr int kOutOfRange = 0x7fffffff;      // a per-lane offset beyond every range
 constexpr int kRowOutOfRange = 0x40000000;   // a scalar offset beyond every range (images < 1 GB)
 constexpr int kRB = 2;                       // output rows per wave
-// grid sizes (waves) where this kernel runs; outside them the VALU register
-// kernel of k_grouped3x3.hip measured as fast or faster.  At N8 C256 G16:
-// 28x28 (1792 waves) 13.9 us against 15.3, 112x112 at N1 (1792) 20.5 against
-// 24.2, 56x56 (3584) 41.0 against 41.1, 112x112 (14336) 129 against 125.
-// Both kernels stream B through the vector memory path; this one issues a
-// dword load per (row, block, shift), and at the largest size the texture
-// address units (about half busy) and the load latency, not the matrix
-// cores (about half busy), set its time.
-constexpr int kMfmaMinWaves = 1536;
-constexpr int kMfmaMaxWaves = 8192;
+
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -175,6 +177,131 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     }
 }
 
+// LDS-staged form (W a multiple of 4 and x 16-byte aligned): a workgroup of
+// 4 waves owns kTH = 8 output rows x 64 columns of one (image, group).  Its
+// band (the group's 16 channels x 10 input rows x 72 columns, from column
+// ow0 - 4, in whole 16-byte pieces) is read once with 128-bit buffer loads
+// (pieces outside the image read zero) into LDS; after one barrier every B
+// operand is an LDS read at a compile-time offset from the lane's base.
+constexpr int kTH = 8;                        // output rows per workgroup (2 per wave)
+constexpr int kLPitch = 72;                   // band row pitch (floats): columns ow0-4 .. ow0+67
+constexpr int kLRows = kTH + 2;
+constexpr int kLPieces = 16 * kLRows * (kLPitch / 4);   // 16-byte pieces of a band
+
+struct GlParams {
+    int C, H, W, K, G;
+    int n_seg;    // 64-column segments per row
+    int n_rb;     // 8-row blocks per image
+    int wgs;      // workgroups: N * G * n_rb * n_seg
+};
+
+__global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float *__restrict__ x,
+                                                                    const float *__restrict__ w,
+                                                                    const float *__restrict__ bias,
+                                                                    float *__restrict__ y, GlParams p) {
+    __shared__ float4 band4[kLPieces];
+    const float *band = reinterpret_cast<const float *>(band4);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    // workgroup -> (image, group, row block, column segment), segment fastest
+    int t = blockIdx.x;
+    const int seg = t % p.n_seg;
+    t /= p.n_seg;
+    const int rb = t % p.n_rb;
+    t /= p.n_rb;
+    const int g = t % p.G, n = t / p.G;
+    const int oh0 = kTH * rb, ow0 = 64 * seg;
+    const int j = lane & 15, kq = lane >> 4;
+    const int HW = p.H * p.W;
+
+    // ---- band: piece f = (c * kLRows + lr) * 18 + c4 holds input columns
+    //      ow0 - 4 + 4c4 .. +3 of row oh0 - 1 + lr, channel c of the group
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * 16) * HW), (short)0, 16 * HW * (int)sizeof(float),
+        kBufferWord3);
+    constexpr int NPT = (kLPieces + kBlock - 1) / kBlock;
+    float4 pv[NPT];
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int f = i * kBlock + tid;
+        const int c = f / (kLRows * 18), rem = f - c * (kLRows * 18);
+        const int lr = rem / 18, c4 = rem - lr * 18;
+        const int ih = oh0 - 1 + lr, iw = ow0 - 4 + 4 * c4;
+        const bool ok = f < kLPieces && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+        const int off = ok ? (c * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+        pv[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
+    }
+
+    // A operands while the band is in flight
+    float A[4][9];
+    {
+        const float *wl = w + ((size_t)(g * 16 + j) * 16 + kq) * 9;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int tp = 0; tp < 9; ++tp) A[q][tp] = wl[q * 36 + tp];
+    }
+    floatx4 acc[kRB][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const float bv = bias ? bias[g * 16 + 4 * kq + v] : 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < kRB; ++rr)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[rr][b][v] = bv;
+    }
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        const int f = i * kBlock + tid;
+        if (f < kLPieces) band4[f] = pv[i];
+    }
+    __syncthreads();
+
+    // ---- MFMAs: B of (quad q, output row rr, tap (r, s), block b) is band
+    //      channel 4q + kq, row 2*wave + rr + r, column 16b + j + s - 1 + 4
+    const float *bl = band + (kq * kLRows + kRB * wave) * kLPitch + j + 3;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float B[kRB + 2][4][3];
+#pragma unroll
+        for (int i = 0; i < kRB + 2; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int s = 0; s < 3; ++s) B[i][b][s] = bl[(4 * q * kLRows + i) * kLPitch + 16 * b + s];
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int s = 0; s < 3; ++s)
+#pragma unroll
+                for (int rr = 0; rr < kRB; ++rr)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[rr][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[q][r * 3 + s], B[rr + r][b][s],
+                                                                          acc[rr][b], 0, 0, 0);
+    }
+
+    // ---- stores, as in grouped16_mfma_kernel
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+        y + ((size_t)n * p.K + (size_t)g * 16) * HW, (short)0, 16 * HW * (int)sizeof(float), kBufferWord3);
+#pragma unroll
+    for (int rr = 0; rr < kRB; ++rr) {
+        const int oh = oh0 + kRB * wave + rr;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int ow = ow0 + 16 * b + j;
+            const int vo = (oh < p.H && ow < p.W) ? ((4 * kq) * HW + oh * p.W + ow) * (int)sizeof(float)
+                                                  : kRowOutOfRange;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float val = acc[rr][b][v];  // see grouped16_mfma_kernel
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, val), ys, vo,
+                                                      v * HW * (int)sizeof(float), 0);
+            }
+        }
+    }
+}
+
 template <int NB>
 hipError_t launch_nb(const GmParams &p, const float *x, const float *w, const float *bias, float *y,
                      hipStream_t st) {
@@ -206,11 +333,23 @@ bool grouped16_mfma_applies(const gconv_desc *d) {
     // 32-bit buffer offsets: a group's 16 planes stay below 1 GB
     if ((long long)16 * d->H * d->W * (long long)sizeof(float) >= kRowOutOfRange) return false;
     GmParams p;
-    return plan(d, pick_nb(d->W), &p) && p.units >= kMfmaMinWaves && p.units < kMfmaMaxWaves;
+    return plan(d, pick_nb(d->W), &p);
 }
 
 hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const float *w, const float *bias,
                                  float *y, hipStream_t st) {
+    if (d->W % 4 == 0 && ((uintptr_t)x & 15u) == 0) {
+        GlParams q;
+        q.C = d->C; q.H = d->H; q.W = d->W; q.K = d->K; q.G = d->groups;
+        q.n_seg = (d->W + 63) / 64;
+        q.n_rb = (d->H + kTH - 1) / kTH;
+        const long long wgs = (long long)d->N * d->groups * q.n_rb * q.n_seg;
+        if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        q.wgs = (int)wgs;
+        clear_stale_launch_error();
+        hipLaunchKernelGGL(grouped16_mfma_lds_kernel, dim3((unsigned)q.wgs), dim3(kBlock), 0, st, x, w, bias, y, q);
+        return hipGetLastError();
+    }
     const int NB = pick_nb(d->W);
     GmParams p;
     if (!plan(d, NB, &p)) return hipErrorInvalidConfiguration;

@@ -325,6 +325,7 @@ EDGE = [
     # wide groups with W not a multiple of 4: the LDS band kernel (and wider
     # than 256 with a band over 64 KB: the implicit GEMM)
     synth.Workload("band_cpg16_w14", 2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 4, 67, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("band_cpg16_cout8_w14", 2, 32, 14, 14, 16, 3, 3, 1, 1, 1, 2, 74, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("band_cpg8_w30", 8, 256, 9, 30, 256, 3, 3, 1, 1, 1, 32, 68, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("wide_w260_igemm", 1, 32, 6, 260, 32, 3, 3, 1, 1, 1, 4, 69, ("uniform", -1, 1), ("uniform", -1, 1)),
     # 16 input and 16 output channels per group with enough waves: the FP32
@@ -334,8 +335,10 @@ EDGE = [
     synth.Workload("mfma16_h193_w20", 2, 128, 193, 20, 128, 3, 3, 1, 1, 1, 8, 71, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("mfma16_h100_w9", 4, 128, 100, 9, 128, 3, 3, 1, 1, 1, 8, 72, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("mfma16_h200_w150", 2, 64, 200, 150, 64, 3, 3, 1, 1, 1, 4, 73, ("uniform", -1, 1), ("uniform", -1, 1)),
-    # enough waves for 2 output channels per lane, not for 4
+    # enough waves for 2 output channels per lane, not for 4 (16 in / 16 out
+    # per group takes the matrix cores; 16 in / 8 out the register kernel)
     synth.Workload("rows_cpg16_co2", 4, 64, 37, 256, 64, 3, 3, 1, 1, 1, 4, 66, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("rows_cpg16_cout8_co2", 6, 64, 37, 256, 32, 3, 3, 1, 1, 1, 4, 75, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k8", 1, 16, 12, 40, 8, 3, 3, 1, 0, 1, 1, 46, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_cin5_pad2", 2, 5, 13, 70, 40, 5, 5, 1, 2, 1, 1, 47, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
