@@ -203,8 +203,15 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     const float *band = reinterpret_cast<const float *>(band4);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    // workgroup -> (image, group, row block, column segment), segment fastest
-    int t = blockIdx.x;
+    // workgroup -> (image, group, row block, column segment), segment
+    // fastest, XCD-aware: the hardware deals consecutive workgroup ids to the
+    // 8 XCDs in turn, so each XCD is given a contiguous run of tiles instead,
+    // and vertically neighbouring tiles, whose bands share two halo rows,
+    // run on one XCD close in time
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int per = p.wgs >> 3, rem = p.wgs & 7;
+    int t = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int seg = t % p.n_seg;
     t /= p.n_seg;
     const int rb = t % p.n_rb;
