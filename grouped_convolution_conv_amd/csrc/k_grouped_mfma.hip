@@ -16,7 +16,7 @@
 // every B operand from LDS.  grouped16_mfma_kernel (any other W or
 // alignment) reads B straight from memory, described next.  Measured on the
 // 16 cpg-16 shapes of the grouped 3x3 grid, the two beat the VALU register
-// kernel everywhere but one tie (N8 C256 112x112: 91 us against 126;
+// kernel everywhere but one tie (N8 C256 112x112: 87 us against 126;
 // N8 C256 14x14: 6.5 against 18.9); the direct-load form alone was slower
 // than the VALU kernel at N8 C256 112x112 (129 against 125 us): its dword
 // load per B operand keeps the texture address units and the load latency,
@@ -51,6 +51,14 @@ constexpr int kRB = 2;                       // output rows per wave
 
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for the wave's outstanding global loads (the band's second half).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 struct GmParams {
     int C, H, W, K, G;
@@ -221,25 +229,10 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     const int j = lane & 15, kq = lane >> 4;
     const int HW = p.H * p.W;
 
-    // ---- band: piece f = (c * kLRows + lr) * 18 + c4 holds input columns
-    //      ow0 - 4 + 4c4 .. +3 of row oh0 - 1 + lr, channel c of the group
-    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * 16) * HW), (short)0, 16 * HW * (int)sizeof(float),
-        kBufferWord3);
-    constexpr int NPT = (kLPieces + kBlock - 1) / kBlock;
-    float4 pv[NPT];
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int f = i * kBlock + tid;
-        const int c = f / (kLRows * 18), rem = f - c * (kLRows * 18);
-        const int lr = rem / 18, c4 = rem - lr * 18;
-        const int ih = oh0 - 1 + lr, iw = ow0 - 4 + 4 * c4;
-        const bool ok = f < kLPieces && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
-        const int off = ok ? (c * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
-        pv[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
-    }
-
-    // A operands while the band is in flight
+    // A operands and the bias first: they are waited for before the band,
+    // and loads complete in issue order.  The bias comes through a buffer
+    // resource that is empty when there is none (its loads read zero), so no
+    // branch makes the compiler wait for every outstanding load.
     float A[4][9];
     {
         const float *wl = w + ((size_t)(g * 16 + j) * 16 + kq) * 9;
@@ -248,27 +241,68 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
             for (int tp = 0; tp < 9; ++tp) A[q][tp] = wl[q * 36 + tp];
     }
+    const __amdgpu_buffer_rsrc_t bs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(bias ? bias + g * 16 : w), (short)0, bias ? 16 * (int)sizeof(float) : 0, kBufferWord3);
+    float bv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        bv[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs, (4 * kq + v) * (int)sizeof(float), 0, 0));
+    // keep that issue order: loads count down in order, so a wait for the
+    // operands must not also wait for band loads scheduled before them
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- band: piece f = (c * kLRows + lr) * 18 + c4 holds input columns
+    //      ow0 - 4 + 4c4 .. +3 of row oh0 - 1 + lr, channel c of the group
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * 16) * HW), (short)0, 16 * HW * (int)sizeof(float),
+        kBufferWord3);
+    // the band in two halves (channels 0-7, 8-15), all loads issued up front:
+    // the MFMAs of quads 0 and 1 start once the first half is in LDS, while
+    // the second half is still arriving
+    constexpr int HALF = kLPieces / 2;
+    constexpr int NPH = (HALF + kBlock - 1) / kBlock;
+    float4 pv[2][NPH];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < NPH; ++i) {
+            const int f = hf * HALF + i * kBlock + tid;
+            const int c = f / (kLRows * 18), rem = f - c * (kLRows * 18);
+            const int lr = rem / 18, c4 = rem - lr * 18;
+            const int ih = oh0 - 1 + lr, iw = ow0 - 4 + 4 * c4;
+            const bool ok = i * kBlock + tid < HALF && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+            const int off = ok ? (c * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+            pv[hf][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
+            if (i == NPH - 1) __builtin_amdgcn_sched_barrier(0);  // first half before the second
+        }
+
     floatx4 acc[kRB][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const float bv = bias ? bias[g * 16 + 4 * kq + v] : 0.0f;
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int rr = 0; rr < kRB; ++rr)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[rr][b][v] = bv;
-    }
+            for (int b = 0; b < 4; ++b) acc[rr][b][v] = bv[v];
+    auto commit = [&](int hf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        const int f = i * kBlock + tid;
-        if (f < kLPieces) band4[f] = pv[i];
-    }
-    __syncthreads();
+        for (int i = 0; i < NPH; ++i) {
+            const int fi = i * kBlock + tid;
+            if (fi < HALF) band4[hf * HALF + fi] = pv[hf][i];
+        }
+    };
 
     // ---- MFMAs: B of (quad q, output row rr, tap (r, s), block b) is band
     //      channel 4q + kq, row 2*wave + rr + r, column 16b + j + s - 1 + 4
     const float *bl = band + (kq * kLRows + kRB * wave) * kLPitch + j + 3;
+    commit(0);
+    lds_barrier();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+        if (q == 2) {
+            // quads 2 and 3 read channels 8-15: the second half
+            commit(1);
+            lds_barrier();
+        }
         float B[kRB + 2][4][3];
 #pragma unroll
         for (int i = 0; i < kRB + 2; ++i)
