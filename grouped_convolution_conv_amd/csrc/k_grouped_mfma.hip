@@ -207,7 +207,9 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
                                                                     const float *__restrict__ w,
                                                                     const float *__restrict__ bias,
                                                                     float *__restrict__ y, GlParams p) {
-    __shared__ float4 band4[kLPieces];
+    // one half-band buffer (8 channels, 23 KB): both halves are loaded into
+    // registers up front and committed in turn, so five workgroups fit a CU
+    __shared__ float4 band4[kLPieces / 2];
     const float *band = reinterpret_cast<const float *>(band4);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
         for (int i = 0; i < NPH; ++i) {
             const int fi = i * kBlock + tid;
-            if (fi < HALF) band4[hf * HALF + fi] = pv[hf][i];
+            if (fi < HALF) band4[fi] = pv[hf][i];
         }
     };
 
@@ -299,7 +301,9 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         if (q == 2) {
-            // quads 2 and 3 read channels 8-15: the second half
+            // quads 2 and 3 read channels 8-15: once every wave is done with
+            // the first half, the second half replaces it
+            lds_barrier();
             commit(1);
             lds_barrier();
         }
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int s = 0; s < 3; ++s) B[i][b][s] = bl[(4 * q * kLRows + i) * kLPitch + 16 * b + s];
+                for (int s = 0; s < 3; ++s) B[i][b][s] = bl[(4 * (q & 1) * kLRows + i) * kLPitch + 16 * b + s];
 #pragma unroll
         for (int r = 0; r < 3; ++r)
 #pragma unroll
