@@ -70,10 +70,17 @@ extern "C" {
 /* Algorithm choices for conv_desc_set_algo.  AUTO lets the dispatcher pick. */
 #define GCONV_ALGO_AUTO 0
 #define GCONV_ALGO_DIRECT 1     /* one output per lane, any geometry                           */
-#define GCONV_ALGO_GROUPED3X3 2 /* 3x3 stride 1 pad 1 dil 1, <= 4 input channels per group     */
+#define GCONV_ALGO_GROUPED3X3 2 /* 3x3 stride 1 pad 1 dil 1: 1, 2 or 4 input channels per
+                                   group; 8 or 16 (groups > 1, <= 16 output channels per group
+                                   in multiples of 4) when W % 4 == 0 and W <= 256 or the band
+                                   fits 64 KB; 16 in / 16 out per group at any W (run on the
+                                   FP32 matrix cores)                                          */
 #define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
-#define GCONV_ALGO_DEPTHWISE 4  /* depthwise KxK, padding dil*(K/2): (K, stride, dil) = (5,1,1),
-                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2)                          */
+#define GCONV_ALGO_DEPTHWISE 4  /* KxK with padding dil*(K/2), (K, stride, dil) = (5,1,1),
+                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2): depthwise (one input and
+                                   one output channel per group) or groups > 1 of 2 or 4 input
+                                   channels; output width a multiple of 4 up to 256,
+                                   W = stride * output width                                   */
 
 /* How conv_fused_gn_fwd organizes its passes (conv_desc_set_fused_variant). */
 #define GCONV_FUSED_AUTO 0
