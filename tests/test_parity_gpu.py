@@ -379,6 +379,40 @@ def test_wide_groups_register_kernel(wl):
     check_conv(y, y_ref, A, wl.name + " bias")
 
 
+def _fast_path_cases(n, seed):
+    """Random shapes aimed at the register, band, general-geometry and
+    matrix-core paths: channels per group in {1, 2, 4, 8, 16}, output
+    channels per group a multiple of 4 (or equal to the input), the five
+    (K, stride, dilation) geometries with "same" padding and 3x3 stride 1."""
+    rng = np.random.default_rng(seed)
+    geoms = [(3, 1, 1)] * 5 + [(5, 1, 1), (7, 1, 1), (3, 2, 1), (5, 2, 1), (3, 1, 2)]
+    out = []
+    while len(out) < n:
+        cin = int(rng.choice([1, 2, 4, 8, 16]))
+        R, st, dil = geoms[int(rng.integers(len(geoms)))]
+        if (R, st, dil) != (3, 1, 1) and cin > 4:
+            continue
+        cout = cin if cin == 1 and (R, st, dil) != (3, 1, 1) else int(rng.choice([cin, 4, 8, 16]))
+        if (R, st, dil) == (3, 1, 1) and cin > 4 and cout > 16:
+            continue
+        groups = int(rng.integers(2, 5))
+        wo = 4 * int(rng.integers(1, 20)) if rng.random() < 0.8 else int(rng.integers(3, 70))
+        W = st * wo
+        H = int(rng.integers(1, 30))
+        out.append(synth.Workload("fast%d_c%d_k%d_r%ds%dd%d" % (len(out), cin, cout, R, st, dil), int(rng.integers(1, 4)),
+                                  groups * cin, H, W, groups * cout, R, R, st, dil * (R // 2), dil, groups,
+                                  4000 + len(out), ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _fast_path_cases(30, 23), ids=lambda w: w.name)
+def test_fast_path_fuzz(wl):
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    y, algo = gpu_conv(wl, inp)
+    check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
+
+
 def test_repeatable_bitwise():
     for name in ("c4_dense_5x9", "c3a_grouped_g64"):
         wl = SMALL[name]
