@@ -7,7 +7,7 @@
 // arithmetic, HBM-bound for K = 3 and 5.
 //
 // The same register-streaming design as grouped3x3_rows_kernel, for one
-// input channel per group (depthwise) or groups of 2 or 4 input channels,
+// input channel per group (depthwise) or groups of 2, 4, 8 or 16 input channels,
 // with CO output channels per lane:
 //  - a wave owns whole output rows of one (n, group, block of CO output
 //    channels) plane; a lane owns RB output rows x 4 output columns of each
@@ -173,6 +173,16 @@ template <int KS, int ST, int DL>
 hipError_t launch_geom(int CI, int CO, const DwParams &p, const float *x, const float *w, const float *bias,
                        float *y, hipStream_t st) {
     if (CI == 1) return launch_t<KS, ST, DL, 1, 1>(p, x, w, bias, y, st);
+    if (CI == 16) {
+        if (CO == 4) return launch_t<KS, ST, DL, 16, 4>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 16, 2>(p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 16, 1>(p, x, w, bias, y, st);
+    }
+    if (CI == 8) {
+        if (CO == 4) return launch_t<KS, ST, DL, 8, 4>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 8, 2>(p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 8, 1>(p, x, w, bias, y, st);
+    }
     if (CI == 2) {
         if (CO == 2) return launch_t<KS, ST, DL, 2, 2>(p, x, w, bias, y, st);
         return launch_t<KS, ST, DL, 2, 1>(p, x, w, bias, y, st);
@@ -201,15 +211,15 @@ int variant_of(int ks, int st, int dl) {
 // Output channels per lane: the channels per group, up to 4 (1 for depthwise).
 int dw_co(const gconv_desc *d) {
     if (d->cin == 1) return 1;
-    const int lim = d->cin;  // 2 or 4: as many output channels per lane as inputs
+    const int lim = d->cin < 4 ? d->cin : 4;  // as many output channels per lane as inputs, up to 4
     return d->cout % lim == 0 ? lim : (d->cout % 2 == 0 ? 2 : 1);
 }
 
 bool depthwise_supported(const gconv_desc *d) {
-    // depthwise (one input and one output channel per group), or groups of 2
-    // or 4 input channels (any output channels per group)
+    // depthwise (one input and one output channel per group), or groups of
+    // 2, 4, 8 or 16 input channels (any output channels per group)
     const bool dw = d->cin == 1 && d->cout == 1;
-    const bool small_groups = (d->cin == 2 || d->cin == 4) && d->groups > 1;
+    const bool small_groups = (d->cin == 2 || d->cin == 4 || d->cin == 8 || d->cin == 16) && d->groups > 1;
     if (!(dw || small_groups) || d->R != d->S) return false;
     if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;
     const int ks = d->R, st = d->stride_h, dl = d->dil_h;

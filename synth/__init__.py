@@ -149,6 +149,10 @@ EXTRA_WORKLOADS = {
     # grouped layer)
     "g3s2_cpg4_256x56": Workload("g3s2_cpg4_256x56", 16, 256, 56, 56, 256, 3, 3, 2, 1, 1, 64,
                                  216, ("uniform", -1.0, 1.0), _u(1 / 6)),
+    # the same at 8 channels per group (32 groups: a ResNeXt-style
+    # downsampling layer)
+    "g3s2_cpg8_256x56": Workload("g3s2_cpg8_256x56", 16, 256, 56, 56, 256, 3, 3, 2, 1, 1, 32,
+                                 217, ("uniform", -1.0, 1.0), _u(1 / math.sqrt(72))),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

@@ -67,6 +67,12 @@ SMALL = [
     _grp("grp3d2_cpg4", 2, 8, 13, 16, 8, 3, 1, 2, 226, dil=2),
     _grp("grp5s2_cpg2_cout4", 1, 4, 10, 40, 8, 5, 2, 2, 227),
     _grp("grp3s2_cpg4_w512", 1, 8, 9, 512, 8, 3, 2, 2, 228),
+    # groups of 8 or 16 input channels
+    _grp("grp3s2_cpg8", 2, 32, 15, 24, 32, 3, 2, 4, 229),
+    _grp("grp3s2_cpg16_cout8", 1, 32, 10, 32, 16, 3, 2, 2, 230),
+    _grp("grp5_cpg8_cout4", 2, 16, 7, 12, 8, 5, 1, 2, 231),
+    _grp("grp3d2_cpg16", 1, 32, 11, 20, 32, 3, 1, 2, 232, dil=2),
+    _grp("grp7_cpg8_cout6", 1, 16, 9, 8, 12, 7, 1, 2, 233),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
