@@ -87,7 +87,9 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
             for (int q = 0; q < 4; ++q) acc[co][rr][q] = b;
     }
 
-#pragma unroll 1
+    // two input channels per iteration: the second channel's loads can be
+    // issued before the first one's FMAs
+#pragma unroll 2
     for (int ci = 0; ci < CI; ++ci) {
         // weights of the block's output channels for input channel ci
         // (wave-uniform: scalar loads)
