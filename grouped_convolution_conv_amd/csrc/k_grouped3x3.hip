@@ -36,7 +36,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfPlane = 0x7fffffff;
 constexpr int kSmallWaves = 256;    // below this many waves at 2 rows per lane, use 1
 constexpr int kLargeWaves = 8192;   // depthwise with at least this many waves at 4 rows per lane uses 4
-constexpr int kWideWaves = 1536;    // 8 or 16 channels per group: halve the output channels per lane below this
+constexpr int kWideWaves = 1536;    // halve the output channels per lane below this many waves
 constexpr int kWideBlocks = 1024;   // the same for the LDS band kernel's workgroups
 constexpr size_t kWideBandLds = 64 * 1024;  // largest LDS band a wide group may stage
 
@@ -481,10 +481,10 @@ hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w
         // problem is so small that the critical path of one wave dominates
         G3Rows rp;
         int CO = rows_co(d);
-        if (d->cin > 4) {
-            // wide groups: a lane runs 9 * cin FMAs per output it owns, so on
-            // small problems one wave's chain of channels sets the time;
-            // fewer output channels per lane then buy more waves
+        {
+            // a lane runs 9 * cin FMAs per output it owns, so on small
+            // problems one wave's chain of channels sets the time; fewer
+            // output channels per lane then buy more waves
             while (CO > 1) {
                 if (!rows_plan(d, x, y, 2, CO, &rp)) break;
                 if (rp.waves < kSmallWaves) rows_plan(d, x, y, 1, CO, &rp);
