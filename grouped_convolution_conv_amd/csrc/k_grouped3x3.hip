@@ -37,7 +37,7 @@ constexpr int kOutOfPlane = 0x7fffffff;
 constexpr int kSmallWaves = 256;    // below this many waves at 2 rows per lane, use 1
 constexpr int kLargeWaves = 8192;   // depthwise with at least this many waves at 4 rows per lane uses 4
 constexpr int kWideWaves = 1536;    // halve the output channels per lane below this many waves
-constexpr int kWideBlocks = 1024;   // the same for the LDS band kernel's workgroups
+constexpr int kWideBlocks = 512;    // the same for the LDS band kernel's workgroups
 constexpr size_t kWideBandLds = 64 * 1024;  // largest LDS band a wide group may stage
 
 struct G3Params {
@@ -506,18 +506,16 @@ hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w
     int Q;
     long long gx = 0;
     size_t lds = band_plan(d, CO, &p, &Q, &gx);
-    if (d->cin > 4) {
-        if (lds > kWideBandLds) {
-            // wide groups on a band that does not fit (wide rows that are
-            // not 16-byte aligned): the implicit GEMM or the direct kernel
-            if (igemm_supported(d)) return launch_igemm(d, x, w, bias, y, st);
-            return launch_direct(d, x, w, bias, y, st);
-        }
-        // fewer output channels per workgroup buy more workgroups
-        while (CO > 1 && gx * d->groups * (d->cout / CO) * d->N < kWideBlocks) {
-            CO /= 2;
-            lds = band_plan(d, CO, &p, &Q, &gx);
-        }
+    if (d->cin > 4 && lds > kWideBandLds) {
+        // wide groups on a band that does not fit (wide rows that are not
+        // 16-byte aligned): the implicit GEMM or the direct kernel
+        if (igemm_supported(d)) return launch_igemm(d, x, w, bias, y, st);
+        return launch_direct(d, x, w, bias, y, st);
+    }
+    // fewer output channels per workgroup buy more workgroups on small grids
+    while (CO > 1 && gx * d->groups * (d->cout / CO) * d->N < kWideBlocks) {
+        CO /= 2;
+        lds = band_plan(d, CO, &p, &Q, &gx);
     }
     p.vec_load = (d->W % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     p.vec_store = (d->W % 4 == 0) && (((uintptr_t)y & 15u) == 0);
