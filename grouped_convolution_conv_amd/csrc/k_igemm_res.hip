@@ -163,7 +163,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     // The grid walks workgroup tiles (n, kTH output rows, kTW columns); wave
     // w computes rows kNBR*w .. kNBR*w + kNBR-1 of its tile.
     const int G = gridDim.x;
-    int u = blockIdx.x;
+    // Tile of round k for this workgroup.  Rounds that every workgroup runs
+    // (k < kfull) are XCD-aware: the hardware deals consecutive workgroup ids
+    // to the 8 XCDs in turn, and a bijection pb of [0, G) gives each XCD a
+    // contiguous run of tiles instead, so an XCD works on neighbouring tiles,
+    // whose bands share halo rows.  The last, partial round keeps the plain
+    // order, which spreads its tiles over every XCD.
+    const int kfull = p.units / G;
+    int pb;
+    {
+        const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+        const int per = G >> 3, rem = G & 7;
+        pb = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    }
+    auto tile_of = [&](int k) __attribute__((always_inline)) {
+        return k * G + (k < kfull ? pb : (int)blockIdx.x);
+    };
+    int u = tile_of(0);
 
     // ---- band prefetch through registers: pf holds this lane's 16-byte
     //      pieces of a tile's band, zero outside the image
@@ -431,25 +447,26 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     //      keeps the code free of branches around the loads.
     if (u >= p.units) return;
     float2 gst[MB][4];
+    int k = 0;
     load(u);
     commit(bufA4, gsA);
-    load(min(u + G, p.units - 1));
+    load(min(tile_of(1), p.units - 1));
     while (true) {
         lds_barrier();
         mfma_tile(bufA4);
         read_gstat(gsA, gst);
         commit(bufB4, gsB);
-        load(min(u + 2 * G, p.units - 1));
+        load(min(tile_of(k + 2), p.units - 1));
         epilogue(u, gst);
-        u += G;
+        u = tile_of(++k);
         if (u >= p.units) break;
         lds_barrier();
         mfma_tile(bufB4);
         read_gstat(gsB, gst);
         commit(bufA4, gsA);
-        load(min(u + 2 * G, p.units - 1));
+        load(min(tile_of(k + 2), p.units - 1));
         epilogue(u, gst);
-        u += G;
+        u = tile_of(++k);
         if (u >= p.units) break;
     }
 }
