@@ -174,7 +174,11 @@ hipError_t launch_t(const DwParams &p, const float *x, const float *w, const flo
 template <int KS, int ST, int DL>
 hipError_t launch_geom(int CI, int CO, const DwParams &p, const float *x, const float *w, const float *bias,
                        float *y, hipStream_t st) {
-    if (CI == 1) return launch_t<KS, ST, DL, 1, 1>(p, x, w, bias, y, st);
+    if (CI == 1) {
+        if (CO == 4) return launch_t<KS, ST, DL, 1, 4>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 1, 2>(p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 1, 1>(p, x, w, bias, y, st);
+    }
     if (CI == 16) {
         if (CO == 4) return launch_t<KS, ST, DL, 16, 4>(p, x, w, bias, y, st);
         if (CO == 2) return launch_t<KS, ST, DL, 16, 2>(p, x, w, bias, y, st);
@@ -210,17 +214,19 @@ int variant_of(int ks, int st, int dl) {
 
 }  // namespace
 
-// Output channels per lane: the channels per group, up to 4 (1 for depthwise).
+// Output channels per lane: as many as the group has input channels, up to 4;
+// with one input channel per group (a depthwise channel multiplier) up to 4
+// as well, since each loaded input window then feeds only KS * KS FMAs per
+// output channel.  Always a divisor of the group's output channels.
 int dw_co(const gconv_desc *d) {
-    if (d->cin == 1) return 1;
-    const int lim = d->cin < 4 ? d->cin : 4;  // as many output channels per lane as inputs, up to 4
+    const int lim = d->cin == 1 || d->cin >= 4 ? 4 : d->cin;
     return d->cout % lim == 0 ? lim : (d->cout % 2 == 0 ? 2 : 1);
 }
 
 bool depthwise_supported(const gconv_desc *d) {
-    // depthwise (one input and one output channel per group), or groups of
-    // 2, 4, 8 or 16 input channels (any output channels per group)
-    const bool dw = d->cin == 1 && d->cout == 1;
+    // one input channel per group (depthwise, with any channel multiplier),
+    // or groups of 2, 4, 8 or 16 input channels; any output channels per group
+    const bool dw = d->cin == 1;
     const bool small_groups = (d->cin == 2 || d->cin == 4 || d->cin == 8 || d->cin == 16) && d->groups > 1;
     if (!(dw || small_groups) || d->R != d->S) return false;
     if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;

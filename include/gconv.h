@@ -77,9 +77,10 @@ extern "C" {
                                    FP32 matrix cores)                                          */
 #define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
 #define GCONV_ALGO_DEPTHWISE 4  /* KxK with padding dil*(K/2), (K, stride, dil) = (5,1,1),
-                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2): depthwise (one input and
-                                   one output channel per group) or groups > 1 of 2, 4, 8 or 16
-                                   input channels; output width a multiple of 4 up to 256,
+                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2): one input channel per
+                                   group (depthwise, any channel multiplier) or groups > 1 of
+                                   2, 4, 8 or 16 input channels, any output channels per group;
+                                   output width a multiple of 4 up to 256,
                                    W = stride * output width                                   */
 
 /* How conv_fused_gn_fwd organizes its passes (conv_desc_set_fused_variant). */

@@ -153,6 +153,10 @@ EXTRA_WORKLOADS = {
     # downsampling layer)
     "g3s2_cpg8_256x56": Workload("g3s2_cpg8_256x56", 16, 256, 56, 56, 256, 3, 3, 2, 1, 1, 32,
                                  217, ("uniform", -1.0, 1.0), _u(1 / math.sqrt(72))),
+    # depthwise 5x5 with a channel multiplier of 2 (one input and two output
+    # channels per group)
+    "dwm5_mult2_96x56": Workload("dwm5_mult2_96x56", 16, 96, 56, 56, 192, 5, 5, 1, 2, 1, 96,
+                                 218, ("uniform", -1.0, 1.0), _u(1 / 5)),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

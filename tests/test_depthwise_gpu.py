@@ -73,6 +73,14 @@ SMALL = [
     _grp("grp5_cpg8_cout4", 2, 16, 7, 12, 8, 5, 1, 2, 231),
     _grp("grp3d2_cpg16", 1, 32, 11, 20, 32, 3, 1, 2, 232, dil=2),
     _grp("grp7_cpg8_cout6", 1, 16, 9, 8, 12, 7, 1, 2, 233),
+    # one input channel per group with a channel multiplier of 2, 3, 4, 6
+    # and 8 (4, 2 or 1 output channels per lane), also with groups = 1
+    _grp("dwm5_cout2", 2, 6, 13, 20, 12, 5, 1, 6, 234),
+    _grp("dwm3s2_cout4", 2, 4, 14, 16, 16, 3, 2, 4, 235),
+    _grp("dwm7_cout3", 1, 3, 9, 12, 9, 7, 1, 3, 236),
+    _grp("dwm3d2_cout6", 2, 4, 11, 16, 24, 3, 1, 4, 237, dil=2),
+    _grp("dwm5s2_c1_k8", 2, 1, 10, 40, 8, 5, 2, 1, 238),
+    _grp("dwm3s2_cout2_w512", 1, 3, 9, 512, 6, 3, 2, 3, 239),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style

@@ -287,12 +287,16 @@ def test_depthwise_dispatch():
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, H, W, R, st, pad)
         gc.conv_desc_set_algo(d, gc.ALGO_DIRECT)
         gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
-    # groups of 2, 4, 8 or 16 input channels (any output channels per group)
-    # at the same geometries: (C, K, G, H, W, R, stride, pad, dil)
+    # groups of 1, 2, 4, 8 or 16 input channels (any output channels per
+    # group) at the same geometries: (C, K, G, H, W, R, stride, pad, dil)
     for C, K, G, H, W, R, st, pad, dil in [(16, 16, 4, 14, 16, 3, 2, 1, 1), (8, 12, 4, 9, 24, 3, 2, 1, 1),
                                            (8, 16, 2, 11, 20, 5, 1, 2, 1), (4, 4, 2, 9, 12, 7, 1, 3, 1),
                                            (8, 8, 2, 13, 16, 3, 1, 2, 2), (4, 8, 2, 10, 40, 5, 2, 2, 1),
-                                           (32, 32, 4, 14, 16, 3, 2, 1, 1), (32, 16, 2, 9, 24, 5, 1, 2, 1)]:
+                                           (32, 32, 4, 14, 16, 3, 2, 1, 1), (32, 16, 2, 9, 24, 5, 1, 2, 1),
+                                           # one input channel per group, 2, 3 or 8 outputs (channel
+                                           # multiplier), also with a single input channel (groups 1)
+                                           (16, 32, 16, 20, 20, 5, 1, 2, 1), (4, 12, 4, 9, 12, 7, 1, 3, 1),
+                                           (1, 8, 1, 10, 40, 5, 2, 2, 1), (8, 16, 8, 13, 16, 3, 1, 2, 2)]:
         d = gc.conv_desc_create(2, C, H, W, K, R, R, st, pad, dil, G)
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, K, G, H, W, R, st)
     refused = [
@@ -305,7 +309,6 @@ def test_depthwise_dispatch():
         (2, 16, 20, 20, 16, 3, 3, 2, 2, 2, 16),    # 3x3 at stride 2 and dilation 2
         (2, 16, 20, 20, 16, 3, 3, 1, 1, 2, 16),    # dilation 2 with padding 1
         (2, 16, 21, 21, 16, 5, 5, 2, 2, 1, 16),    # 5x5 stride 2 with an odd input width
-        (2, 16, 20, 20, 32, 5, 5, 1, 2, 1, 16),    # two output channels per group
         (2, 12, 20, 20, 12, 5, 5, 1, 2, 1, 4),     # three input channels per group
         (2, 64, 20, 20, 64, 5, 5, 1, 2, 1, 2),     # thirty-two input channels per group
         (2, 4, 20, 20, 8, 3, 3, 2, 1, 1, 1),       # dense (groups = 1)
