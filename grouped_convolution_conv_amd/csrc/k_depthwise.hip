@@ -16,6 +16,10 @@
 //    two 16-byte buffer loads, zero outside the image) and takes the padding
 //    columns to its left and the columns past its right edge from the
 //    neighbouring lanes with cross-lane moves;
+//  - ragged rows (an output width that is not a multiple of 4, an input row
+//    not 16-byte aligned, or an odd input width at stride 2) take the same
+//    kernel with one 4-byte load per column, each zero past the row's end,
+//    and masked 4-byte stores;
 //  - no LDS, no barriers; rows shared by neighbouring lanes and waves come
 //    from the L2.
 #include "dev_common.h"
@@ -34,14 +38,27 @@ struct DwParams {
     int G;        // groups
     int cout;     // output channels per group
     int n_cob;    // blocks of CO output channels per group
-    int cg;       // 4-column output groups per row (Wo / 4)
+    int cg;       // 4-column output groups per row: ceil(Wo / 4)
     int rpw;      // lane strips (of kRB output rows) per wave: 64 / cg
     int strips;   // strips per plane: ceil(Ho / kRB)
     int wpp;      // waves per plane: ceil(strips / rpw)
-    int waves;    // N * G * n_cob * wpp
+    int waves;    // N * G * n_cob * wpp (packed planes: ceil(planes / ppw))
+    // packed planes only
+    int lpp;      // lanes per plane: cg * strips (at most 32)
+    int ppw;      // planes per wave: 64 / lpp
+    int planes;   // N * G * n_cob
+    int x_bytes;  // size of x (below 2^31)
 };
 
-template <int KS, int ST, int DL, int CI, int CO>
+// Row forms.  kAligned: every row holds exactly 4 * ST input columns and 4
+// output columns per lane, 16-byte aligned.  kRagged: one 4-byte load per
+// column, zero past the row's end, masked stores.  kPacked: ragged rows of
+// small planes, several (n, group, channel block) planes per wave, each lane
+// with its own plane (per-lane weights and offsets); for planes that would
+// leave most of a wave's lanes idle (7x7 or 14x14 outputs).
+constexpr int kAligned = 0, kRagged = 1, kPacked = 2;
+
+template <int KS, int ST, int DL, int CI, int CO, int RM>
 __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__restrict__ x,
                                                                 const float *__restrict__ w,
                                                                 const float *__restrict__ bias,
@@ -54,28 +71,54 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
     constexpr int WL = PAD + OWN + RIGHT;            // window: input columns ST*oc0 - PAD ...
     static_assert(PAD <= OWN && RIGHT >= 0 && RIGHT <= OWN, "neighbour exchange reaches one lane");
 
+    constexpr bool RAG = RM != kAligned;
+
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane((int)blockIdx.x * (kBlock / 64) + (int)(threadIdx.x >> 6));
     if (wv >= p.waves) return;  // whole waves only
-    // wave -> (n, group, wave in plane, output-channel block), block fastest:
-    // blocks that read the same input rows are neighbouring waves
-    const int cob = wv % p.n_cob;
-    const int t0 = wv / p.n_cob;
-    const int wip = t0 % p.wpp;
-    const int t1 = t0 / p.wpp;
-    const int g = t1 % p.G, n = t1 / p.G;
+    const int HW = p.H * p.W;
+    int cob, g, n, strip, cgi;
+    bool active;
+    __amdgpu_buffer_rsrc_t rs;
+    int base = 0;  // byte offset of the group's first input plane in rs
+    if constexpr (RM == kPacked) {
+        // lane -> (plane slot, strip, column group); plane -> (n, group,
+        // output-channel block), block fastest
+        const int pl = lane / p.lpp, r = lane - pl * p.lpp;
+        const int sl = r / p.cg;
+        cgi = r - sl * p.cg;
+        strip = sl;
+        const int plane = wv * p.ppw + pl;
+        active = pl < p.ppw && plane < p.planes;
+        const int pc = active ? plane : 0;
+        cob = pc % p.n_cob;
+        const int t1 = pc / p.n_cob;
+        g = t1 % p.G;
+        n = t1 / p.G;
+        // one resource over all of x (below 2^31 bytes)
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x), (short)0, p.x_bytes, kBufferWord3);
+        base = (n * p.C + g * CI) * HW * (int)sizeof(float);
+    } else {
+        // wave -> (n, group, wave in plane, output-channel block), block
+        // fastest: blocks that read the same input rows are neighbouring waves
+        cob = wv % p.n_cob;
+        const int t0 = wv / p.n_cob;
+        const int wip = t0 % p.wpp;
+        const int t1 = t0 / p.wpp;
+        g = t1 % p.G;
+        n = t1 / p.G;
+        const int sl = lane / p.cg;
+        cgi = lane - sl * p.cg;
+        strip = wip * p.rpw + sl;
+        active = sl < p.rpw && strip < p.strips;
+        // one resource over the group's CI input planes
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * CI) * HW),
+                                               (short)0, CI * HW * (int)sizeof(float), kBufferWord3);
+    }
     const int k0 = g * p.cout + cob * CO;
-    const int sl = lane / p.cg, cgi = lane - sl * p.cg;
-    const int strip = wip * p.rpw + sl;
-    const bool active = sl < p.rpw && strip < p.strips;
     const int oh0 = strip * kRB, oc0 = cgi * 4;
     const int ih0 = ST * oh0 - PAD, ic0 = ST * oc0;
     const bool has_left = cgi > 0, has_right = cgi < p.cg - 1;
-    const int HW = p.H * p.W;
-    // one resource over the group's CI input planes
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * CI) * HW), (short)0, CI * HW * (int)sizeof(float),
-        kBufferWord3);
 
     float acc[CO][kRB][4];
 #pragma unroll
@@ -106,12 +149,23 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
 #pragma unroll
         for (int i = 0; i < NIR; ++i) {
             const int ih = ih0 + i;
-            const int rowb = ((ci * p.H + ih) * p.W + ic0) * (int)sizeof(float);
+            const int rowb = base + ((ci * p.H + ih) * p.W + ic0) * (int)sizeof(float);
+            const bool row_in = active && ih >= 0 && ih < p.H;
+            if constexpr (RAG) {
 #pragma unroll
-            for (int v = 0; v < ST; ++v) {
-                const int off = active && ih >= 0 && ih < p.H ? rowb + 16 * v : kOutOfPlane;
-                const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-                own[i][4 * v + 0] = f.x; own[i][4 * v + 1] = f.y; own[i][4 * v + 2] = f.z; own[i][4 * v + 3] = f.w;
+                for (int t = 0; t < OWN; ++t) {
+                    const int off = row_in && ic0 + t < p.W ? rowb + 4 * t : kOutOfPlane;
+                    own[i][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < ST; ++v) {
+                    const int off = row_in ? rowb + 16 * v : kOutOfPlane;
+                    const float4 f =
+                        __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+                    own[i][4 * v + 0] = f.x; own[i][4 * v + 1] = f.y;
+                    own[i][4 * v + 2] = f.z; own[i][4 * v + 3] = f.w;
+                }
             }
         }
 #pragma unroll
@@ -154,48 +208,66 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
 #pragma unroll
         for (int rr = 0; rr < kRB; ++rr) {
             const int oh = oh0 + rr;
-            if (oh < p.Ho)
-                *reinterpret_cast<float4 *>(yb + co * plane_out + (size_t)oh * p.Wo) =
+            if (oh >= p.Ho) continue;
+            float *yr = yb + co * plane_out + (size_t)oh * p.Wo;
+            if constexpr (RAG) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (oc0 + q < p.Wo) yr[q] = acc[co][rr][q];
+            } else {
+                *reinterpret_cast<float4 *>(yr) =
                     make_float4(acc[co][rr][0], acc[co][rr][1], acc[co][rr][2], acc[co][rr][3]);
+            }
         }
 }
 
 template <int KS, int ST, int DL, int CI, int CO>
-hipError_t launch_t(const DwParams &p, const float *x, const float *w, const float *bias, float *y,
+hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, const float *bias, float *y,
                     hipStream_t st) {
     const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
-    hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO>), dim3(grid), dim3(kBlock), 0, st, x, w, bias,
-                       y, p);
+    if (rm == kPacked) {
+        if constexpr (CI == 1)  // packed planes are instantiated for one input channel per group
+            hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kPacked>), dim3(grid), dim3(kBlock), 0,
+                               st, x, w, bias, y, p);
+        else
+            return hipErrorInvalidValue;
+    } else if (rm == kRagged) {
+        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged>), dim3(grid), dim3(kBlock), 0, st,
+                           x, w, bias, y, p);
+    } else {
+        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned>), dim3(grid), dim3(kBlock), 0, st,
+                           x, w, bias, y, p);
+    }
     return hipGetLastError();
 }
 
 // channels per group (CI) and output channels per lane (CO) for one geometry
 template <int KS, int ST, int DL>
-hipError_t launch_geom(int CI, int CO, const DwParams &p, const float *x, const float *w, const float *bias,
+hipError_t launch_geom(int rm, int CI, int CO, const DwParams &p, const float *x, const float *w, const float *bias,
                        float *y, hipStream_t st) {
     if (CI == 1) {
-        if (CO == 4) return launch_t<KS, ST, DL, 1, 4>(p, x, w, bias, y, st);
-        if (CO == 2) return launch_t<KS, ST, DL, 1, 2>(p, x, w, bias, y, st);
-        return launch_t<KS, ST, DL, 1, 1>(p, x, w, bias, y, st);
+        if (CO == 4) return launch_t<KS, ST, DL, 1, 4>(rm, p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 1, 2>(rm, p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 1, 1>(rm, p, x, w, bias, y, st);
     }
     if (CI == 16) {
-        if (CO == 4) return launch_t<KS, ST, DL, 16, 4>(p, x, w, bias, y, st);
-        if (CO == 2) return launch_t<KS, ST, DL, 16, 2>(p, x, w, bias, y, st);
-        return launch_t<KS, ST, DL, 16, 1>(p, x, w, bias, y, st);
+        if (CO == 4) return launch_t<KS, ST, DL, 16, 4>(rm, p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 16, 2>(rm, p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 16, 1>(rm, p, x, w, bias, y, st);
     }
     if (CI == 8) {
-        if (CO == 4) return launch_t<KS, ST, DL, 8, 4>(p, x, w, bias, y, st);
-        if (CO == 2) return launch_t<KS, ST, DL, 8, 2>(p, x, w, bias, y, st);
-        return launch_t<KS, ST, DL, 8, 1>(p, x, w, bias, y, st);
+        if (CO == 4) return launch_t<KS, ST, DL, 8, 4>(rm, p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 8, 2>(rm, p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 8, 1>(rm, p, x, w, bias, y, st);
     }
     if (CI == 2) {
-        if (CO == 2) return launch_t<KS, ST, DL, 2, 2>(p, x, w, bias, y, st);
-        return launch_t<KS, ST, DL, 2, 1>(p, x, w, bias, y, st);
+        if (CO == 2) return launch_t<KS, ST, DL, 2, 2>(rm, p, x, w, bias, y, st);
+        return launch_t<KS, ST, DL, 2, 1>(rm, p, x, w, bias, y, st);
     }
-    if (CO == 4) return launch_t<KS, ST, DL, 4, 4>(p, x, w, bias, y, st);
-    if (CO == 2) return launch_t<KS, ST, DL, 4, 2>(p, x, w, bias, y, st);
-    return launch_t<KS, ST, DL, 4, 1>(p, x, w, bias, y, st);
+    if (CO == 4) return launch_t<KS, ST, DL, 4, 4>(rm, p, x, w, bias, y, st);
+    if (CO == 2) return launch_t<KS, ST, DL, 4, 2>(rm, p, x, w, bias, y, st);
+    return launch_t<KS, ST, DL, 4, 1>(rm, p, x, w, bias, y, st);
 }
 
 }  // namespace
@@ -233,39 +305,56 @@ bool depthwise_supported(const gconv_desc *d) {
     const int ks = d->R, st = d->stride_h, dl = d->dil_h;
     if (d->pad_h != dl * (ks / 2) || d->pad_w != dl * (ks / 2)) return false;
     if (!variant_of(ks, st, dl)) return false;
-    // whole 4-column output groups, one lane's own input columns in whole
-    // 16-byte pieces, a row within one wave, buffer offsets in 32 bits
-    if (d->Wo < 4 || d->Wo % 4 != 0 || d->Wo / 4 > 64 || d->Ho < 1) return false;
-    if (st == 2 && d->W != 2 * d->Wo) return false;
-    if (st == 1 && d->W != d->Wo) return false;
+    // an output row within one wave (64 lanes of 4 columns); the input row
+    // no wider than stride * output width, which this padding implies, so
+    // the last lane of a row needs no columns from a lane it does not have;
+    // buffer offsets in 32 bits
+    if (d->Wo < 1 || d->Wo > 256 || d->Ho < 1) return false;
+    if (d->W > st * d->Wo) return false;
     return (long long)d->cin * (d->H + 16) * d->W * 4 < 0x7fffffffLL;
+}
+
+// Whole rows of 4 * stride input and 4 output columns per lane, 16-byte
+// aligned; anything else takes the ragged form of the kernel.
+static bool depthwise_aligned(const gconv_desc *d, const float *x, const float *y) {
+    return d->Wo % 4 == 0 && d->W == d->stride_h * d->Wo && ((((uintptr_t)x) | ((uintptr_t)y)) & 15u) == 0;
 }
 
 hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w, const float *bias, float *y,
                             hipStream_t st) {
     if (!depthwise_supported(d)) return hipErrorInvalidValue;
-    // 16-byte row pieces need 16-byte aligned planes; other pointers take the
-    // direct kernel, which computes the same outputs
-    if ((((uintptr_t)x) | ((uintptr_t)y)) & 15u) return launch_direct(d, x, w, bias, y, st);
+    int rm = depthwise_aligned(d, x, y) ? kAligned : kRagged;
     const int CO = dw_co(d);
     DwParams p;
     p.C = d->C; p.H = d->H; p.W = d->W; p.Ho = d->Ho; p.Wo = d->Wo; p.K = d->K;
     p.G = d->groups;
     p.cout = d->cout;
     p.n_cob = d->cout / CO;
-    p.cg = d->Wo / 4;
+    p.cg = (d->Wo + 3) / 4;
     p.rpw = 64 / p.cg;
     p.strips = (d->Ho + kRB - 1) / kRB;
     p.wpp = (p.strips + p.rpw - 1) / p.rpw;
     const long long waves = (long long)d->N * d->groups * p.n_cob * p.wpp;
     if (waves > 0x7fffffffLL - 64) return hipErrorInvalidConfiguration;
     p.waves = (int)waves;
+    // small planes with one input channel per group: several planes per
+    // wave when one plane fills at most half of it
+    const long long x_bytes = (long long)d->N * d->C * d->H * d->W * (long long)sizeof(float);
+    const long long planes = (long long)d->N * d->groups * p.n_cob;
+    p.lpp = p.cg * p.strips;
+    if (d->cin == 1 && p.lpp <= 32 && x_bytes < 0x7fffffffLL && planes < 0x7fffffffLL - 64 * 64) {
+        rm = kPacked;
+        p.ppw = 64 / p.lpp;
+        p.planes = (int)planes;
+        p.x_bytes = (int)x_bytes;
+        p.waves = (int)((planes + p.ppw - 1) / p.ppw);
+    }
     switch (variant_of(d->R, d->stride_h, d->dil_h)) {
-        case 1: return launch_geom<5, 1, 1>(d->cin, CO, p, x, w, bias, y, st);
-        case 2: return launch_geom<7, 1, 1>(d->cin, CO, p, x, w, bias, y, st);
-        case 3: return launch_geom<3, 2, 1>(d->cin, CO, p, x, w, bias, y, st);
-        case 4: return launch_geom<5, 2, 1>(d->cin, CO, p, x, w, bias, y, st);
-        default: return launch_geom<3, 1, 2>(d->cin, CO, p, x, w, bias, y, st);
+        case 1: return launch_geom<5, 1, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
+        case 2: return launch_geom<7, 1, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
+        case 3: return launch_geom<3, 2, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
+        case 4: return launch_geom<5, 2, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
+        default: return launch_geom<3, 1, 2>(rm, d->cin, CO, p, x, w, bias, y, st);
     }
 }
 

@@ -157,6 +157,14 @@ EXTRA_WORKLOADS = {
     # channels per group)
     "dwm5_mult2_96x56": Workload("dwm5_mult2_96x56", 16, 96, 56, 56, 192, 5, 5, 1, 2, 1, 96,
                                  218, ("uniform", -1.0, 1.0), _u(1 / 5)),
+    # late-stage depthwise layers whose output width is not a multiple of 4
+    # (14 and 7 columns)
+    "dw5_efficientnet_672x14": Workload("dw5_efficientnet_672x14", 16, 672, 14, 14, 672, 5, 5, 1, 2, 1, 672,
+                                        219, ("uniform", -1.0, 1.0), _u(1 / 5)),
+    "dw7_convnext_768x7": Workload("dw7_convnext_768x7", 16, 768, 7, 7, 768, 7, 7, 1, 3, 1, 768,
+                                   220, ("uniform", -1.0, 1.0), _u(1 / 7)),
+    "dw3s2_mobilenet_576x14": Workload("dw3s2_mobilenet_576x14", 16, 576, 14, 14, 576, 3, 3, 2, 1, 1, 576,
+                                       221, ("uniform", -1.0, 1.0), _u(1 / 3)),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

@@ -81,6 +81,31 @@ SMALL = [
     _grp("dwm3d2_cout6", 2, 4, 11, 16, 24, 3, 1, 4, 237, dil=2),
     _grp("dwm5s2_c1_k8", 2, 1, 10, 40, 8, 5, 2, 1, 238),
     _grp("dwm3s2_cout2_w512", 1, 3, 9, 512, 6, 3, 2, 3, 239),
+    # ragged rows: output widths that are not a multiple of 4 (one lane
+    # partly past the row end), odd input widths at stride 2, one partial
+    # lane, the widest row (64 lanes, the last one partial), 256 outputs
+    # from an odd 511-column input
+    _dw("rag_dw5_h14_w14", 2, 6, 14, 14, 5, 1, 240),
+    _dw("rag_dw7_h7_w7", 2, 5, 7, 7, 7, 1, 241),
+    _dw("rag_dw3s2_h14_w14", 2, 6, 14, 14, 3, 2, 242),
+    _dw("rag_dw3s2_h13_w13", 2, 5, 13, 13, 3, 2, 243),
+    _dw("rag_dw5s2_h11_w21", 1, 4, 11, 21, 5, 2, 244),
+    _dw("rag_dw3d2_h10_w10", 2, 4, 10, 10, 3, 1, 245, dil=2),
+    _dw("rag_dw7_h5_w3", 3, 4, 5, 3, 7, 1, 246),
+    _dw("rag_dw5_h9_w254", 1, 3, 9, 254, 5, 1, 247),
+    _dw("rag_dw3s2_h5_w511", 1, 2, 5, 511, 3, 2, 248),
+    _dw("rag_dw5s2_h1_w9", 2, 3, 1, 9, 5, 2, 249),
+    _grp("rag_grp5_cpg4_w14", 2, 8, 14, 14, 8, 5, 1, 2, 250),
+    _grp("rag_grp3s2_cpg8_w13", 1, 16, 13, 13, 16, 3, 2, 2, 251),
+    _grp("rag_grp3d2_cpg16_cout4_w6", 1, 32, 7, 6, 8, 3, 1, 2, 252, dil=2),
+    _grp("rag_dwm7_cout2_w7", 2, 4, 7, 7, 8, 7, 1, 4, 253),
+    # small planes packed several to a wave (one input channel per group,
+    # a plane filling at most 32 lanes): many waves, a multiplier of 3, a
+    # whole-row-aligned 8x8 plane
+    _dw("pk_dw5_h14_w14_planes", 4, 40, 14, 14, 5, 1, 254),
+    _grp("pk_dwm5_cout3_h3_w3", 3, 7, 3, 3, 21, 5, 1, 7, 255),
+    _dw("pk_dw3d2_h8_w8", 2, 6, 8, 8, 3, 1, 256, dil=2),
+    _dw("pk_dw3s2_h28_w28_planes", 2, 70, 28, 28, 3, 2, 257),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
@@ -94,14 +119,20 @@ def _dev(a):
     return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _run(wl, inp, bias=None, algo=gc.ALGO_AUTO, y_offset=0):
+def _run(wl, inp, bias=None, algo=gc.ALGO_AUTO, y_offset=0, x_offset=0):
+    """Offsets (in floats) place x or y 4 bytes past a 16-byte boundary."""
     d = gc.conv_desc_create(wl.N, wl.C, wl.H, wl.W, wl.K, wl.R, wl.S, wl.stride, wl.pad, wl.dil, wl.groups)
     gc.conv_desc_set_algo(d, algo)
     ho, wo = gc.conv_desc_get_output_dims(d)
     n_out = wl.N * wl.K * ho * wo
     ybuf = torch.full((n_out + y_offset,), float("nan"), device="cuda")
     y = ybuf[y_offset:]
-    gc.conv_fwd(d, _dev(inp["x"]), _dev(inp["w"]), _dev(bias), y.data_ptr() if y_offset else y)
+    x = _dev(inp["x"])
+    if x_offset:
+        xbuf = torch.empty((x.numel() + x_offset,), device="cuda")
+        xbuf[x_offset:] = x.reshape(-1)
+        x = xbuf[x_offset:].data_ptr()
+    gc.conv_fwd(d, x, _dev(inp["w"]), _dev(bias), y.data_ptr() if y_offset else y)
     torch.cuda.synchronize()
     return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
 
@@ -128,9 +159,12 @@ def test_depthwise_small(wl):
         y, used = _run(wl, inp, b)
         assert used == gc.ALGO_DEPTHWISE
         _check(y, y_ref, A, wl.name)
-        # a 4-byte aligned output takes the direct kernel; same outputs
-        y1, _ = _run(wl, inp, b, y_offset=1)
+        # 4-byte aligned output or input: the kernel's ragged-row form
+        y1, used = _run(wl, inp, b, y_offset=1)
+        assert used == gc.ALGO_DEPTHWISE
         _check(y1, y_ref, A, wl.name + " misaligned y")
+        y1, _ = _run(wl, inp, b, x_offset=1)
+        _check(y1, y_ref, A, wl.name + " misaligned x")
 
 
 @pytest.mark.parametrize("wl", SMALL[::3], ids=lambda w: w.name)

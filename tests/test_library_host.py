@@ -278,10 +278,14 @@ def test_per_axis_descriptor_rejects_bad_values():
 
 def test_depthwise_dispatch():
     # (C, H, W, R, stride, pad, dil): depthwise 5x5 / 7x7 stride 1, 3x3 / 5x5
-    # stride 2, 3x3 dilation 2, padding dil * (R // 2), output width a
-    # multiple of 4 up to 256
+    # stride 2, 3x3 dilation 2, padding dil * (R // 2), output width up to
+    # 256
     taken = [(16, 20, 20, 5, 1, 2, 1), (16, 9, 256, 7, 1, 3, 1), (8, 7, 8, 3, 2, 1, 1), (8, 33, 512, 3, 2, 1, 1),
-             (8, 9, 8, 5, 2, 2, 1), (8, 30, 512, 5, 2, 2, 1), (8, 11, 12, 3, 1, 2, 2), (8, 5, 256, 3, 1, 2, 2)]
+             (8, 9, 8, 5, 2, 2, 1), (8, 30, 512, 5, 2, 2, 1), (8, 11, 12, 3, 1, 2, 2), (8, 5, 256, 3, 1, 2, 2),
+             # ragged rows: output widths not a multiple of 4, odd input
+             # widths at stride 2, 256 outputs from 511 input columns
+             (16, 20, 22, 5, 1, 2, 1), (8, 7, 7, 7, 1, 3, 1), (8, 21, 21, 3, 2, 1, 1), (8, 21, 21, 5, 2, 2, 1),
+             (8, 10, 10, 3, 1, 2, 2), (4, 5, 511, 3, 2, 1, 1), (4, 5, 3, 7, 1, 3, 1)]
     for C, H, W, R, st, pad, dil in taken:
         d = gc.conv_desc_create(2, C, H, W, C, R, R, st, pad, dil, C)
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, H, W, R, st, pad)
@@ -301,14 +305,12 @@ def test_depthwise_dispatch():
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, (C, K, G, H, W, R, st)
     refused = [
         (2, 16, 20, 20, 16, 5, 5, 1, 1, 1, 16),    # padding other than R // 2
-        (2, 16, 20, 22, 16, 5, 5, 1, 2, 1, 16),    # output width not a multiple of 4
         (2, 16, 20, 520, 16, 5, 5, 1, 2, 1, 16),   # output row wider than one wave
-        (2, 16, 20, 21, 16, 3, 3, 2, 1, 1, 16),    # stride 2 with an odd input width
+        (2, 16, 20, 514, 16, 3, 3, 2, 1, 1, 16),   # the same at stride 2 (257 outputs)
         (2, 16, 20, 20, 16, 7, 7, 2, 3, 1, 16),    # 7x7 at stride 2
         (2, 16, 20, 20, 16, 5, 5, 1, 4, 2, 16),    # 5x5 at dilation 2
         (2, 16, 20, 20, 16, 3, 3, 2, 2, 2, 16),    # 3x3 at stride 2 and dilation 2
         (2, 16, 20, 20, 16, 3, 3, 1, 1, 2, 16),    # dilation 2 with padding 1
-        (2, 16, 21, 21, 16, 5, 5, 2, 2, 1, 16),    # 5x5 stride 2 with an odd input width
         (2, 12, 20, 20, 12, 5, 5, 1, 2, 1, 4),     # three input channels per group
         (2, 64, 20, 20, 64, 5, 5, 1, 2, 1, 2),     # thirty-two input channels per group
         (2, 4, 20, 20, 8, 3, 3, 2, 1, 1, 1),       # dense (groups = 1)
