@@ -31,7 +31,6 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access, gfx9 family
 constexpr int kOutOfPlane = 0x7fffffff;
-constexpr int kRB = 2;                     // output rows per lane
 
 struct DwParams {
     int C, H, W, Ho, Wo, K;
@@ -39,8 +38,8 @@ struct DwParams {
     int cout;     // output channels per group
     int n_cob;    // blocks of CO output channels per group
     int cg;       // 4-column output groups per row: ceil(Wo / 4)
-    int rpw;      // lane strips (of kRB output rows) per wave: 64 / cg
-    int strips;   // strips per plane: ceil(Ho / kRB)
+    int rpw;      // lane strips (of RB output rows) per wave: 64 / cg
+    int strips;   // strips per plane: ceil(Ho / RB)
     int wpp;      // waves per plane: ceil(strips / rpw)
     int waves;    // N * G * n_cob * wpp (packed planes: ceil(planes / ppw))
     // packed planes only
@@ -48,6 +47,7 @@ struct DwParams {
     int ppw;      // planes per wave: 64 / lpp
     int planes;   // N * G * n_cob
     int x_bytes;  // size of x (below 2^31)
+    int rb;       // output rows per lane (the kernel's RB)
 };
 
 // Row forms.  kAligned: every row holds exactly 4 * ST input columns and 4
@@ -58,14 +58,15 @@ struct DwParams {
 // leave most of a wave's lanes idle (7x7 or 14x14 outputs).
 constexpr int kAligned = 0, kRagged = 1, kPacked = 2;
 
-template <int KS, int ST, int DL, int CI, int CO, int RM>
+// RB: output rows per lane.
+template <int KS, int ST, int DL, int CI, int CO, int RM, int RB>
 __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__restrict__ x,
                                                                 const float *__restrict__ w,
                                                                 const float *__restrict__ bias,
                                                                 float *__restrict__ y, DwParams p) {
     constexpr int PAD = DL * (KS / 2);
     constexpr int SPAN = DL * (KS - 1) + 1;          // input rows (columns) one output sees
-    constexpr int NIR = ST * (kRB - 1) + SPAN;       // input rows a lane reads
+    constexpr int NIR = ST * (RB - 1) + SPAN;       // input rows a lane reads
     constexpr int OWN = 4 * ST;                      // input columns a lane loads itself
     constexpr int RIGHT = SPAN - PAD - ST;           // columns needed past the lane's own ones
     constexpr int WL = PAD + OWN + RIGHT;            // window: input columns ST*oc0 - PAD ...
@@ -116,16 +117,16 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
                                                (short)0, CI * HW * (int)sizeof(float), kBufferWord3);
     }
     const int k0 = g * p.cout + cob * CO;
-    const int oh0 = strip * kRB, oc0 = cgi * 4;
+    const int oh0 = strip * RB, oc0 = cgi * 4;
     const int ih0 = ST * oh0 - PAD, ic0 = ST * oc0;
     const bool has_left = cgi > 0, has_right = cgi < p.cg - 1;
 
-    float acc[CO][kRB][4];
+    float acc[CO][RB][4];
 #pragma unroll
     for (int co = 0; co < CO; ++co) {
         const float b = bias ? bias[k0 + co] : 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < kRB; ++rr)
+        for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[co][rr][q] = b;
     }
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
                 // input row i feeds output row rr through kernel row kr when
                 // i = ST*rr + DL*kr
                 const int di = i - DL * kr;
-                if (di < 0 || di % ST != 0 || di / ST >= kRB) continue;
+                if (di < 0 || di % ST != 0 || di / ST >= RB) continue;
                 const int rr = di / ST;
 #pragma unroll
                 for (int co = 0; co < CO; ++co)
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
 #pragma unroll
     for (int co = 0; co < CO; ++co)
 #pragma unroll
-        for (int rr = 0; rr < kRB; ++rr) {
+        for (int rr = 0; rr < RB; ++rr) {
             const int oh = oh0 + rr;
             if (oh >= p.Ho) continue;
             float *yr = yb + co * plane_out + (size_t)oh * p.Wo;
@@ -227,16 +228,32 @@ hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, c
     const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
     if (rm == kPacked) {
-        if constexpr (CI == 1)  // packed planes are instantiated for one input channel per group
-            hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kPacked>), dim3(grid), dim3(kBlock), 0,
+        // packed planes are instantiated for one input channel per group,
+        // one output row per lane at stride 2 only
+        if constexpr (CI == 1 && ST == 2) {
+            if (p.rb == 1) {
+                hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kPacked, 1>), dim3(grid), dim3(kBlock),
+                                   0, st, x, w, bias, y, p);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (CI == 1)
+            hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kPacked, 2>), dim3(grid), dim3(kBlock), 0,
                                st, x, w, bias, y, p);
         else
             return hipErrorInvalidValue;
     } else if (rm == kRagged) {
-        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged>), dim3(grid), dim3(kBlock), 0, st,
+        if constexpr (CI == 1 && ST == 2) {
+            if (p.rb == 1) {
+                hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged, 1>), dim3(grid), dim3(kBlock),
+                                   0, st, x, w, bias, y, p);
+                return hipGetLastError();
+            }
+        }
+        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged, 2>), dim3(grid), dim3(kBlock), 0, st,
                            x, w, bias, y, p);
     } else {
-        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned>), dim3(grid), dim3(kBlock), 0, st,
+        hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned, 2>), dim3(grid), dim3(kBlock), 0, st,
                            x, w, bias, y, p);
     }
     return hipGetLastError();
@@ -332,7 +349,12 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
     p.n_cob = d->cout / CO;
     p.cg = (d->Wo + 3) / 4;
     p.rpw = 64 / p.cg;
-    p.strips = (d->Ho + kRB - 1) / kRB;
+    // output rows per lane: 2, or 1 for ragged depthwise rows at stride 2,
+    // where a second output row costs 2 more input rows of 2 + K - 1 and
+    // shorter lanes hide more latency (14 -> 7 columns: 8.7 -> 7.4 us; at
+    // stride 1 one row per lane measured no faster)
+    p.rb = rm == kRagged && d->cin == 1 && d->stride_h == 2 ? 1 : 2;
+    p.strips = (d->Ho + p.rb - 1) / p.rb;
     p.wpp = (p.strips + p.rpw - 1) / p.rpw;
     const long long waves = (long long)d->N * d->groups * p.n_cob * p.wpp;
     if (waves > 0x7fffffffLL - 64) return hipErrorInvalidConfiguration;
