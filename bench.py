@@ -64,7 +64,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time the 80-shape grouped 3x3 grid instead of the shape rows: the dispatcher's "
                          "choice against the direct kernel and PyTorch's conv2d, paired batches")
-    ap.add_argument("--sweep-shapes", default="", help="comma-separated subset of the grid (default: all 80)")
+    ap.add_argument("--sweep-shapes", default="",
+                    help="comma-separated grid shapes or general-geometry layers (default: the 80 grid shapes)")
     ap.add_argument("--sweep-out", default="", help="write the per-shape sweep records to this JSON file")
     ap.add_argument("--sweep-no-torch", action="store_true", help="leave PyTorch's conv2d out of the sweep")
     ap.add_argument("--block", action="store_true",
@@ -548,16 +549,19 @@ def sweep(args):
     # the first call (outside every timed region); FP32 arithmetic only
     torch.backends.cudnn.benchmark = True
     torch.backends.cudnn.allow_tf32 = False
+    # the 80-shape grid by default; any grid shape or general-geometry layer
+    # by name
+    known = dict(synth.ATLAS_GRID, **synth.EXTRA_WORKLOADS)
     names = args.sweep_shapes.split(",") if args.sweep_shapes else list(synth.ATLAS_GRID)
-    unknown = [n for n in names if n not in synth.ATLAS_GRID]
+    unknown = [n for n in names if n not in known]
     if unknown:
-        print("bench.py: unknown grid shapes %s" % unknown, file=sys.stderr)
+        print("bench.py: unknown sweep shapes %s" % unknown, file=sys.stderr)
         sys.exit(2)
     log("[sweep] device:", torch.cuda.get_device_name(0), " shapes:", len(names))
     t0 = time.perf_counter()
     records = []
     for i, n in enumerate(names):
-        rec = sweep_shape(synth.ATLAS_GRID[n], gc, torch, args)
+        rec = sweep_shape(known[n], gc, torch, args)
         records.append(rec)
         g = rec["graph"]
         parts = ["%-26s %-10s auto %8.2f us" % (n, rec["algo"], g["auto"]["us"])]
@@ -596,7 +600,8 @@ def sweep(args):
                                               if r["graph"].get("torch_over_auto")]),
                      auto_roofline_frac=geomean([r["graph"]["auto"]["roofline_frac"] for r in rs]))
         for c, rs in sorted(by_cpg.items())}
-    out = dict(metric="grouped 3x3 shape sweep: baseline latency / dispatcher latency (above 1 favours the library), "
+    out = dict(metric=("grouped 3x3 shape sweep" if all(n in synth.ATLAS_GRID for n in names) else "shape sweep") +
+               ": baseline latency / dispatcher latency (above 1 favours the library), "
                       "geomean over shapes, paired batches with 95% bootstrap intervals and a 5% practical threshold",
                shapes=len(records), batches=args.batches, samples=args.samples,
                checks_failed=[r["name"] for r in records if "FAIL" in r["check"].values()],
