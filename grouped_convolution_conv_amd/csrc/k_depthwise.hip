@@ -7,8 +7,8 @@
 // arithmetic, HBM-bound for K = 3 and 5.
 //
 // The same register-streaming design as grouped3x3_rows_kernel, for one
-// input channel per group (depthwise) or groups of 2, 4, 8 or 16 input channels,
-// with CO output channels per lane:
+// input channel per group (depthwise, with any channel multiplier) or groups
+// of 2, 4, 8 or 16 input channels, with CO output channels per lane:
 //  - a wave owns whole output rows of one (n, group, block of CO output
 //    channels) plane; a lane owns RB output rows x 4 output columns of each
 //    of the CO channels, and walks the group's input channels one by one;
@@ -19,7 +19,8 @@
 //  - ragged rows (an output width that is not a multiple of 4, an input row
 //    not 16-byte aligned, or an odd input width at stride 2) take the same
 //    kernel with one 4-byte load per column, each zero past the row's end,
-//    and masked 4-byte stores;
+//    and masked 4-byte stores; small depthwise planes are packed several to
+//    a wave;
 //  - no LDS, no barriers; rows shared by neighbouring lanes and waves come
 //    from the L2.
 #include "dev_common.h"
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kBlock) void depthwise_rows_kernel(const float *__r
                                                                 float *__restrict__ y, DwParams p) {
     constexpr int PAD = DL * (KS / 2);
     constexpr int SPAN = DL * (KS - 1) + 1;          // input rows (columns) one output sees
-    constexpr int NIR = ST * (RB - 1) + SPAN;       // input rows a lane reads
+    constexpr int NIR = ST * (RB - 1) + SPAN;        // input rows a lane reads
     constexpr int OWN = 4 * ST;                      // input columns a lane loads itself
     constexpr int RIGHT = SPAN - PAD - ST;           // columns needed past the lane's own ones
     constexpr int WL = PAD + OWN + RIGHT;            // window: input columns ST*oc0 - PAD ...
