@@ -51,6 +51,7 @@ struct IgParams {
     int vec;           // W, pad multiples of 4 and x 16-byte aligned: 16-byte band loads
     int G;             // groups
     int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
+    int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -321,14 +322,22 @@ __device__ __forceinline__ void lds_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int R, int S, int MB, int CC, bool VEC>
+// ST: stride (1 or 2, both axes).  At stride 2 the band holds the input rows
+// ST*oh0 - pad ... of the tile, and each row's columns in two phases, even
+// input columns first, then odd ones (HW2 of each): output column ow at tap s
+// reads input column 2*ow + s, which is phase s%2, position ow + s/2, so the
+// 32 lanes of a block still read 32 consecutive LDS words.  Stride 2 takes
+// the 4-byte (gather) band loads.
+template <int R, int S, int MB, int CC, bool VEC, int ST>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
+    static_assert(ST == 1 || (ST == 2 && !VEC), "stride 2 gathers its band with 4-byte loads");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
-    constexpr int TIH = kTH + R - 1;
-    constexpr int TIW = kTW + S - 1;
+    constexpr int TIH = ST * (kTH - 1) + R;
+    constexpr int HW2 = kTW + (S - 1) / 2;   // stride 2: columns per phase
+    constexpr int TIW = ST == 1 ? kTW + S - 1 : 2 * HW2;
     constexpr int PITCH = (TIW + 3) & ~3;    // band row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CC * TIH * P4;       // 16-byte pieces of a chunk's band
@@ -396,7 +405,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int e = ii * 64 + lane;
                 const int row = e / PITCH, col = e - row * PITCH;  // row = cl * TIH + lr
                 const int cl = row / TIH, lr = row - cl * TIH;
-                const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + col;
+                const int ih = ST * oh0 - p.pad_h + lr;
+                int iw;
+                if constexpr (ST == 1) {
+                    iw = ow0 - p.pad_w + col;
+                } else {
+                    // band column col: phase col / HW2, position col % HW2
+                    // (columns past both phases read zero)
+                    const int ph = col >= HW2 ? 1 : 0;
+                    iw = col < 2 * HW2 ? ST * ow0 - p.pad_w + 2 * (col - ph * HW2) + ph : -1;
+                }
                 const bool ok = e < XE && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
                 const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64), 4, off, 0, 0, 0);
@@ -472,7 +490,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
-            const float *xq = xin + (cl * TIH + wave * kNBR) * PITCH + j;
+            const float *xq = xin + (cl * TIH + ST * wave * kNBR) * PITCH + j;
             const float *wq = wb + cl * RS * KW + j;
             // kernel rows one at a time: unrolling them all lets the compiler
             // hoist every row's LDS reads and spill with two output blocks
@@ -486,7 +504,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                     for (int br = 0; br < kNBR; ++br)
 #pragma unroll
-                        for (int bc = 0; bc < kNBC; ++bc) b[br * kNBC + bc] = xq[(br + r) * PITCH + bc * 32 + s];
+                        for (int bc = 0; bc < kNBC; ++bc)
+                            b[br * kNBC + bc] = xq[(ST * br + r) * PITCH +
+                                                   (ST == 1 ? bc * 32 + s : (s & 1) * HW2 + bc * 32 + (s >> 1))];
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -557,10 +577,22 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
         // work items itself)
         const dim3 g1((unsigned)p.n_wg);
         clear_stale_launch_error();
-        if (p.vec)
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
-        else
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
+        if (p.st == 2) {
+            // a stride-2 band is about twice as tall and wide per channel:
+            // fewer channels per chunk keep the two buffers within 64 KB
+            if constexpr ((R == 1 && S == 1) || (R == 3 && S == 3)) {
+                constexpr int CC2 = R * S == 1 ? 4 : 2;
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2>), g1, dim3(kBlock), 0, st, x, w, bias,
+                                   y, p);
+            } else {
+                return hipErrorInvalidValue;
+            }
+        } else if (p.vec) {
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
+        } else {
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1>), g1, dim3(kBlock), 0, st, x, w, bias, y,
+                               p);
+        }
         return hipGetLastError();
     } else {
         const size_t lds = lds_bytes(R, S, MB, CC, p.pitch);
@@ -614,6 +646,7 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.vec = 0;
     p.G = d->groups;
     p.n_wg = 0;
+    p.st = d->stride_h;
     return p;
 }
 
@@ -622,14 +655,18 @@ IgParams make_params(const gconv_desc *d, int MB) {
 bool igemm_supported(const gconv_desc *d) {
     // buffer offsets are signed 32-bit: one group's input channels of one
     // image must stay below 2 GB
-    return d->stride_h == 1 && d->stride_w == 1 && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
+    // stride 1, or stride 2 on both axes at 1x1 and 3x3
+    const bool stride_ok = d->stride_h == d->stride_w &&
+                           (d->stride_h == 1 || (d->stride_h == 2 && d->R == d->S && (d->R == 1 || d->R == 3)));
+    return stride_ok && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
            d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
 
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // every output channel of every 32*MB block must exist, and a GroupNorm
     // group must be 4 channels
-    return igemm_supported(d) && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4;
+    // (the fused kernel runs at stride 1 only)
+    return igemm_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4;
 }
 
 int igemm_fused_parts_per_group(const gconv_desc *d, int) {
@@ -643,7 +680,7 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     // read once per block, in exchange for no register spills
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
-    p.vec = (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    p.vec = d->stride_h == 1 && (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_kb;
     const long long n_wg = gy * p.n_tiles * d->N;
     if (gy > 65535 || d->N > 65535 || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

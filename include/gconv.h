@@ -75,7 +75,9 @@ extern "C" {
                                    in multiples of 4) when W % 4 == 0 and W <= 256 or the band
                                    fits 64 KB; 16 in / 16 out per group at any W (run on the
                                    FP32 matrix cores)                                          */
-#define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input channels per group      */
+#define GCONV_ALGO_IGEMM 3      /* FP32 MFMA implicit GEMM, >= 4 input and >= 8 output channels
+                                   per group, dilation 1, stride 1 (R x S in {1x1, 3x3, 5x5,
+                                   5x9, 7x7}) or stride 2 on both axes at 1x1 and 3x3         */
 #define GCONV_ALGO_DEPTHWISE 4  /* KxK with padding dil*(K/2), (K, stride, dil) = (5,1,1),
                                    (7,1,1), (3,2,1), (5,2,1), (3,1,2): one input channel per
                                    group (depthwise, any channel multiplier) or groups > 1 of

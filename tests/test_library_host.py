@@ -134,13 +134,30 @@ def test_dispatch_of_wide_groups():
     assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 64, 20, 32, 64, 3, 3, 1, 1, 1, 2)) == gc.ALGO_IGEMM
 
 
+def test_dispatch_of_stride2_dense_and_wide_groups():
+    # dense and 32-channel-group convs at stride 2, 1x1 and 3x3: the implicit
+    # GEMM (N, C, H, W, K, R, S, stride, pad, dil, groups)
+    for geom in [(2, 64, 56, 56, 64, 3, 3, 2, 1, 1, 1), (2, 256, 56, 56, 128, 1, 1, 2, 0, 1, 1),
+                 (2, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32), (1, 8, 5, 600, 16, 3, 3, 2, 1, 1, 2)]:
+        assert gc.conv_desc_get_algo(gc.conv_desc_create(*geom)) == gc.ALGO_IGEMM, geom
+    # not there: stride 2 at 5x5, dilation 2, unequal strides
+    for geom in [(2, 16, 20, 20, 32, 5, 5, 2, 2, 1, 1), (2, 16, 20, 20, 32, 3, 3, 1, 2, 2, 1)]:
+        d = gc.conv_desc_create(*geom)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_DIRECT, geom
+        with pytest.raises(gc.GconvError) as ei:
+            gc.conv_desc_set_algo(d, gc.ALGO_IGEMM)
+        assert ei.value.status == gc.GCONV_ERR_UNSUPPORTED
+    d = gc.conv_desc_create_2d(2, 16, 20, 20, 32, 3, 3, (2, 1), (1, 1), (1, 1), 1)
+    assert gc.conv_desc_get_algo(d) == gc.ALGO_DIRECT
+
+
 def test_forcing_an_unsupported_algorithm_is_refused():
     d = gc.conv_desc_create(2, 32, 20, 20, 64, 5, 9, 1, 0, 1, 1)
     with pytest.raises(gc.GconvError) as ei:
         gc.conv_desc_set_algo(d, gc.ALGO_GROUPED3X3)
     assert ei.value.status == gc.GCONV_ERR_UNSUPPORTED
     assert gc.conv_desc_get_algo(d) == gc.ALGO_IGEMM   # unchanged
-    d2 = gc.conv_desc_create(2, 4, 20, 20, 4, 3, 3, 2, 1, 1, 4)  # stride 2
+    d2 = gc.conv_desc_create(2, 4, 20, 20, 4, 3, 3, 2, 1, 1, 4)  # one input channel per group
     with pytest.raises(gc.GconvError):
         gc.conv_desc_set_algo(d2, gc.ALGO_IGEMM)
     with pytest.raises(gc.GconvError) as ei:

@@ -344,6 +344,16 @@ EDGE = [
     synth.Workload("igemm_k96_1x1", 1, 12, 9, 65, 96, 1, 1, 1, 0, 1, 1, 48, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_groups2", 1, 16, 11, 35, 128, 7, 7, 1, 3, 1, 2, 49, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_5x9_K130", 1, 6, 12, 40, 130, 5, 9, 1, 1, 1, 1, 50, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # stride 2 on the implicit GEMM (1x1 and 3x3): ragged row and column
+    # tiles, a partial channel chunk, a partial 32-channel block, no padding,
+    # 32 channels per group, and a grouped layer too wide for the register
+    # kernel
+    synth.Workload("igemm_s2_dense3", 2, 8, 19, 70, 40, 3, 3, 2, 1, 1, 1, 76, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_1x1", 2, 6, 17, 131, 16, 1, 1, 2, 0, 1, 1, 77, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_cpg32", 1, 64, 14, 14, 64, 3, 3, 2, 1, 1, 2, 78, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_p0", 1, 16, 20, 20, 32, 3, 3, 2, 0, 1, 1, 79, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_tall", 1, 4, 40, 9, 8, 3, 3, 2, 1, 1, 1, 80, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_grouped_w600", 1, 8, 5, 600, 16, 3, 3, 2, 1, 1, 2, 81, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
@@ -353,6 +363,8 @@ def test_conv_edge_cases(wl):
     y_ref, A = oracle_conv(wl, inp)
     y, algo = gpu_conv(wl, inp)
     _say("[parity] edge", wl.name, gc.ALGO_NAMES[algo])
+    if wl.name.startswith("igemm_s2"):
+        assert algo == gc.ALGO_IGEMM, gc.ALGO_NAMES[algo]
     check_conv(y, y_ref, A, wl.name)
     # an output pointer that is only 4-byte aligned takes the scalar stores
     y1, _ = gpu_conv(wl, inp, y_offset=1)
