@@ -52,6 +52,7 @@ struct IgParams {
     int G;             // groups
     int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
     int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
+    int nbc;           // 32-column blocks per wave row of the DMA kernel (1 at stride 2 on narrow outputs)
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -328,16 +329,23 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // reads input column 2*ow + s, which is phase s%2, position ow + s/2, so the
 // 32 lanes of a block still read 32 consecutive LDS words.  Stride 2 takes
 // the 4-byte (gather) band loads.
-template <int R, int S, int MB, int CC, bool VEC, int ST>
+template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
     static_assert(ST == 1 || (ST == 2 && !VEC), "stride 2 gathers its band with 4-byte loads");
+    static_assert(NBC == NBC || ST == 2, "a one-block-wide tile is a stride-2 form");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
-    constexpr int TIH = ST * (kTH - 1) + R;
-    constexpr int HW2 = kTW + (S - 1) / 2;   // stride 2: columns per phase
-    constexpr int TIW = ST == 1 ? kTW + S - 1 : 2 * HW2;
+    // stride 2: one output row per wave (a 4 x 64 tile), so that narrow
+    // outputs still give enough workgroups and a chunk's band stays small
+    constexpr int NBR = ST == 1 ? kNBR : 1;
+    constexpr int TH = 4 * NBR;
+    // NBC 32-column blocks per wave row (1 on outputs at most 32 wide)
+    constexpr int TW = 32 * NBC;
+    constexpr int TIH = ST * (TH - 1) + R;
+    constexpr int HW2 = TW + (S - 1) / 2;   // stride 2: columns per phase
+    constexpr int TIW = ST == 1 ? TW + S - 1 : 2 * HW2;
     constexpr int PITCH = (TIW + 3) & ~3;    // band row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CC * TIH * P4;       // 16-byte pieces of a chunk's band
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int XI1 = (XE + 63) / 64;      // band DMA instructions (4-byte elements)
     constexpr int WE = CC * RS * KW;         // weight words of a chunk, [q][KW]
     constexpr int WI = (WE + 63) / 64;       // weight DMA instructions
-    constexpr int NB = kNBR * kNBC;
+    constexpr int NB = NBR * NBC;
     constexpr int HALF = CC / 2;
     constexpr int NWAVE = kBlock / 64;
 
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int t2 = t1 / p.n_tiles;
     const int g = t2 % p.G, n = t2 / p.G;
     const int th = tile / p.n_tw, tw = tile - th * p.n_tw;
-    const int oh0 = th * kTH, ow0 = tw * kTW;
+    const int oh0 = th * TH, ow0 = tw * TW;
     const int kg0 = kb * KW;
     const int k0 = g * p.cout + kg0;
     const int kvalid = min(KW, p.cout - kg0);
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
-            const float *xq = xin + (cl * TIH + ST * wave * kNBR) * PITCH + j;
+            const float *xq = xin + (cl * TIH + ST * wave * NBR) * PITCH + j;
             const float *wq = wb + cl * RS * KW + j;
             // kernel rows one at a time: unrolling them all lets the compiler
             // hoist every row's LDS reads and spill with two output blocks
@@ -502,10 +510,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                     for (int m = 0; m < MB; ++m) a[m] = wq[(r * S + s) * KW + m * 32];
 #pragma unroll
-                    for (int br = 0; br < kNBR; ++br)
+                    for (int br = 0; br < NBR; ++br)
 #pragma unroll
-                        for (int bc = 0; bc < kNBC; ++bc)
-                            b[br * kNBC + bc] = xq[(ST * br + r) * PITCH +
+                        for (int bc = 0; bc < NBC; ++bc)
+                            b[br * NBC + bc] = xq[(ST * br + r) * PITCH +
                                                    (ST == 1 ? bc * 32 + s : (s & 1) * HW2 + bc * 32 + (s >> 1))];
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
@@ -538,17 +546,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int br = 0; br < kNBR; ++br) {
-            const int oh = oh0 + wave * kNBR + br;
+        for (int br = 0; br < NBR; ++br) {
+            const int oh = oh0 + wave * NBR + br;
 #pragma unroll
-            for (int bc = 0; bc < kNBC; ++bc) {
+            for (int bc = 0; bc < NBC; ++bc) {
                 const int ow = ow0 + bc * 32 + j;
                 if (oh >= p.Ho || ow >= p.Wo) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int k = m * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                     if (k < kvalid) {
-                        float o = acc[m][br * kNBC + bc][v];
+                        float o = acc[m][br * NBC + bc][v];
                         if (bias) o += bias[k0 + k];
                         yb[(size_t)k * plane + (size_t)oh * p.Wo + ow] = o;
                     }
@@ -578,20 +586,25 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
         const dim3 g1((unsigned)p.n_wg);
         clear_stale_launch_error();
         if (p.st == 2) {
-            // a stride-2 band is about twice as tall and wide per channel:
-            // fewer channels per chunk keep the two buffers within 64 KB
+            // a stride-2 band is twice as wide per channel: fewer channels
+            // per chunk at 3x3 keep the two buffers within 64 KB
             if constexpr ((R == 1 && S == 1) || (R == 3 && S == 3)) {
-                constexpr int CC2 = R * S == 1 ? 4 : 2;
-                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2>), g1, dim3(kBlock), 0, st, x, w, bias,
-                                   y, p);
+                constexpr int CC2 = R * S == 1 ? 8 : 4;
+                if (p.nbc == 1)
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, 1>), g1, dim3(kBlock), 0, st, x, w,
+                                       bias, y, p);
+                else
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, kNBC>), g1, dim3(kBlock), 0, st, x,
+                                       w, bias, y, p);
             } else {
                 return hipErrorInvalidValue;
             }
         } else if (p.vec) {
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1>), g1, dim3(kBlock), 0, st, x, w, bias, y, p);
-        } else {
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1>), g1, dim3(kBlock), 0, st, x, w, bias, y,
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w, bias, y,
                                p);
+        } else {
+            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w, bias,
+                               y, p);
         }
         return hipGetLastError();
     } else {
@@ -640,8 +653,13 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.pad_h = d->pad_h; p.pad_w = d->pad_w;
     p.cin = d->cin; p.cout = d->cout;
     p.n_kb = (d->cout + 32 * MB - 1) / (32 * MB);
-    p.n_tw = (d->Wo + kTW - 1) / kTW;
-    p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
+    // the DMA kernel's stride-2 tile: 4 rows, and one 32-column block on
+    // outputs at most 32 wide
+    p.nbc = d->stride_h == 2 && d->Wo <= 32 ? 1 : kNBC;
+    const int tw = 32 * p.nbc;
+    p.n_tw = (d->Wo + tw - 1) / tw;
+    const int th = d->stride_h == 2 ? 4 : kTH;  // the DMA kernel's stride-2 tile is 4 rows tall
+    p.n_tiles = p.n_tw * ((d->Ho + th - 1) / th);
     p.pitch = kTW + d->S - 1;
     p.vec = 0;
     p.G = d->groups;

@@ -354,6 +354,10 @@ EDGE = [
     synth.Workload("igemm_s2_p0", 1, 16, 20, 20, 32, 3, 3, 2, 0, 1, 1, 79, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_s2_tall", 1, 4, 40, 9, 8, 3, 3, 2, 1, 1, 1, 80, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_s2_grouped_w600", 1, 8, 5, 600, 16, 3, 3, 2, 1, 1, 2, 81, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # exactly 32 output columns (the one-block-wide tile), 3 channel chunks,
+    # a partial third 32-channel block
+    synth.Workload("igemm_s2_w32_k72", 1, 12, 10, 64, 72, 3, 3, 2, 1, 1, 1, 82, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_1x1_w32", 2, 9, 9, 64, 40, 1, 1, 2, 0, 1, 1, 83, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
