@@ -52,7 +52,7 @@ struct IgParams {
     int G;             // groups
     int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
     int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
-    int nbc;           // 32-column blocks per wave row of the DMA kernel (1 at stride 2 on narrow outputs)
+    int nbc;           // 32-column blocks per wave row of the DMA kernel (1 on outputs at most 32 wide)
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -334,7 +334,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
     static_assert(ST == 1 || (ST == 2 && !VEC), "stride 2 gathers its band with 4-byte loads");
-    static_assert(NBC == NBC || ST == 2, "a one-block-wide tile is a stride-2 form");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
     // stride 2: one output row per wave (a 4 x 64 tile), so that narrow
@@ -600,11 +599,19 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
                 return hipErrorInvalidValue;
             }
         } else if (p.vec) {
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w, bias, y,
-                               p);
+            if (p.nbc == 1)
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, 1>), g1, dim3(kBlock), 0, st, x, w, bias,
+                                   y, p);
+            else
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w,
+                                   bias, y, p);
         } else {
-            hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w, bias,
-                               y, p);
+            if (p.nbc == 1)
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, 1>), g1, dim3(kBlock), 0, st, x, w, bias,
+                                   y, p);
+            else
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w,
+                                   bias, y, p);
         }
         return hipGetLastError();
     } else {
@@ -653,13 +660,11 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.pad_h = d->pad_h; p.pad_w = d->pad_w;
     p.cin = d->cin; p.cout = d->cout;
     p.n_kb = (d->cout + 32 * MB - 1) / (32 * MB);
-    // the DMA kernel's stride-2 tile: 4 rows, and one 32-column block on
-    // outputs at most 32 wide
-    p.nbc = d->stride_h == 2 && d->Wo <= 32 ? 1 : kNBC;
-    const int tw = 32 * p.nbc;
-    p.n_tw = (d->Wo + tw - 1) / tw;
-    const int th = d->stride_h == 2 ? 4 : kTH;  // the DMA kernel's stride-2 tile is 4 rows tall
-    p.n_tiles = p.n_tw * ((d->Ho + th - 1) / th);
+    // kTH x kTW tiles (the fused kernel's; launch_igemm sets the DMA
+    // kernel's own)
+    p.nbc = kNBC;
+    p.n_tw = (d->Wo + kTW - 1) / kTW;
+    p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.pitch = kTW + d->S - 1;
     p.vec = 0;
     p.G = d->groups;
@@ -699,6 +704,12 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
     p.vec = d->stride_h == 1 && (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    // the DMA kernel's tile: 8 rows (4 at stride 2) by 64 columns, or by one
+    // 32-column block on outputs at most 32 wide
+    p.nbc = d->Wo <= 32 ? 1 : kNBC;
+    const int th = d->stride_h == 2 ? 4 : kTH, tw = 32 * p.nbc;
+    p.n_tw = (d->Wo + tw - 1) / tw;
+    p.n_tiles = p.n_tw * ((d->Ho + th - 1) / th);
     const long long gy = (long long)d->groups * p.n_kb;
     const long long n_wg = gy * p.n_tiles * d->N;
     if (gy > 65535 || d->N > 65535 || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -358,6 +358,12 @@ EDGE = [
     # a partial third 32-channel block
     synth.Workload("igemm_s2_w32_k72", 1, 12, 10, 64, 72, 3, 3, 2, 1, 1, 1, 82, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_s2_1x1_w32", 2, 9, 9, 64, 40, 1, 1, 2, 0, 1, 1, 83, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # stride 1 on outputs at most 32 wide (the one-block-wide tile): with
+    # the 16-byte band loads (W and padding multiples of 4) and without
+    synth.Workload("igemm_n_w32_1x1_vec", 2, 16, 10, 32, 40, 1, 1, 1, 0, 1, 1, 84, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_w12_5x5_vec", 1, 8, 16, 16, 32, 5, 5, 1, 0, 1, 1, 85, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_w28_cpg32", 2, 64, 28, 28, 64, 3, 3, 1, 1, 1, 2, 86, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_w15_7x7", 1, 6, 9, 15, 16, 7, 7, 1, 3, 1, 1, 87, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
@@ -367,7 +373,7 @@ def test_conv_edge_cases(wl):
     y_ref, A = oracle_conv(wl, inp)
     y, algo = gpu_conv(wl, inp)
     _say("[parity] edge", wl.name, gc.ALGO_NAMES[algo])
-    if wl.name.startswith("igemm_s2"):
+    if wl.name.startswith(("igemm_s2", "igemm_n_")):
         assert algo == gc.ALGO_IGEMM, gc.ALGO_NAMES[algo]
     check_conv(y, y_ref, A, wl.name)
     # an output pointer that is only 4-byte aligned takes the scalar stores
