@@ -65,7 +65,8 @@ def parse():
                     help="time the 80-shape grouped 3x3 grid instead of the shape rows: the dispatcher's "
                          "choice against the direct kernel and PyTorch's conv2d, paired batches")
     ap.add_argument("--sweep-shapes", default="",
-                    help="comma-separated grid shapes or general-geometry layers (default: the 80 grid shapes)")
+                    help="comma-separated grid shapes, general-geometry or implicit-GEMM layers "
+                         "(default: the 80 grid shapes)")
     ap.add_argument("--sweep-out", default="", help="write the per-shape sweep records to this JSON file")
     ap.add_argument("--sweep-no-torch", action="store_true", help="leave PyTorch's conv2d out of the sweep")
     ap.add_argument("--block", action="store_true",
@@ -551,7 +552,7 @@ def sweep(args):
     torch.backends.cudnn.allow_tf32 = False
     # the 80-shape grid by default; any grid shape or general-geometry layer
     # by name
-    known = dict(synth.ATLAS_GRID, **synth.EXTRA_WORKLOADS)
+    known = dict(synth.ATLAS_GRID, **synth.EXTRA_WORKLOADS, **synth.IGEMM_WORKLOADS)
     names = args.sweep_shapes.split(",") if args.sweep_shapes else list(synth.ATLAS_GRID)
     unknown = [n for n in names if n not in known]
     if unknown:

@@ -167,6 +167,22 @@ EXTRA_WORKLOADS = {
                                        221, ("uniform", -1.0, 1.0), _u(1 / 3)),
 }
 
+# Dense and 32-channel-group layers on the implicit GEMM (ResNet- and
+# ResNeXt-style shapes at batch 16), 3x3 at stride 1 and 2 and a 1x1
+# reduction; x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
+IGEMM_WORKLOADS = {
+    "g3s2_cpg32_1024x28": Workload("g3s2_cpg32_1024x28", 16, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32, 901,
+                                   ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
+    "g3_cpg32_512x28": Workload("g3_cpg32_512x28", 16, 512, 28, 28, 512, 3, 3, 1, 1, 1, 16, 903,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
+    "dense3_64x56": Workload("dense3_64x56", 16, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 904,
+                             ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 9))),
+    "dense3s2_128x56": Workload("dense3s2_128x56", 16, 128, 56, 56, 128, 3, 3, 2, 1, 1, 1, 905,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
+    "dense1_256x56": Workload("dense1_256x56", 16, 256, 56, 56, 64, 1, 1, 1, 0, 1, 1, 906,
+                              ("uniform", -1.0, 1.0), _u(1 / 16.0)),
+}
+
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the
 # fixed experiment of the GroupConv Atlas): 80 shapes standing in for the
 # Atlas's own 80-shape list, which is not published.  Batch {1, 8} x
