@@ -53,6 +53,7 @@ struct IgParams {
     int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
     int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
     int nbc;           // 32-column blocks per wave row of the DMA kernel (1 on outputs at most 32 wide)
+    int nbr;           // output rows per wave of the DMA kernel (1 at stride 2 and on small grids)
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -308,6 +309,8 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access, gfx9 fami
 // MFMA loop's operands spill at two waves per SIMD (measured slower)
 constexpr int kPlainMB = 1;
 constexpr int kOutOfRange = 0x7fffffff;
+// below this many workgroups the DMA kernel takes 4-row tiles (two per CU)
+constexpr long long kSmallGridWorkgroups = 512;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
@@ -329,16 +332,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // reads input column 2*ow + s, which is phase s%2, position ow + s/2, so the
 // 32 lanes of a block still read 32 consecutive LDS words.  Stride 2 takes
 // the 4-byte (gather) band loads.
-template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC>
+// NBR output rows per wave (a 4*NBR-row tile): 2, or 1 at stride 2 and on
+// grids too small to fill the chip.
+template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC, int NBR>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
     static_assert(ST == 1 || (ST == 2 && !VEC), "stride 2 gathers its band with 4-byte loads");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
-    // stride 2: one output row per wave (a 4 x 64 tile), so that narrow
-    // outputs still give enough workgroups and a chunk's band stays small
-    constexpr int NBR = ST == 1 ? kNBR : 1;
     constexpr int TH = 4 * NBR;
     // NBC 32-column blocks per wave row (1 on outputs at most 32 wide)
     constexpr int TW = 32 * NBC;
@@ -590,28 +592,34 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
             if constexpr ((R == 1 && S == 1) || (R == 3 && S == 3)) {
                 constexpr int CC2 = R * S == 1 ? 8 : 4;
                 if (p.nbc == 1)
-                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, 1>), g1, dim3(kBlock), 0, st, x, w,
-                                       bias, y, p);
-                else
-                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, kNBC>), g1, dim3(kBlock), 0, st, x,
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, 1, 1>), g1, dim3(kBlock), 0, st, x,
                                        w, bias, y, p);
+                else
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, kNBC, 1>), g1, dim3(kBlock), 0, st,
+                                       x, w, bias, y, p);
             } else {
                 return hipErrorInvalidValue;
             }
         } else if (p.vec) {
             if (p.nbc == 1)
-                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, 1>), g1, dim3(kBlock), 0, st, x, w, bias,
-                                   y, p);
-            else
-                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w,
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, 1, kNBR>), g1, dim3(kBlock), 0, st, x, w,
                                    bias, y, p);
+            else if (p.nbr == 1)
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC, 1>), g1, dim3(kBlock), 0, st, x, w,
+                                   bias, y, p);
+            else
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, true, 1, kNBC, kNBR>), g1, dim3(kBlock), 0, st, x,
+                                   w, bias, y, p);
         } else {
             if (p.nbc == 1)
-                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, 1>), g1, dim3(kBlock), 0, st, x, w, bias,
-                                   y, p);
-            else
-                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC>), g1, dim3(kBlock), 0, st, x, w,
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, 1, kNBR>), g1, dim3(kBlock), 0, st, x, w,
                                    bias, y, p);
+            else if (p.nbr == 1)
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC, 1>), g1, dim3(kBlock), 0, st, x, w,
+                                   bias, y, p);
+            else
+                hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC, false, 1, kNBC, kNBR>), g1, dim3(kBlock), 0, st, x,
+                                   w, bias, y, p);
         }
         return hipGetLastError();
     } else {
@@ -663,6 +671,7 @@ IgParams make_params(const gconv_desc *d, int MB) {
     // kTH x kTW tiles (the fused kernel's; launch_igemm sets the DMA
     // kernel's own)
     p.nbc = kNBC;
+    p.nbr = kNBR;
     p.n_tw = (d->Wo + kTW - 1) / kTW;
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.pitch = kTW + d->S - 1;
@@ -705,13 +714,23 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     IgParams p = make_params(d, MB);
     p.vec = d->stride_h == 1 && (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     // the DMA kernel's tile: 8 rows (4 at stride 2) by 64 columns, or by one
-    // 32-column block on outputs at most 32 wide
+    // 32-column block on outputs at most 32 wide; 4 rows as well when 8-row
+    // tiles would leave fewer than two workgroups per CU (more, smaller
+    // workgroups keep more loads in flight)
     p.nbc = d->Wo <= 32 ? 1 : kNBC;
-    const int th = d->stride_h == 2 ? 4 : kTH, tw = 32 * p.nbc;
-    p.n_tw = (d->Wo + tw - 1) / tw;
-    p.n_tiles = p.n_tw * ((d->Ho + th - 1) / th);
+    p.nbr = d->stride_h == 2 ? 1 : kNBR;
     const long long gy = (long long)d->groups * p.n_kb;
-    const long long n_wg = gy * p.n_tiles * d->N;
+    auto tiles = [&]() {
+        const int th = 4 * p.nbr, tw = 32 * p.nbc;
+        p.n_tw = (d->Wo + tw - 1) / tw;
+        p.n_tiles = p.n_tw * ((d->Ho + th - 1) / th);
+        return gy * p.n_tiles * d->N;
+    };
+    long long n_wg = tiles();
+    if (p.nbr == kNBR && p.nbc == kNBC && n_wg < kSmallGridWorkgroups) {
+        p.nbr = 1;
+        n_wg = tiles();
+    }
     if (gy > 65535 || d->N > 65535 || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     p.n_wg = (int)n_wg;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
