@@ -27,6 +27,7 @@ bool fits_int32(long long a, long long b, long long c, long long d) {
 
 int resolve_algo(const gconv_desc *d) {
     if (d->algo != GCONV_ALGO_AUTO) return d->algo;
+    if (gconv::depthwise_small_3x3_preferred(d)) return GCONV_ALGO_DEPTHWISE;
     if (gconv::grouped3x3_supported(d)) return GCONV_ALGO_GROUPED3X3;
     if (gconv::depthwise_supported(d)) return GCONV_ALGO_DEPTHWISE;
     if (gconv::igemm_supported(d)) return GCONV_ALGO_IGEMM;

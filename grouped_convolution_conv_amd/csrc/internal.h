@@ -55,6 +55,8 @@ struct FusedEpilogue {
 bool grouped3x3_supported(const gconv_desc *d);
 bool igemm_supported(const gconv_desc *d);
 bool depthwise_supported(const gconv_desc *d);
+bool depthwise_small_3x3(const gconv_desc *d);            // small depthwise 3x3 planes (packed kernel)
+bool depthwise_small_3x3_preferred(const gconv_desc *d);  // ... and enough of them to prefer it
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups);
 
 // grouped 3x3 with 16 input and 16 output channels per group on the FP32

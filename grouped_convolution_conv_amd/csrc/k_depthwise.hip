@@ -299,6 +299,7 @@ int variant_of(int ks, int st, int dl) {
     if (ks == 3 && st == 2 && dl == 1) return 3;
     if (ks == 5 && st == 2 && dl == 1) return 4;
     if (ks == 3 && st == 1 && dl == 2) return 5;
+    if (ks == 3 && st == 1 && dl == 1) return 6;  // small depthwise planes only
     return 0;
 }
 
@@ -313,6 +314,33 @@ int dw_co(const gconv_desc *d) {
     return d->cout % lim == 0 ? lim : (d->cout % 2 == 0 ? 2 : 1);
 }
 
+// 3x3, stride 1, padding 1, one input channel per group, on planes small
+// enough that the packed form puts at least two of them in a wave (outputs of
+// about 16 x 16 or less): there the grouped 3x3 kernels would give each plane
+// a wave or a workgroup of its own and leave most lanes idle.
+bool depthwise_small_3x3(const gconv_desc *d) {
+    if (!(d->R == 3 && d->S == 3 && d->stride_h == 1 && d->stride_w == 1 && d->dil_h == 1 && d->dil_w == 1 &&
+          d->pad_h == 1 && d->pad_w == 1 && d->cin == 1))
+        return false;
+    // the launcher's packing rule at two output rows per lane
+    const long long lpp = (long long)((d->Wo + 3) / 4) * ((d->Ho + 1) / 2);
+    const long long x_bytes = (long long)d->N * d->C * d->H * d->W * (long long)sizeof(float);
+    const long long planes = (long long)d->N * d->groups * (d->cout / dw_co(d));
+    return lpp <= 32 && x_bytes < 0x7fffffffLL && planes < 0x7fffffffLL - 64 * 64;
+}
+
+// The dispatcher's choice among the small-plane 3x3 layers: the packed kernel
+// once it has a wave per SIMD (1024 waves); below that the grouped 3x3
+// register kernel, which gives each plane its own wave, measured faster
+// (about 2.8-3.1 against 3.4-3.5 us on 64-512 planes of 14 x 14).
+bool depthwise_small_3x3_preferred(const gconv_desc *d) {
+    if (!depthwise_small_3x3(d)) return false;
+    const long long lpp = (long long)((d->Wo + 3) / 4) * ((d->Ho + 1) / 2);
+    const long long planes = (long long)d->N * d->groups * (d->cout / dw_co(d));
+    const long long ppw = 64 / lpp;
+    return (planes + ppw - 1) / ppw >= 1024;
+}
+
 bool depthwise_supported(const gconv_desc *d) {
     // one input channel per group (depthwise, with any channel multiplier),
     // or groups of 2, 4, 8 or 16 input channels; any output channels per group
@@ -322,7 +350,8 @@ bool depthwise_supported(const gconv_desc *d) {
     if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;
     const int ks = d->R, st = d->stride_h, dl = d->dil_h;
     if (d->pad_h != dl * (ks / 2) || d->pad_w != dl * (ks / 2)) return false;
-    if (!variant_of(ks, st, dl)) return false;
+    const int var = variant_of(ks, st, dl);
+    if (!var || (var == 6 && !depthwise_small_3x3(d))) return false;
     // an output row within one wave (64 lanes of 4 columns); the input row
     // no wider than stride * output width, which this padding implies, so
     // the last lane of a row needs no columns from a lane it does not have;
@@ -377,7 +406,11 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
         case 2: return launch_geom<7, 1, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
         case 3: return launch_geom<3, 2, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
         case 4: return launch_geom<5, 2, 1>(rm, d->cin, CO, p, x, w, bias, y, st);
-        default: return launch_geom<3, 1, 2>(rm, d->cin, CO, p, x, w, bias, y, st);
+        case 5: return launch_geom<3, 1, 2>(rm, d->cin, CO, p, x, w, bias, y, st);
+        default:  // 3x3 stride 1: packed depthwise planes (one input channel per group)
+            if (CO == 4) return launch_t<3, 1, 1, 1, 4>(rm, p, x, w, bias, y, st);
+            if (CO == 2) return launch_t<3, 1, 1, 1, 2>(rm, p, x, w, bias, y, st);
+            return launch_t<3, 1, 1, 1, 1>(rm, p, x, w, bias, y, st);
     }
 }
 

@@ -79,11 +79,12 @@ extern "C" {
                                    per group, dilation 1, stride 1 (R x S in {1x1, 3x3, 5x5,
                                    5x9, 7x7}) or stride 2 on both axes at 1x1 and 3x3         */
 #define GCONV_ALGO_DEPTHWISE 4  /* KxK with padding dil*(K/2), (K, stride, dil) = (5,1,1),
-                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2): one input channel per
+                                   (7,1,1), (3,2,1), (5,2,1), (3,1,2), and (3,1,1) for one input
+                                   channel per group on planes of at most 32 lanes (4-column
+                                   groups x 2-row strips, x below 2 GB): one input channel per
                                    group (depthwise, any channel multiplier) or groups > 1 of
                                    2, 4, 8 or 16 input channels, any output channels per group;
-                                   output width a multiple of 4 up to 256,
-                                   W = stride * output width                                   */
+                                   output width up to 256                                      */
 
 /* How conv_fused_gn_fwd organizes its passes (conv_desc_set_fused_variant). */
 #define GCONV_FUSED_AUTO 0

@@ -165,6 +165,11 @@ EXTRA_WORKLOADS = {
                                    220, ("uniform", -1.0, 1.0), _u(1 / 7)),
     "dw3s2_mobilenet_576x14": Workload("dw3s2_mobilenet_576x14", 16, 576, 14, 14, 576, 3, 3, 2, 1, 1, 576,
                                        221, ("uniform", -1.0, 1.0), _u(1 / 3)),
+    # late-stage depthwise 3x3 stride-1 layers (14x14 and 7x7 planes)
+    "dw3_mobilenet_576x14": Workload("dw3_mobilenet_576x14", 16, 576, 14, 14, 576, 3, 3, 1, 1, 1, 576,
+                                     222, ("uniform", -1.0, 1.0), _u(1 / 3)),
+    "dw3_mobilenet_960x7": Workload("dw3_mobilenet_960x7", 16, 960, 7, 7, 960, 3, 3, 1, 1, 1, 960,
+                                    223, ("uniform", -1.0, 1.0), _u(1 / 3)),
 }
 
 # Dense and 32-channel-group layers on the implicit GEMM (ResNet- and

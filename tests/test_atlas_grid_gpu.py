@@ -29,9 +29,12 @@ CONV_RTOL, CONV_ATOL = 1e-4, 1e-6
 
 
 def _expected_algo(wl):
-    """Every grid shape runs on the grouped kernels: the register kernel when
-    W is a multiple of 4, else the LDS band kernel (its band fits at these
-    widths for 16 channels per group too)."""
+    """The grid's largest depthwise 14x14 shape (2048 planes, two per wave)
+    runs on the packed depthwise kernel; every other shape on the grouped
+    kernels: the register kernel when W is a multiple of 4, else the LDS band
+    kernel (its band fits at these widths for 16 channels per group too)."""
+    if wl.C // wl.groups == 1 and wl.H == 14 and wl.N * wl.C >= 2048:
+        return gc.ALGO_DEPTHWISE
     return gc.ALGO_GROUPED3X3
 
 

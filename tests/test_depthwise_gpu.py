@@ -106,6 +106,14 @@ SMALL = [
     _grp("pk_dwm5_cout3_h3_w3", 3, 7, 3, 3, 21, 5, 1, 7, 255),
     _dw("pk_dw3d2_h8_w8", 2, 6, 8, 8, 3, 1, 256, dil=2),
     _dw("pk_dw3s2_h28_w28_planes", 2, 70, 28, 28, 3, 2, 257),
+    # 3x3 stride 1 on small depthwise planes (packed, chosen over the grouped
+    # 3x3 kernels): 7x7, 14x14 with many waves, a whole-row-aligned 16x16,
+    # a channel multiplier, a single 3-column row
+    _dw("pk_dw3_h7_w7", 2, 5, 7, 7, 3, 1, 258),
+    _dw("pk_dw3_h14_w14_planes", 4, 40, 14, 14, 3, 1, 259),
+    _dw("pk_dw3_h16_w16", 2, 6, 16, 16, 3, 1, 260),
+    _grp("pk_dwm3_cout2_h9_w9", 2, 4, 9, 9, 8, 3, 1, 4, 261),
+    _dw("pk_dw3_h1_w3", 3, 4, 1, 3, 3, 1, 262),
 ]
 
 # The depthwise layers of MobileNet-, EfficientNet- and ConvNeXt-style
@@ -156,14 +164,16 @@ def test_depthwise_small(wl):
     for b in (None, bias):
         _say("[parity] depthwise", wl.name, "bias" if b is not None else "")
         y_ref, A = oracle.conv2d(inp["x"], inp["w"], b, wl.stride, wl.pad, wl.dil, wl.groups)
-        y, used = _run(wl, inp, b)
+        # forced: the dispatcher gives a few small 3x3 planes to the grouped
+        # kernels
+        y, used = _run(wl, inp, b, algo=gc.ALGO_DEPTHWISE)
         assert used == gc.ALGO_DEPTHWISE
         _check(y, y_ref, A, wl.name)
         # 4-byte aligned output or input: the kernel's ragged-row form
-        y1, used = _run(wl, inp, b, y_offset=1)
+        y1, used = _run(wl, inp, b, algo=gc.ALGO_DEPTHWISE, y_offset=1)
         assert used == gc.ALGO_DEPTHWISE
         _check(y1, y_ref, A, wl.name + " misaligned y")
-        y1, _ = _run(wl, inp, b, x_offset=1)
+        y1, _ = _run(wl, inp, b, algo=gc.ALGO_DEPTHWISE, x_offset=1)
         _check(y1, y_ref, A, wl.name + " misaligned x")
 
 
@@ -172,7 +182,7 @@ def test_depthwise_integer_inputs_bit_exact(wl):
     wl = wl.with_(x_dist=("int", -3, 3), w_dist=("int", -2, 2), seed=wl.seed + 500)
     _say("[parity] depthwise int", wl.name)
     inp = synth.make_inputs(wl)
-    y, used = _run(wl, inp)
+    y, used = _run(wl, inp, algo=gc.ALGO_DEPTHWISE)
     assert used == gc.ALGO_DEPTHWISE
     y_ref, _ = oracle.conv2d(inp["x"], inp["w"], None, wl.stride, wl.pad, wl.dil, wl.groups)
     assert np.array_equal(y.astype(np.float64), y_ref)

@@ -134,6 +134,31 @@ def test_dispatch_of_wide_groups():
     assert gc.conv_desc_get_algo(gc.conv_desc_create(2, 64, 20, 32, 64, 3, 3, 1, 1, 1, 2)) == gc.ALGO_IGEMM
 
 
+def test_dispatch_of_small_depthwise_3x3_planes():
+    # 3x3 stride 1 padding 1, one input channel per group, outputs small enough
+    # that a wave holds two or more planes, and at least 1024 such waves: the
+    # packed depthwise kernel (N, C, H, W, K, R, S, stride, pad, dil, groups)
+    for geom in [(16, 960, 7, 7, 960, 3, 3, 1, 1, 1, 960), (16, 576, 14, 14, 576, 3, 3, 1, 1, 1, 576),
+                 (8, 256, 14, 14, 256, 3, 3, 1, 1, 1, 256), (16, 256, 9, 9, 512, 3, 3, 1, 1, 1, 256)]:
+        d = gc.conv_desc_create(*geom)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_DEPTHWISE, geom
+        gc.conv_desc_set_algo(d, gc.ALGO_GROUPED3X3)   # still valid when forced
+    # fewer planes: the grouped kernels by default, the packed one when forced
+    for geom in [(8, 64, 14, 14, 64, 3, 3, 1, 1, 1, 64), (2, 8, 16, 16, 8, 3, 3, 1, 1, 1, 8),
+                 (2, 4, 9, 9, 8, 3, 3, 1, 1, 1, 4), (1, 3, 1, 3, 3, 3, 3, 1, 1, 1, 3)]:
+        d = gc.conv_desc_create(*geom)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3, geom
+        gc.conv_desc_set_algo(d, gc.ALGO_DEPTHWISE)
+    # larger planes, or more input channels per group: the grouped kernels
+    for geom in [(16, 384, 28, 28, 384, 3, 3, 1, 1, 1, 384), (2, 8, 17, 17, 8, 3, 3, 1, 1, 1, 8),
+                 (2, 8, 7, 7, 8, 3, 3, 1, 1, 1, 4)]:
+        d = gc.conv_desc_create(*geom)
+        assert gc.conv_desc_get_algo(d) == gc.ALGO_GROUPED3X3, geom
+    with pytest.raises(gc.GconvError) as ei:
+        gc.conv_desc_set_algo(gc.conv_desc_create(16, 384, 28, 28, 384, 3, 3, 1, 1, 1, 384), gc.ALGO_DEPTHWISE)
+    assert ei.value.status == gc.GCONV_ERR_UNSUPPORTED
+
+
 def test_dispatch_of_stride2_dense_and_wide_groups():
     # dense and 32-channel-group convs at stride 2, 1x1 and 3x3: the implicit
     # GEMM (N, C, H, W, K, R, S, stride, pad, dil, groups)
