@@ -1,6 +1,7 @@
 // k_depthwise.hip -- depthwise K x K convolution with zero padding
 // dilation * (K/2) ("same" padding): K = 5 or 7 at stride 1, K = 3 or 5 at
-// stride 2, and K = 3 at dilation 2 (stride 1).  The GroupConv Atlas
+// stride 2, K = 3 at dilation 2 (stride 1), and K = 3 at stride 1 on small
+// depthwise planes packed several to a wave.  The GroupConv Atlas
 // project page's direct kernel (k0, "Direct mapping") takes any geometry;
 // its k3 card computes four adjacent outputs per thread.  This kernel is the
 // four-outputs-per-lane form for these depthwise geometries.  VALU

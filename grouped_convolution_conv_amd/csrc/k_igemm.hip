@@ -1,5 +1,6 @@
 // k_igemm.hip -- FP32 MFMA implicit GEMM for dense and wide-group
-// convolution (stride 1, dilation 1, any padding).
+// convolution (dilation 1, any padding; stride 1, and stride 2 at 1x1 and
+// 3x3 in the DMA-staged kernel).
 //
 // The implicit-GEMM view of the POPCORNBENCH traces ("Kimi-K2.6 l2_p21",
 // GEMM framing; "Kimi-K2.6 l1_p62", output-channel blocking): per group,
