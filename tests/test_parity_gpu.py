@@ -435,6 +435,61 @@ def test_fast_path_fuzz(wl):
     check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
 
 
+def _wide_path_cases(n, seed):
+    """Random shapes aimed at the depthwise channel multiplier, ragged and
+    packed small planes (any output width, odd stride-2 inputs, 3x3 stride 1
+    forced onto the depthwise kernel), and the implicit GEMM at stride 2 and
+    on narrow or small grids (1x1 and 3x3, dense or grouped)."""
+    rng = np.random.default_rng(seed)
+    geoms = [(3, 1, 1), (5, 1, 1), (7, 1, 1), (3, 2, 1), (5, 2, 1), (3, 1, 2)]
+    out = []
+    while len(out) < n:
+        N = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 24))
+        if rng.random() < 0.5:
+            # one input channel per group, 1-8 outputs per group, any width
+            R, st, dil = geoms[int(rng.integers(len(geoms)))]
+            groups = int(rng.integers(1, 9))
+            cout = int(rng.integers(1, 9))
+            W = int(rng.integers(1, 80))
+            pad = dil * (R // 2)
+            if (W + 2 * pad - dil * (R - 1) - 1) // st + 1 < 1 or (H + 2 * pad - dil * (R - 1) - 1) // st + 1 < 1:
+                continue
+            # 3x3 stride 1 runs on the depthwise kernel only on small planes
+            # (at most 32 lanes: 4-column groups x 2-row strips)
+            if (R, st, dil) == (3, 1, 1) and -(-W // 4) * -(-H // 2) > 32:
+                continue
+            algo = gc.ALGO_DEPTHWISE
+            out.append((synth.Workload("wide%d_dw_m%d_r%ds%dd%d_w%d" % (len(out), cout, R, st, dil, W), N, groups, H, W,
+                                       groups * cout, R, R, st, pad, dil, groups, 5000 + len(out),
+                                       ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)), algo))
+        else:
+            # implicit GEMM: 1x1 or 3x3, stride 1 or 2, dense or grouped
+            R = int(rng.choice([1, 3]))
+            st = int(rng.choice([1, 2]))
+            pad = int(rng.integers(0, R // 2 + 1))
+            groups = int(rng.choice([1, 1, 2]))
+            cin = int(rng.integers(4, 41))
+            cout = int(rng.integers(8, 73))
+            W = int(rng.integers(R, 140))
+            H = max(H, R)
+            out.append((synth.Workload("wide%d_ig_c%d_k%d_r%ds%dp%d_w%d" % (len(out), cin, cout, R, st, pad, W), N,
+                                       groups * cin, H, W, groups * cout, R, R, st, pad, 1, groups, 5000 + len(out),
+                                       ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)), gc.ALGO_IGEMM))
+    return out
+
+
+@pytest.mark.parametrize("case", _wide_path_cases(30, 29), ids=lambda c: c[0].name)
+def test_wide_path_fuzz(case):
+    wl, algo = case
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    _say("[parity] fuzz", wl.name, gc.ALGO_NAMES[algo])
+    y, used = gpu_conv(wl, inp, algo=algo)
+    assert used == algo
+    check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[used]))
+
+
 def test_repeatable_bitwise():
     for name in ("c4_dense_5x9", "c3a_grouped_g64"):
         wl = SMALL[name]
