@@ -545,6 +545,56 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_graph_capture_of_every_kernel_family():
+    """One conv per kernel family captured in a single HIP graph (grouped
+    register and band kernels, matrix-core 16/16 groups, depthwise aligned,
+    ragged and packed, implicit GEMM at stride 1, stride 2 and on a narrow
+    small grid, the direct kernel); every replay equals the eager runs."""
+    shapes = [  # (N, C, H, W, K, R, stride, pad, dil, groups)
+        (2, 16, 20, 32, 16, 3, 1, 1, 1, 4),       # grouped register kernel
+        (2, 16, 13, 30, 16, 3, 1, 1, 1, 4),       # grouped band kernel (W % 4 != 0)
+        (2, 64, 24, 40, 64, 3, 1, 1, 1, 4),       # 16 in / 16 out: matrix cores
+        (2, 8, 20, 40, 8, 5, 1, 2, 1, 8),         # depthwise, aligned rows
+        (2, 8, 21, 21, 16, 3, 2, 1, 1, 8),        # depthwise multiplier, ragged stride-2 rows
+        (16, 1024, 7, 7, 1024, 3, 1, 1, 1, 1024), # depthwise 3x3 small planes, packed
+        (2, 8, 20, 70, 40, 3, 1, 1, 1, 1),        # implicit GEMM, stride 1
+        (2, 8, 19, 70, 40, 3, 2, 1, 1, 1),        # implicit GEMM, stride 2
+        (1, 64, 14, 14, 64, 3, 1, 1, 1, 2),       # implicit GEMM, narrow small grid
+        (2, 6, 11, 13, 9, 3, 2, 1, 2, 3),         # direct kernel
+    ]
+    runs = []
+    for i, (N, C, H, W, K, R, st, pad, dil, G) in enumerate(shapes):
+        wl = synth.Workload("graph%d" % i, N, C, H, W, K, R, R, st, pad, dil, G, 6000 + i,
+                            ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5))
+        inp = synth.make_inputs(wl)
+        d = _desc(wl)
+        ho, wo = gc.conv_desc_get_output_dims(d)
+        x, w = _dev(inp["x"]), _dev(inp["w"])
+        y_eager = torch.empty((N, K, ho, wo), device="cuda")
+        gc.conv_fwd(d, x, w, None, y_eager)
+        runs.append((d, x, w, y_eager, torch.zeros_like(y_eager), gc.ALGO_NAMES[gc.conv_desc_get_algo(d)]))
+    torch.cuda.synchronize()
+    assert {r[5] for r in runs} == {"grouped3x3", "depthwise", "igemm", "direct"}
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for d, x, w, _, y_g, _ in runs:
+                gc.conv_fwd(d, x, w, None, y_g)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        for r in runs:
+            r[4].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, r in enumerate(runs):
+            assert torch.equal(r[4], r[3]), (rep, i, r[5])
+        runs[0][3].add_(0.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_time_graph_helper_outputs_match_eager():
     """gconv_time_graph: positive per-launch times, and the rotated outputs
     equal eager calls on the same buffers (conv and fused entry points)."""
