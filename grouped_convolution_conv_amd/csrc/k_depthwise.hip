@@ -255,6 +255,13 @@ hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, c
         hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged, 2>), dim3(grid), dim3(kBlock), 0, st,
                            x, w, bias, y, p);
     } else {
+        if constexpr (CI == 1 && ST == 2) {
+            if (p.rb == 1) {
+                hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned, 1>), dim3(grid), dim3(kBlock),
+                                   0, st, x, w, bias, y, p);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned, 2>), dim3(grid), dim3(kBlock), 0, st,
                            x, w, bias, y, p);
     }
@@ -380,11 +387,12 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
     p.n_cob = d->cout / CO;
     p.cg = (d->Wo + 3) / 4;
     p.rpw = 64 / p.cg;
-    // output rows per lane: 2, or 1 for ragged depthwise rows at stride 2,
-    // where a second output row costs 2 more input rows of 2 + K - 1 and
-    // shorter lanes hide more latency (14 -> 7 columns: 8.7 -> 7.4 us; at
-    // stride 1 one row per lane measured no faster)
-    p.rb = rm == kRagged && d->cin == 1 && d->stride_h == 2 ? 1 : 2;
+    // output rows per lane: 2, or 1 for depthwise rows at stride 2, where a
+    // second output row costs 2 more input rows of 2 + K - 1 and shorter
+    // lanes hide more latency (3x3 from 144 x 112: 31.9 -> 30.6 us, 5x5 from
+    // 144 x 56: 11.1 -> 10.0 us, 14 -> 7 columns: 8.7 -> 7.4 us; at stride 1
+    // one row per lane measured no faster)
+    p.rb = d->cin == 1 && d->stride_h == 2 ? 1 : 2;
     p.strips = (d->Ho + p.rb - 1) / p.rb;
     p.wpp = (p.strips + p.rpw - 1) / p.rpw;
     const long long waves = (long long)d->N * d->groups * p.n_cob * p.wpp;
