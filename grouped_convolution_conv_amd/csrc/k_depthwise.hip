@@ -230,7 +230,7 @@ hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, c
     const int grid = (p.waves + kBlock / 64 - 1) / (kBlock / 64);
     clear_stale_launch_error();
     if (rm == kPacked) {
-        // packed planes are instantiated for one input channel per group,
+        // packed planes are instantiated for one input channel per group;
         // one output row per lane at stride 2 only
         if constexpr (CI == 1 && ST == 2) {
             if (p.rb == 1) {
@@ -245,7 +245,7 @@ hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, c
         else
             return hipErrorInvalidValue;
     } else if (rm == kRagged) {
-        if constexpr (CI == 1 && ST == 2) {
+        if constexpr (ST == 2) {
             if (p.rb == 1) {
                 hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged, 1>), dim3(grid), dim3(kBlock),
                                    0, st, x, w, bias, y, p);
@@ -255,7 +255,7 @@ hipError_t launch_t(int rm, const DwParams &p, const float *x, const float *w, c
         hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kRagged, 2>), dim3(grid), dim3(kBlock), 0, st,
                            x, w, bias, y, p);
     } else {
-        if constexpr (CI == 1 && ST == 2) {
+        if constexpr (ST == 2) {
             if (p.rb == 1) {
                 hipLaunchKernelGGL((depthwise_rows_kernel<KS, ST, DL, CI, CO, kAligned, 1>), dim3(grid), dim3(kBlock),
                                    0, st, x, w, bias, y, p);
@@ -387,12 +387,13 @@ hipError_t launch_depthwise(const gconv_desc *d, const float *x, const float *w,
     p.n_cob = d->cout / CO;
     p.cg = (d->Wo + 3) / 4;
     p.rpw = 64 / p.cg;
-    // output rows per lane: 2, or 1 for depthwise rows at stride 2, where a
-    // second output row costs 2 more input rows of 2 + K - 1 and shorter
-    // lanes hide more latency (3x3 from 144 x 112: 31.9 -> 30.6 us, 5x5 from
-    // 144 x 56: 11.1 -> 10.0 us, 14 -> 7 columns: 8.7 -> 7.4 us; at stride 1
-    // one row per lane measured no faster)
-    p.rb = d->cin == 1 && d->stride_h == 2 ? 1 : 2;
+    // output rows per lane: 2, or 1 at stride 2, where a second output row
+    // costs 2 more input rows of 2 + K - 1 and shorter lanes hide more
+    // latency (depthwise 3x3 from 144 x 112: 31.9 -> 30.6 us, 5x5 from
+    // 144 x 56: 11.1 -> 10.0 us, 14 -> 7 columns: 8.7 -> 7.4 us; grouped 3x3
+    // with 4 and 8 channels per group: 18.7 -> 16.9 and 22.9 -> 20.9 us; at
+    // stride 1 one row per lane measured slower)
+    p.rb = d->stride_h == 2 ? 1 : 2;
     p.strips = (d->Ho + p.rb - 1) / p.rb;
     p.wpp = (p.strips + p.rpw - 1) / p.rpw;
     const long long waves = (long long)d->N * d->groups * p.n_cob * p.wpp;
