@@ -20,6 +20,7 @@ GCONV_ERR_INVALID_ARG = 1
 GCONV_ERR_WORKSPACE = 2
 GCONV_ERR_UNSUPPORTED = 3
 GCONV_ERR_LAUNCH = 4
+GCONV_ERR_SCRATCH_LIMIT = 5
 
 ALGO_AUTO = 0
 ALGO_DIRECT = 1
@@ -37,8 +38,8 @@ FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recom
 EXPORTED = (
     "conv_desc_create", "conv_desc_create_2d", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
     "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
-    "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "gconv_time_graph", "gconv_probe_peaks",
-    "gconv_status_string", "gconv_last_launch_error",
+    "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "conv_fused_gn_fwd_noalloc", "gconv_time_graph",
+    "gconv_probe_peaks", "conv_fused_gn_noalloc_limit", "gconv_status_string", "gconv_last_launch_error",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -65,6 +66,8 @@ _lib.conv_desc_get_fused_variant.argtypes = [_p, _i, ctypes.POINTER(_i)]
 _lib.conv_fwd.argtypes = [_p, _p, _p, _p, _p, _p]
 _lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
 _lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
+_lib.conv_fused_gn_fwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p]
+_lib.conv_fused_gn_noalloc_limit.argtypes = []
 _lib.gconv_time_graph.argtypes = [_p, _i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _p, _p, _p, _p, _p, _i,
                                   ctypes.c_float, _p, _sz, _i, _i, ctypes.POINTER(ctypes.c_float), _p]
 _lib.gconv_probe_peaks.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _p, _p]
@@ -74,6 +77,7 @@ _lib.gconv_last_launch_error.argtypes = []
 _lib.gconv_last_launch_error.restype = ctypes.c_char_p
 for _name in EXPORTED[:-2]:
     getattr(_lib, _name).restype = _i
+_lib.conv_fused_gn_noalloc_limit.restype = _sz
 
 
 class GconvError(RuntimeError):
@@ -214,6 +218,21 @@ def conv_fused_gn_fwd(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups:
     _check("conv_fused_gn_fwd", _lib.conv_fused_gn_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale),
                                                        _ptr(gamma), _ptr(beta), gn_groups, float(eps), _ptr(y),
                                                        wsp, workspace_bytes, _stream(stream)))
+
+
+def conv_fused_gn_fwd_noalloc(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups: int, eps: float, y,
+                              stream=None) -> None:
+    """The fused chain without a caller workspace: the library's static
+    scratch array (conv_fused_gn_noalloc_limit() bytes per GPU) holds the
+    GroupNorm statistics.  Calls that overlap on one GPU race."""
+    _check("conv_fused_gn_fwd_noalloc",
+           _lib.conv_fused_gn_fwd_noalloc(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(gamma),
+                                          _ptr(beta), gn_groups, float(eps), _ptr(y), _stream(stream)))
+
+
+def conv_fused_gn_noalloc_limit() -> int:
+    """Bytes of the static scratch array behind conv_fused_gn_fwd_noalloc."""
+    return int(_lib.conv_fused_gn_noalloc_limit())
 
 
 def gconv_time_graph(desc: ConvDesc, xs, ys, w, bias=None, launches: int = 1, replays: int = 1, fused=None,

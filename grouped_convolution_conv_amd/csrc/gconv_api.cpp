@@ -87,13 +87,98 @@ size_t partials_bytes(const gconv_desc *d, int gn_groups) {
 // HIP error behind the most recent GCONV_ERR_LAUNCH of the calling thread.
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
+}  // namespace
+
+namespace gconv {
+
 int launch_status(hipError_t e) {
     if (e == hipSuccess) return GCONV_OK;
     g_last_hip_error = e;
     return GCONV_ERR_LAUNCH;
 }
 
+}  // namespace gconv
+
+namespace {
+using gconv::launch_status;
 }  // namespace
+
+namespace gconv {
+
+int fused_workspace_bytes(const gconv_desc *d, int gn_groups, size_t *bytes) {
+    if (!d || !bytes) return GCONV_ERR_INVALID_ARG;
+    if (gn_groups < 1 || d->K % gn_groups != 0) return GCONV_ERR_INVALID_ARG;
+    size_t b = partials_bytes(d, gn_groups);
+    if (resolve_fused_variant(d, gn_groups) == GCONV_FUSED_RECOMPUTE)
+        b += (sizeof(float2) * (size_t)d->N * (size_t)gn_groups + 15) & ~(size_t)15;
+    *bytes = b;
+    return GCONV_OK;
+}
+
+int fused_gn_run(const gconv_desc *d, const float *x, const float *w, const float *bias,
+                 const float *scale, const float *gamma, const float *beta, int gn_groups, float eps, float *y,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!d || !x || !w || !bias || !scale || !y) return GCONV_ERR_INVALID_ARG;
+    if (gn_groups < 1 || d->K % gn_groups != 0 || !(eps > 0.0f)) return GCONV_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y | (uintptr_t)bias | (uintptr_t)scale |
+         (uintptr_t)gamma | (uintptr_t)beta) & 3u)
+        return GCONV_ERR_INVALID_ARG;
+    size_t need = 0;
+    fused_workspace_bytes(d, gn_groups, &need);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return GCONV_ERR_WORKSPACE;
+    hipStream_t st = (hipStream_t)stream;
+    const StageA stage = fused_stage_a(d, gn_groups);
+    const int variant = resolve_fused_variant(d, gn_groups);
+    if (variant == GCONV_FUSED_RECOMPUTE && stage != kStageResident) return GCONV_ERR_UNSUPPORTED;
+    gconv::FusedEpilogue ep;
+    ep.bias = bias;
+    ep.scale = scale;
+    ep.parts = (gconv::Partial *)workspace;
+    ep.gn_groups = gn_groups;
+    ep.gn_cpg = d->K / gn_groups;
+    ep.parts_per_group = fused_parts_per_group(d, gn_groups);
+    int rc;
+    if (variant == GCONV_FUSED_RECOMPUTE) {
+        float2 *gstat = (float2 *)((char *)workspace + partials_bytes(d, gn_groups));
+        rc = launch_status(gconv::launch_igemm_res_stats(d, x, w, nullptr, false, ep, st));
+        if (rc != GCONV_OK) return rc;
+        rc = launch_status(gconv::launch_gn_merge(d, ep.parts, gn_groups, ep.parts_per_group, eps, gstat, st));
+        if (rc != GCONV_OK) return rc;
+        return launch_status(gconv::launch_igemm_res_normalize(d, x, w, y, ep, gstat, gamma, beta, st));
+    }
+    // The store variant writes v and then normalizes it in place.  It runs
+    // over slices of the batch whose v fits the GPU's last-level (Infinity)
+    // cache with room to spare, so the normalize pass finds v there and HBM
+    // sees x read once and the output written once.  A GroupNorm group never
+    // spans two images, so slicing the batch changes no arithmetic.
+    const size_t x_img = (size_t)d->C * d->H * d->W;
+    const size_t y_img = (size_t)d->K * d->Ho * d->Wo;
+    long long per = (long long)(kStoreSliceBytes / (y_img * sizeof(float)));
+    if (per < 1) per = 1;
+    const int slice = per < d->N ? (int)per : d->N;
+    for (int n0 = 0; n0 < d->N; n0 += slice) {
+        gconv_desc ds = *d;
+        ds.N = d->N - n0 < slice ? d->N - n0 : slice;
+        const float *xs = x + (size_t)n0 * x_img;
+        float *ys = y + (size_t)n0 * y_img;
+        gconv::FusedEpilogue es = ep;
+        es.parts = ep.parts + (size_t)n0 * gn_groups * ep.parts_per_group;
+        hipError_t e;
+        switch (stage) {
+            case kStageResident: e = gconv::launch_igemm_res_stats(&ds, xs, w, ys, true, es, st); break;
+            case kStageIgemm: e = gconv::launch_igemm_fused(&ds, xs, w, ys, es, st); break;
+            default: e = gconv::launch_direct_fused(&ds, xs, w, ys, es, st); break;
+        }
+        rc = launch_status(e);
+        if (rc != GCONV_OK) return rc;
+        rc = launch_status(gconv::launch_gn_normalize(&ds, ys, es.parts, gn_groups, es.parts_per_group, gamma,
+                                                      beta, eps, st));
+        if (rc != GCONV_OK) return rc;
+    }
+    return GCONV_OK;
+}
+
+}  // namespace gconv
 
 extern "C" {
 
@@ -191,76 +276,14 @@ int conv_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias, 
 }
 
 int conv_fused_gn_workspace_size(gconv_desc_t d, int gn_groups, size_t *bytes) {
-    if (!d || !bytes) return GCONV_ERR_INVALID_ARG;
-    if (gn_groups < 1 || d->K % gn_groups != 0) return GCONV_ERR_INVALID_ARG;
-    size_t b = partials_bytes(d, gn_groups);
-    if (resolve_fused_variant(d, gn_groups) == GCONV_FUSED_RECOMPUTE)
-        b += (sizeof(float2) * (size_t)d->N * (size_t)gn_groups + 15) & ~(size_t)15;
-    *bytes = b;
-    return GCONV_OK;
+    return gconv::fused_workspace_bytes(d, gn_groups, bytes);
 }
 
 int conv_fused_gn_fwd(gconv_desc_t d, const float *x, const float *w, const float *bias,
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream) {
-    if (!d || !x || !w || !bias || !scale || !y) return GCONV_ERR_INVALID_ARG;
-    if (gn_groups < 1 || d->K % gn_groups != 0 || !(eps > 0.0f)) return GCONV_ERR_INVALID_ARG;
-    if (((uintptr_t)x | (uintptr_t)w | (uintptr_t)y | (uintptr_t)bias | (uintptr_t)scale |
-         (uintptr_t)gamma | (uintptr_t)beta) & 3u)
-        return GCONV_ERR_INVALID_ARG;
-    size_t need = 0;
-    conv_fused_gn_workspace_size(d, gn_groups, &need);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u)) return GCONV_ERR_WORKSPACE;
-    hipStream_t st = (hipStream_t)stream;
-    const StageA stage = fused_stage_a(d, gn_groups);
-    const int variant = resolve_fused_variant(d, gn_groups);
-    if (variant == GCONV_FUSED_RECOMPUTE && stage != kStageResident) return GCONV_ERR_UNSUPPORTED;
-    gconv::FusedEpilogue ep;
-    ep.bias = bias;
-    ep.scale = scale;
-    ep.parts = (gconv::Partial *)workspace;
-    ep.gn_groups = gn_groups;
-    ep.gn_cpg = d->K / gn_groups;
-    ep.parts_per_group = fused_parts_per_group(d, gn_groups);
-    int rc;
-    if (variant == GCONV_FUSED_RECOMPUTE) {
-        float2 *gstat = (float2 *)((char *)workspace + partials_bytes(d, gn_groups));
-        rc = launch_status(gconv::launch_igemm_res_stats(d, x, w, nullptr, false, ep, st));
-        if (rc != GCONV_OK) return rc;
-        rc = launch_status(gconv::launch_gn_merge(d, ep.parts, gn_groups, ep.parts_per_group, eps, gstat, st));
-        if (rc != GCONV_OK) return rc;
-        return launch_status(gconv::launch_igemm_res_normalize(d, x, w, y, ep, gstat, gamma, beta, st));
-    }
-    // The store variant writes v and then normalizes it in place.  It runs
-    // over slices of the batch whose v fits the GPU's last-level (Infinity)
-    // cache with room to spare, so the normalize pass finds v there and HBM
-    // sees x read once and the output written once.  A GroupNorm group never
-    // spans two images, so slicing the batch changes no arithmetic.
-    const size_t x_img = (size_t)d->C * d->H * d->W;
-    const size_t y_img = (size_t)d->K * d->Ho * d->Wo;
-    long long per = (long long)(kStoreSliceBytes / (y_img * sizeof(float)));
-    if (per < 1) per = 1;
-    const int slice = per < d->N ? (int)per : d->N;
-    for (int n0 = 0; n0 < d->N; n0 += slice) {
-        gconv_desc ds = *d;
-        ds.N = d->N - n0 < slice ? d->N - n0 : slice;
-        const float *xs = x + (size_t)n0 * x_img;
-        float *ys = y + (size_t)n0 * y_img;
-        gconv::FusedEpilogue es = ep;
-        es.parts = ep.parts + (size_t)n0 * gn_groups * ep.parts_per_group;
-        hipError_t e;
-        switch (stage) {
-            case kStageResident: e = gconv::launch_igemm_res_stats(&ds, xs, w, ys, true, es, st); break;
-            case kStageIgemm: e = gconv::launch_igemm_fused(&ds, xs, w, ys, es, st); break;
-            default: e = gconv::launch_direct_fused(&ds, xs, w, ys, es, st); break;
-        }
-        rc = launch_status(e);
-        if (rc != GCONV_OK) return rc;
-        rc = launch_status(gconv::launch_gn_normalize(&ds, ys, es.parts, gn_groups, es.parts_per_group, gamma,
-                                                      beta, eps, st));
-        if (rc != GCONV_OK) return rc;
-    }
-    return GCONV_OK;
+    return gconv::fused_gn_run(d, x, w, bias, scale, gamma, beta, gn_groups, eps, y, workspace, workspace_bytes,
+                               stream);
 }
 
 const char *gconv_last_launch_error(void) {
@@ -274,6 +297,8 @@ const char *gconv_status_string(int status) {
         case GCONV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case GCONV_ERR_UNSUPPORTED: return "algorithm does not support this geometry";
         case GCONV_ERR_LAUNCH: return "kernel launch failed";
+        case GCONV_ERR_SCRATCH_LIMIT:
+            return "problem needs more scratch than the allocation-free entry point's static buffer holds";
         default: return "unknown status";
     }
 }

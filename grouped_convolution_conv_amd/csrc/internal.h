@@ -34,6 +34,10 @@ namespace gconv {
 // the error they return belongs to their own launch.
 inline void clear_stale_launch_error() { (void)hipGetLastError(); }
 
+// GCONV_OK for hipSuccess; otherwise records `e` for gconv_last_launch_error
+// and returns GCONV_ERR_LAUNCH.
+int launch_status(hipError_t e);
+
 // Per-tile GroupNorm statistics written by a fused stage-A kernel and read by
 // the normalize kernel: element count, mean and sum of squared deviations
 // from that mean (the fourth slot is padding).
@@ -99,6 +103,15 @@ hipError_t launch_gn_merge(const gconv_desc *d, const Partial *parts, int gn_gro
 hipError_t launch_igemm_res_normalize(const gconv_desc *d, const float *x, const float *w, float *y,
                                       const FusedEpilogue &ep, const float2 *gstat,
                                       const float *gamma, const float *beta, hipStream_t st);
+
+// ---- the fused chain as a whole (both compute entry points of the chain) -
+// Device workspace bytes of the fused chain for gn_groups groups.
+int fused_workspace_bytes(const gconv_desc *d, int gn_groups, size_t *bytes);
+// Validates the arguments and enqueues the fused chain on `stream` with the
+// given workspace; returns a GCONV_* status.
+int fused_gn_run(const gconv_desc *d, const float *x, const float *w, const float *bias, const float *scale,
+                 const float *gamma, const float *beta, int gn_groups, float eps, float *y, void *workspace,
+                 size_t workspace_bytes, void *stream);
 
 // ---- fused chain, stage B: merge statistics, normalize y in place -------
 hipError_t launch_gn_normalize(const gconv_desc *d, float *y, const Partial *parts,

@@ -66,6 +66,8 @@ extern "C" {
 #define GCONV_ERR_WORKSPACE 2   /* workspace missing or smaller than required                  */
 #define GCONV_ERR_UNSUPPORTED 3 /* a forced algorithm does not cover this geometry             */
 #define GCONV_ERR_LAUNCH 4      /* the HIP runtime refused a kernel launch                     */
+#define GCONV_ERR_SCRATCH_LIMIT 5 /* conv_fused_gn_fwd_noalloc: the problem needs more scratch
+                                     than the library's static buffer holds                     */
 
 /* Algorithm choices for conv_desc_set_algo.  AUTO lets the dispatcher pick. */
 #define GCONV_ALGO_AUTO 0
@@ -164,6 +166,28 @@ int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes
 int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * chain and arguments as conv_fused_gn_fwd, without the workspace.  The
+ * chain's scratch memory (per-tile GroupNorm partials and merged
+ * statistics) is a static device array inside the library,
+ * conv_fused_gn_noalloc_limit() bytes (16 MiB) on every GPU the library
+ * runs on, held until the process ends.  The call allocates and frees
+ * nothing.  Its first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress); make that first call outside stream capture.
+ * Returns GCONV_ERR_SCRATCH_LIMIT, before enqueuing anything, when
+ * conv_fused_gn_workspace_size exceeds the limit (the fused 8 -> 32 chain
+ * on 64 images of 256 x 256 needs 4 MiB).  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (concurrent streams or host
+ * threads) race: serialize them.  Nothing in the array needs to start at
+ * zero; every value is written by the call before it is read. */
+int conv_fused_gn_fwd_noalloc(gconv_desc_t desc, const float *x, const float *w, const float *bias,
+                              const float *scale, const float *gamma, const float *beta, int gn_groups,
+                              float eps, float *y, void *stream);
+
+/* Bytes of the static scratch array behind conv_fused_gn_fwd_noalloc. */
+size_t conv_fused_gn_noalloc_limit(void);
 
 /* Timing harness for the graph boundary of the GroupConv Atlas page
  * ("Method": device events around launches captured in a CUDA graph).

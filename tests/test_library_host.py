@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert gc.gconv_status_string(code)
     assert gc.gconv_status_string(99) == "unknown status"
 
@@ -376,3 +376,23 @@ def test_probe_peaks_validates_before_any_device_call():
     assert lib.gconv_probe_peaks(None, ctypes.byref(f), ctypes.c_void_p(16), None) == gc.GCONV_ERR_INVALID_ARG
     assert lib.gconv_probe_peaks(ctypes.byref(f), None, ctypes.c_void_p(16), None) == gc.GCONV_ERR_INVALID_ARG
     assert lib.gconv_probe_peaks(ctypes.byref(f), ctypes.byref(f), None, None) == gc.GCONV_ERR_INVALID_ARG
+
+
+def test_noalloc_entry_point_refuses_before_any_device_call():
+    """conv_fused_gn_fwd_noalloc checks the descriptor, the group count and
+    the static scratch limit before touching the device."""
+    lib = gc.library()
+    assert gc.conv_fused_gn_noalloc_limit() == 16 << 20
+    fake = 1 << 20
+    wl = synth.WORKLOADS["c5_fused_gn"]
+    d = _desc(wl.with_(N=1024))  # 64 MiB of GroupNorm partials
+    assert gc.conv_fused_gn_workspace_size(d, 8) > gc.conv_fused_gn_noalloc_limit()
+    args = [fake] * 6
+    assert lib.conv_fused_gn_fwd_noalloc(d.handle, *args, 8, ctypes.c_float(1e-5), fake, None) == \
+        gc.GCONV_ERR_SCRATCH_LIMIT
+    assert lib.conv_fused_gn_fwd_noalloc(None, *args, 8, ctypes.c_float(1e-5), fake, None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.conv_fused_gn_fwd_noalloc(d.handle, *args, 5, ctypes.c_float(1e-5), fake, None) == \
+        gc.GCONV_ERR_INVALID_ARG
+    # the full fused workload fits
+    assert gc.conv_fused_gn_workspace_size(_desc(wl), 8) <= gc.conv_fused_gn_noalloc_limit()
+
