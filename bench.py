@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 METRIC = "per-shape GB/s + GFLOP/s, % roofline, geomean; hipGraph vs sync-API timing"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense FP32 matrix, published
-FP32_VALU_PEAK_TFLOPS = 78.6   # 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz (no packed FP32)
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X FP32 vector, published (non-packed FMA chains measure above the
+                               # 78.6 TFLOP/s that one FMA per lane per clock would allow)
 COLD_BYTES = 512 << 20
 
 
@@ -79,24 +80,20 @@ def parse():
 COPY_BYTES = 256 << 20  # bytes read (and as many written) by one calibration copy
 
 
-def copy_calibration(torch, reps=20):
-    """Plain device-to-device copy of COPY_BYTES: the practical streaming rate
-    (read + write bytes / time) and the reference launch for scaling HBM
-    traffic counters (its FETCH_SIZE and WRITE_SIZE are each COPY_BYTES)."""
+def copy_calibration(torch, gc):
+    """The library's own streaming copy (gconv_probe_copy) over COPY_BYTES,
+    well beyond the 256 MB last-level cache: the measured HBM rate (bytes
+    read + written per second, fastest of five launches).  Its dispatches
+    (copy_probe_kernel) are also the reference launch for scaling HBM
+    traffic counters: each reads and writes exactly COPY_BYTES."""
     n = COPY_BYTES // 4
     src = torch.empty(n, device="cuda").uniform_()
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    b.record()
-    torch.cuda.synchronize()
-    t = a.elapsed_time(b) / 1e3 / reps
-    return dict(bytes_per_launch=2 * COPY_BYTES, ms=t * 1e3, gbs=2 * COPY_BYTES / t / 1e9)
+    gbs = gc.gconv_probe_copy(dst, src)
+    ok = bool(torch.equal(dst, src))
+    del src, dst
+    return dict(bytes_per_launch=2 * COPY_BYTES, gbs=gbs, kernel="copy_probe_kernel", copy_equal=ok)
 
 
 # ------------------------------------------------------------------ work accounting
@@ -111,7 +108,7 @@ def row_accounting(wl, ho, wo):
     macs = y * (wl.C // wl.groups) * wl.R * wl.S
     flops = 2 * macs
     byts = 4 * (x + w + y + vec)
-    # dense rows run on FP32 MFMA, grouped rows on the (non-packed) FP32 VALU
+    # dense rows run on FP32 MFMA, grouped rows on the FP32 VALU
     peak = FP32_MFMA_PEAK_TFLOPS if wl.groups == 1 else FP32_VALU_PEAK_TFLOPS
     t_mem, t_cmp = byts / (HBM_PEAK_GBS * 1e9), flops / (peak * 1e12)
     if t_mem >= t_cmp:
@@ -279,7 +276,18 @@ def sync_boundary(row, torch, batches, samples):
 
 # ------------------------------------------------------------------ CPU baseline
 
-CPU_ROW_SECONDS = 2.5   # target oracle time per row: ~7 rows x 2.5 s of host work
+CPU_ROW_SECONDS = 1.0   # target oracle time per row and run: 7 rows x 3 runs x ~1 s of host work
+CPU_RUNS = 3            # timed runs per row; the median is reported
+
+
+def cpu_threads():
+    """Host threads for the oracle: OMP_NUM_THREADS when the environment
+    sets it (the CPU share a job on this host is given), else every CPU this
+    process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
 
 
 def cpu_baseline(rows):
@@ -287,10 +295,10 @@ def cpu_baseline(rows):
 
     Each row runs on its first n images, n chosen from a one-image probe so
     that the row takes about CPU_ROW_SECONDS; rows whose whole batch is
-    faster than that are repeated.  The probe is timed too and its time is
-    folded into the row's figure when it is the sample itself (n = 1)."""
+    faster than that are repeated within a run.  Every row is timed
+    CPU_RUNS times and the median run is reported."""
     import oracle
-    threads = oracle.default_threads()
+    threads = cpu_threads()
     per_row = {}
     total = 0.0
 
@@ -313,23 +321,24 @@ def cpu_baseline(rows):
         reps = 1
         if n == wl.N:
             reps = int(max(1, min(1000, round(CPU_ROW_SECONDS / max(t1 * wl.N, 1e-6)))))
-        if n == 1 and reps == 1:
-            dt = t1
-        else:
+        runs = []
+        for _ in range(CPU_RUNS):
             dt = 0.0
             for _ in range(reps):
                 dt += run(wl, inp, n)
-            dt /= reps
-            total += dt * reps
+            total += dt
+            runs.append(dt / reps)
+        dt = float(np.median(runs))
         a = row_accounting(wl.with_(N=n), r.ho, r.wo)
-        per_row[r.name] = dict(samples_n=n, repeats=reps, seconds=dt, gbs=a["bytes"] / dt / 1e9,
+        per_row[r.name] = dict(samples_n=n, repeats=reps, runs_s=runs, seconds=dt, gbs=a["bytes"] / dt / 1e9,
                                gflops=a["flops"] / dt / 1e9)
-        log("[cpu] %-20s N=%d x%d  %.3f s  %.3f GB/s  %.3f GFLOP/s"
-            % (r.name, n, reps, dt, per_row[r.name]["gbs"], per_row[r.name]["gflops"]))
+        log("[cpu] %-20s N=%d x%d  median of %d: %.3f s  %.3f GB/s  %.3f GFLOP/s"
+            % (r.name, n, reps, CPU_RUNS, dt, per_row[r.name]["gbs"], per_row[r.name]["gflops"]))
     return dict(value=geomean([v["gbs"] for v in per_row.values()]),
                 unit="GB/s (geomean of rows, oracle fp64 on the host)", cores=threads, kind="oracle",
-                cpu_model=cpu_model(),
-                sample="each row on its first n images (repeated when the whole batch is short): " +
+                cpu_model=cpu_model(), host_cpus=os.cpu_count(),
+                sample="each row on its first n images (repeated when the whole batch is short), median of %d "
+                       "runs: " % CPU_RUNS +
                        ", ".join("%s n=%d x%d" % (k, v["samples_n"], v["repeats"]) for k, v in per_row.items()),
                 seconds=total, rows=per_row)
 
@@ -346,8 +355,9 @@ def cpu_model():
 
 
 def measured_floor_s(acct, wl, peaks):
-    """Floor time against what this GPU sustains: the measured copy rate and
-    the measured FP32 MFMA (dense rows) or FMA (grouped rows) peak."""
+    """Floor time against what this GPU sustains: the library's measured copy
+    rate and the measured FP32 MFMA (dense rows) or FP32 FMA (grouped rows)
+    rate."""
     peak = peaks["fp32_mfma_tflops"] if wl.groups == 1 else peaks["fp32_fma_tflops"]
     return max(acct["bytes"] / (peaks["hbm_copy_gbs"] * 1e9), acct["flops"] / (peak * 1e12))
 
@@ -781,12 +791,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    copy = copy_calibration(torch)
-    log("[bench] plain copy of %d MiB: %.1f GB/s (read + write)" % (COPY_BYTES >> 20, copy["gbs"]))
+    copy = copy_calibration(torch, gc)
+    log("[bench] library copy of %d MiB: %.1f GB/s (read + write)" % (COPY_BYTES >> 20, copy["gbs"]))
     sink = torch.zeros(4, device="cuda")
-    mfma_meas, fma_meas = gc.gconv_probe_peaks(sink)
-    peaks = dict(fp32_mfma_tflops=mfma_meas, fp32_fma_tflops=fma_meas, hbm_copy_gbs=copy["gbs"])
-    log("[bench] measured peaks: FP32 MFMA %.1f TFLOP/s, FP32 FMA %.1f TFLOP/s" % (mfma_meas, fma_meas))
+    mfma_meas, _ = gc.gconv_probe_peaks(sink)
+    fma_meas, fp64_meas = gc.gconv_probe_vector_peaks(sink)
+    peaks = dict(fp32_mfma_tflops=mfma_meas, fp32_fma_tflops=fma_meas, fp64_fma_tflops=fp64_meas,
+                 hbm_copy_gbs=copy["gbs"])
+    log("[bench] measured peaks: FP32 MFMA %.1f TFLOP/s, FP32 FMA %.1f TFLOP/s, FP64 FMA %.1f TFLOP/s"
+        % (mfma_meas, fma_meas, fp64_meas))
     if args.copy_only:
         print(json.dumps({"copy_calibration": copy}), flush=True)
         return

@@ -39,11 +39,11 @@ EXPORTED = (
     "conv_desc_create", "conv_desc_create_2d", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
     "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
     "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "conv_fused_gn_fwd_noalloc", "gconv_time_graph",
-    "gconv_probe_peaks", "conv_fused_gn_noalloc_limit", "gconv_status_string", "gconv_last_launch_error",
+    "gconv_probe_peaks", "gconv_probe_vector_peaks", "gconv_probe_copy", "conv_fused_gn_noalloc_limit", "gconv_status_string", "gconv_last_launch_error",
 )
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libgconv.so is not built; run `python -m grouped_convolution_conv_amd.build` "
+    raise ImportError("libgconv.so is not built; run `python grouped_convolution_conv_amd/build.py` "
                       "(or __graft_entry__.build())")
 
 # One HIP runtime per process: torch ships its own libamdhip64 (soname
@@ -71,6 +71,8 @@ _lib.conv_fused_gn_noalloc_limit.argtypes = []
 _lib.gconv_time_graph.argtypes = [_p, _i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _p, _p, _p, _p, _p, _i,
                                   ctypes.c_float, _p, _sz, _i, _i, ctypes.POINTER(ctypes.c_float), _p]
 _lib.gconv_probe_peaks.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _p, _p]
+_lib.gconv_probe_vector_peaks.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float), _p, _p]
+_lib.gconv_probe_copy.argtypes = [ctypes.POINTER(ctypes.c_float), _p, _p, _sz, _p]
 _lib.gconv_status_string.argtypes = [_i]
 _lib.gconv_status_string.restype = ctypes.c_char_p
 _lib.gconv_last_launch_error.argtypes = []
@@ -271,6 +273,26 @@ def gconv_probe_peaks(sink, stream=None):
     m, f = ctypes.c_float(), ctypes.c_float()
     _check("gconv_probe_peaks", _lib.gconv_probe_peaks(ctypes.byref(m), ctypes.byref(f), _ptr(sink), _stream(stream)))
     return float(m.value), float(f.value)
+
+
+def gconv_probe_vector_peaks(sink, stream=None):
+    """Measured (non-packed FP32 FMA, FP64 FMA) rates of the current GPU in
+    TFLOP/s.  sink: a device tensor (or raw pointer) of at least 4 bytes."""
+    a, b = ctypes.c_float(), ctypes.c_float()
+    _check("gconv_probe_vector_peaks",
+           _lib.gconv_probe_vector_peaks(ctypes.byref(a), ctypes.byref(b), _ptr(sink), _stream(stream)))
+    return float(a.value), float(b.value)
+
+
+def gconv_probe_copy(dst, src, nbytes: int = None, stream=None) -> float:
+    """Streaming copy rate (bytes read + written per second, in GB/s) of the
+    library's own copy kernel over `nbytes` (default: all of src)."""
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    g = ctypes.c_float()
+    _check("gconv_probe_copy", _lib.gconv_probe_copy(ctypes.byref(g), _ptr(dst), _ptr(src), int(nbytes),
+                                                     _stream(stream)))
+    return float(g.value)
 
 
 def library():

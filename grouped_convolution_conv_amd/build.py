@@ -1,6 +1,6 @@
 """Builds libgconv.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m grouped_convolution_conv_amd.build
+    python grouped_convolution_conv_amd/build.py
 
 Each source under csrc/ is compiled to an object in parallel, then linked
 into grouped_convolution_conv_amd/libgconv.so.  Packed FP32 instructions are

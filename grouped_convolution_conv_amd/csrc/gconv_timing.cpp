@@ -6,6 +6,7 @@
 // that what lies between the two events is nothing but the captured kernels.
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <vector>
 
 #include "gconv.h"
@@ -140,6 +141,52 @@ __global__ __launch_bounds__(kProbeBlock) void fma_peak_kernel(float *sink, int 
     if (s == kNever) sink[0] = s;
 }
 
+// Vector-ALU peaks: kVecChains independent FMA chains per lane, eight
+// workgroups (32 waves) per CU, in FP32 and in FP64.  The FP64 probe is the
+// control: its datasheet peak (256 CUs x 4 SIMDs x 16 lanes x 2 flop x
+// 2.4 GHz = 78.6 TFLOP/s) is what the same loop shape reaches when each lane
+// retires one FMA per clock.
+constexpr int kVecChains = 16;
+
+template <typename T>
+__global__ __launch_bounds__(kProbeBlock) void vec_fma_peak_kernel(float *sink, int iters) {
+    T v[kVecChains];
+    for (int i = 0; i < kVecChains; ++i) v[i] = (T)threadIdx.x * (T)1e-3 + (T)i;
+    const T a = (T)0.999, b = (T)0.001;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < kVecChains; ++i) v[i] = fma(v[i], a, b);
+    }
+    T s = 0;
+    for (int i = 0; i < kVecChains; ++i) s += v[i];
+    if (s == (T)kNever) sink[0] = (float)s;
+}
+
+// Streaming copy for the measured HBM rate: each lane moves kCopyUnroll
+// 16-byte pieces per round (all loads issued before the stores), rounds
+// grid-strided over the buffer.
+constexpr int kCopyUnroll = 4;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(kProbeBlock) void copy_probe_kernel(f32x4 *__restrict__ dst,
+                                                                 const f32x4 *__restrict__ src, size_t n4) {
+    const size_t stride = (size_t)gridDim.x * kProbeBlock * kCopyUnroll;
+    for (size_t base = (size_t)blockIdx.x * kProbeBlock * kCopyUnroll + threadIdx.x; base < n4; base += stride) {
+        f32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + (size_t)u * kProbeBlock;
+            if (i < n4) v[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t i = base + (size_t)u * kProbeBlock;
+            if (i < n4) __builtin_nontemporal_store(v[u], dst + i);
+        }
+    }
+}
+
 struct EventPair {
     hipEvent_t a = nullptr, b = nullptr;
     ~EventPair() {
@@ -165,6 +212,61 @@ int time_probe(K kern, int blocks, float *sink, int iters, hipStream_t st, float
 }
 
 }  // namespace
+
+extern "C" int gconv_probe_vector_peaks(float *fp32_tflops, float *fp64_tflops, float *sink, void *stream) {
+    if (!fp32_tflops || !fp64_tflops || !sink) return GCONV_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return GCONV_ERR_LAUNCH;
+    const int blocks = 8 * cus;  // eight workgroups (32 waves) per CU
+    const int iters = 4096;      // a few ms per probe
+    const double flops = (double)blocks * kProbeBlock * iters * kVecChains * 2.0;
+    float ms = 0.0f;
+    int rc = time_probe(vec_fma_peak_kernel<float>, blocks, sink, iters, st, &ms);
+    if (rc != GCONV_OK) return rc;
+    *fp32_tflops = (float)(flops / (ms * 1e-3) / 1e12);
+    rc = time_probe(vec_fma_peak_kernel<double>, blocks, sink, iters, st, &ms);
+    if (rc != GCONV_OK) return rc;
+    *fp64_tflops = (float)(flops / (ms * 1e-3) / 1e12);
+    return GCONV_OK;
+}
+
+extern "C" int gconv_probe_copy(float *gbs, float *dst, const float *src, size_t bytes, void *stream) {
+    if (!gbs || !dst || !src || bytes < 16 || (bytes & 15u) || (((uintptr_t)dst | (uintptr_t)src) & 15u))
+        return GCONV_ERR_INVALID_ARG;
+    const uintptr_t d0 = (uintptr_t)dst, s0 = (uintptr_t)src;
+    if (d0 < s0 + bytes && s0 < d0 + bytes) return GCONV_ERR_INVALID_ARG;  // overlapping buffers
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return GCONV_ERR_LAUNCH;
+    const size_t n4 = bytes / 16;
+    const size_t per_block = (size_t)kProbeBlock * kCopyUnroll;
+    const size_t want = (n4 + per_block - 1) / per_block;
+    // at most 16 workgroups per CU: enough loads in flight, few rounds per lane
+    const int blocks = (int)(want < (size_t)16 * cus ? want : (size_t)16 * cus);
+    EventPair ev;
+    if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess) return GCONV_ERR_LAUNCH;
+    (void)hipGetLastError();
+    float best = 0.0f;
+    for (int rep = 0; rep < 6; ++rep) {  // one warm-up, then the fastest of five
+        if (hipEventRecord(ev.a, st) != hipSuccess) return GCONV_ERR_LAUNCH;
+        hipLaunchKernelGGL(copy_probe_kernel, dim3(blocks), dim3(kProbeBlock), 0, st, (f32x4 *)dst,
+                           (const f32x4 *)src, n4);
+        if (hipEventRecord(ev.b, st) != hipSuccess) return GCONV_ERR_LAUNCH;
+        if (hipGetLastError() != hipSuccess) return GCONV_ERR_LAUNCH;
+        if (hipEventSynchronize(ev.b) != hipSuccess) return GCONV_ERR_LAUNCH;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess || !(ms > 0.0f)) return GCONV_ERR_LAUNCH;
+        const float rate = (float)(2.0 * (double)bytes / (ms * 1e-3) / 1e9);
+        if (rep > 0 && rate > best) best = rate;
+    }
+    *gbs = best;
+    return GCONV_OK;
+}
 
 extern "C" int gconv_probe_peaks(float *mfma_tflops, float *fma_tflops, float *sink, void *stream) {
     if (!mfma_tflops || !fma_tflops || !sink) return GCONV_ERR_INVALID_ARG;

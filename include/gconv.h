@@ -222,6 +222,29 @@ int gconv_time_graph(gconv_desc_t desc, int fused, const float *const *xs, float
  * argument, GCONV_ERR_LAUNCH if the runtime refuses a call. */
 int gconv_probe_peaks(float *mfma_tflops, float *fma_tflops, float *sink, void *stream);
 
+/* Measured vector-ALU peaks of the current device: *fp32_tflops from
+ * chains of non-packed FP32 FMAs (v_fma_f32), *fp64_tflops from the same
+ * loop in FP64 (v_fma_f64), sixteen independent chains per lane and eight
+ * workgroups of 256 lanes per CU, one timed launch each after a warm-up
+ * launch on `stream`.  The FP64 figure is the control for the loop: on
+ * MI355X its datasheet peak is one FMA per lane per clock (78.6 TFLOP/s).
+ * sink: a caller-owned device buffer of at least 4 bytes the probes never
+ * write in practice.  Synchronizes on the stream.  Returns
+ * GCONV_ERR_INVALID_ARG for a null argument, GCONV_ERR_LAUNCH if the runtime
+ * refuses a call. */
+int gconv_probe_vector_peaks(float *fp32_tflops, float *fp64_tflops, float *sink, void *stream);
+
+/* Measured streaming rate of the device memory: copies `bytes` from src to
+ * dst (caller-owned device buffers, 16-byte aligned, not overlapping, bytes
+ * a positive multiple of 16) with the library's own copy kernel (16-byte
+ * non-temporal loads and stores, four pieces in flight per lane), one
+ * warm-up launch and five timed launches on `stream`; *gbs receives the
+ * fastest launch's rate, counting the bytes read and the bytes written
+ * (2 * bytes per launch).  Use buffers well beyond the last-level cache
+ * (256 MB) to measure HBM.  Synchronizes on the stream.  dst receives a copy
+ * of src. */
+int gconv_probe_copy(float *gbs, float *dst, const float *src, size_t bytes, void *stream);
+
 /* Static text for a status code. */
 const char *gconv_status_string(int status);
 

@@ -396,3 +396,17 @@ def test_noalloc_entry_point_refuses_before_any_device_call():
     # the full fused workload fits
     assert gc.conv_fused_gn_workspace_size(_desc(wl), 8) <= gc.conv_fused_gn_noalloc_limit()
 
+
+def test_copy_and_vector_probes_validate_before_any_device_call():
+    lib = gc.library()
+    f = ctypes.c_float()
+    P = ctypes.c_void_p
+    assert lib.gconv_probe_vector_peaks(None, ctypes.byref(f), P(16), None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_vector_peaks(ctypes.byref(f), ctypes.byref(f), None, None) == gc.GCONV_ERR_INVALID_ARG
+    a, b = 1 << 20, 1 << 30  # never dereferenced: every call below fails validation first
+    assert lib.gconv_probe_copy(None, P(a), P(b), 4096, None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_copy(ctypes.byref(f), None, P(b), 4096, None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_copy(ctypes.byref(f), P(a), P(b), 4100, None) == gc.GCONV_ERR_INVALID_ARG  # not x16
+    assert lib.gconv_probe_copy(ctypes.byref(f), P(a + 4), P(b), 4096, None) == gc.GCONV_ERR_INVALID_ARG
+    assert lib.gconv_probe_copy(ctypes.byref(f), P(a), P(a + 2048), 4096, None) == gc.GCONV_ERR_INVALID_ARG  # overlap
+    assert lib.gconv_probe_copy(ctypes.byref(f), P(a), P(b), 0, None) == gc.GCONV_ERR_INVALID_ARG
