@@ -110,6 +110,13 @@ class ConvDesc:
     def __init__(self, handle: int, geom: tuple):
         self._h = ctypes.c_void_p(handle)
         self.geom = geom  # (N, C, H, W, K, R, S, stride, pad, dilation, groups)
+        ho, wo = _i(), _i()
+        _check("conv_desc_get_output_dims", _lib.conv_desc_get_output_dims(self._h, ctypes.byref(ho),
+                                                                           ctypes.byref(wo)))
+        N, C, H, W, K, R, S = geom[:7]
+        # element counts of x, w, y and a per-channel vector, checked against
+        # tensor arguments before every call
+        self.sizes = dict(x=N * C * H * W, w=K * (C // geom[10]) * R * S, y=N * K * ho.value * wo.value, vec=K)
 
     @property
     def handle(self):
@@ -174,20 +181,33 @@ def conv_desc_get_fused_variant(desc: ConvDesc, gn_groups: int) -> int:
     return v.value
 
 
-def _ptr(t):
-    """Device address of a torch tensor (checked: cuda, float32, contiguous) or a raw int."""
+def _ptr(t, numel=None, name="tensor"):
+    """Device address of a torch tensor (checked: cuda, float32, contiguous,
+    and `numel` elements when given) or a raw int, which is passed as is."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
     import torch
     if not t.is_cuda:
-        raise ValueError("tensor must live on the GPU")
+        raise ValueError("%s must live on the GPU" % name)
     if t.dtype != torch.float32:
-        raise ValueError("tensor must be float32, got %s" % t.dtype)
+        raise ValueError("%s must be float32, got %s" % (name, t.dtype))
     if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
+        raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s has %d elements; the descriptor needs %d" % (name, t.numel(), numel))
     return t.data_ptr()
+
+
+def _workspace_ptr(ws):
+    if ws is None or isinstance(ws, int):
+        return ws
+    if not ws.is_cuda:
+        raise ValueError("workspace must live on the GPU")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.data_ptr()
 
 
 def _stream(stream):
@@ -201,7 +221,9 @@ def _stream(stream):
 
 def conv_fwd(desc: ConvDesc, x, w, bias, y, stream=None) -> None:
     """y = conv(x, w) [+ bias] on `stream` (default: torch's current stream)."""
-    _check("conv_fwd", _lib.conv_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(y), _stream(stream)))
+    n = desc.sizes
+    _check("conv_fwd", _lib.conv_fwd(desc.handle, _ptr(x, n["x"], "x"), _ptr(w, n["w"], "w"),
+                                     _ptr(bias, n["vec"], "bias"), _ptr(y, n["y"], "y"), _stream(stream)))
 
 
 def conv_fused_gn_workspace_size(desc: ConvDesc, gn_groups: int) -> int:
@@ -216,10 +238,13 @@ def conv_fused_gn_fwd(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups:
     """conv -> +bias -> *scale -> sigmoid -> GroupNorm(gn_groups, eps, gamma, beta) into y."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    wsp = None if workspace is None else (workspace if isinstance(workspace, int) else workspace.data_ptr())
-    _check("conv_fused_gn_fwd", _lib.conv_fused_gn_fwd(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale),
-                                                       _ptr(gamma), _ptr(beta), gn_groups, float(eps), _ptr(y),
-                                                       wsp, workspace_bytes, _stream(stream)))
+    n = desc.sizes
+    v = n["vec"]
+    _check("conv_fused_gn_fwd", _lib.conv_fused_gn_fwd(desc.handle, _ptr(x, n["x"], "x"), _ptr(w, n["w"], "w"),
+                                                       _ptr(bias, v, "bias"), _ptr(scale, v, "scale"),
+                                                       _ptr(gamma, v, "gamma"), _ptr(beta, v, "beta"), gn_groups,
+                                                       float(eps), _ptr(y, n["y"], "y"), _workspace_ptr(workspace),
+                                                       workspace_bytes, _stream(stream)))
 
 
 def conv_fused_gn_fwd_noalloc(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn_groups: int, eps: float, y,
@@ -227,9 +252,13 @@ def conv_fused_gn_fwd_noalloc(desc: ConvDesc, x, w, bias, scale, gamma, beta, gn
     """The fused chain without a caller workspace: the library's static
     scratch array (conv_fused_gn_noalloc_limit() bytes per GPU) holds the
     GroupNorm statistics.  Calls that overlap on one GPU race."""
+    n = desc.sizes
+    v = n["vec"]
     _check("conv_fused_gn_fwd_noalloc",
-           _lib.conv_fused_gn_fwd_noalloc(desc.handle, _ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(gamma),
-                                          _ptr(beta), gn_groups, float(eps), _ptr(y), _stream(stream)))
+           _lib.conv_fused_gn_fwd_noalloc(desc.handle, _ptr(x, n["x"], "x"), _ptr(w, n["w"], "w"),
+                                          _ptr(bias, v, "bias"), _ptr(scale, v, "scale"), _ptr(gamma, v, "gamma"),
+                                          _ptr(beta, v, "beta"), gn_groups, float(eps), _ptr(y, n["y"], "y"),
+                                          _stream(stream)))
 
 
 def conv_fused_gn_noalloc_limit() -> int:
@@ -248,8 +277,9 @@ def gconv_time_graph(desc: ConvDesc, xs, ys, w, bias=None, launches: int = 1, re
     if len(xs) != len(ys) or not xs:
         raise ValueError("xs and ys must be non-empty sequences of the same length")
     n = len(xs)
-    xa = (_p * n)(*[_ptr(t) for t in xs])
-    ya = (_p * n)(*[_ptr(t) for t in ys])
+    sz = desc.sizes
+    xa = (_p * n)(*[_ptr(t, sz["x"], "x") for t in xs])
+    ya = (_p * n)(*[_ptr(t, sz["y"], "y") for t in ys])
     out = (ctypes.c_float * replays)()
     if fused is None:
         args = (0, None, None, None, 0, 0.0, None, 0)
@@ -258,11 +288,13 @@ def gconv_time_graph(desc: ConvDesc, xs, ys, w, bias=None, launches: int = 1, re
         wsb = fused.get("workspace_bytes")
         if wsb is None:
             wsb = ws.numel() * ws.element_size() if ws is not None else 0
-        wsp = None if ws is None else (ws if isinstance(ws, int) else ws.data_ptr())
-        args = (1, _ptr(fused["scale"]), _ptr(fused.get("gamma")), _ptr(fused.get("beta")), int(fused["gn_groups"]),
-                float(fused["eps"]), wsp, wsb)
+        v = sz["vec"]
+        args = (1, _ptr(fused["scale"], v, "scale"), _ptr(fused.get("gamma"), v, "gamma"),
+                _ptr(fused.get("beta"), v, "beta"), int(fused["gn_groups"]), float(fused["eps"]), _workspace_ptr(ws),
+                wsb)
     fl, sc, ga, be, gg, eps, wsp, wsb = args
-    _check("gconv_time_graph", _lib.gconv_time_graph(desc.handle, fl, xa, ya, n, _ptr(w), _ptr(bias), sc, ga, be, gg,
+    _check("gconv_time_graph", _lib.gconv_time_graph(desc.handle, fl, xa, ya, n, _ptr(w, sz["w"], "w"),
+                                                     _ptr(bias, sz["vec"], "bias"), sc, ga, be, gg,
                                                      eps, wsp, wsb, launches, replays, out, _stream(stream)))
     return list(out)
 

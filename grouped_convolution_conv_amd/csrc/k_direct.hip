@@ -17,7 +17,26 @@ constexpr int kBlock = 256;
 
 struct DirectGeom {
     int C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, cin, cout, Ho, Wo;
+    int pblocks;  // 256-pixel blocks per output plane
 };
+
+// The grid is one-dimensional: block b covers pixel block b % pblocks of
+// output plane (n, k) = (b / pblocks / K, b / pblocks % K).  N * K * pblocks
+// stays below 2^31 for every descriptor (each block holds at least one of
+// the fewer than 2^31 outputs), so any N and K fit.
+struct BlockCoord {
+    int n, k, pb;
+};
+
+__device__ __forceinline__ BlockCoord block_coord(const DirectGeom &g) {
+    const int b = blockIdx.x;
+    const int nk = b / g.pblocks;
+    BlockCoord c;
+    c.pb = b - nk * g.pblocks;
+    c.n = nk / g.K;
+    c.k = nk - c.n * g.K;
+    return c;
+}
 
 __device__ __forceinline__ float direct_point(const float *__restrict__ x,
                                               const float *__restrict__ w, const DirectGeom &g,
@@ -51,9 +70,10 @@ __global__ __launch_bounds__(kBlock) void direct_conv_kernel(const float *__rest
                                                              const float *__restrict__ bias,
                                                              float *__restrict__ y, DirectGeom g) {
     const int plane = g.Ho * g.Wo;
-    const int p = blockIdx.x * kBlock + threadIdx.x;
+    const BlockCoord bc = block_coord(g);
+    const int p = bc.pb * kBlock + threadIdx.x;
     if (p >= plane) return;
-    const int k = blockIdx.y, n = blockIdx.z;
+    const int k = bc.k, n = bc.n;
     const int oh = p / g.Wo, ow = p - oh * g.Wo;
     float acc = direct_point(x, w, g, n, k, oh, ow);
     if (bias) acc += bias[k];
@@ -66,8 +86,9 @@ __global__ __launch_bounds__(kBlock) void direct_fused_kernel(const float *__res
                                                               FusedEpilogue ep) {
     __shared__ float scratch[4];
     const int plane = g.Ho * g.Wo;
-    const int p = blockIdx.x * kBlock + threadIdx.x;
-    const int k = blockIdx.y, n = blockIdx.z;
+    const BlockCoord bc = block_coord(g);
+    const int p = bc.pb * kBlock + threadIdx.x;
+    const int k = bc.k, n = bc.n;
     const bool valid = p < plane;
     float v = 0.0f;
     if (valid) {
@@ -77,14 +98,14 @@ __global__ __launch_bounds__(kBlock) void direct_fused_kernel(const float *__res
         y[((size_t)n * g.K + k) * plane + p] = v;
     }
     // two-pass statistics of this block's values
-    const int cnt = min(kBlock, plane - (int)blockIdx.x * kBlock);
+    const int cnt = min(kBlock, plane - bc.pb * kBlock);
     const float mean = block256_sum(valid ? v : 0.0f, scratch) / (float)cnt;
     const float d = valid ? v - mean : 0.0f;
     const float m2 = block256_sum(d * d, scratch);
     if (threadIdx.x == 0) {
         const int gg = k / ep.gn_cpg, kl = k - gg * ep.gn_cpg;
         const size_t idx = ((size_t)n * ep.gn_groups + gg) * ep.parts_per_group +
-                           (size_t)kl * gridDim.x + blockIdx.x;
+                           (size_t)kl * g.pblocks + bc.pb;
         Partial pt;
         pt.count = (float)cnt;
         pt.mean = mean;
@@ -99,12 +120,18 @@ DirectGeom make_geom(const gconv_desc *d) {
     g.C = d->C; g.H = d->H; g.W = d->W; g.K = d->K; g.R = d->R; g.S = d->S;
     g.sh = d->stride_h; g.sw = d->stride_w; g.ph = d->pad_h; g.pw = d->pad_w; g.dh = d->dil_h; g.dw = d->dil_w;
     g.cin = d->cin; g.cout = d->cout; g.Ho = d->Ho; g.Wo = d->Wo;
+    g.pblocks = (d->Ho * d->Wo + kBlock - 1) / kBlock;
     return g;
 }
 
-dim3 direct_grid(const gconv_desc *d) {
-    const int plane = d->Ho * d->Wo;
-    return dim3((unsigned)((plane + kBlock - 1) / kBlock), (unsigned)d->K, (unsigned)d->N);
+// N * K * pblocks blocks; below 2^31 for every valid descriptor (checked
+// anyway: the caller gets hipErrorInvalidConfiguration, never a wrapped grid)
+bool direct_blocks(const gconv_desc *d, unsigned *blocks) {
+    const long long pb = ((long long)d->Ho * d->Wo + kBlock - 1) / kBlock;
+    const long long b = (long long)d->N * d->K * pb;
+    if (b > 0x7fffffffLL) return false;
+    *blocks = (unsigned)b;
+    return true;
 }
 
 }  // namespace
@@ -116,19 +143,19 @@ int direct_fused_parts_per_group(const gconv_desc *d, int gn_groups) {
 
 hipError_t launch_direct(const gconv_desc *d, const float *x, const float *w, const float *bias,
                          float *y, hipStream_t st) {
-    if (d->K > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    unsigned blocks = 0;
+    if (!direct_blocks(d, &blocks)) return hipErrorInvalidConfiguration;
     clear_stale_launch_error();
-    hipLaunchKernelGGL(direct_conv_kernel, direct_grid(d), dim3(kBlock), 0, st, x, w, bias, y,
-                       make_geom(d));
+    hipLaunchKernelGGL(direct_conv_kernel, dim3(blocks), dim3(kBlock), 0, st, x, w, bias, y, make_geom(d));
     return hipGetLastError();
 }
 
 hipError_t launch_direct_fused(const gconv_desc *d, const float *x, const float *w, float *y,
                                const FusedEpilogue &ep, hipStream_t st) {
-    if (d->K > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    unsigned blocks = 0;
+    if (!direct_blocks(d, &blocks)) return hipErrorInvalidConfiguration;
     clear_stale_launch_error();
-    hipLaunchKernelGGL(direct_fused_kernel, direct_grid(d), dim3(kBlock), 0, st, x, w, y,
-                       make_geom(d), ep);
+    hipLaunchKernelGGL(direct_fused_kernel, dim3(blocks), dim3(kBlock), 0, st, x, w, y, make_geom(d), ep);
     return hipGetLastError();
 }
 

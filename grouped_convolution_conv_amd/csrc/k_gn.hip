@@ -33,7 +33,7 @@ __device__ __forceinline__ Moments merge(Moments a, Moments b) {
     return r;
 }
 
-// grid: x = channel-in-group * nsplit + split, y = n * G + gg
+// one-dimensional grid: block b = (n * G + gg) * (cpg * nsplit) + channel-in-group * nsplit + split
 __global__ __launch_bounds__(kBlock) void gn_normalize_kernel(float *__restrict__ y,
                                                               const Partial *__restrict__ parts,
                                                               int P, const float *__restrict__ gamma,
@@ -41,7 +41,9 @@ __global__ __launch_bounds__(kBlock) void gn_normalize_kernel(float *__restrict_
                                                               int G, int cpg, int plane, int nsplit,
                                                               float eps, int vec4) {
     __shared__ double sn[kBlock], smean[kBlock], sm2[kBlock];
-    const int ng = blockIdx.y;
+    const int per_group = cpg * nsplit;
+    const int ng = (int)blockIdx.x / per_group;
+    const int within = (int)blockIdx.x - ng * per_group;
     const int tid = threadIdx.x;
 
     Moments acc = {0.0, 0.0, 0.0};
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(kBlock) void gn_normalize_kernel(float *__restrict_
     const float rstd = (float)(1.0 / sqrt(var + (double)eps));
 
     const int gg = ng % G, n = ng / G;
-    const int cl = blockIdx.x / nsplit, part = blockIdx.x - cl * nsplit;
+    const int cl = within / nsplit, part = within - cl * nsplit;
     const int k = gg * cpg + cl;
     const float a = gamma ? rstd * gamma[k] : rstd;
     const float b = beta ? beta[k] : 0.0f;
@@ -118,12 +120,13 @@ hipError_t launch_gn_normalize(const gconv_desc *d, float *y, const Partial *par
     // about 32K elements per workgroup
     int nsplit = (plane + 32767) / 32768;
     if (nsplit < 1) nsplit = 1;
-    const long long gx = (long long)cpg * nsplit;
-    const long long gy = (long long)d->N * gn_groups;
-    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+    // N * K * nsplit blocks: below 2^31 for every valid descriptor (each
+    // block normalizes at least one of the fewer than 2^31 outputs)
+    const long long blocks = (long long)d->N * gn_groups * cpg * nsplit;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const int vec4 = (plane % 4 == 0) && (((uintptr_t)y & 15u) == 0);
     clear_stale_launch_error();
-    hipLaunchKernelGGL(gn_normalize_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kBlock), 0, st, y,
+    hipLaunchKernelGGL(gn_normalize_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, y,
                        parts, parts_per_group, gamma, beta, d->K, gn_groups, cpg, plane, nsplit, eps,
                        vec4);
     return hipGetLastError();

@@ -520,7 +520,9 @@ hipError_t launch_grouped3x3(const gconv_desc *d, const float *x, const float *w
     p.vec_load = (d->W % 4 == 0) && (((uintptr_t)x & 15u) == 0);
     p.vec_store = (d->W % 4 == 0) && (((uintptr_t)y & 15u) == 0);
     const long long gy = (long long)d->groups * p.n_cob;
-    if (gx > 0x7fffffffLL || gy > 65535 || d->N > 65535) return hipErrorInvalidConfiguration;
+    // the band kernel's grid is (tiles, group x channel block, n): beyond
+    // the hardware's 65535 limit on y and z the direct kernel takes over
+    if (gx > 0x7fffffffLL || gy > 65535 || d->N > 65535) return launch_direct(d, x, w, bias, y, st);
     dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)d->N);
     if (Q == 8) return launch_ci<8>(d->cin, CO, p, grid, lds, x, w, bias, y, st);
     return launch_ci<4>(d->cin, CO, p, grid, lds, x, w, bias, y, st);

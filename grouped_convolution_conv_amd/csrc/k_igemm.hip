@@ -699,7 +699,11 @@ bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // every output channel of every 32*MB block must exist, and a GroupNorm
     // group must be 4 channels
     // (the fused kernel runs at stride 1 only)
-    return igemm_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4;
+    // its grid is (tiles, group x channel block, n), within the hardware's
+    // 65535 limit on y and z
+    const long long gy = (long long)d->groups * ((d->cout + 32 * pick_mb(d) - 1) / (32 * pick_mb(d)));
+    return igemm_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
+           gy <= 65535 && d->N <= 65535;
 }
 
 int igemm_fused_parts_per_group(const gconv_desc *d, int) {
@@ -732,7 +736,9 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
         p.nbr = 1;
         n_wg = tiles();
     }
-    if (gy > 65535 || d->N > 65535 || n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // the DMA kernel runs a one-dimensional grid of n_wg workgroups (below
+    // 2^31 for every valid descriptor: each holds at least one output)
+    if (n_wg > 0x7fffffffLL) return launch_direct(d, x, w, bias, y, st);
     p.n_wg = (int)n_wg;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
     FusedEpilogue none{};

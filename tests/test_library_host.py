@@ -410,3 +410,52 @@ def test_copy_and_vector_probes_validate_before_any_device_call():
     assert lib.gconv_probe_copy(ctypes.byref(f), P(a + 4), P(b), 4096, None) == gc.GCONV_ERR_INVALID_ARG
     assert lib.gconv_probe_copy(ctypes.byref(f), P(a), P(a + 2048), 4096, None) == gc.GCONV_ERR_INVALID_ARG  # overlap
     assert lib.gconv_probe_copy(ctypes.byref(f), P(a), P(b), 0, None) == gc.GCONV_ERR_INVALID_ARG
+
+
+class _FakeDeviceTensor:
+    """Stands in for a float32 CUDA tensor on a host without a GPU: the
+    binding's checks read only these attributes.  Every call below passes at
+    least one mismatched tensor, and the binding checks all arguments before
+    it calls the library, so the address is never dereferenced."""
+
+    def __init__(self, numel, dtype=None, contiguous=True):
+        import torch
+        self.is_cuda, self.dtype, self._numel, self._contig = True, dtype or torch.float32, numel, contiguous
+
+    def numel(self):
+        return self._numel
+
+    def is_contiguous(self):
+        return self._contig
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+def test_binding_checks_tensor_sizes_against_the_descriptor():
+    d = gc.conv_desc_create(2, 4, 8, 8, 6, 3, 3, 1, 1, 1, 2)
+    assert d.sizes == dict(x=2 * 4 * 8 * 8, w=6 * 2 * 3 * 3, y=2 * 6 * 8 * 8, vec=6)
+    T = _FakeDeviceTensor
+    good = dict(x=T(512), w=T(108), y=T(768))
+    for name, bad in (("x", T(511)), ("w", T(109)), ("y", T(767))):
+        args = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            gc.conv_fwd(d, args["x"], args["w"], None, args["y"])
+    with pytest.raises(ValueError, match="bias"):
+        gc.conv_fwd(d, T(512), T(108), T(5), T(768))
+    for name in ("bias", "scale", "gamma", "beta"):
+        vec = dict(bias=T(6), scale=T(6), gamma=T(6), beta=T(6))
+        vec[name] = T(7)
+        with pytest.raises(ValueError, match=name):
+            gc.conv_fused_gn_fwd(d, T(512), T(108), vec["bias"], vec["scale"], vec["gamma"], vec["beta"], 2, 1e-5,
+                                 T(768), 1 << 20, 4096)
+        with pytest.raises(ValueError, match=name):
+            gc.conv_fused_gn_fwd_noalloc(d, T(512), T(108), vec["bias"], vec["scale"], vec["gamma"], vec["beta"], 2,
+                                         1e-5, T(768))
+    import torch
+    with pytest.raises(ValueError, match="float32"):
+        gc.conv_fwd(d, T(512, dtype=torch.float16), T(108), None, T(768))
+    with pytest.raises(ValueError, match="contiguous"):
+        gc.conv_fwd(d, T(512, contiguous=False), T(108), None, T(768))
+    with pytest.raises(ValueError, match="GPU"):
+        gc.conv_fwd(d, torch.zeros(512), T(108), None, T(768))

@@ -800,3 +800,29 @@ def test_vector_and_copy_probes_are_plausible():
     _say("[parity] library copy: %.1f GB/s" % gbs)
     assert torch.equal(dst, src)
     assert 500.0 < gbs < 8400.0, gbs
+
+
+def test_grids_beyond_65535_planes_or_images():
+    """More than 65535 output channels or images: the direct kernel and the
+    in-place GroupNorm normalize run one-dimensional grids, and the band
+    kernel hands such batches to the direct kernel, instead of refusing the
+    launch."""
+    cases = [  # (N, C, H, W, K, R, pad, groups)
+        (1, 1, 1, 1, 70000, 1, 0, 1),     # 70000 output planes, direct kernel
+        (70000, 1, 2, 2, 1, 3, 1, 1),     # 70000 images, grouped 3x3 band path -> direct
+        (66000, 2, 3, 5, 2, 3, 1, 2),     # the same, two groups
+    ]
+    for i, (N, C, H, W, K, R, pad, G) in enumerate(cases):
+        wl = synth.Workload("grid%d" % i, N, C, H, W, K, R, R, 1, pad, 1, G, 7000 + i, ("uniform", -1.0, 1.0),
+                            ("uniform", -0.5, 0.5))
+        _say("[parity] grid limits", wl)
+        inp = synth.make_inputs(wl)
+        y, _ = gpu_conv(wl, inp)
+        y_ref, A = oracle_conv(wl, inp)
+        check_conv(y, y_ref, A, wl.name)
+    # the fused chain on 70000 images: stage A on the direct kernel, then the
+    # normalize over 70000 (image, group) pairs
+    wl = W["c5_fused_gn"].with_(N=70000, C=4, K=4, H=2, W=2, pad=1, gn_groups=1)
+    _say("[parity] grid limits, fused", wl)
+    inp = synth.make_inputs(wl)
+    check_gn(gpu_fused(wl, inp), oracle_fused(wl, inp), "fused 70000 images")
