@@ -822,7 +822,7 @@ def test_grids_beyond_65535_planes_or_images():
         check_conv(y, y_ref, A, wl.name)
     # the fused chain on 70000 images: stage A on the direct kernel, then the
     # normalize over 70000 (image, group) pairs
-    wl = W["c5_fused_gn"].with_(N=70000, C=4, K=4, H=2, W=2, pad=1, gn_groups=1)
+    wl = synth.WORKLOADS["c5_fused_gn"].with_(N=70000, C=4, K=4, H=2, W=2, pad=1, gn_groups=1)
     _say("[parity] grid limits, fused", wl)
     inp = synth.make_inputs(wl)
     check_gn(gpu_fused(wl, inp), oracle_fused(wl, inp), "fused 70000 images")
