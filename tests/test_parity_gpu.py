@@ -623,6 +623,46 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_graph_capture_of_store_variant_slices():
+    """The store variant runs its conv and in-place normalize over batch
+    slices (16 full-size images: slices of 15 and 1): captured in a HIP
+    graph, every replay equals the eager run, and the eager run matches the
+    oracle on the images at the slice edges."""
+    wl = W["c5_fused_gn"].with_(N=16)
+    inp = synth.make_inputs(wl)
+    d = _desc(wl)
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_STORE)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    t = {k: _dev(v) for k, v in inp.items()}
+    ws = torch.empty(gc.conv_fused_gn_workspace_size(d, wl.gn_groups), dtype=torch.uint8, device="cuda")
+    f_eager = torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda")
+    gc.conv_fused_gn_fwd(d, t["x"], t["w"], t["bias"], t["scale"], t["gamma"], t["beta"], wl.gn_groups, wl.eps,
+                         f_eager, ws)
+    torch.cuda.synchronize()
+    out = f_eager.cpu().numpy()
+    for n in (0, 14, 15):
+        sl = dict(inp)
+        sl["x"] = inp["x"][n:n + 1]
+        check_gn(out[n:n + 1], oracle_fused(wl.with_(N=1), sl), "store variant slices, image %d" % n)
+    f_g = torch.zeros_like(f_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            gc.conv_fused_gn_fwd(d, t["x"], t["w"], t["bias"], t["scale"], t["gamma"], t["beta"], wl.gn_groups,
+                                 wl.eps, f_g, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        f_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(f_g, f_eager), rep
+        f_eager.add_(0.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_graph_capture_of_every_kernel_family():
     """One conv per kernel family captured in a single HIP graph (grouped
     register and band kernels, matrix-core 16/16 groups, depthwise aligned,

@@ -66,11 +66,14 @@ def test_noalloc_matches_workspace_entry_point_twice(algo, variant):
         _check(y, y_ref, "%s %s N=%d %dx%d" % (gc.ALGO_NAMES[algo], gc.FUSED_NAMES[variant], wl.N, wl.H, wl.W))
 
 
-def test_noalloc_full_size_fused_workload():
-    """The full fused workload (64 images, 4 MiB of statistics) fits the scratch array."""
-    _say("[noalloc] full-size fused workload")
-    y, y_ref = _run_both(C5)
-    _check(y, y_ref, "full fused workload")
+@pytest.mark.parametrize("variant", [gc.FUSED_AUTO, gc.FUSED_STORE])
+def test_noalloc_full_size_fused_workload(variant):
+    """The full fused workload (64 images, 4 MiB of statistics) fits the
+    scratch array, in the recompute organisation (the default there) and in
+    the store organisation (batch slices)."""
+    _say("[noalloc] full-size fused workload", gc.FUSED_NAMES[variant])
+    y, y_ref = _run_both(C5, variant=variant)
+    _check(y, y_ref, "full fused workload " + gc.FUSED_NAMES[variant])
 
 
 def test_noalloc_refuses_problems_beyond_the_scratch_limit():
