@@ -118,40 +118,47 @@ def row_accounting(wl, ho, wo):
     return dict(bytes=byts, flops=flops, bound=bound, floor_s=max(t_mem, t_cmp), compute_peak_tflops=peak)
 
 
-KERNEL_SOURCES = {
-    "igemm": ["k_igemm.hip"],
-    "grouped3x3": ["k_grouped3x3.hip"],
-    "direct": ["k_direct.hip"],
-    "depthwise": ["k_depthwise.hip"],
+# Sources each benchmark row's kernels are built from (beside the shared
+# headers): a committed HBM-traffic record counts only while they are unchanged.
+ROW_SOURCES = {
+    "c1_grouped_cpg4": ["k_grouped3x3.hip"],
+    "c2_depthwise_144": ["k_grouped3x3.hip"],
+    "c3a_grouped_g64": ["k_grouped3x3.hip"],
+    "c3b_grouped_g128": ["k_grouped3x3.hip"],
+    "c3c_depthwise_g256": ["k_grouped3x3.hip"],
+    "c4_dense_5x9": ["k_igemm.hip"],
+    "c5_fused_gn": ["k_igemm_res.hip", "gconv_api.cpp"],
 }
+TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "hbm_traffic_seven_rows.md")
 
 
-def kernel_source_hash(algo):
-    """sha256 over the sources a kernel is built from (its file + shared headers)."""
+def row_source_hash(row):
+    """sha256 over the sources a row's kernels are built from (+ shared headers)."""
     import hashlib
     csrc = os.path.join(ROOT, "grouped_convolution_conv_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES.get(algo, []) + ["dev_common.h", "internal.h"]:
+    for f in ROW_SOURCES[row] + ["dev_common.h", "internal.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(algo, row):
-    """HBM bytes per launch of a kernel from its committed counter summary.
+def measured_traffic(row):
+    """HBM bytes per launch of a row (every kernel of one library call) from
+    the committed counter record.
 
-    profiles/<algo>_<row>_traffic.md carries one line
-      traffic-record: sha256=<kernel_source_hash> fetch_kib=F write_kib=W fetch_scale=a write_scale=b
-    with rocprofv3 FETCH_SIZE / WRITE_SIZE averages (KiB per dispatch) and the
-    factors that map a plain copy's counters onto its known size.  Returns None
-    when the file is missing or the kernel's sources changed since."""
+    profiles/hbm_traffic_seven_rows.md carries one line per row
+      traffic-record: row=<row> sha256=<row_source_hash> fetch_kib=F write_kib=W fetch_scale=a write_scale=b
+    with the rocprofv3 FETCH_SIZE / WRITE_SIZE averages (KiB per call, summed
+    over the row's kernels) and the factors that map the library copy probe's
+    counters onto its known size.  Returns None when the row has no record or
+    its kernels' sources changed since."""
     import re
-    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (algo, row))
-    if not os.path.exists(path):
+    if row not in ROW_SOURCES or not os.path.exists(TRAFFIC_RECORDS):
         return None
-    m = re.search(r"traffic-record: sha256=(\w+) fetch_kib=([\d.]+) write_kib=([\d.]+) "
-                  r"fetch_scale=([\d.]+) write_scale=([\d.]+)", open(path).read())
-    if not m or m.group(1) != kernel_source_hash(algo):
+    m = re.search(r"traffic-record: row=%s sha256=(\w+) fetch_kib=([\d.]+) write_kib=([\d.]+) "
+                  r"fetch_scale=([\d.]+) write_scale=([\d.]+)" % re.escape(row), open(TRAFFIC_RECORDS).read())
+    if not m or m.group(1) != row_source_hash(row):
         return None
     f, w, fs, ws = (float(m.group(i)) for i in range(2, 6))
     return (f * fs + w * ws) * 1024.0
@@ -855,6 +862,8 @@ def main():
         rec["step"] = r.figures(med)
         rec["step"]["mean_ms"] = float(np.mean(step_times[r.name])) * 1e3
         rec["floor_us_measured_peaks"] = measured_floor_s(r.acct, r.wl, peaks) * 1e6
+        tb = measured_traffic(r.name)
+        rec["traffic"] = None if tb is None else dict(bytes_per_launch=tb, ratio_to_algorithmic=tb / r.acct["bytes"])
         out_rows.append(rec)
         log("[bench] %-20s step  %.4f ms  %8.1f GB/s  %8.1f GFLOP/s  frac %.3f"
             % (r.name, rec["step"]["ms"], rec["step"]["gbs"], rec["step"]["gflops"], rec["step"]["roofline_frac"]))
@@ -893,7 +902,7 @@ def main():
             achieved = dom_rec["bytes"] / t / 1e9
             roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
                         measured_peak=peaks["hbm_copy_gbs"], frac_of_measured_peak=achieved / peaks["hbm_copy_gbs"])
-        roof.update(traffic=measured_traffic(dom_row.algo, dom_rec["name"]), traffic_unit="bytes per launch",
+        roof.update(traffic=measured_traffic(dom_rec["name"]), traffic_unit="bytes per launch",
                     algorithmic_bytes=dom_rec["bytes"], algorithmic_flops=dom_rec["flops"],
                     kernel=dom_row.algo, row=dom_rec["name"],
                     avg_launch_ms=dom_rec["step"]["mean_ms"])
