@@ -886,6 +886,11 @@ def main():
         for key in ("step", "graph", "sync"):
             if key in rec:
                 rec[key]["roofline_frac_measured_peaks"] = rec["floor_us_measured_peaks"] / (rec[key]["ms"] * 1e3)
+        if "sync" in rec and "graph" in rec:
+            # host time of the synchronized call beyond the device time of a
+            # graph replay: Python and ctypes marshalling, the HIP launch and
+            # the synchronization round trip
+            rec["sync_minus_graph_us"] = (rec["sync"]["ms"] - rec["graph"]["ms"]) * 1e3
 
     # ---- dominant kernel roofline (single-kernel rows: one launch = one kernel)
     single = [(rec, r) for rec, r in zip(out_rows, rows) if not r.wl.fused]
@@ -907,6 +912,15 @@ def main():
                     kernel=dom_row.algo, row=dom_rec["name"],
                     avg_launch_ms=dom_rec["step"]["mean_ms"])
 
+    # the synchronization round trip alone, on an idle device
+    torch.cuda.synchronize()
+    idle = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        torch.cuda.synchronize()
+        idle.append(time.perf_counter() - t0)
+    host_sync_us = float(np.median(idle)) * 1e6
+
     value = geomean([rec["step"]["gbs"] for rec in out_rows])
     result = {
         "metric": METRIC,
@@ -922,6 +936,7 @@ def main():
         },
         "roofline": roof,
         "hbm_copy_calibration": copy,
+        "host_sync_idle_us": host_sync_us,
         "measured_peaks": peaks,
         "rows": out_rows,
     }

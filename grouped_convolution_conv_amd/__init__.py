@@ -13,7 +13,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgconv.so")
+# GCONV_SANITIZED=1 loads the build whose host code carries AddressSanitizer
+# and UndefinedBehaviorSanitizer (build.py --sanitize; the process must
+# preload clang's ASan runtime, as tests/sanitize_host.py does)
+LIB_PATH = os.path.join(_HERE, "libgconv_san.so" if os.environ.get("GCONV_SANITIZED") == "1" else "libgconv.so")
 
 GCONV_OK = 0
 GCONV_ERR_INVALID_ARG = 1

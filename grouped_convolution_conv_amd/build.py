@@ -35,9 +35,20 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source and link libgconv.so; returns its path."""
-    extra = list(extra_flags or [])
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (the device code
+# is built as always): every -fsanitize flag goes to the host compilation only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+LIB_SANITIZED = os.path.join(PKG, "libgconv_san.so")
+
+
+def build(verbose: bool = False, extra_flags=None, sanitize: bool = False) -> str:
+    """Compile every source and link libgconv.so; returns its path.  With
+    sanitize, the host code is instrumented with AddressSanitizer and
+    UndefinedBehaviorSanitizer and the result is libgconv_san.so."""
+    extra = list(extra_flags or []) + (SANITIZE_HOST if sanitize else [])
+    lib_out = LIB_SANITIZED if sanitize else LIB
     with tempfile.TemporaryDirectory(prefix="gconv_build_") as tmp:
         procs = []
         objs = []
@@ -59,14 +70,17 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         if failed:
             msg = "\n".join("%s:\n%s" % (s, t) for s, t in failed)
             raise RuntimeError("hipcc failed:\n" + msg)
-        tmp_lib = LIB + ".tmp%d" % os.getpid()
+        tmp_lib = lib_out + ".tmp%d" % os.getpid()
         # every symbol resolved at link time: a kernel whose host launch stub
-        # is missing fails the build, not the first load
-        link = [HIPCC, "-shared", "-fPIC", "-Wl,--no-undefined", "--offload-arch=" + ARCH, "-o", tmp_lib] + objs
+        # is missing fails the build, not the first load (the sanitized build
+        # leaves the sanitizer runtime's symbols to the preloaded runtime)
+        link = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp_lib] + objs
+        link += (["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-shared-libsan"] if sanitize
+                 else ["-Wl,--no-undefined"])
         subprocess.run(link, check=True)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib_out)
+    return lib_out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -25,19 +25,35 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# GCONV_SANITIZED=1 selects the AddressSanitizer/UndefinedBehaviorSanitizer
+# build (see build(sanitize=True)); the process must then preload clang's
+# ASan runtime, as tests/sanitize_host.py does.
+_SANITIZED = os.environ.get("GCONV_SANITIZED") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZED else "liboracle.so")
 _lib = None
+CLANG = "/opt/rocm/llvm/bin/clang"
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+                  "-shared-libsan", "-g"]
 
 
-def build(force: bool = False) -> str:
-    """Compile oracle.c -> liboracle.so with gcc (-O2, no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
+def build(force: bool = False, sanitize: bool = None) -> str:
+    """Compile oracle.c -> liboracle.so with gcc (-O2, no fast-math), or with
+    sanitize -> liboracle_san.so with clang, AddressSanitizer and
+    UndefinedBehaviorSanitizer (-O1, the same OpenMP loops)."""
+    if sanitize is None:
+        sanitize = _SANITIZED
+    lib = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp%d" % os.getpid()
+        if sanitize:
+            cmd = [CLANG, "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"] + SANITIZE_FLAGS + \
+                  [_SRC, "-o", tmp, "-lm"]
+        else:
+            cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                   "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, lib)
+    return lib
 
 
 def _load():
