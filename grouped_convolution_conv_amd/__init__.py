@@ -36,11 +36,13 @@ ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_DIRECT: "direct", ALGO_GROUPED3X3: "groupe
 FUSED_AUTO = 0
 FUSED_STORE = 1
 FUSED_RECOMPUTE = 2
-FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recompute"}
+FUSED_ONEPASS = 3
+FUSED_NAMES = {FUSED_AUTO: "auto", FUSED_STORE: "store", FUSED_RECOMPUTE: "recompute", FUSED_ONEPASS: "onepass"}
 
 EXPORTED = (
     "conv_desc_create", "conv_desc_create_2d", "conv_desc_destroy", "conv_desc_get_output_dims", "conv_desc_set_algo",
-    "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_fwd",
+    "conv_desc_get_algo", "conv_desc_set_fused_variant", "conv_desc_get_fused_variant", "conv_desc_set_fused_wait",
+    "conv_fwd",
     "conv_fused_gn_workspace_size", "conv_fused_gn_fwd", "conv_fused_gn_fwd_noalloc", "gconv_time_graph",
     "gconv_probe_peaks", "gconv_probe_vector_peaks", "gconv_probe_copy", "conv_fused_gn_noalloc_limit", "gconv_status_string", "gconv_last_launch_error",
 )
@@ -66,6 +68,7 @@ _lib.conv_desc_set_algo.argtypes = [_p, _i]
 _lib.conv_desc_get_algo.argtypes = [_p, ctypes.POINTER(_i)]
 _lib.conv_desc_set_fused_variant.argtypes = [_p, _i]
 _lib.conv_desc_get_fused_variant.argtypes = [_p, _i, ctypes.POINTER(_i)]
+_lib.conv_desc_set_fused_wait.argtypes = [_p, _i]
 _lib.conv_fwd.argtypes = [_p, _p, _p, _p, _p, _p]
 _lib.conv_fused_gn_workspace_size.argtypes = [_p, _i, ctypes.POINTER(_sz)]
 _lib.conv_fused_gn_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, ctypes.c_float, _p, _p, _sz, _p]
@@ -176,6 +179,10 @@ def conv_desc_get_algo(desc: ConvDesc) -> int:
 
 def conv_desc_set_fused_variant(desc: ConvDesc, variant: int) -> None:
     _check("conv_desc_set_fused_variant", _lib.conv_desc_set_fused_variant(desc.handle, variant))
+
+
+def conv_desc_set_fused_wait(desc: ConvDesc, wait_us: int) -> None:
+    _check("conv_desc_set_fused_wait", _lib.conv_desc_set_fused_wait(desc.handle, wait_us))
 
 
 def conv_desc_get_fused_variant(desc: ConvDesc, gn_groups: int) -> int:

@@ -49,10 +49,14 @@ bool algo_supported(const gconv_desc *d, int algo) {
 // with LDS-resident weights, the chunked MFMA kernel, or the direct kernel.
 enum StageA { kStageDirect, kStageIgemm, kStageResident };
 
-// The recompute variant measured faster on MI355X for the shapes the
-// resident kernel takes (it trades re-reading and re-writing v for a second
-// MFMA pass).
+// The recompute variant measured fastest on MI355X for the shapes the
+// resident kernel takes: it trades re-reading and re-writing v for a second
+// MFMA pass, where the store and one-pass variants move v through memory
+// (measured at the fused 8 -> 32 chain on 64 images of 256 x 256: recompute
+// 450-472 us, one-pass 493-514 us, store over batch slices 454-464 us).
 constexpr int kDefaultResidentVariant = GCONV_FUSED_RECOMPUTE;
+constexpr int kDefaultWaitUs = 200;
+constexpr int kMaxWaitUs = 10000000;
 
 // Bytes of v per slice of the store variant (the Infinity Cache holds 256 MB;
 // measured at the fused 8 -> 32 chain: 32 MB 667 us, 64 MB 519 us, 128 MB
@@ -71,6 +75,8 @@ int resolve_fused_variant(const gconv_desc *d, int gn_groups) {
     if (d->fused_variant != GCONV_FUSED_AUTO) return d->fused_variant;
     return fused_stage_a(d, gn_groups) == kStageResident ? kDefaultResidentVariant : GCONV_FUSED_STORE;
 }
+
+size_t align16(size_t b) { return (b + 15) & ~(size_t)15; }
 
 int fused_parts_per_group(const gconv_desc *d, int gn_groups) {
     switch (fused_stage_a(d, gn_groups)) {
@@ -109,8 +115,12 @@ int fused_workspace_bytes(const gconv_desc *d, int gn_groups, size_t *bytes) {
     if (!d || !bytes) return GCONV_ERR_INVALID_ARG;
     if (gn_groups < 1 || d->K % gn_groups != 0) return GCONV_ERR_INVALID_ARG;
     size_t b = partials_bytes(d, gn_groups);
-    if (resolve_fused_variant(d, gn_groups) == GCONV_FUSED_RECOMPUTE)
-        b += (sizeof(float2) * (size_t)d->N * (size_t)gn_groups + 15) & ~(size_t)15;
+    const int variant = resolve_fused_variant(d, gn_groups);
+    if (variant == GCONV_FUSED_RECOMPUTE || variant == GCONV_FUSED_ONEPASS)
+        b += align16(sizeof(float2) * (size_t)d->N * (size_t)gn_groups);
+    if (variant == GCONV_FUSED_ONEPASS && fused_stage_a(d, gn_groups) == kStageResident &&
+        gconv::igemm_res_onepass_supported(d, gn_groups))
+        b += align16(sizeof(int) * gconv::igemm_res_onepass_sync_ints(d));
     *bytes = b;
     return GCONV_OK;
 }
@@ -130,6 +140,8 @@ int fused_gn_run(const gconv_desc *d, const float *x, const float *w, const floa
     const StageA stage = fused_stage_a(d, gn_groups);
     const int variant = resolve_fused_variant(d, gn_groups);
     if (variant == GCONV_FUSED_RECOMPUTE && stage != kStageResident) return GCONV_ERR_UNSUPPORTED;
+    if (variant == GCONV_FUSED_ONEPASS && (stage != kStageResident || !gconv::igemm_res_onepass_supported(d, gn_groups)))
+        return GCONV_ERR_UNSUPPORTED;
     gconv::FusedEpilogue ep;
     ep.bias = bias;
     ep.scale = scale;
@@ -138,6 +150,13 @@ int fused_gn_run(const gconv_desc *d, const float *x, const float *w, const floa
     ep.gn_cpg = d->K / gn_groups;
     ep.parts_per_group = fused_parts_per_group(d, gn_groups);
     int rc;
+    if (variant == GCONV_FUSED_ONEPASS) {
+        char *base = (char *)workspace + partials_bytes(d, gn_groups);
+        float2 *gstat = (float2 *)base;
+        int *sync = (int *)(base + align16(sizeof(float2) * (size_t)d->N * (size_t)gn_groups));
+        return launch_status(gconv::launch_igemm_res_onepass(d, x, w, y, ep, gstat, sync, gamma, beta, eps,
+                                                             d->fused_wait_us, st));
+    }
     if (variant == GCONV_FUSED_RECOMPUTE) {
         float2 *gstat = (float2 *)((char *)workspace + partials_bytes(d, gn_groups));
         rc = launch_status(gconv::launch_igemm_res_stats(d, x, w, nullptr, false, ep, st));
@@ -211,6 +230,7 @@ int conv_desc_create_2d(gconv_desc_t *out, int N, int C, int H, int W, int K, in
     d->Ho = Ho; d->Wo = Wo; d->cin = C / groups; d->cout = K / groups;
     d->algo = GCONV_ALGO_AUTO;
     d->fused_variant = GCONV_FUSED_AUTO;
+    d->fused_wait_us = kDefaultWaitUs;
     *out = d;
     return GCONV_OK;
 }
@@ -248,8 +268,14 @@ int conv_desc_get_algo(gconv_desc_t d, int *algo) {
 
 int conv_desc_set_fused_variant(gconv_desc_t d, int variant) {
     if (!d) return GCONV_ERR_INVALID_ARG;
-    if (variant < GCONV_FUSED_AUTO || variant > GCONV_FUSED_RECOMPUTE) return GCONV_ERR_INVALID_ARG;
+    if (variant < GCONV_FUSED_AUTO || variant > GCONV_FUSED_ONEPASS) return GCONV_ERR_INVALID_ARG;
     d->fused_variant = variant;
+    return GCONV_OK;
+}
+
+int conv_desc_set_fused_wait(gconv_desc_t d, int wait_us) {
+    if (!d || wait_us < -1 || wait_us > kMaxWaitUs) return GCONV_ERR_INVALID_ARG;
+    d->fused_wait_us = wait_us;
     return GCONV_OK;
 }
 

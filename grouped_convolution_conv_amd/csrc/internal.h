@@ -24,6 +24,7 @@ struct gconv_desc {
     int cout;  // output channels per group (K / groups)
     int algo;           // GCONV_ALGO_* requested by the caller (AUTO by default)
     int fused_variant;  // GCONV_FUSED_* requested by the caller (AUTO by default)
+    int fused_wait_us;  // one-pass variant: bounded wait for an image's statistics, microseconds
 };
 
 namespace gconv {
@@ -100,6 +101,14 @@ hipError_t launch_igemm_res_stats(const gconv_desc *d, const float *x, const flo
 hipError_t launch_gn_merge(const gconv_desc *d, const Partial *parts, int gn_groups,
                            int parts_per_group, float eps, float2 *gstat, hipStream_t st);
 // conv + bias/scale/sigmoid + normalization with merged statistics, stored to y
+// The whole fused chain in one conv pass (variant GCONV_FUSED_ONEPASS): gstat
+// [N][gn_groups] (mean, rstd) and sync [igemm_res_onepass_sync_ints] ints are
+// workspace the call clears and fills itself.
+bool igemm_res_onepass_supported(const gconv_desc *d, int gn_groups);
+size_t igemm_res_onepass_sync_ints(const gconv_desc *d);
+hipError_t launch_igemm_res_onepass(const gconv_desc *d, const float *x, const float *w, float *y,
+                                    const FusedEpilogue &fe, float2 *gstat, int *sync, const float *gamma,
+                                    const float *beta, float eps, int wait_us, hipStream_t st);
 hipError_t launch_igemm_res_normalize(const gconv_desc *d, const float *x, const float *w, float *y,
                                       const FusedEpilogue &ep, const float2 *gstat,
                                       const float *gamma, const float *beta, hipStream_t st);

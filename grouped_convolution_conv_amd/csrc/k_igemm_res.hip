@@ -32,6 +32,17 @@
 //  kStatsStore  kStats, and v is stored to y
 //  kNormalize   v as above, then out = (v - mean) * rstd * gamma + beta with
 //               the group statistics already merged, stored to y
+//  kOnePass     the whole chain in one conv pass: v is stored as in
+//               kStatsStore and each wave publishes its tile's partials
+//               (device-scope stores, then an arrival count per image); the
+//               wave whose arrival completes an image merges its partials
+//               and publishes (mean, rstd).  A fixed number of tiles later
+//               the workgroup reads the tile's v back (from the last-level
+//               cache, where it still is) and normalizes it in place.  A wave
+//               whose image is not ready after a bounded wait leaves v and
+//               lists its rows for a trailing in-place pass, so no wave ever
+//               waits on work that is not running: the result never depends
+//               on how many workgroups are resident.
 #include <atomic>
 #include <type_traits>
 
@@ -46,8 +57,9 @@ constexpr int kNBR = 2;  // output rows per wave
 constexpr int kNBC = 2;  // 32-column blocks per wave row
 constexpr int kTH = 4 * kNBR;
 constexpr int kTW = 32 * kNBC;
+constexpr int kLag = 3;   // kOnePass: tiles between a tile's conv and its normalization
 
-constexpr int kPlain = 0, kStats = 1, kNormalize = 2, kStatsStore = 3;
+constexpr int kPlain = 0, kStats = 1, kNormalize = 2, kStatsStore = 3, kOnePass = 4;
 constexpr int kResWaves = 3;  // waves per SIMD the register budget is sized for
 
 // buffer resource descriptor word 3 for raw (untyped, unswizzled) 32-bit
@@ -56,6 +68,11 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7fffffff;
 constexpr int kStoreOutOfRange = 0x40000000;  // with a scalar offset below 1 GB added
 constexpr float kLog2e = 1.44269504088896340736f;
+// cache policy of a device-scope (all XCDs) access on gfx950: sc1
+constexpr int kCpolSc1 = 16;
+// s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: expcnt
+// and lgkmcnt fields at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +82,7 @@ struct ResParams {
     int pad_h, pad_w;  // zero padding above/below and left/right
     int cin, cout;
     int n_tw, n_tiles, units;   // tiles per image row band, per image, in total
+    int parts_stride;           // partials per (image, group) in the workspace
     int x_bytes;                // bytes of one input image (C * H * W floats)
     int y_bytes;                // bytes of one output image (K * Ho * Wo floats)
     int parts_bytes;            // bytes of one image's GroupNorm partials
@@ -73,11 +91,20 @@ struct ResParams {
 struct ResEpilogue {
     const float *bias;      // kPlain: nullable conv bias; other modes: required
     const float *scale;     // all modes but kPlain
-    Partial *parts;         // kStats*: [N][gn_groups][n_tiles * 4 waves]
+    Partial *parts;         // kStats*, kOnePass: [N][gn_groups][n_tiles * 4 waves]
     const float2 *gstat;    // kNormalize: (mean, rstd) per (n, gn group)
-    const float *gamma;     // kNormalize, nullable
-    const float *beta;      // kNormalize, nullable
+    const float *gamma;     // kNormalize, kOnePass: nullable
+    const float *beta;      // kNormalize, kOnePass: nullable
     int gn_groups;
+    // kOnePass only
+    float2 *gstat_out;      // (mean, rstd) per (n, gn group), written by the merging wave
+    int *arrive;            // [N] tiles whose partial is published, zero at launch
+    int *ready;             // [N] 1 once gstat_out of the image is published, zero at launch
+    int *ndefer;            // [1] entries of defer, zero at launch
+    int *defer;             // [N * n_tiles * 4] (tile * 4 + wave) left for the trailing pass
+    float eps;
+    int wait_ticks;         // bounded wait for an image's statistics, in 100 MHz ticks;
+                            // < 0: never normalize in the conv pass
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int bytes) {
@@ -92,26 +119,113 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// GroupNorm moments merged by Chan-Golub-LeVeque pairwise updates, in double.
+struct Moments {
+    double n, mean, m2;
+};
+
+__device__ __forceinline__ Moments merge_m(Moments a, Moments b) {
+    if (b.n == 0.0) return a;
+    if (a.n == 0.0) return b;
+    Moments r;
+    r.n = a.n + b.n;
+    const double delta = b.mean - a.mean;
+    r.mean = a.mean + delta * (b.n / r.n);
+    r.m2 = a.m2 + b.m2 + delta * delta * (a.n * b.n / r.n);
+    return r;
+}
+
+// One-pass chain: merges one image's per-tile partials (group g's T
+// partials at parts[g * stride + t]) into (mean, rstd) per group, publishes
+// them, then the image's ready flag.  Run by the wave whose arrival completed
+// the image (all 64 lanes).  Eight lanes per GroupNorm group (at most 8
+// groups) take every eighth partial; the total count and sum, then the sum of
+// squared deviations from the merged mean, are accumulated in double in a
+// fixed order and summed over the eight lanes by xor shuffles (addition
+// commutes exactly, so every lane holds the same bits): the result does not
+// depend on which wave merges.  Partials, statistics and flag are read and
+// written at device scope (sc1); the flag is stored after the statistics
+// complete.
+__device__ __forceinline__ void onepass_merge_image(const Partial *parts, int stride, int T, int gn_groups,
+                                                               float eps, float2 *gstat, int *ready) {
+    constexpr int kBatch = 16;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 3, sub = lane & 7;
+    const __amdgpu_buffer_rsrc_t ps = rsrc(parts, stride * gn_groups * (int)sizeof(Partial));
+    const int base = g * stride * (int)sizeof(Partial);
+    float cnt[kBatch], mean[kBatch], m2[kBatch];
+    auto load_batch = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            // a slot past the end reads zeros: an empty partial
+            const int i = i0 + 8 * b;
+            const int off = g < gn_groups && i < T ? base + i * (int)sizeof(Partial) : kOutOfRange;
+            const u32x4 pt = __builtin_amdgcn_raw_buffer_load_b128(ps, off, 0, kCpolSc1);
+            const unsigned int c0 = pt.x, c1 = pt.y, c2 = pt.z;
+            cnt[b] = __builtin_bit_cast(float, c0);
+            mean[b] = __builtin_bit_cast(float, c1);
+            m2[b] = __builtin_bit_cast(float, c2);
+        }
+    };
+    auto lane_sum = [&](double v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) v += __shfl_xor(v, o);
+        return v;
+    };
+    const bool one_batch = T <= 8 * kBatch;
+    double n = 0.0, sum = 0.0;
+    for (int i0 = sub; i0 < T; i0 += 8 * kBatch) {
+        load_batch(i0);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            n += (double)cnt[b];
+            sum = fma((double)cnt[b], (double)mean[b], sum);
+        }
+    }
+    n = lane_sum(n);
+    const double mu = lane_sum(sum) / n;
+    double dev = 0.0;
+    for (int i0 = sub; i0 < T; i0 += 8 * kBatch) {
+        if (!one_batch) load_batch(i0);
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const double d = (double)mean[b] - mu;
+            dev += fma((double)cnt[b] * d, d, (double)m2[b]);
+        }
+    }
+    const double var = lane_sum(dev) / n;
+    if (sub == 0 && g < gn_groups) {
+        const float mf = (float)mu, rf = (float)(1.0 / sqrt(var + (double)eps));
+        __hip_atomic_store(&gstat[g].x, mf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&gstat[g].y, rf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    if (lane == 0) __hip_atomic_store(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int R, int S, int MB, int CP, int MODE, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 ? kResWaves : 2))) void igemm_res_kernel(const float *__restrict__ x,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 && MODE != kOnePass ? kResWaves : 2))) void igemm_res_kernel(const float *__restrict__ x,
                                                            const float *__restrict__ w,
                                                            float *__restrict__ y, ResParams p,
                                                            ResEpilogue ep) {
     constexpr int RS = R * S;
+    constexpr int NBC = kNBC;  // 32-column blocks per wave row
+    constexpr int TW = kTW;    // tile width
     constexpr int KW = 32 * MB;
     constexpr int NROW = kNBR + R - 1;        // band rows one wave reads
     constexpr int TIH = kTH + R - 1;          // band rows of a workgroup tile
-    constexpr int TIW = kTW + S - 1;
+    constexpr int TIW = TW + S - 1;
     constexpr int PITCH = (TIW + 3) & ~3;     // LDS row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CP * TIH * P4;        // 16-byte pieces of a tile's band
     constexpr int NSLOT = (XE4 + kBlock - 1) / kBlock;
     constexpr int WP = (CP * RS) | 1;         // weight row pitch (odd)
-    constexpr int NB = kNBR * kNBC;
+    constexpr int NB = kNBR * NBC;
     constexpr int HALF = CP / 2;
     constexpr int NWAVE = kBlock / 64;
     constexpr int NGS = 16 * MB;              // kNormalize: floats of (mean, rstd) per image
-    constexpr bool kStatsMode = MODE == kStats || MODE == kStatsStore;
+    constexpr bool kStatsMode = MODE == kStats || MODE == kStatsStore || MODE == kOnePass;
+    static_assert(MODE != kOnePass || MB == 1, "one-pass chain: 32 output channels, 8 groups of 4");
 
     __shared__ float wl[KW * WP];
     // per-channel constants, staged once: LDS reads in the epilogue count on
@@ -126,6 +240,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     __shared__ float4 bufB4[XE4];
     __shared__ float gsA[NGS];
     __shared__ float gsB[NGS];
+    // kOnePass: each wave's (count, mean, M2) per group of the current tile,
+    // merged by wave 0 into the tile's one partial
+    __shared__ float4 wstage[MODE == kOnePass ? NWAVE * 8 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -160,7 +277,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             chan_bs[k] = make_float2(-sc * kLog2e, -b * sc * kLog2e);
         chan_gb[k] = make_float2(ga, be);
     }
-    // The grid walks workgroup tiles (n, kTH output rows, kTW columns); wave
+    // The grid walks workgroup tiles (n, kTH output rows, TW columns); wave
     // w computes rows kNBR*w .. kNBR*w + kNBR-1 of its tile.
     const int G = gridDim.x;
     // Tile of round k for this workgroup.  Rounds that every workgroup runs
@@ -201,7 +318,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     auto load = [&](int v) __attribute__((always_inline)) {
         const int t = v % p.n_tiles, n = v / p.n_tiles;
         const int th = t / p.n_tw, tw = t - th * p.n_tw;
-        const int ih0 = th * kTH - p.pad_h, iw0 = tw * kTW - p.pad_w;
+        const int ih0 = th * kTH - p.pad_h, iw0 = tw * TW - p.pad_w;
         const __amdgpu_buffer_rsrc_t rs = rsrc(x + (size_t)n * p.C * HW, p.x_bytes);
         if constexpr (MODE == kNormalize) {
             const __amdgpu_buffer_rsrc_t gr = rsrc(ep.gstat + (size_t)n * ep.gn_groups, NGS * (int)sizeof(float));
@@ -211,10 +328,27 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         if constexpr (VEC) {
             if (ih0 >= 0 && ih0 + TIH <= p.H && iw0 >= 0 && iw0 + 4 * P4 <= p.W) {
                 const int corner = (ih0 * p.W + iw0) * (int)sizeof(float);
+                if constexpr (MODE == kOnePass) {
+                    // the held accumulator set leaves no registers for the
+                    // per-slot offsets: recompute them from an opaque
+                    // copy of the thread id
+                    int tid_o = tid;
+                    asm volatile("" : "+v"(tid_o));
 #pragma unroll
-                for (int i = 0; i < NSLOT; ++i) {
-                    const int lo = lane_off[i];
-                    pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, corner, 0));
+                    for (int i = 0; i < NSLOT; ++i) {
+                        const int f = i * kBlock + tid_o;
+                        const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
+                        const int lr = rem / P4, c4 = rem - lr * P4;
+                        const int lo = f < XE4 && cl < p.cin ? (cl * HW + lr * p.W + 4 * c4) * (int)sizeof(float)
+                                                             : kOutOfRange;
+                        pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, corner, 0));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NSLOT; ++i) {
+                        const int lo = lane_off[i];
+                        pf[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, corner, 0));
+                    }
                 }
                 return;
             }
@@ -262,8 +396,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     };
 
     // ---- MFMAs of the tile whose band is in LDS
-    floatx16 acc[MB][NB];
-    auto mfma_tile = [&](const float4 *buf4) __attribute__((always_inline)) {
+    floatx16 accs[1][MB][NB];
+    auto mfma_tile = [&](const float4 *buf4, floatx16 (&acc)[MB][NB]) __attribute__((always_inline)) {
         const float *band = reinterpret_cast<const float *>(buf4);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
@@ -275,9 +409,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         for (int ci = 0; ci < HALF; ++ci) {
             // operands of one input channel (per half): the weights of the
             // lane's output channel at every tap, and the NROW band rows x
-            // kNBC column blocks x S shifts of the lane's input column
+            // NBC column blocks x S shifts of the lane's input column
             float A[MB][RS];
-            float B[NROW][kNBC][S];
+            float B[NROW][NBC][S];
             const int cl = h * HALF + ci;
             const float *xq = band + (cl * TIH + wave * kNBR) * PITCH + j;
             const float *wq = wl + j * WP + cl * RS;
@@ -288,7 +422,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
 #pragma unroll
             for (int row = 0; row < NROW; ++row)
 #pragma unroll
-                for (int bc = 0; bc < kNBC; ++bc)
+                for (int bc = 0; bc < NBC; ++bc)
 #pragma unroll
                     for (int s = 0; s < S; ++s) B[row][bc][s] = xq[row * PITCH + bc * 32 + s];
 #pragma unroll
@@ -300,17 +434,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
 #pragma unroll
                         for (int br = 0; br < kNBR; ++br)
 #pragma unroll
-                            for (int bc = 0; bc < kNBC; ++bc)
-                                acc[m][br * kNBC + bc] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                    A[m][r * S + s], B[br + r][bc][s], acc[m][br * kNBC + bc], 0, 0, 0);
+                            for (int bc = 0; bc < NBC; ++bc)
+                                acc[m][br * NBC + bc] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                    A[m][r * S + s], B[br + r][bc][s], acc[m][br * NBC + bc], 0, 0, 0);
         }
     };
 
     // ---- epilogue of tile v from acc
-    auto epilogue = [&](int v, const float2 (&gst)[MB][4]) __attribute__((always_inline)) {
+    auto epilogue = [&](int v, floatx16 (&acc)[MB][NB], const float2 (&gst)[MB][4]) __attribute__((always_inline)) {
         const int t = v % p.n_tiles, n = v / p.n_tiles;
         const int th = t / p.n_tw, tw = t - th * p.n_tw;
-        const int oh0 = th * kTH + wave * kNBR, ow0 = tw * kTW;
+        const int oh0 = th * kTH + wave * kNBR, ow0 = tw * TW;
         const __amdgpu_buffer_rsrc_t ys = rsrc(y + (size_t)n * p.K * plane, p.y_bytes);
         // byte offset of (channel 0, row oh, column ow) for this lane's
         // pixels, or -1 where the pixel is outside the output
@@ -318,9 +452,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
 #pragma unroll
         for (int br = 0; br < kNBR; ++br)
 #pragma unroll
-            for (int bc = 0; bc < kNBC; ++bc) {
+            for (int bc = 0; bc < NBC; ++bc) {
                 const int oh = oh0 + br, ow = ow0 + bc * 32 + j;
-                pix[br * kNBC + bc] = (oh < p.Ho && ow < p.Wo) ? (oh * p.Wo + ow) * (int)sizeof(float) : -1;
+                pix[br * NBC + bc] = (oh < p.Ho && ow < p.Wo) ? (oh * p.Wo + ow) * (int)sizeof(float) : -1;
             }
         auto store = [&](int nb, int k, float val) __attribute__((always_inline)) {
             const int off = pix[nb] >= 0 && k < p.cout ? pix[nb] + k * plane * (int)sizeof(float) : kOutOfRange;
@@ -379,10 +513,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             // the registers, no cross-wave reduction: one partial per (tile,
             // wave, group)
             const int rows_ok = max(0, min(kNBR, p.Ho - oh0));
-            const int cols_ok = min(kTW, p.Wo - ow0);
+            const int cols_ok = min(TW, p.Wo - ow0);
             const float count = 4.0f * (float)(rows_ok * cols_ok);
             const float inv = count > 0.0f ? 1.0f / count : 0.0f;
-            const __amdgpu_buffer_rsrc_t ps = rsrc(ep.parts + (size_t)n * ep.gn_groups * (NWAVE * p.n_tiles),
+            const __amdgpu_buffer_rsrc_t ps = rsrc(ep.parts + (size_t)n * ep.gn_groups * p.parts_stride,
                                                    p.parts_bytes);
             // both passes skip the pixel masks when the wave's rows lie wholly
             // inside the output (most tiles), which the masks would otherwise
@@ -413,17 +547,161 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                             }
                         }
                         const float m2 = half_wave_sum(tq);
-                        const int idx = (8 * m + 2 * q + h) * (NWAVE * p.n_tiles) + t * NWAVE + wave;
+                        const int idx = (8 * m + 2 * q + h) * p.parts_stride + t * NWAVE + wave;
                         const u32x4 pt = {__builtin_bit_cast(unsigned int, count), __builtin_bit_cast(unsigned int, mu),
                                           __builtin_bit_cast(unsigned int, m2), 0u};
-                        __builtin_amdgcn_raw_buffer_store_b128(pt, ps, j == 0 ? idx * (int)sizeof(Partial) : kOutOfRange,
-                                                               0, 0);
+                        if constexpr (MODE == kOnePass) {
+                            if (j == 0) wstage[wave * 8 + 2 * q + h] = make_float4(count, mu, m2, 0.0f);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                pt, ps, j == 0 ? idx * (int)sizeof(Partial) : kOutOfRange, 0, 0);
+                        }
                     }
             };
-            if (oh0 + kNBR <= p.Ho && ow0 + kTW <= p.Wo)
+            if (oh0 + kNBR <= p.Ho && ow0 + TW <= p.Wo)
                 stats(std::false_type{});
             else
                 stats(std::true_type{});
+            if constexpr (MODE == kOnePass) {
+                // wave 0 merges the four waves' partials of each group (in
+                // wave order, in double) into the tile's partial, stores it
+                // at device scope, waits for the store to complete, then
+                // counts the tile's arrival on the image; the wave whose
+                // arrival completes the count merges the image
+                lds_barrier();
+                if (__builtin_amdgcn_readfirstlane(wave) == 0) {
+                    Moments mt = {0.0, 0.0, 0.0};
+                    if (lane < 8) {
+#pragma unroll
+                        for (int wv = 0; wv < NWAVE; ++wv) {
+                            const float4 f = wstage[wv * 8 + lane];
+                            mt = merge_m(mt, Moments{(double)f.x, (double)f.y, (double)f.z});
+                        }
+                    }
+                    const u32x4 pt = {__builtin_bit_cast(unsigned int, (float)mt.n),
+                                      __builtin_bit_cast(unsigned int, (float)mt.mean),
+                                      __builtin_bit_cast(unsigned int, (float)mt.m2), 0u};
+                    const int idx = lane * p.parts_stride + t;
+                    __builtin_amdgcn_raw_buffer_store_b128(pt, ps, lane < ep.gn_groups ? idx * (int)sizeof(Partial)
+                                                                                      : kOutOfRange,
+                                                           0, kCpolSc1);
+                    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+                    int old = 0;
+                    if (lane == 0) old = __hip_atomic_fetch_add(ep.arrive + n, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (__builtin_amdgcn_readfirstlane(old) == p.n_tiles - 1)
+                        onepass_merge_image(ep.parts + (size_t)n * ep.gn_groups * p.parts_stride, p.parts_stride,
+                                            p.n_tiles, ep.gn_groups, ep.eps, ep.gstat_out + (size_t)n * ep.gn_groups,
+                                            ep.ready + n);
+                }
+                // v to y after the arrival, so the arrival's wait for its
+                // partial store does not wait for these stores
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) store_fast(nb, m, vv, acc[m][nb][vv]);
+            }
+        }
+    };
+
+    // ---- kOnePass: tile v, whose v is in y, is normalized in place once
+    //      its image's (mean, rstd) is published; after the bounded wait it
+    //      is left as v, its wave's rows listed for the trailing pass, which
+    //      applies the same fmaf(v, gk, ck) and so gives the same bits.  The
+    //      check, the statistics loads and the loads of v are issued before
+    //      the next band's loads, so waiting for them never waits for those.
+    auto finish_check = [&](int v, int &rd, float (&gk4)[4], float (&ck4)[4]) __attribute__((always_inline)) {
+        if constexpr (MODE == kOnePass) {
+            const int n = v / p.n_tiles;
+            rd = 0;
+            if (ep.wait_ticks >= 0) {
+                auto ready_now = [&]() __attribute__((always_inline)) {
+                    return __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(ep.ready + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                };
+                rd = ready_now();
+                if (!rd) {
+                    const long long t0 = (long long)__builtin_amdgcn_s_memrealtime();
+                    while (!rd && (long long)__builtin_amdgcn_s_memrealtime() - t0 < (long long)ep.wait_ticks) {
+                        __builtin_amdgcn_s_sleep(4);
+                        rd = ready_now();
+                    }
+                }
+            }
+            if (rd) {
+                // (mean, rstd) of the lane's groups 2q + h, device-scope loads
+                const __amdgpu_buffer_rsrc_t gs =
+                    rsrc(ep.gstat_out + (size_t)n * ep.gn_groups, ep.gn_groups * (int)sizeof(float2));
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned long long raw = __builtin_bit_cast(
+                        unsigned long long,
+                        __builtin_amdgcn_raw_buffer_load_b64(gs, (2 * q + h) * (int)sizeof(float2), 0, kCpolSc1));
+                    gk4[q] = __builtin_bit_cast(float, (unsigned int)(raw >> 32));   // rstd
+                    ck4[q] = __builtin_bit_cast(float, (unsigned int)raw);           // mean
+                }
+            }
+        }
+    };
+    float lv[NB][16];
+    auto lag_load = [&](int v, int rd) __attribute__((always_inline)) {
+        if constexpr (MODE == kOnePass) {
+            if (rd) {
+                const int t = v % p.n_tiles, n = v / p.n_tiles;
+                const int th = t / p.n_tw, tw = t - th * p.n_tw;
+                const int oh0 = th * kTH + wave * kNBR, ow0 = tw * TW;
+                const __amdgpu_buffer_rsrc_t ys = rsrc(y + (size_t)n * p.K * plane, p.y_bytes);
+#pragma unroll
+                for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                    for (int bc = 0; bc < NBC; ++bc) {
+                        const int oh = oh0 + br, ow = ow0 + bc * 32 + j;
+                        const int vo = (oh < p.Ho && ow < p.Wo) ? (oh * p.Wo + ow + 4 * h * plane) * (int)sizeof(float)
+                                                               : kStoreOutOfRange;
+#pragma unroll
+                        for (int vv = 0; vv < 16; ++vv) {
+                            const int so = (8 * (vv >> 2) + (vv & 3)) * plane * (int)sizeof(float);
+                            lv[br * NBC + bc][vv] =
+                                __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ys, vo, so, 0));
+                        }
+                    }
+            }
+        }
+    };
+    auto lag_store = [&](int v, int rd, const float (&gk4)[4], const float (&ck4)[4]) __attribute__((always_inline)) {
+        if constexpr (MODE == kOnePass) {
+            if (rd) {
+                const int t = v % p.n_tiles, n = v / p.n_tiles;
+                const int th = t / p.n_tw, tw = t - th * p.n_tw;
+                const int oh0 = th * kTH + wave * kNBR, ow0 = tw * TW;
+                const __amdgpu_buffer_rsrc_t ys = rsrc(y + (size_t)n * p.K * plane, p.y_bytes);
+                int vofs[NB];
+#pragma unroll
+                for (int br = 0; br < kNBR; ++br)
+#pragma unroll
+                    for (int bc = 0; bc < NBC; ++bc) {
+                        const int oh = oh0 + br, ow = ow0 + bc * 32 + j;
+                        vofs[br * NBC + bc] = (oh < p.Ho && ow < p.Wo)
+                                                  ? (oh * p.Wo + ow + 4 * h * plane) * (int)sizeof(float)
+                                                  : kStoreOutOfRange;
+                    }
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv) {
+                    const int k = 8 * (vv >> 2) + 4 * h + (vv & 3);
+                    const float2 gb = chan_gb[k];
+                    const float gk = gk4[vv >> 2] * gb.x;
+                    const float ck = fmaf(-ck4[vv >> 2], gk, gb.y);
+                    const int so = (8 * (vv >> 2) + (vv & 3)) * plane * (int)sizeof(float);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, fmaf(lv[nb][vv], gk, ck)),
+                                                              ys, vofs[nb], so, 0);
+                }
+            } else if (lane == 0) {
+                const int e = __hip_atomic_fetch_add(ep.ndefer, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ep.defer[e] = v * NWAVE + wave;
+            }
         }
     };
 
@@ -447,47 +725,75 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     //      keeps the code free of branches around the loads.
     if (u >= p.units) return;
     float2 gst[MB][4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gst[m][q] = make_float2(0.0f, 0.0f);
     int k = 0;
     load(u);
     commit(bufA4, gsA);
     load(min(tile_of(1), p.units - 1));
+    if constexpr (MODE == kOnePass) {
+        // kOnePass: barrier -> MFMAs of tile u -> commit the next band ->
+        // sigmoid, partials, arrival and stores of v of tile u -> check the
+        // image of the tile kLag tiles back and load its v -> start loading
+        // the band after next -> normalize that tile in place.  A
+        // workgroup's tiles are a whole round of the grid apart (the host
+        // sizes the grid to whole images per round), so that tile's image
+        // was completed by tiles every workgroup multiplied kLag - 1 rounds
+        // earlier, and its v (kLag rounds of output back) is still in the
+        // last-level cache.
+        int rd = 0;
+        float gk4[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ck4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto step = [&](const float4 *bcur, float4 *bnext, float *gnext) __attribute__((always_inline)) {
+            lds_barrier();
+            mfma_tile(bcur, accs[0]);
+            commit(bnext, gnext);
+            epilogue(u, accs[0], gst);
+            const bool lag = k >= kLag;
+            const int vl = lag ? tile_of(k - kLag) : 0;
+            if (lag) {
+                finish_check(vl, rd, gk4, ck4);
+                lag_load(vl, rd);
+            }
+            load(min(tile_of(k + 2), p.units - 1));
+            if (lag) lag_store(vl, rd, gk4, ck4);
+            u = tile_of(++k);
+            return u < p.units;
+        };
+        while (step(bufA4, bufB4, gsB) && step(bufB4, bufA4, gsA)) {
+        }
+        // the last kLag tiles
+        for (int jj = max(0, k - kLag); jj < k; ++jj) {
+            const int vl = tile_of(jj);
+            finish_check(vl, rd, gk4, ck4);
+            lag_load(vl, rd);
+            lag_store(vl, rd, gk4, ck4);
+        }
+        return;
+    }
     while (true) {
         lds_barrier();
-        mfma_tile(bufA4);
+        mfma_tile(bufA4, accs[0]);
         read_gstat(gsA, gst);
         commit(bufB4, gsB);
         load(min(tile_of(k + 2), p.units - 1));
-        epilogue(u, gst);
+        epilogue(u, accs[0], gst);
         u = tile_of(++k);
         if (u >= p.units) break;
         lds_barrier();
-        mfma_tile(bufB4);
+        mfma_tile(bufB4, accs[0]);
         read_gstat(gsB, gst);
         commit(bufA4, gsA);
         load(min(tile_of(k + 2), p.units - 1));
-        epilogue(u, gst);
+        epilogue(u, accs[0], gst);
         u = tile_of(++k);
         if (u >= p.units) break;
     }
 }
 
 // Merged (mean, rstd) of every (n, GroupNorm group) from the per-tile
-// partials, Chan-Golub-LeVeque pairwise updates in double, fixed order.
-struct Moments {
-    double n, mean, m2;
-};
-
-__device__ __forceinline__ Moments merge_m(Moments a, Moments b) {
-    if (b.n == 0.0) return a;
-    if (a.n == 0.0) return b;
-    Moments r;
-    r.n = a.n + b.n;
-    const double delta = b.mean - a.mean;
-    r.mean = a.mean + delta * (b.n / r.n);
-    r.m2 = a.m2 + b.m2 + delta * delta * (a.n * b.n / r.n);
-    return r;
-}
-
+// partials, in a fixed order.
 __global__ __launch_bounds__(kBlock) void gn_merge_kernel(const Partial *__restrict__ parts, int P,
                                                           float eps, float2 *__restrict__ gstat) {
     __shared__ double sn[kBlock], smean[kBlock], sm2[kBlock];
@@ -515,15 +821,58 @@ __global__ __launch_bounds__(kBlock) void gn_merge_kernel(const Partial *__restr
     if (tid == 0) gstat[ng] = make_float2((float)smean[0], (float)(1.0 / sqrt(sm2[0] / sn[0] + (double)eps)));
 }
 
+// Clears the one-pass chain's arrival counts, ready flags and deferral
+// count (a kernel, not a memset, so that captured graphs replay it).
+__global__ __launch_bounds__(kBlock) void onepass_clear_kernel(int *__restrict__ sync, int count) {
+    for (int i = blockIdx.x * kBlock + threadIdx.x; i < count; i += gridDim.x * kBlock) sync[i] = 0;
+}
+
+// Trailing pass of the one-pass chain: normalizes in place the rows of the
+// (tile, wave) units whose wave stored v because its image's statistics were
+// not published within the bounded wait.  Same arithmetic as the conv pass's
+// own normalization: out = fmaf(v, gk, ck), gk = rstd * gamma,
+// ck = fmaf(-mean, gk, beta).
+__global__ __launch_bounds__(kBlock) void onepass_fixup_kernel(float *__restrict__ y, const int *__restrict__ defer,
+                                                               const int *__restrict__ ndefer,
+                                                               const float2 *__restrict__ gstat,
+                                                               const float *__restrict__ gamma,
+                                                               const float *__restrict__ beta, ResParams p,
+                                                               int gn_groups) {
+    constexpr int NWAVE = kBlock / 64;
+    const int cnt = *ndefer;
+    const int cpg = p.K / gn_groups;
+    const int plane = p.Ho * p.Wo;
+    for (int e = blockIdx.x; e < cnt; e += gridDim.x) {
+        const int unit = defer[e];
+        const int v = unit / NWAVE, wave = unit - v * NWAVE;
+        const int t = v % p.n_tiles, n = v / p.n_tiles;
+        const int th = t / p.n_tw, tw = t - th * p.n_tw;
+        const int oh0 = th * kTH + wave * kNBR, ow0 = tw * kTW;
+        float *yn = y + (size_t)n * p.K * plane;
+        for (int i = threadIdx.x; i < p.K * kNBR * kTW; i += kBlock) {
+            const int k = i / (kNBR * kTW), rc = i - k * (kNBR * kTW);
+            const int oh = oh0 + rc / kTW, ow = ow0 + rc % kTW;
+            if (oh < p.Ho && ow < p.Wo) {
+                const float2 st = gstat[(size_t)n * gn_groups + k / cpg];
+                const float ga = gamma ? gamma[k] : 1.0f, be = beta ? beta[k] : 0.0f;
+                const float gk = st.y * ga;
+                const float ck = fmaf(-st.x, gk, be);
+                float *o = yn + (size_t)k * plane + (size_t)oh * p.Wo + ow;
+                *o = fmaf(*o, gk, ck);
+            }
+        }
+    }
+}
+
 // ---- host side
 
-constexpr int kMaxResLds = 64 * 1024;  // keep at least two workgroups per CU
+constexpr int kMaxResLds = 80 * 1024;  // keep at least two workgroups per CU
 constexpr int kMaxDevices = 64;
 
-template <int R, int S, int MB, int CP>
+template <int R, int S, int MB, int CP, int MODE>
 constexpr int res_lds_bytes() {
     return 4 * (32 * MB * ((CP * R * S) | 1) + 2 * (CP * (kTH + R - 1) * ((kTW + S - 1 + 3) & ~3) + 16 * MB)) +
-           2 * 8 * 32 * MB;
+           2 * 8 * 32 * MB + (MODE == kOnePass ? 16 * (kBlock / 64) * 8 : 0);
 }
 
 // one GroupNorm partial per (tile of kTH rows x kTW columns, wave, group)
@@ -532,12 +881,16 @@ int res_parts_per_group(const gconv_desc *d) {
     return (kBlock / 64) * n_tw * ((d->Ho + kTH - 1) / kTH);
 }
 
+// tiles (kTH rows x kTW columns) per image
+int res_tiles(const gconv_desc *d) { return ((d->Wo + kTW - 1) / kTW) * ((d->Ho + kTH - 1) / kTH); }
+
 ResParams make_params(const gconv_desc *d, int gn_groups) {
     ResParams p;
     p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo;
     p.pad_h = d->pad_h; p.pad_w = d->pad_w;
     p.cin = d->cin; p.cout = d->cout;
     p.n_tw = (d->Wo + kTW - 1) / kTW;
+    p.parts_stride = res_parts_per_group(d);
     p.n_tiles = p.n_tw * ((d->Ho + kTH - 1) / kTH);
     p.units = d->N * p.n_tiles;
     p.x_bytes = (int)((size_t)d->C * d->H * d->W * sizeof(float));
@@ -556,7 +909,7 @@ int res_cp(const gconv_desc *d) { return d->cin <= 4 ? 4 : 8; }
 template <int R, int S, int MB, int CP, int MODE, bool VEC>
 hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y, const ResEpilogue &ep,
                     hipStream_t st) {
-    static_assert(res_lds_bytes<R, S, MB, CP>() <= kMaxResLds, "LDS budget");
+    static_assert(res_lds_bytes<R, S, MB, CP, MODE>() <= kMaxResLds, "LDS budget");
     auto kern = igemm_res_kernel<R, S, MB, CP, MODE, VEC>;
     // resident workgroups per device for this kernel: queried once per
     // device and kept (the query costs host time on every launch otherwise)
@@ -573,7 +926,15 @@ hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y
         cap = cus * per_cu;
         if (dev < kMaxDevices) capacity[dev].store(cap, std::memory_order_relaxed);
     }
-    const long long want = cap;
+    long long want = cap;
+    if constexpr (MODE == kOnePass) {
+        // whole images per round of the grid, so that a workgroup's previous
+        // tile belongs to an image every workgroup has finished multiplying
+        // (an image of more tiles than the capacity still computes
+        // correctly: its tiles then wait and leave more to the trailing pass)
+        const long long per_round = cap / p.n_tiles;
+        if (per_round >= 1) want = per_round * p.n_tiles;
+    }
     const int grid = (int)(p.units < want ? p.units : want);
     clear_stale_launch_error();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kBlock), 0, st, x, w, y, p, ep);
@@ -584,21 +945,33 @@ template <int MODE, bool VEC>
 hipError_t launch_mode_v(const gconv_desc *d, const ResParams &p, const float *x, const float *w, float *y,
                          const ResEpilogue &ep, hipStream_t st) {
     const int mb = res_mb(d), cp = res_cp(d);
-    if (d->R == 3 && d->S == 3) {
-        if (mb == 1)
+    if constexpr (MODE == kOnePass) {
+        // one accumulator block only (igemm_res_onepass_supported)
+        if (mb != 1) return hipErrorInvalidValue;
+        if (d->R == 3 && d->S == 3)
             return cp == 4 ? launch_t<3, 3, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
                            : launch_t<3, 3, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
-        return cp == 4 ? launch_t<3, 3, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
-                       : launch_t<3, 3, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
-    }
-    if (d->R == 1 && d->S == 1) {
-        if (mb == 1)
+        if (d->R == 1 && d->S == 1)
             return cp == 4 ? launch_t<1, 1, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
                            : launch_t<1, 1, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
-        return cp == 4 ? launch_t<1, 1, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
-                       : launch_t<1, 1, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
+        return hipErrorInvalidValue;
+    } else {
+        if (d->R == 3 && d->S == 3) {
+            if (mb == 1)
+                return cp == 4 ? launch_t<3, 3, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
+                               : launch_t<3, 3, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
+            return cp == 4 ? launch_t<3, 3, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
+                           : launch_t<3, 3, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
+        }
+        if (d->R == 1 && d->S == 1) {
+            if (mb == 1)
+                return cp == 4 ? launch_t<1, 1, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
+                               : launch_t<1, 1, 1, 8, MODE, VEC>(p, x, w, y, ep, st);
+            return cp == 4 ? launch_t<1, 1, 2, 4, MODE, VEC>(p, x, w, y, ep, st)
+                           : launch_t<1, 1, 2, 8, MODE, VEC>(p, x, w, y, ep, st);
+        }
+        return hipErrorInvalidValue;
     }
-    return hipErrorInvalidValue;
 }
 
 template <int MODE>
@@ -627,6 +1000,17 @@ bool igemm_res_fused_supported(const gconv_desc *d, int gn_groups) {
 
 int igemm_res_parts_per_group(const gconv_desc *d) { return res_parts_per_group(d); }
 
+bool igemm_res_onepass_supported(const gconv_desc *d, int gn_groups) {
+    // one accumulator block of 32 output channels (8 groups of 4); the
+    // deferral list indexes (tile, wave) units with an int
+    return igemm_res_fused_supported(d, gn_groups) && res_mb(d) == 1 && d->cout == 32 &&
+           (long long)d->N * (kBlock / 64) * res_tiles(d) < 0x7fffffffLL;
+}
+
+size_t igemm_res_onepass_sync_ints(const gconv_desc *d) {
+    return 2 * (size_t)d->N + 1 + (size_t)d->N * (size_t)(kBlock / 64) * (size_t)res_tiles(d);
+}
+
 hipError_t launch_igemm_res(const gconv_desc *d, const float *x, const float *w, const float *bias, float *y,
                             hipStream_t st) {
     if (!igemm_res_supported(d)) return hipErrorInvalidValue;
@@ -654,6 +1038,41 @@ hipError_t launch_gn_merge(const gconv_desc *d, const Partial *parts, int gn_gro
     if (ng > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     clear_stale_launch_error();
     hipLaunchKernelGGL(gn_merge_kernel, dim3((unsigned)ng), dim3(kBlock), 0, st, parts, parts_per_group, eps, gstat);
+    return hipGetLastError();
+}
+
+hipError_t launch_igemm_res_onepass(const gconv_desc *d, const float *x, const float *w, float *y,
+                                    const FusedEpilogue &fe, float2 *gstat, int *sync, const float *gamma,
+                                    const float *beta, float eps, int wait_us, hipStream_t st) {
+    if (!igemm_res_onepass_supported(d, fe.gn_groups)) return hipErrorInvalidValue;
+    const ResParams p = make_params(d, fe.gn_groups);
+    const int nsync = 2 * d->N + 1;
+    clear_stale_launch_error();
+    hipLaunchKernelGGL(onepass_clear_kernel, dim3((unsigned)((nsync + kBlock - 1) / kBlock < 1024 ? (nsync + kBlock - 1) / kBlock : 1024)),
+                       dim3(kBlock), 0, st, sync, nsync);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ResEpilogue ep{};
+    ep.bias = fe.bias;
+    ep.scale = fe.scale;
+    ep.parts = fe.parts;
+    ep.gamma = gamma;
+    ep.beta = beta;
+    ep.gn_groups = fe.gn_groups;
+    ep.gstat_out = gstat;
+    ep.arrive = sync;
+    ep.ready = sync + d->N;
+    ep.ndefer = sync + 2 * d->N;
+    ep.defer = sync + nsync;
+    ep.eps = eps;
+    // the wait in ticks of the 100 MHz real-time counter
+    ep.wait_ticks = wait_us < 0 ? -1 : (wait_us > 10000000 ? 1000000000 : wait_us * 100);
+    e = launch_mode<kOnePass>(d, p, x, w, y, ep, st);
+    if (e != hipSuccess) return e;
+    const int units = p.units * (kBlock / 64);
+    clear_stale_launch_error();
+    hipLaunchKernelGGL(onepass_fixup_kernel, dim3((unsigned)(units < 1024 ? units : 1024)), dim3(kBlock), 0, st, y,
+                       ep.defer, ep.ndefer, (const float2 *)gstat, gamma, beta, p, fe.gn_groups);
     return hipGetLastError();
 }
 

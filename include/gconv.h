@@ -92,6 +92,8 @@ extern "C" {
 #define GCONV_FUSED_AUTO 0
 #define GCONV_FUSED_STORE 1     /* conv+epilogue+stats storing v, then normalize v in place    */
 #define GCONV_FUSED_RECOMPUTE 2 /* conv+epilogue+stats, merge, then conv again + normalize     */
+#define GCONV_FUSED_ONEPASS 3   /* one conv pass: v held in registers until its image's
+                                   statistics are merged, then normalized and stored           */
 
 typedef struct gconv_desc *gconv_desc_t;
 
@@ -135,11 +137,23 @@ int conv_desc_get_algo(gconv_desc_t desc, int *algo);
 /* Forces how conv_fused_gn_fwd organizes its passes (GCONV_FUSED_*).
  * GCONV_FUSED_RECOMPUTE needs the MFMA kernel with LDS-resident weights
  * (stride 1, dilation 1, 3x3 or 1x1, 4..8 input and 8..64 output channels,
- * groups 1, 4 channels per GroupNorm group); otherwise it returns
- * GCONV_ERR_UNSUPPORTED when the fused call is made.  Both variants compute
- * the same function; they trade HBM traffic (storing and re-reading v) for
- * a second convolution pass. */
+ * groups 1, 4 channels per GroupNorm group); GCONV_FUSED_ONEPASS needs the
+ * same kernel with exactly 32 output channels (8 GroupNorm groups of 4).
+ * Otherwise the fused call returns GCONV_ERR_UNSUPPORTED.  All variants
+ * compute the same function; they trade HBM traffic (storing and re-reading
+ * v) against a second convolution pass, or (one-pass) against holding v in
+ * registers while the image's statistics are merged. */
 int conv_desc_set_fused_variant(gconv_desc_t desc, int variant);
+
+/* One-pass variant only: the longest time, in microseconds, a wave waits
+ * for its image's merged GroupNorm statistics before it stores v as is and
+ * leaves that part of the tile to a trailing in-place pass.  0 = do not
+ * wait; -1 = leave every tile to the trailing pass; at most 10,000,000.
+ * The default is 200.  The output is bit-for-bit the same for every
+ * setting; only the time differs.  Because no wave waits past this bound,
+ * the call completes whether or not the GPU runs all of its workgroups at
+ * once (other work on other streams, say). */
+int conv_desc_set_fused_wait(gconv_desc_t desc, int wait_us);
 
 /* The variant conv_fused_gn_fwd will run for gn_groups groups (never AUTO). */
 int conv_desc_get_fused_variant(gconv_desc_t desc, int gn_groups, int *variant);
@@ -150,7 +164,7 @@ int conv_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bia
              float *y, void *stream);
 
 /* Bytes of device workspace conv_fused_gn_fwd needs for gn_groups groups
- * (gn_groups >= 1 dividing K). */
+ * (gn_groups >= 1 dividing K), for the variant the descriptor resolves to. */
 int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes);
 
 /* The fused chain above.  bias and scale are required [K] vectors; gamma
@@ -162,7 +176,11 @@ int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes
  * and per-tile group statistics (storing v in y), then merges the
  * statistics and normalizes y in place; GCONV_FUSED_RECOMPUTE runs the conv
  * with the epilogue for the statistics only, merges them, then runs the
- * conv again and writes the normalized output. */
+ * conv again and writes the normalized output; GCONV_FUSED_ONEPASS clears
+ * its counters, runs the conv once (each image's statistics are merged by
+ * the wave that completes them, in a fixed order, and tiles are normalized
+ * from registers), then normalizes in place whatever the conv pass left
+ * (see conv_desc_set_fused_wait). */
 int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);

@@ -199,6 +199,11 @@ def test_fused_workspace_size():
     parts = 4 * ((254 + 7) // 8) * ((254 + 63) // 64)
     assert gc.conv_desc_get_fused_variant(d, 8) == gc.FUSED_RECOMPUTE
     assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * parts + 8 * 64 * 8
+    # the one-pass variant adds 2N + 1 counters and one deferral slot per
+    # (sample, tile, wave), as ints rounded up to 16 bytes
+    sync = 4 * (2 * 64 + 1 + 64 * parts)
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_ONEPASS)
+    assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * parts + 8 * 64 * 8 + (sync + 15) // 16 * 16
     gc.conv_desc_set_fused_variant(d, gc.FUSED_STORE)
     assert gc.conv_fused_gn_workspace_size(d, 8) == 16 * 64 * 8 * parts
     gc.conv_desc_set_fused_variant(d, gc.FUSED_AUTO)
@@ -236,10 +241,12 @@ def test_destroy_accepts_null():
 
 def test_fused_variant_setting():
     d = gc.conv_desc_create(2, 8, 20, 20, 32, 3, 3, 1, 0, 1, 1)
-    for v in (gc.FUSED_STORE, gc.FUSED_RECOMPUTE, gc.FUSED_AUTO):
+    for v in (gc.FUSED_STORE, gc.FUSED_RECOMPUTE, gc.FUSED_ONEPASS, gc.FUSED_AUTO):
         gc.conv_desc_set_fused_variant(d, v)
     with pytest.raises(gc.GconvError):
-        gc.conv_desc_set_fused_variant(d, 3)
+        gc.conv_desc_set_fused_variant(d, 4)
+    with pytest.raises(gc.GconvError):
+        gc.conv_desc_set_fused_variant(d, -1)
     with pytest.raises(gc.GconvError):
         gc.conv_desc_get_fused_variant(d, 5)
     # the recompute variant needs the resident-weight MFMA kernel: with the
@@ -251,6 +258,26 @@ def test_fused_variant_setting():
     lib = gc.library()
     assert lib.conv_fused_gn_fwd(d.handle, fake, fake, fake, fake, None, None, 8, ctypes.c_float(1e-5), fake, fake,
                                  ws, None) == gc.GCONV_ERR_UNSUPPORTED
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_ONEPASS)
+    assert lib.conv_fused_gn_fwd(d.handle, fake, fake, fake, fake, None, None, 8, ctypes.c_float(1e-5), fake, fake,
+                                 1 << 30, None) == gc.GCONV_ERR_UNSUPPORTED
+    # the one-pass variant needs exactly 32 output channels (one MFMA block)
+    d64 = gc.conv_desc_create(2, 8, 20, 20, 64, 3, 3, 1, 0, 1, 1)
+    assert gc.conv_desc_get_fused_variant(d64, 16) == gc.FUSED_RECOMPUTE
+    gc.conv_desc_set_fused_variant(d64, gc.FUSED_ONEPASS)
+    assert lib.conv_fused_gn_fwd(d64.handle, fake, fake, fake, fake, None, None, 16, ctypes.c_float(1e-5), fake,
+                                 fake, 1 << 30, None) == gc.GCONV_ERR_UNSUPPORTED
+
+
+def test_fused_wait_setting():
+    d = gc.conv_desc_create(2, 8, 20, 20, 32, 3, 3, 1, 0, 1, 1)
+    for us in (-1, 0, 1, 200, 10_000_000):
+        gc.conv_desc_set_fused_wait(d, us)
+    for us in (-2, 10_000_001):
+        with pytest.raises(gc.GconvError) as ei:
+            gc.conv_desc_set_fused_wait(d, us)
+        assert ei.value.status == gc.GCONV_ERR_INVALID_ARG
+    assert gc.library().conv_desc_set_fused_wait(None, 0) == gc.GCONV_ERR_INVALID_ARG
 
 
 def test_time_graph_validates_before_any_device_call():

@@ -51,11 +51,13 @@ def gpu_conv(wl, inp, algo=gc.ALGO_AUTO, bias=None, y_offset=0):
     return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
 
 
-def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO):
+def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO, wait_us=None):
     gn_groups = gn_groups or wl.gn_groups
     d = _desc(wl)
     gc.conv_desc_set_algo(d, algo)
     gc.conv_desc_set_fused_variant(d, variant)
+    if wait_us is not None:
+        gc.conv_desc_set_fused_wait(d, wait_us)
     ho, wo = gc.conv_desc_get_output_dims(d)
     ws = torch.empty(max(1, gc.conv_fused_gn_workspace_size(d, gn_groups)), dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)  # the kernels must not rely on its contents
@@ -230,7 +232,7 @@ def oracle_fused(wl, inp, gn_groups=None):
 
 
 @pytest.mark.parametrize("algo,variant", [(gc.ALGO_AUTO, gc.FUSED_RECOMPUTE), (gc.ALGO_AUTO, gc.FUSED_STORE),
-                                           (gc.ALGO_DIRECT, gc.FUSED_AUTO)])
+                                           (gc.ALGO_AUTO, gc.FUSED_ONEPASS), (gc.ALGO_DIRECT, gc.FUSED_AUTO)])
 def test_fused_small(algo, variant):
     wl = SMALL["c5_fused_gn"]
     _say("[parity] fused small", gc.ALGO_NAMES[algo], gc.FUSED_NAMES[variant])
@@ -265,14 +267,14 @@ def test_fused_other_geometries():
     for wl in cases:
         inp = synth.make_inputs(wl)
         ref = oracle_fused(wl, inp)
-        for variant in (gc.FUSED_AUTO, gc.FUSED_STORE, gc.FUSED_RECOMPUTE):
+        for variant in (gc.FUSED_AUTO, gc.FUSED_STORE, gc.FUSED_RECOMPUTE, gc.FUSED_ONEPASS):
             d = _desc(wl)
             gc.conv_desc_set_fused_variant(d, variant)
             try:
                 gc.conv_desc_get_fused_variant(d, wl.gn_groups)
                 out = gpu_fused(wl, inp, variant=variant)
             except gc.GconvError as e:
-                assert variant == gc.FUSED_RECOMPUTE and e.status == gc.GCONV_ERR_UNSUPPORTED
+                assert variant in (gc.FUSED_RECOMPUTE, gc.FUSED_ONEPASS) and e.status == gc.GCONV_ERR_UNSUPPORTED
                 continue
             _say("[parity] fused geometry", wl, gc.FUSED_NAMES[variant])
             check_gn(out, ref, "%s %s" % (wl, gc.FUSED_NAMES[variant]))
@@ -295,7 +297,7 @@ def _fused_full_reference(wl, inp, chunk=8):
     return _FUSED_FULL_REF[wl]
 
 
-@pytest.mark.parametrize("variant", [gc.FUSED_AUTO, gc.FUSED_STORE, gc.FUSED_RECOMPUTE])
+@pytest.mark.parametrize("variant", [gc.FUSED_AUTO, gc.FUSED_STORE, gc.FUSED_RECOMPUTE, gc.FUSED_ONEPASS])
 def test_fused_full_size_whole_output(variant):
     """The full fused workload in the benchmark's launch configuration
     (AUTO is the recompute organisation there), all 64 images compared
@@ -317,9 +319,30 @@ def test_fused_mid_size_vec_resident():
     wl = W["c5_fused_gn"].with_(N=3, H=42, W=68)
     inp = synth.make_inputs(wl)
     ref = oracle_fused(wl, inp)
-    for variant in (gc.FUSED_RECOMPUTE, gc.FUSED_STORE):
+    for variant in (gc.FUSED_RECOMPUTE, gc.FUSED_STORE, gc.FUSED_ONEPASS):
         _say("[parity] fused mid-size vec", gc.FUSED_NAMES[variant])
         check_gn(gpu_fused(wl, inp, variant=variant), ref, "fused vec " + gc.FUSED_NAMES[variant])
+
+
+@pytest.mark.parametrize("case", ["small", "mid vec", "mid ragged", "full"])
+def test_onepass_normalizes_the_same_bits_on_every_path(case):
+    """The one-pass variant normalizes a tile in the conv pass once its
+    image's statistics are ready, or leaves v for the trailing in-place pass
+    after its bounded wait.  Forcing every tile onto the trailing pass (wait
+    -1) or never waiting (wait 0, a mix of both paths) gives the same bits as
+    the default, and the result matches the oracle."""
+    wl = {"small": SMALL["c5_fused_gn"], "mid vec": W["c5_fused_gn"].with_(N=3, H=42, W=68),
+          "mid ragged": W["c5_fused_gn"].with_(N=5, H=37, W=70), "full": W["c5_fused_gn"]}[case]
+    inp = synth.make_inputs(wl)
+    _say("[parity] one-pass paths,", case)
+    base = gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS)
+    for wait in (0, -1):
+        other = gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS, wait_us=wait)
+        assert np.array_equal(base, other), "%s: wait %d differs from the default" % (case, wait)
+    n = min(wl.N, 4)
+    sl = dict(inp)
+    sl["x"] = inp["x"][:n]
+    check_gn(base[:n], oracle_fused(wl.with_(N=n), sl), "one-pass %s, first %d images" % (case, n))
 
 
 def test_fused_store_batch_slices_direct_stage():
@@ -578,6 +601,9 @@ def test_repeatable_bitwise():
     wl = SMALL["c5_fused_gn"]
     inp = synth.make_inputs(wl)
     assert np.array_equal(gpu_fused(wl, inp), gpu_fused(wl, inp))
+    wl = W["c5_fused_gn"].with_(N=8, H=130, W=132)
+    inp = synth.make_inputs(wl)
+    assert np.array_equal(gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS), gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS))
 
 
 def test_graph_capture_replays_match_eager():
@@ -659,6 +685,45 @@ def test_graph_capture_of_store_variant_slices():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(f_g, f_eager), rep
+        f_eager.add_(0.0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_graph_capture_of_onepass_variant():
+    """The one-pass variant (counter clear, conv pass, trailing pass) captured
+    twice in one HIP graph: every replay equals the eager run, so the counters
+    start from zero on every replay."""
+    wl = W["c5_fused_gn"].with_(N=8, H=130, W=132)
+    inp = synth.make_inputs(wl)
+    d = _desc(wl)
+    gc.conv_desc_set_fused_variant(d, gc.FUSED_ONEPASS)
+    ho, wo = gc.conv_desc_get_output_dims(d)
+    t = {k: _dev(v) for k, v in inp.items()}
+    ws = torch.empty(gc.conv_fused_gn_workspace_size(d, wl.gn_groups), dtype=torch.uint8, device="cuda")
+    f_eager = torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda")
+    gc.conv_fused_gn_fwd(d, t["x"], t["w"], t["bias"], t["scale"], t["gamma"], t["beta"], wl.gn_groups, wl.eps,
+                         f_eager, ws)
+    torch.cuda.synchronize()
+    check_gn(f_eager.cpu().numpy()[:2], oracle_fused(wl.with_(N=2), dict(inp, x=inp["x"][:2])), "one-pass eager")
+    f_g = torch.zeros_like(f_eager)
+    f_g2 = torch.zeros_like(f_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for out in (f_g, f_g2):
+                gc.conv_fused_gn_fwd(d, t["x"], t["w"], t["bias"], t["scale"], t["gamma"], t["beta"], wl.gn_groups,
+                                     wl.eps, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        f_g.fill_(float("nan"))
+        f_g2.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(f_g, f_eager), rep
+        assert torch.equal(f_g2, f_eager), rep
         f_eager.add_(0.0)  # unrelated eager work between replays
         torch.cuda.synchronize()
 

@@ -55,7 +55,7 @@ C5 = synth.WORKLOADS["c5_fused_gn"]
 
 
 @pytest.mark.parametrize("algo,variant", [(gc.ALGO_AUTO, gc.FUSED_AUTO), (gc.ALGO_AUTO, gc.FUSED_STORE),
-                                          (gc.ALGO_DIRECT, gc.FUSED_AUTO)])
+                                          (gc.ALGO_AUTO, gc.FUSED_ONEPASS), (gc.ALGO_DIRECT, gc.FUSED_AUTO)])
 def test_noalloc_matches_workspace_entry_point_twice(algo, variant):
     """A larger call, then a smaller one on the same scratch array."""
     big = C5.with_(N=8, H=130, W=132)
