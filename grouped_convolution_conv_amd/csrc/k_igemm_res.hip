@@ -68,7 +68,14 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kOutOfRange = 0x7fffffff;
 constexpr int kStoreOutOfRange = 0x40000000;  // with a scalar offset below 1 GB added
 constexpr float kLog2e = 1.44269504088896340736f;
-// cache policy of a device-scope (all XCDs) access on gfx950: sc1
+// cache policy of a device-scope (all XCDs) access on gfx950: sc1.  The
+// one-pass chain publishes partials, statistics and flags with such accesses
+// and orders them with explicit vmcnt waits (a device-scope access has
+// completed at device scope when the wait returns), instead of C++
+// release/acquire atomics: at agent scope those write back the whole L2
+// (buffer_wbl2) on every release and invalidate it (buffer_inv) on every
+// acquire, which on this path would cost more than the conv's stores
+// themselves.
 constexpr int kCpolSc1 = 16;
 // s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: expcnt
 // and lgkmcnt fields at their maxima)
