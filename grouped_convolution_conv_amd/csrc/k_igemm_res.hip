@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         if (k < p.cout) {
             if (ep.bias) b = ep.bias[k];
             if constexpr (MODE != kPlain) sc = ep.scale[k];
-            if constexpr (MODE == kNormalize) {
+            if constexpr (MODE == kNormalize || MODE == kOnePass) {
                 if (ep.gamma) ga = ep.gamma[k];
                 if (ep.beta) be = ep.beta[k];
             }

@@ -315,9 +315,12 @@ def test_fused_full_size_whole_output(variant):
 
 def test_fused_mid_size_vec_resident():
     """The fused chain on the resident-weight kernel with 16-byte band loads
-    (W a multiple of 4), both organisations, compared whole."""
+    (W a multiple of 4), every organisation, with a random GroupNorm affine,
+    compared whole."""
     wl = W["c5_fused_gn"].with_(N=3, H=42, W=68)
     inp = synth.make_inputs(wl)
+    inp["gamma"] = synth.uniform((wl.K,), 0.5, 1.5, wl.seed, 14)
+    inp["beta"] = synth.uniform((wl.K,), -0.5, 0.5, wl.seed, 15)
     ref = oracle_fused(wl, inp)
     for variant in (gc.FUSED_RECOMPUTE, gc.FUSED_STORE, gc.FUSED_ONEPASS):
         _say("[parity] fused mid-size vec", gc.FUSED_NAMES[variant])
@@ -343,6 +346,38 @@ def test_onepass_normalizes_the_same_bits_on_every_path(case):
     sl = dict(inp)
     sl["x"] = inp["x"][:n]
     check_gn(base[:n], oracle_fused(wl.with_(N=n), sl), "one-pass %s, first %d images" % (case, n))
+
+
+@pytest.mark.parametrize("affine", ["random", "none"])
+def test_onepass_group_norm_affine(affine):
+    """The one-pass variant applies gamma and beta (random, or absent: 1
+    and 0) the same way on both of its paths: in the conv pass and in the
+    trailing pass."""
+    wl = W["c5_fused_gn"].with_(N=3, H=42, W=68)
+    inp = synth.make_inputs(wl)
+    if affine == "random":
+        inp["gamma"] = synth.uniform((wl.K,), 0.5, 1.5, wl.seed, 12)
+        inp["beta"] = synth.uniform((wl.K,), -0.5, 0.5, wl.seed, 13)
+    else:
+        inp["gamma"] = inp["beta"] = None
+    _say("[parity] one-pass affine", affine)
+    base = gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS)
+    assert np.array_equal(base, gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS, wait_us=-1))
+    check_gn(base, oracle_fused(wl, inp), "one-pass affine " + affine)
+
+
+def test_onepass_images_larger_than_a_round():
+    """Images of more tiles than the grid holds (1030 x 1030: 2193 tiles
+    against at most a few hundred resident workgroups), so an image spans
+    rounds of the grid and tiles wait for, or leave to the trailing pass,
+    statistics that complete rounds later: every output matches the oracle
+    and equals the all-trailing-pass result."""
+    wl = W["c5_fused_gn"].with_(N=2, H=1030, W=1030)
+    inp = synth.make_inputs(wl)
+    _say("[parity] one-pass, images larger than a round")
+    base = gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS)
+    assert np.array_equal(base, gpu_fused(wl, inp, variant=gc.FUSED_ONEPASS, wait_us=-1))
+    check_gn(base, oracle_fused(wl, inp), "one-pass 2 x 1030 x 1030")
 
 
 def test_fused_store_batch_slices_direct_stage():
