@@ -447,18 +447,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // once here, so a full chunk's DMA costs no vector instructions.  An
     // element outside the image or past kvalid gets an offset beyond every
     // range (kOutOfRange plus a scalar offset below 2^31 does not wrap).
-    constexpr int XPW = (XI + NWAVE - 1) / NWAVE;  // band instructions per wave (VEC)
+    // band instructions per wave: 16-byte pieces (VEC) or 4-byte elements
+    constexpr int XPW = VEC ? (XI + NWAVE - 1) / NWAVE : (XI1 + NWAVE - 1) / NWAVE;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     int xo[XPW];
 #pragma unroll
     for (int t = 0; t < XPW; ++t) {
         const int ii = wv + t * NWAVE;
-        const int f = ii * 64 + lane;
-        const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
-        const int lr = rem / P4, c4 = rem - lr * P4;
-        const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + 4 * c4;
-        const bool ok = f < XE4 && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;  // then cl < CC
-        xo[t] = ok ? (cl * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+        if constexpr (VEC) {
+            const int f = ii * 64 + lane;
+            const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
+            const int lr = rem / P4, c4 = rem - lr * P4;
+            const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + 4 * c4;
+            const bool ok = f < XE4 && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;  // then cl < CC
+            xo[t] = ok ? (cl * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+        } else {
+            // element e of the band, as in dma() but without the chunk
+            const int e = ii * 64 + lane;
+            const int row = e / PITCH, col = e - row * PITCH;  // row = cl * TIH + lr
+            const int cl = row / TIH, lr = row - cl * TIH;
+            const int ih = ST * oh0 - p.pad_h + lr;
+            int iw;
+            if constexpr (ST == 1) {
+                iw = ow0 - p.pad_w + col;
+            } else {
+                const int ph = col >= HW2 ? 1 : 0;
+                iw = col < 2 * HW2 ? ST * ow0 - p.pad_w + 2 * (col - ph * HW2) + ph : -1;
+            }
+            const bool ok = e < XE && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;  // then cl < CC
+            xo[t] = ok ? (cl * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+        }
     }
     // weights: element e = ii*64 + lane of a chunk is (q, k) = (e / KW, e % KW),
     // so lane l holds k = l % KW and q = ii*(64/KW) + l / KW
@@ -473,8 +491,14 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             // (an array element passed straight to the builtin makes the
             // host compilation drop this kernel's launch stub)
             const int vo = xo[t];
-            if (ii < XI)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb4 + ii * 64), 16, vo, xso, 0, 0);
+            if constexpr (VEC) {
+                if (ii < XI)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb4 + ii * 64), 16, vo, xso, 0, 0);
+            } else {
+                if (ii < XI1)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        xs, (lds_void_t *)(reinterpret_cast<float *>(xb4) + ii * 64), 4, vo, xso, 0, 0);
+            }
         }
         const int wso = c0 * RS * (int)sizeof(float);
         for (int ii = wv; ii < WI; ii += NWAVE)
@@ -482,7 +506,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                                                      wso + ii * (64 / KW) * (int)sizeof(float), 0, 0);
     };
     auto dma_any = [&](int c, float4 *xb4, float *wb) __attribute__((always_inline)) {
-        if (VEC && c * CC + CC <= p.cin)
+        if (c * CC + CC <= p.cin)
             dma_full(c, xb4, wb);
         else
             dma(c, xb4, wb);
