@@ -26,6 +26,12 @@
 //  - The fused variant applies (acc + bias) * scale -> sigmoid before the
 //    store and writes, per workgroup and GroupNorm group of 4 channels, the
 //    count, mean and M2 of its values (two passes over the registers).
+//  - Narrow 1x1 and 3x3 outputs, which rows x 32-column tiles fit badly,
+//    take tiles of consecutive pixels of the flattened batch instead
+//    (igemm_flat_kernel).
+#include <algorithm>
+#include <climits>
+
 #include "dev_common.h"
 #include "internal.h"
 
@@ -591,6 +597,258 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
 }
 
+// ---- Flattened-pixel tiles (outputs that rows x 32-column tiles fit badly)
+//
+// The tiles above waste lanes where the output is narrow: a 28-wide output
+// fills 28 of a block's 32 columns, a 14-wide one 14.  Here the batch's
+// output pixels are numbered in NCHW order, P = (n*Ho + oh)*Wo + ow, and a
+// workgroup takes T = 128*NB consecutive ones: wave w's NB blocks of 32
+// pixels are P0 + (w*NB + b)*32 + j.  A block may run over row and image
+// boundaries, so only the batch's last tile has idle lanes.  The GEMM is the
+// same: the pixel axis of D[k][p] is just enumerated across rows and images.
+//
+// The band holds whole input rows of "virtual" row numbers: the batch's
+// images stacked with their zero padding, image n's padded row ihp (input row
+// ihp - pad_h) being virtual row n*HV + ihp, HV = H + 2*pad_h.  Output pixel
+// (n, oh, ow) at kernel row r reads virtual row n*HV + ST*oh + r, so each
+// lane's operands sit at a fixed offset from the band's first row, which is
+// that of the tile's first pixel.  The host bounds the band's height (tih
+// rows, at most 64) over every tile.
+//
+// Band layout: [band row][channel of the chunk][pitch], the pitch a power of
+// two so that a lane finds its element with shifts:
+//  - band column c holds input column c - pad_w - ds, where ds (0..3) makes
+//    pad_w + ds a multiple of 4, so 16-byte pieces of the band are 16-byte
+//    pieces of x (VEC: W % 4 == 0, x 16-byte aligned); pixel ow's tap s is
+//    column ST*ow + s + ds (at stride 2 the 32 lanes of a block read every
+//    other word);
+//  - stride 2 with 4-byte loads (W % 4 != 0 or x unaligned): two phases as
+//    in the tile kernel, band column c < pitch/2 holding padded column 2c
+//    and pitch/2 + c padded column 2c+1, so a block reads consecutive words.
+// The 16-byte pieces take a quarter of the DMA instructions of 4-byte
+// loads (at stride 2 on MI355X: 40.5 -> 34.3 us on a 14-wide 32-channel-group
+// layer, 76.7 -> 58.2 us on a 28-wide dense one).
+// Each band row's input row offset (or "none": padding, or past the batch)
+// is computed once per workgroup by lane = row and fetched with a lane
+// shuffle, so no lane divides while it finds its DMA elements.
+struct FlatParams {
+    int C, H, W, K, Ho, Wo;
+    int pad_h, pad_w;
+    int cin, cout;
+    int n_kb;     // output-channel blocks of 32 per group
+    int G, N;
+    int np;       // output pixels of the batch, N*Ho*Wo
+    int howo;     // Ho*Wo
+    int hv;       // virtual rows per image, H + 2*pad_h
+    int lp;       // log2 of the band pitch (floats)
+    int tih;      // band rows, at most 64
+    int ds;       // column shift of the band (0 unless 16-byte pieces)
+    int xi;       // band DMA instructions of 64 lanes per chunk
+    int n_tf;     // tiles of the batch, ceil(np / T)
+    int n_wg;     // G * n_tf * n_kb
+    int x_bytes;  // bytes of x from the group's first channel of image 0 to the end of image N-1's group
+};
+
+constexpr int kFlatMaxBandInsts = 64;  // band DMA instructions per chunk (16 per wave)
+
+template <int R, int S, int CC, bool VEC, int ST, int NB>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_flat_kernel(
+    const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
+    float *__restrict__ y, FlatParams p) {
+    static_assert(ST == 1 || ST == 2, "stride 1 or 2");
+    static_assert((CC & (CC - 1)) == 0, "the chunk is a power of two");
+    constexpr int RS = R * S;
+    constexpr int KW = 32;
+    constexpr int NWAVE = kBlock / 64;
+    constexpr int T = 32 * NB * NWAVE;
+    constexpr int UNIT = VEC ? 4 : 1;  // floats per lane of a band DMA instruction
+    constexpr int WE = CC * RS * KW;   // weight words of a chunk, [q][KW]
+    constexpr int WI = (WE + 63) / 64;
+    constexpr int HALF = CC / 2;
+    constexpr int XPW = kFlatMaxBandInsts / NWAVE;
+    // stride 2 with 4-byte loads: the band's columns in two phases
+    constexpr bool PHASES = ST == 2 && !VEC;
+
+    // two band buffers of p.xi*64*UNIT floats each (dynamic), two weight buffers
+    extern __shared__ float4 flat_band4[];
+    __shared__ float wA[WI * 64];
+    __shared__ float wB[WI * 64];
+    float *const bandA = reinterpret_cast<float *>(flat_band4);
+    float *const bandB = bandA + p.xi * 64 * UNIT;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, j = lane & 31;
+    // workgroup -> (group, tile, channel block), each XCD taking a contiguous
+    // run (as in the tile kernel): neighbouring tiles share band rows in L2
+    const int L = blockIdx.x;
+    const int xcd = L & 7, slot = L >> 3;
+    const int per = p.n_wg >> 3, rem = p.n_wg & 7;
+    const int item = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int kb = item % p.n_kb;
+    const int t1 = item / p.n_kb;
+    const int tile = t1 % p.n_tf;
+    const int g = t1 / p.n_tf;
+    const int kg0 = kb * KW;
+    const int k0 = g * p.cout + kg0;
+    const int kvalid = min(KW, p.cout - kg0);
+    const int HW = p.H * p.W;
+    const int CHW = p.C * HW;
+    const int pitch = 1 << p.lp;
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + (size_t)g * p.cin * HW, p.x_bytes);
+    const __amdgpu_buffer_rsrc_t ws = make_rsrc(w + (size_t)k0 * p.cin * RS, kvalid * p.cin * RS * (int)sizeof(float));
+    const int nchunks = (p.cin + CC - 1) / CC;
+
+    // the tile's first pixel and the virtual row of its kernel row 0
+    const int P0 = tile * T;
+    const int n0 = P0 / p.howo;
+    const int oh0 = (P0 - n0 * p.howo) / p.Wo;
+    const int vr0 = n0 * p.hv + ST * oh0;
+    // lane l: element offset (from the group's first channel of image 0) of
+    // band row l's input row, or -1 for a row of zeros
+    int rb;
+    {
+        const int vr = vr0 + lane;
+        const int nl = vr / p.hv;
+        const int ih = vr - nl * p.hv - p.pad_h;
+        rb = (lane < p.tih && nl < p.N && ih >= 0 && ih < p.H) ? nl * CHW + ih * p.W : -1;
+    }
+
+    // Per-lane band DMA offsets for a full chunk (the chunk's first channel
+    // goes in the scalar offset): instruction ii = wave + t*4 writes band
+    // floats [ii*64*UNIT, (ii+1)*64*UNIT).
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    int xo[XPW];
+#pragma unroll
+    for (int t = 0; t < XPW; ++t) {
+        const int ii = wv + t * NWAVE;
+        const int u = (ii * 64 + lane) * UNIT;
+        const int row = u >> p.lp, c = u & (pitch - 1);
+        const int i = row / CC, cl = row & (CC - 1);
+        const int rbi = __shfl(rb, i & 63);
+        int iw;
+        if constexpr (!PHASES) {
+            iw = c - p.pad_w - p.ds;
+        } else {
+            const int hp = pitch >> 1;
+            const int ph = c >= hp ? 1 : 0;
+            iw = 2 * (c - ph * hp) + ph - p.pad_w;
+        }
+        const bool ok = ii < p.xi && i < p.tih && rbi >= 0 && iw >= 0 && iw < p.W;
+        xo[t] = ok ? (rbi + cl * HW + iw) * (int)sizeof(float) : kOutOfRange;
+    }
+    const int kl = lane % KW, ql = lane / KW;
+    const int wo = kl < kvalid ? (kl * p.cin * RS + ql) * (int)sizeof(float) : kOutOfRange;
+    auto dma = [&](int c, float *xb, float *wb) __attribute__((always_inline)) {
+        const int c0 = c * CC;
+        const bool full = c0 + CC <= p.cin;
+        const int xso = c0 * HW * (int)sizeof(float);
+#pragma unroll
+        for (int t = 0; t < XPW; ++t) {
+            const int ii = wv + t * NWAVE;
+            if (ii < p.xi) {
+                int vo = xo[t];
+                if (!full) {
+                    // the last, partial chunk: channels past cin read zero
+                    const int cl = (((ii * 64 + lane) * UNIT) >> p.lp) & (CC - 1);
+                    if (c0 + cl >= p.cin) vo = kOutOfRange;
+                }
+                if constexpr (VEC)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64 * UNIT), 16, vo, xso, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64 * UNIT), 4, vo, xso, 0, 0);
+            }
+        }
+        const int wso = c0 * RS * (int)sizeof(float);
+        for (int ii = wv; ii < WI; ii += NWAVE) {
+            int vo = wo;
+            if (!full) {
+                const int cl = (ii * (64 / KW) + ql) / RS;
+                if (c0 + cl >= p.cin) vo = kOutOfRange;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, vo,
+                                                     wso + ii * (64 / KW) * (int)sizeof(float), 0, 0);
+        }
+    };
+
+    // Per-lane band offset of each block's pixel (kernel row 0, channel
+    // h*HALF, tap column 0).  A pixel past the batch takes the batch's last
+    // one (its result is not stored).
+    int bo[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int P = min(P0 + (wave * NB + b) * 32 + j, p.np - 1);
+        const int n = P / p.howo, q = P - n * p.howo;
+        const int oh = q / p.Wo, ow = q - oh * p.Wo;
+        const int vrow = n * p.hv + ST * oh;
+        bo[b] = (((vrow - vr0) * CC + h * HALF) << p.lp) + (PHASES ? ow : ST * ow + p.ds);
+    }
+    const int hp = pitch >> 1;
+
+    floatx16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+    auto mfma_chunk = [&](const float *xb, const float *wb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ci = 0; ci < HALF; ++ci) {
+            const float *wq = wb + (h * HALF + ci) * RS * KW + j;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int ro = (r * CC + ci) << p.lp;
+                const float *xq[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) xq[b] = xb + bo[b] + ro;
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float a = wq[(r * S + s) * KW];
+                    float bv[NB];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        bv[b] = !PHASES ? xq[b][s] : ((s & 1) ? xq[b][hp + (s >> 1)] : xq[b][s >> 1]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[b], acc[b], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // the tile kernel's two-buffer chunk pipeline
+    dma(0, bandA, wA);
+    for (int c = 0; c < nchunks; c += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (c + 1 < nchunks) dma(c + 1, bandB, wB);
+        mfma_chunk(bandA, wA);
+        if (c + 1 >= nchunks) break;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (c + 2 < nchunks) dma(c + 2, bandA, wA);
+        mfma_chunk(bandB, wB);
+    }
+
+    // ---- epilogue: lanes j of a block store 32 consecutive pixels of the
+    // batch (consecutive addresses within an image)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int P = P0 + (wave * NB + b) * 32 + j;
+        if (P >= p.np) continue;
+        const int n = P / p.howo, q = P - n * p.howo;
+        float *yp = y + ((size_t)n * p.K + k0) * p.howo + q;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int k = 8 * (v >> 2) + 4 * h + (v & 3);
+            if (k < kvalid) {
+                float o = acc[b][v];
+                if (bias) o += bias[k0 + k];
+                yp[(size_t)k * p.howo] = o;
+            }
+        }
+    }
+}
+
 // Input-channel chunk for a kernel size: the weights of one chunk stay
 // within about 24 KB for a 64-channel block.
 template <int R, int S>
@@ -707,6 +965,124 @@ IgParams make_params(const gconv_desc *d, int MB) {
     return p;
 }
 
+
+// ---- Flattened-pixel launch
+
+// below this fraction of useful lanes in the row x column tiles (per image),
+// a narrow output takes flattened-pixel tiles.  Their band carries more rows
+// per pixel (whole rows, the tallest tile's height) and they run one block
+// per wave, so they pay only where the tiles waste more than a fifth of
+// their lanes (measured on MI355X at batch 16: a 28-wide 32-channel-group
+// 3x3 layer 63.7 -> 56.6 us and a 14-wide stride-2 one 65.9 -> 34.3 us,
+// while 56-wide and 28-wide dense layers, their tiles 87.5 % full, ran
+// 5-25 % slower flattened)
+constexpr int kFlatBelowPercent = 80;
+// two blocks per wave once the grid still has this many workgroups
+constexpr long long kFlatTwoBlockWorkgroups = 1024;
+constexpr long long kFlatMaxLds = 64 * 1024;
+
+int flat_chunk(int R, int S, int ST) { return ST == 2 && R * S == 9 ? 4 : 8; }
+
+// The flattened-pixel plan for NB blocks per wave, or false where it does
+// not apply: kernel sizes other than 1x1 and 3x3, a band over 64 rows or
+// over the LDS budget, offsets past int32.
+bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
+    const int ST = d->stride_h;
+    if (!((d->R == 1 && d->S == 1) || (d->R == 3 && d->S == 3))) return false;
+    const long long T = 128LL * NB;
+    const long long np = (long long)d->N * d->Ho * d->Wo;
+    const long long xbytes = (long long)d->N * d->C * d->H * d->W * (long long)sizeof(float);
+    if (np + T > INT_MAX || xbytes > INT_MAX - 64) return false;
+    const int CC = flat_chunk(d->R, d->S, ST);
+    // band rows: T consecutive pixels span at most dmax + 1 output rows of
+    // the batch; each step down a row moves ST virtual rows, and a step into
+    // the next image hv - ST*Ho more (at most cross such steps)
+    const int hv = d->H + 2 * d->pad_h;
+    const long long extra = std::max(0, hv - ST * d->Ho);
+    const long long dmax = (d->Wo - 1 + T - 1) / d->Wo;
+    const long long cross = (dmax + d->Ho - 1) / d->Ho;
+    const long long tih = ST * dmax + cross * extra + d->R;
+    if (tih > 64) return false;
+    const int ds = vec ? (4 - d->pad_w % 4) % 4 : 0;
+    const int width = ST == 2 && !vec ? 2 * (d->Wo + (d->S - 1) / 2) : ST * (d->Wo - 1) + d->S + ds;
+    int lp = 2;
+    while ((1 << lp) < width) ++lp;
+    const int unit = vec ? 4 : 1;
+    const long long band = (tih * CC) << lp;
+    const long long xi = (band + 64 * unit - 1) / (64 * unit);
+    if (xi > kFlatMaxBandInsts) return false;
+    const long long wwords = ((long long)CC * d->R * d->S * 32 + 63) / 64 * 64;
+    if (2 * xi * 64 * unit * (long long)sizeof(float) + 2 * wwords * (long long)sizeof(float) > kFlatMaxLds) return false;
+    const long long n_tf = (np + T - 1) / T;
+    const int n_kb = (d->cout + 31) / 32;
+    const long long n_wg = (long long)d->groups * n_tf * n_kb;
+    if (n_wg > INT_MAX) return false;
+    p.C = d->C; p.H = d->H; p.W = d->W; p.K = d->K; p.Ho = d->Ho; p.Wo = d->Wo;
+    p.pad_h = d->pad_h; p.pad_w = d->pad_w;
+    p.cin = d->cin; p.cout = d->cout;
+    p.n_kb = n_kb;
+    p.G = d->groups; p.N = d->N;
+    p.np = (int)np;
+    p.howo = d->Ho * d->Wo;
+    p.hv = hv;
+    p.lp = lp;
+    p.tih = (int)tih;
+    p.ds = ds;
+    p.xi = (int)xi;
+    p.n_tf = (int)n_tf;
+    p.n_wg = (int)n_wg;
+    p.x_bytes = (int)(((long long)(d->N - 1) * d->C + d->cin) * d->H * d->W * (long long)sizeof(float));
+    return true;
+}
+
+template <int R, int S, int ST>
+hipError_t launch_flat_t(const FlatParams &p, bool vec, int nb, const float *x, const float *w, const float *bias,
+                         float *y, hipStream_t st) {
+    constexpr int CC = ST == 2 && R * S == 9 ? 4 : 8;
+    const size_t lds = 2 * (size_t)p.xi * 64 * (vec ? 4 : 1) * sizeof(float);
+    const dim3 g1((unsigned)p.n_wg);
+    clear_stale_launch_error();
+    if (vec) {
+        if (nb == 2)
+            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 2>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+        else
+            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 1>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+        return hipGetLastError();
+    }
+    if (nb == 2)
+        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 2>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+    else
+        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 1>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+    return hipGetLastError();
+}
+
+// Flattened-pixel tiles where the row x column tiles (area per image, in
+// pixels) leave too many lanes idle and the plan applies; returns false to
+// keep the tiles.
+bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, const float *w, const float *bias,
+                     float *y, hipStream_t st, hipError_t *err) {
+    if (100LL * d->Ho * d->Wo >= kFlatBelowPercent * tile_area) return false;
+    // 16-byte band pieces unless their column shift widens the pitch (a
+    // 28-wide 3x3 layer with padding 1 needs 33 columns for them, 30 for
+    // 4-byte loads: 64 against 32, and measured 7 % slower)
+    FlatParams p, pv, p4;
+    const bool vec = d->W % 4 == 0 && (((uintptr_t)x & 15u) == 0) && flat_plan(d, 1, true, pv) &&
+                     flat_plan(d, 1, false, p4) && pv.lp == p4.lp;
+    int nb = 2;
+    if (!flat_plan(d, 2, vec, p) || p.n_wg < kFlatTwoBlockWorkgroups) {
+        nb = 1;
+        if (!flat_plan(d, 1, vec, p)) return false;
+    }
+    const int rs = d->R * 16 + d->S;
+    if (d->stride_h == 1)
+        *err = rs == 1 * 16 + 1 ? launch_flat_t<1, 1, 1>(p, vec, nb, x, w, bias, y, st)
+                                : launch_flat_t<3, 3, 1>(p, vec, nb, x, w, bias, y, st);
+    else
+        *err = rs == 1 * 16 + 1 ? launch_flat_t<1, 1, 2>(p, vec, nb, x, w, bias, y, st)
+                                : launch_flat_t<3, 3, 2>(p, vec, nb, x, w, bias, y, st);
+    return true;
+}
+
 }  // namespace
 
 bool igemm_supported(const gconv_desc *d) {
@@ -763,6 +1139,8 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     // the DMA kernel runs a one-dimensional grid of n_wg workgroups (below
     // 2^31 for every valid descriptor: each holds at least one output)
     if (n_wg > 0x7fffffffLL) return launch_direct(d, x, w, bias, y, st);
+    hipError_t err = hipSuccess;
+    if (try_launch_flat(d, (long long)p.n_tiles * (4 * p.nbr) * (32 * p.nbc), x, w, bias, y, st, &err)) return err;
     p.n_wg = (int)n_wg;
     dim3 grid((unsigned)p.n_tiles, (unsigned)gy, (unsigned)d->N);
     FusedEpilogue none{};

@@ -500,6 +500,23 @@ EDGE = [
     synth.Workload("igemm_n_w12_5x5_vec", 1, 8, 16, 16, 32, 5, 5, 1, 0, 1, 1, 85, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_w28_cpg32", 2, 64, 28, 28, 64, 3, 3, 1, 1, 1, 2, 86, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_w15_7x7", 1, 6, 9, 15, 16, 7, 7, 1, 3, 1, 1, 87, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # flattened-pixel tiles (1x1 and 3x3 outputs that fill under 80 % of the
+    # row x column tiles): blocks of 32 pixels running over rows and images,
+    # 4-byte and 16-byte bands (a column shift of 3 for padding 1), stride 1
+    # and 2, partial channel chunks and 32-channel blocks, 5x5 images whose
+    # tiles span six of them, and two blocks per wave on a grid of 1664 and
+    # 2048 workgroups
+    synth.Workload("igemm_flat_w28_cpg32", 3, 64, 28, 28, 64, 3, 3, 1, 1, 1, 2, 88, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_vec_p0_k40", 2, 16, 16, 16, 40, 3, 3, 1, 0, 1, 1, 89, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_vec_shift3", 2, 16, 20, 20, 40, 3, 3, 1, 1, 1, 1, 90, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_s2_c10", 3, 10, 15, 15, 40, 3, 3, 2, 1, 1, 1, 91, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_s2_1x1_k33", 2, 12, 13, 13, 33, 1, 1, 2, 0, 1, 1, 92, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_1x1_vec_c20", 4, 20, 12, 12, 64, 1, 1, 1, 0, 1, 1, 93, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_5x5_images", 9, 32, 5, 5, 32, 3, 3, 1, 1, 1, 1, 94, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_s2_vec", 3, 24, 28, 28, 32, 3, 3, 2, 1, 1, 1, 95, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_s2_vec_1x1", 2, 16, 24, 24, 32, 1, 1, 2, 0, 1, 1, 96, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_nb2_1x1", 16, 512, 14, 14, 1024, 1, 1, 1, 0, 1, 128, 97, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_nb2_vec_1x1", 16, 512, 16, 16, 1024, 1, 1, 1, 0, 1, 128, 98, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
@@ -509,7 +526,7 @@ def test_conv_edge_cases(wl):
     y_ref, A = oracle_conv(wl, inp)
     y, algo = gpu_conv(wl, inp)
     _say("[parity] edge", wl.name, gc.ALGO_NAMES[algo])
-    if wl.name.startswith(("igemm_s2", "igemm_n_")):
+    if wl.name.startswith(("igemm_s2", "igemm_n_", "igemm_flat")):
         assert algo == gc.ALGO_IGEMM, gc.ALGO_NAMES[algo]
     check_conv(y, y_ref, A, wl.name)
     # an output pointer that is only 4-byte aligned takes the scalar stores
