@@ -61,6 +61,7 @@ struct IgParams {
     int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
     int nbc;           // 32-column blocks per wave row of the DMA kernel (1 on outputs at most 32 wide)
     int nbr;           // output rows per wave of the DMA kernel (1 at stride 2 and on small grids)
+    int wvec;          // C/G*R*S a multiple of 4 and w 16-byte aligned: 16-byte weight loads
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -362,6 +363,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int XI1 = (XE + 63) / 64;      // band DMA instructions (4-byte elements)
     constexpr int WE = CC * RS * KW;         // weight words of a chunk, [q][KW]
     constexpr int WI = (WE + 63) / 64;       // weight DMA instructions
+    // Where a chunk's QP = CC*R*S weights per output channel are whole
+    // 16-byte pieces (QP % 4 == 0: 1x1, 3x3, 5x5), the weights sit in LDS as
+    // [output channel][WQP] instead, WQP = QP or QP + 4 (4 mod 8, so the 32
+    // lanes reading 32 channels' weight q touch at most two words per
+    // bank), and a full chunk loads them in 16-byte pieces: a quarter of the
+    // DMA instructions, which on small layers are what the time follows.
+    constexpr int QP = CC * RS;
+    constexpr bool WK = QP % 4 == 0;
+    constexpr int WQP = QP % 8 == 0 ? QP + 4 : QP;
+    constexpr int WL = KW * WQP;             // (WK) weight floats of a chunk in LDS
+    constexpr int WI16 = (WL / 4 + 63) / 64; // (WK) 16-byte weight DMA instructions
+    constexpr int WI4 = (WL + 63) / 64;      // (WK) 4-byte weight DMA instructions
+    constexpr int WPW = (WI16 + 3) / 4;      // (WK) 16-byte weight DMA instructions per wave
+    constexpr int WCAP = WK ? WI16 * 256 : WI * 64;
     constexpr int NB = NBR * NBC;
     constexpr int HALF = CC / 2;
     constexpr int NWAVE = kBlock / 64;
@@ -369,8 +384,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // buffers padded to whole DMA instructions (idle lanes write zeros there)
     __shared__ float4 xA4[XI * 64];
     __shared__ float4 xB4[XI * 64];
-    __shared__ float wA[WI * 64];
-    __shared__ float wB[WI * 64];
+    __shared__ float wA[WCAP];
+    __shared__ float wB[WCAP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -436,13 +451,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb + ii * 64), 4, off, 0, 0, 0);
             }
         }
-        for (int ii = wave; ii < WI; ii += NWAVE) {
-            const int e = ii * 64 + lane;            // e = q * KW + k
-            const int q = e / KW, k = e - q * KW;    // q = cl * RS + t
-            const int cl = q / RS;
-            const bool ok = e < WE && k < kvalid && c0 + cl < p.cin;
-            const int off = ok ? (k * p.cin * RS + c0 * RS + q) * (int)sizeof(float) : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, off, 0, 0, 0);
+        if constexpr (WK) {
+            for (int ii = wave; ii < WI4; ii += NWAVE) {
+                const int e = ii * 64 + lane;            // e = k * WQP + q
+                const int k = e / WQP, q = e - k * WQP;  // q = cl * RS + t
+                const bool ok = e < WL && k < kvalid && q < QP && c0 + q / RS < p.cin;
+                const int off = ok ? (k * p.cin * RS + c0 * RS + q) * (int)sizeof(float) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, off, 0, 0, 0);
+            }
+        } else {
+            for (int ii = wave; ii < WI; ii += NWAVE) {
+                const int e = ii * 64 + lane;            // e = q * KW + k
+                const int q = e / KW, k = e - q * KW;    // q = cl * RS + t
+                const int cl = q / RS;
+                const bool ok = e < WE && k < kvalid && c0 + cl < p.cin;
+                const int off = ok ? (k * p.cin * RS + c0 * RS + q) * (int)sizeof(float) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, off, 0, 0, 0);
+            }
         }
     };
 
@@ -488,6 +513,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // so lane l holds k = l % KW and q = ii*(64/KW) + l / KW
     const int kl = lane % KW, ql = lane / KW;
     const int wo = kl < kvalid ? (kl * p.cin * RS + ql) * (int)sizeof(float) : kOutOfRange;
+    // (WK) 16-byte weight piece f = ii*64 + lane: channel f / (WQP/4),
+    // weights 4*(f % (WQP/4)) ..+3 of the chunk
+    int wo16[WK ? WPW : 1];
+    if constexpr (WK) {
+#pragma unroll
+        for (int t = 0; t < WPW; ++t) {
+            const int f = (wv + t * NWAVE) * 64 + lane;
+            const int k = f / (WQP / 4), q4 = f - k * (WQP / 4);
+            wo16[t] = (k < kvalid && 4 * q4 < QP) ? (k * p.cin * RS + 4 * q4) * (int)sizeof(float) : kOutOfRange;
+        }
+    }
     auto dma_full = [&](int c, float4 *xb4, float *wb) __attribute__((always_inline)) {
         const int c0 = c * CC;
         const int xso = c0 * HW * (int)sizeof(float);
@@ -507,12 +543,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
         const int wso = c0 * RS * (int)sizeof(float);
-        for (int ii = wv; ii < WI; ii += NWAVE)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, wo,
-                                                     wso + ii * (64 / KW) * (int)sizeof(float), 0, 0);
+        if constexpr (WK) {
+#pragma unroll
+            for (int t = 0; t < WPW; ++t) {
+                const int ii = wv + t * NWAVE;
+                const int vo = wo16[t];
+                if (ii < WI16)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 256), 16, vo, wso, 0, 0);
+            }
+        } else {
+            for (int ii = wv; ii < WI; ii += NWAVE)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, wo,
+                                                         wso + ii * (64 / KW) * (int)sizeof(float), 0, 0);
+        }
     };
     auto dma_any = [&](int c, float4 *xb4, float *wb) __attribute__((always_inline)) {
-        if (c * CC + CC <= p.cin)
+        // 16-byte weight pieces need the tensor's pieces aligned (p.wvec)
+        if (c * CC + CC <= p.cin && (!WK || p.wvec))
             dma_full(c, xb4, wb);
         else
             dma(c, xb4, wb);
@@ -531,7 +578,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
             const float *xq = xin + (cl * TIH + ST * wave * NBR) * PITCH + j;
-            const float *wq = wb + cl * RS * KW + j;
+            const float *wq = WK ? wb + j * WQP + cl * RS : wb + cl * RS * KW + j;
             // kernel rows one at a time: unrolling them all lets the compiler
             // hoist every row's LDS reads and spill with two output blocks
 #pragma unroll 1
@@ -540,7 +587,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int s = 0; s < S; ++s) {
                     float a[MB], b[NB];
 #pragma unroll
-                    for (int m = 0; m < MB; ++m) a[m] = wq[(r * S + s) * KW + m * 32];
+                    for (int m = 0; m < MB; ++m) a[m] = WK ? wq[m * 32 * WQP + r * S + s] : wq[(r * S + s) * KW + m * 32];
 #pragma unroll
                     for (int br = 0; br < NBR; ++br)
 #pragma unroll
@@ -647,6 +694,7 @@ struct FlatParams {
     int n_tf;     // tiles of the batch, ceil(np / T)
     int n_wg;     // G * n_tf * n_kb
     int x_bytes;  // bytes of x from the group's first channel of image 0 to the end of image N-1's group
+    int wvec;     // weights in 16-byte pieces: C/G*R*S a multiple of 4 and w 16-byte aligned
 };
 
 constexpr int kFlatMaxBandInsts = 64;  // band DMA instructions per chunk (16 per wave)
@@ -662,8 +710,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int NWAVE = kBlock / 64;
     constexpr int T = 32 * NB * NWAVE;
     constexpr int UNIT = VEC ? 4 : 1;  // floats per lane of a band DMA instruction
-    constexpr int WE = CC * RS * KW;   // weight words of a chunk, [q][KW]
-    constexpr int WI = (WE + 63) / 64;
+    // Weights of a chunk in LDS as [output channel][QP] with row pitch WQP:
+    // a channel's QP = CC*R*S weights of the chunk are contiguous in w, so
+    // they load in 16-byte pieces (pieces past QP read zero).  WQP is 4 mod
+    // 8, so the 32 lanes reading 32 channels' weight q touch at most two
+    // words per bank.
+    constexpr int QP = CC * RS;
+    constexpr int WQP = ((QP + 3) / 4 * 4) % 8 == 0 ? (QP + 3) / 4 * 4 + 4 : (QP + 3) / 4 * 4;
+    constexpr int WL = KW * WQP;            // weight floats of a chunk in LDS
+    constexpr int WI16 = (WL / 4 + 63) / 64;  // 16-byte weight DMA instructions
+    constexpr int WI4 = (WL + 63) / 64;       // 4-byte weight DMA instructions
+    constexpr int WPW = (WI16 + NWAVE - 1) / NWAVE;
     constexpr int HALF = CC / 2;
     constexpr int XPW = kFlatMaxBandInsts / NWAVE;
     // stride 2 with 4-byte loads: the band's columns in two phases
@@ -671,8 +728,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // two band buffers of p.xi*64*UNIT floats each (dynamic), two weight buffers
     extern __shared__ float4 flat_band4[];
-    __shared__ float wA[WI * 64];
-    __shared__ float wB[WI * 64];
+    __shared__ float4 wA4[WI16 * 64];
+    __shared__ float4 wB4[WI16 * 64];
+    float *const wA = reinterpret_cast<float *>(wA4);
+    float *const wB = reinterpret_cast<float *>(wB4);
     float *const bandA = reinterpret_cast<float *>(flat_band4);
     float *const bandB = bandA + p.xi * 64 * UNIT;
 
@@ -737,8 +796,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         const bool ok = ii < p.xi && i < p.tih && rbi >= 0 && iw >= 0 && iw < p.W;
         xo[t] = ok ? (rbi + cl * HW + iw) * (int)sizeof(float) : kOutOfRange;
     }
-    const int kl = lane % KW, ql = lane / KW;
-    const int wo = kl < kvalid ? (kl * p.cin * RS + ql) * (int)sizeof(float) : kOutOfRange;
+    // 16-byte weight pieces of a full chunk: piece f = ii*64 + lane is
+    // (channel f / (WQP/4), weights 4*(f % (WQP/4)) ..+3); the chunk's first
+    // channel goes in the scalar offset
+    int wo[WPW];
+#pragma unroll
+    for (int t = 0; t < WPW; ++t) {
+        const int f = (wv + t * NWAVE) * 64 + lane;
+        const int k = f / (WQP / 4), q4 = f - k * (WQP / 4);
+        wo[t] = (k < kvalid && 4 * q4 < QP) ? (k * p.cin * RS + 4 * q4) * (int)sizeof(float) : kOutOfRange;
+    }
     auto dma = [&](int c, float *xb, float *wb) __attribute__((always_inline)) {
         const int c0 = c * CC;
         const bool full = c0 + CC <= p.cin;
@@ -760,14 +827,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
         const int wso = c0 * RS * (int)sizeof(float);
-        for (int ii = wv; ii < WI; ii += NWAVE) {
-            int vo = wo;
-            if (!full) {
-                const int cl = (ii * (64 / KW) + ql) / RS;
-                if (c0 + cl >= p.cin) vo = kOutOfRange;
+        if (full && p.wvec) {
+#pragma unroll
+            for (int t = 0; t < WPW; ++t) {
+                const int ii = wv + t * NWAVE;
+                const int vo = wo[t];
+                if (ii < WI16)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 256), 16, vo, wso, 0, 0);
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, vo,
-                                                     wso + ii * (64 / KW) * (int)sizeof(float), 0, 0);
+        } else {
+            // the last, partial chunk (its channels past cin read zero), or
+            // weights that are not in 16-byte pieces: 4-byte loads
+            for (int ii = wv; ii < WI4; ii += NWAVE) {
+                const int e = ii * 64 + lane;
+                const int k = e / WQP, q = e - k * WQP;
+                const bool ok = e < WL && k < kvalid && q < QP && c0 + q / RS < p.cin;
+                const int vo = ok ? (k * p.cin * RS + c0 * RS + q) * (int)sizeof(float) : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ws, (lds_void_t *)(wb + ii * 64), 4, vo, 0, 0, 0);
+            }
         }
     };
 
@@ -793,7 +870,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     auto mfma_chunk = [&](const float *xb, const float *wb) __attribute__((always_inline)) {
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
-            const float *wq = wb + (h * HALF + ci) * RS * KW + j;
+            const float *wq = wb + j * WQP + (h * HALF + ci) * RS;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int ro = (r * CC + ci) << p.lp;
@@ -802,7 +879,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 for (int b = 0; b < NB; ++b) xq[b] = xb + bo[b] + ro;
 #pragma unroll
                 for (int s = 0; s < S; ++s) {
-                    const float a = wq[(r * S + s) * KW];
+                    const float a = wq[r * S + s];
                     float bv[NB];
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
@@ -962,6 +1039,7 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.G = d->groups;
     p.n_wg = 0;
     p.st = d->stride_h;
+    p.wvec = 0;
     return p;
 }
 
@@ -1011,7 +1089,9 @@ bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     const long long band = (tih * CC) << lp;
     const long long xi = (band + 64 * unit - 1) / (64 * unit);
     if (xi > kFlatMaxBandInsts) return false;
-    const long long wwords = ((long long)CC * d->R * d->S * 32 + 63) / 64 * 64;
+    const long long qp = (long long)CC * d->R * d->S;
+    const long long wqp = (qp + 3) / 4 * 4 + (((qp + 3) / 4 * 4) % 8 == 0 ? 4 : 0);
+    const long long wwords = (32 * wqp / 4 + 63) / 64 * 256;
     if (2 * xi * 64 * unit * (long long)sizeof(float) + 2 * wwords * (long long)sizeof(float) > kFlatMaxLds) return false;
     const long long n_tf = (np + T - 1) / T;
     const int n_kb = (d->cout + 31) / 32;
@@ -1032,6 +1112,7 @@ bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     p.n_tf = (int)n_tf;
     p.n_wg = (int)n_wg;
     p.x_bytes = (int)(((long long)(d->N - 1) * d->C + d->cin) * d->H * d->W * (long long)sizeof(float));
+    p.wvec = 0;
     return true;
 }
 
@@ -1073,6 +1154,7 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
         nb = 1;
         if (!flat_plan(d, 1, vec, p)) return false;
     }
+    p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
     const int rs = d->R * 16 + d->S;
     if (d->stride_h == 1)
         *err = rs == 1 * 16 + 1 ? launch_flat_t<1, 1, 1>(p, vec, nb, x, w, bias, y, st)
@@ -1118,6 +1200,7 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
     p.vec = d->stride_h == 1 && (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
     // the DMA kernel's tile: 8 rows (4 at stride 2) by 64 columns, or by one
     // 32-column block on outputs at most 32 wide; 4 rows as well when 8-row
     // tiles would leave fewer than two workgroups per CU (more, smaller
