@@ -12,11 +12,11 @@
 // a row, K = 4 input channels at one tap), so no MFMA row is idle.
 //
 // Two kernels.  grouped16_mfma_lds_kernel (W a multiple of 4, x 16-byte
-// aligned) stages a workgroup's band in LDS with 128-bit loads and reads
-// every B operand from LDS.  grouped16_mfma_kernel (any other W or
-// alignment) reads B straight from memory, described next.  Measured on the
-// 16 cpg-16 shapes of the grouped 3x3 grid, the two beat the VALU register
-// kernel everywhere but one tie (N8 C256 112x112: 87 us against 126;
+// aligned) loads a workgroup's band straight into LDS with 16-byte buffer
+// loads and reads every B operand from LDS.  grouped16_mfma_kernel (any
+// other W or alignment) reads B straight from memory, described next.
+// Measured on the 16 cpg-16 shapes of the grouped 3x3 grid, the two beat the
+// VALU register kernel everywhere (N8 C256 112x112: 83 us against 126;
 // N8 C256 14x14: 6.5 against 18.9); the direct-load form alone was slower
 // than the VALU kernel at N8 C256 112x112 (129 against 125 us): its dword
 // load per B operand keeps the texture address units and the load latency,
@@ -51,14 +51,7 @@ constexpr int kRB = 2;                       // output rows per wave
 
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
-// wait for the wave's outstanding global loads (the band's second half).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct GmParams {
     int C, H, W, K, G;
@@ -186,30 +179,45 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // LDS-staged form (W a multiple of 4 and x 16-byte aligned): a workgroup of
-// 4 waves owns kTH = 8 output rows x 64 columns of one (image, group).  Its
-// band (the group's 16 channels x 10 input rows x 72 columns, from column
-// ow0 - 4, in whole 16-byte pieces) is read once with 128-bit buffer loads
-// (pieces outside the image read zero) into LDS; after one barrier every B
-// operand is an LDS read at a compile-time offset from the lane's base.
-constexpr int kTH = 8;                        // output rows per workgroup (2 per wave)
-constexpr int kLPitch = 72;                   // band row pitch (floats): columns ow0-4 .. ow0+67
-constexpr int kLRows = kTH + 2;
-constexpr int kLPieces = 16 * kLRows * (kLPitch / 4);   // 16-byte pieces of a band
+// 4 waves owns 4*RBW output rows x 64 columns of one (image, group); RBW = 1
+// output row per wave.  Its band (the group's 16 channels x 4*RBW + 2 input
+// rows x 72 columns from column ow0 - 4, in whole 16-byte pieces) goes
+// straight from memory into LDS by buffer loads with the LDS bit (lane l of
+// an instruction writes its 16 bytes at the instruction's LDS base + 16 l;
+// pieces outside the image read zero), channels 0-7 first, then 8-15.  Each
+// wave waits for its own first half (the loads count down in issue order),
+// one barrier admits quads 0 and 1 while channels 8-15 land, a second one
+// quads 2 and 3; every B operand is an LDS read at a compile-time offset
+// from the lane's base.
+//
+// An earlier form staged the band through registers (48 of its 140 VGPRs),
+// which held it to three waves per SIMD with 8-row tiles; with no register
+// holding the band, 4-row tiles use 81 VGPRs and 32 KB of LDS, five
+// workgroups per CU (measured on MI355X, cold buffers: N8 C256 112x112 86.1
+// -> 83.3 us, 56x56 27.4 -> 25.0, N1 C64 56x56 8.5 -> 6.1; 8-row tiles in the
+// same form, three per CU by LDS, were no faster than before).
+constexpr int kLPitch = 72;         // band row pitch (floats): columns ow0-4 .. ow0+67
+constexpr int kG16RowsPerWave = 1;
 
 struct GlParams {
     int C, H, W, K, G;
     int n_seg;    // 64-column segments per row
-    int n_rb;     // 8-row blocks per image
+    int n_rb;     // row blocks (4 * kG16RowsPerWave rows) per image
     int wgs;      // workgroups: N * G * n_rb * n_seg
 };
 
+template <int RBW>
 __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float *__restrict__ x,
                                                                     const float *__restrict__ w,
                                                                     const float *__restrict__ bias,
                                                                     float *__restrict__ y, GlParams p) {
-    // one half-band buffer (8 channels, 23 KB): both halves are loaded into
-    // registers up front and committed in turn, so five workgroups fit a CU
-    __shared__ float4 band4[kLPieces / 2];
+    constexpr int TH = 4 * RBW;
+    constexpr int LROWS = TH + 2;
+    constexpr int P4 = kLPitch / 4;                         // 16-byte pieces per band row
+    constexpr int HPIECES = 8 * LROWS * P4;                 // pieces of a half band (8 channels)
+    constexpr int HI = ((HPIECES + 63) / 64 + 3) / 4 * 4;  // DMA instructions per half, whole rounds of 4 waves
+    constexpr int HIW = HI / 4;                             // per wave and half
+    __shared__ float4 band4[2 * HI * 64];
     const float *band = reinterpret_cast<const float *>(band4);
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -227,14 +235,11 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     const int rb = t % p.n_rb;
     t /= p.n_rb;
     const int g = t % p.G, n = t / p.G;
-    const int oh0 = kTH * rb, ow0 = 64 * seg;
+    const int oh0 = TH * rb, ow0 = 64 * seg;
     const int j = lane & 15, kq = lane >> 4;
     const int HW = p.H * p.W;
 
-    // A operands and the bias first: they are waited for before the band,
-    // and loads complete in issue order.  The bias comes through a buffer
-    // resource that is empty when there is none (its loads read zero), so no
-    // branch makes the compiler wait for every outstanding load.
+    // A operands and the bias first (waited for with the first half)
     float A[4][9];
     {
         const float *wl = w + ((size_t)(g * 16 + j) * 16 + kq) * 9;
@@ -249,77 +254,75 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
     for (int v = 0; v < 4; ++v)
         bv[v] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(bs, (4 * kq + v) * (int)sizeof(float), 0, 0));
-    // keep that issue order: loads count down in order, so a wait for the
-    // operands must not also wait for band loads scheduled before them
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- band: piece f = (c * kLRows + lr) * 18 + c4 holds input columns
-    //      ow0 - 4 + 4c4 .. +3 of row oh0 - 1 + lr, channel c of the group
+    // ---- band: half hf holds channels 8hf..8hf+7; its piece f =
+    //      (c * LROWS + lr) * P4 + c4 holds input columns ow0 - 4 + 4c4 .. +3
+    //      of row oh0 - 1 + lr, channel 8hf + c
     const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(x + ((size_t)n * p.C + (size_t)g * 16) * HW), (short)0, 16 * HW * (int)sizeof(float),
         kBufferWord3);
-    // the band in two halves (channels 0-7, 8-15), all loads issued up front:
-    // the MFMAs of quads 0 and 1 start once the first half is in LDS, while
-    // the second half is still arriving
-    constexpr int HALF = kLPieces / 2;
-    constexpr int NPH = (HALF + kBlock - 1) / kBlock;
-    float4 pv[2][NPH];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int i = 0; i < NPH; ++i) {
-            const int f = hf * HALF + i * kBlock + tid;
-            const int c = f / (kLRows * 18), rem = f - c * (kLRows * 18);
-            const int lr = rem / 18, c4 = rem - lr * 18;
+        for (int ti = 0; ti < HIW; ++ti) {
+            const int ii = ti * 4 + wv;
+            const int f = ii * 64 + lane;
+            const int c = f / (LROWS * P4), r2 = f - c * (LROWS * P4);
+            const int lr = r2 / P4, c4 = r2 - lr * P4;
             const int ih = oh0 - 1 + lr, iw = ow0 - 4 + 4 * c4;
-            const bool ok = i * kBlock + tid < HALF && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
-            const int off = ok ? (c * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
-            pv[hf][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
-            if (i == NPH - 1) __builtin_amdgcn_sched_barrier(0);  // first half before the second
+            const bool ok = f < HPIECES && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
+            const int off = ok ? ((8 * hf + c) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(band4 + (hf * HI + ii) * 64), 16, off, 0,
+                                                     0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
-    floatx4 acc[kRB][4];
+    floatx4 acc[RBW][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int rr = 0; rr < kRB; ++rr)
+        for (int rr = 0; rr < RBW; ++rr)
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[rr][b][v] = bv[v];
-    auto commit = [&](int hf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < NPH; ++i) {
-            const int fi = i * kBlock + tid;
-            if (fi < HALF) band4[fi] = pv[hf][i];
-        }
-    };
 
     // ---- MFMAs: B of (quad q, output row rr, tap (r, s), block b) is band
-    //      channel 4q + kq, row 2*wave + rr + r, column 16b + j + s - 1 + 4
-    const float *bl = band + (kq * kLRows + kRB * wave) * kLPitch + j + 3;
-    commit(0);
-    lds_barrier();
+    //      half q/2, channel 4(q%2) + kq, row RBW*wave + rr + r, column
+    //      16b + j + s - 1 + 4
+    const float *bl = band + (kq * LROWS + RBW * wave) * kLPitch + j + 3;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        if (q == 2) {
-            // quads 2 and 3 read channels 8-15: once every wave is done with
-            // the first half, the second half replaces it
-            lds_barrier();
-            commit(1);
-            lds_barrier();
+        // The waits and barriers are written out: a workgroup-scope release
+        // fence before the barrier would make the compiler wait for every
+        // load that writes LDS, the second half's too.  A load with the LDS bit
+        // counts down once its data is in LDS, and the memory clobber keeps
+        // the LDS reads below the barrier.
+        if (q == 0) {
+            // this wave's first half has landed (its second half's HIW loads
+            // may still be in flight); after the barrier, every wave's has
+            static_assert(HIW == 4 || HIW == 6, "a wait count for this tile");
+            if constexpr (HIW == 4)
+                asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
         }
-        float B[kRB + 2][4][3];
+        if (q == 2) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+        float B[RBW + 2][4][3];
 #pragma unroll
-        for (int i = 0; i < kRB + 2; ++i)
+        for (int i = 0; i < RBW + 2; ++i)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int s = 0; s < 3; ++s) B[i][b][s] = bl[(4 * (q & 1) * kLRows + i) * kLPitch + 16 * b + s];
+                for (int s = 0; s < 3; ++s)
+                    B[i][b][s] = bl[(q >> 1) * HI * 256 + (4 * (q & 1) * LROWS + i) * kLPitch + 16 * b + s];
 #pragma unroll
         for (int r = 0; r < 3; ++r)
 #pragma unroll
             for (int s = 0; s < 3; ++s)
 #pragma unroll
-                for (int rr = 0; rr < kRB; ++rr)
+                for (int rr = 0; rr < RBW; ++rr)
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
                         acc[rr][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[q][r * 3 + s], B[rr + r][b][s],
@@ -330,8 +333,8 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
         y + ((size_t)n * p.K + (size_t)g * 16) * HW, (short)0, 16 * HW * (int)sizeof(float), kBufferWord3);
 #pragma unroll
-    for (int rr = 0; rr < kRB; ++rr) {
-        const int oh = oh0 + kRB * wave + rr;
+    for (int rr = 0; rr < RBW; ++rr) {
+        const int oh = oh0 + RBW * wave + rr;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int ow = ow0 + 16 * b + j;
@@ -387,12 +390,13 @@ hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const floa
         GlParams q;
         q.C = d->C; q.H = d->H; q.W = d->W; q.K = d->K; q.G = d->groups;
         q.n_seg = (d->W + 63) / 64;
-        q.n_rb = (d->H + kTH - 1) / kTH;
+        q.n_rb = (d->H + 4 * kG16RowsPerWave - 1) / (4 * kG16RowsPerWave);
         const long long wgs = (long long)d->N * d->groups * q.n_rb * q.n_seg;
         if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         q.wgs = (int)wgs;
         clear_stale_launch_error();
-        hipLaunchKernelGGL(grouped16_mfma_lds_kernel, dim3((unsigned)q.wgs), dim3(kBlock), 0, st, x, w, bias, y, q);
+        hipLaunchKernelGGL(grouped16_mfma_lds_kernel<kG16RowsPerWave>, dim3((unsigned)q.wgs), dim3(kBlock), 0, st, x,
+                           w, bias, y, q);
         return hipGetLastError();
     }
     const int NB = pick_nb(d->W);
