@@ -697,13 +697,19 @@ struct FlatParams {
     int wvec;     // weights in 16-byte pieces: C/G*R*S a multiple of 4 and w 16-byte aligned
 };
 
-constexpr int kFlatMaxBandInsts = 64;  // band DMA instructions per chunk (16 per wave)
+// band DMA instructions per chunk, at most: 64 (16 per wave, one offset
+// register each), or 128 for 4-byte loads where the band is taller for its
+// pixels (stride 2, dilation 2, 5x5 and 7x7)
+constexpr int flat_max_band_insts(int R, int ST, int DIL, bool VEC) {
+    return VEC || (ST == 1 && DIL == 1 && R <= 3) ? 64 : 128;
+}
 
-template <int R, int S, int CC, bool VEC, int ST, int NB>
+template <int R, int S, int CC, bool VEC, int ST, int NB, int DIL>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_flat_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, FlatParams p) {
     static_assert(ST == 1 || ST == 2, "stride 1 or 2");
+    static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
     static_assert((CC & (CC - 1)) == 0, "the chunk is a power of two");
     constexpr int RS = R * S;
     constexpr int KW = 32;
@@ -717,12 +723,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // words per bank.
     constexpr int QP = CC * RS;
     constexpr int WQP = ((QP + 3) / 4 * 4) % 8 == 0 ? (QP + 3) / 4 * 4 + 4 : (QP + 3) / 4 * 4;
+    // a chunk's weights start on a 16-byte boundary only when QP % 4 == 0
+    // (7x7 chunks of 2 channels, 98 weights, take 4-byte loads)
+    constexpr bool WV16 = QP % 4 == 0;
     constexpr int WL = KW * WQP;            // weight floats of a chunk in LDS
     constexpr int WI16 = (WL / 4 + 63) / 64;  // 16-byte weight DMA instructions
     constexpr int WI4 = (WL + 63) / 64;       // 4-byte weight DMA instructions
     constexpr int WPW = (WI16 + NWAVE - 1) / NWAVE;
     constexpr int HALF = CC / 2;
-    constexpr int XPW = kFlatMaxBandInsts / NWAVE;
+    constexpr int XPW = flat_max_band_insts(R, ST, DIL, VEC) / NWAVE;
     // stride 2 with 4-byte loads: the band's columns in two phases
     constexpr bool PHASES = ST == 2 && !VEC;
 
@@ -827,7 +836,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             }
         }
         const int wso = c0 * RS * (int)sizeof(float);
-        if (full && p.wvec) {
+        if (WV16 && full && p.wvec) {
 #pragma unroll
             for (int t = 0; t < WPW; ++t) {
                 const int ii = wv + t * NWAVE;
@@ -873,7 +882,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             const float *wq = wb + j * WQP + (h * HALF + ci) * RS;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int ro = (r * CC + ci) << p.lp;
+                // kernel row r reads band row (pixel's) + r*DIL, kernel
+                // column s padded column (pixel's) + s*DIL
+                const int ro = (r * DIL * CC + ci) << p.lp;
                 const float *xq[NB];
 #pragma unroll
                 for (int b = 0; b < NB; ++b) xq[b] = xb + bo[b] + ro;
@@ -883,7 +894,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                     float bv[NB];
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
-                        bv[b] = !PHASES ? xq[b][s] : ((s & 1) ? xq[b][hp + (s >> 1)] : xq[b][s >> 1]);
+                        bv[b] = !PHASES ? xq[b][s * DIL]
+                                        : (((s * DIL) & 1) ? xq[b][hp + ((s * DIL) >> 1)] : xq[b][(s * DIL) >> 1]);
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
                         acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, bv[b], acc[b], 0, 0, 0);
@@ -1063,37 +1075,60 @@ constexpr int kFlatBelowPercent = 80;
 constexpr long long kFlatTwoBlockWorkgroups = 1024;
 constexpr long long kFlatMaxLds = 64 * 1024;
 
-// channels per chunk: as in the tile kernel (16 at 1x1 stride 1)
-int flat_chunk(int R, int S, int ST) { return ST == 2 ? (R * S == 9 ? 4 : 8) : (R * S == 1 ? 16 : 8); }
+// channels per chunk: as in the tile kernel (16 at 1x1 stride 1), and 4 at
+// 5x5, 2 at 7x7
+constexpr int flat_chunk_c(int R, int S, int ST) {
+    return R * S == 1 ? (ST == 1 ? 16 : 8) : R * S == 9 ? (ST == 1 ? 8 : 4) : R * S == 25 ? 4 : 2;
+}
+
+// Geometries with a flattened-pixel kernel: square 1x1 and 3x3 at stride 1
+// and 2, 3x3 at dilation 2, and 5x5 and 7x7 at stride 2 (which the tile
+// kernel does not take).  A 1x1 kernel's dilation changes nothing.
+int flat_dil(const gconv_desc *d) { return d->R == 1 && d->S == 1 ? 1 : d->dil_h; }
+
+bool flat_geometry(const gconv_desc *d) {
+    if (d->stride_h != d->stride_w || d->dil_h != d->dil_w || d->R != d->S) return false;
+    if (d->stride_h != 1 && d->stride_h != 2) return false;
+    const int dil = flat_dil(d);
+    switch (d->R) {
+        case 1: return true;
+        case 3: return dil == 1 || dil == 2;
+        case 5:
+        case 7: return dil == 1 && d->stride_h == 2;
+        default: return false;
+    }
+}
 
 // The flattened-pixel plan for NB blocks per wave, or false where it does
-// not apply: kernel sizes other than 1x1 and 3x3, a band over 64 rows or
-// over the LDS budget, offsets past int32.
+// not apply: other geometries, a band over 64 rows or over the LDS budget,
+// offsets past int32.
 bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     const int ST = d->stride_h;
-    if (!((d->R == 1 && d->S == 1) || (d->R == 3 && d->S == 3))) return false;
+    if (!flat_geometry(d) || d->cin < 4 || d->cout < 8) return false;
+    const int dil = flat_dil(d);
     const long long T = 128LL * NB;
     const long long np = (long long)d->N * d->Ho * d->Wo;
     const long long xbytes = (long long)d->N * d->C * d->H * d->W * (long long)sizeof(float);
     if (np + T > INT_MAX || xbytes > INT_MAX - 64) return false;
-    const int CC = flat_chunk(d->R, d->S, ST);
+    const int CC = flat_chunk_c(d->R, d->S, ST);
     // band rows: T consecutive pixels span at most dmax + 1 output rows of
     // the batch; each step down a row moves ST virtual rows, and a step into
-    // the next image hv - ST*Ho more (at most cross such steps)
+    // the next image hv - ST*Ho more (at most cross such steps); the last
+    // pixel's kernel rows reach (R-1)*dil further
     const int hv = d->H + 2 * d->pad_h;
     const long long extra = std::max(0, hv - ST * d->Ho);
     const long long dmax = (d->Wo - 1 + T - 1) / d->Wo;
     const long long cross = (dmax + d->Ho - 1) / d->Ho;
-    const long long tih = ST * dmax + cross * extra + d->R;
+    const long long tih = ST * dmax + cross * extra + (long long)(d->R - 1) * dil + 1;
     if (tih > 64) return false;
     const int ds = vec ? (4 - d->pad_w % 4) % 4 : 0;
-    const int width = ST == 2 && !vec ? 2 * (d->Wo + (d->S - 1) / 2) : ST * (d->Wo - 1) + d->S + ds;
+    const int width = ST == 2 && !vec ? 2 * (d->Wo + (d->S - 1) * dil / 2) : ST * (d->Wo - 1) + (d->S - 1) * dil + 1 + ds;
     int lp = 2;
     while ((1 << lp) < width) ++lp;
     const int unit = vec ? 4 : 1;
     const long long band = (tih * CC) << lp;
     const long long xi = (band + 64 * unit - 1) / (64 * unit);
-    if (xi > kFlatMaxBandInsts) return false;
+    if (xi > flat_max_band_insts(d->R, ST, dil, vec)) return false;
     const long long qp = (long long)CC * d->R * d->S;
     const long long wqp = (qp + 3) / 4 * 4 + (((qp + 3) / 4 * 4) % 8 == 0 ? 4 : 0);
     const long long wwords = (32 * wqp / 4 + 63) / 64 * 256;
@@ -1121,66 +1156,93 @@ bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     return true;
 }
 
-template <int R, int S, int ST>
+template <int R, int S, int ST, int DIL>
 hipError_t launch_flat_t(const FlatParams &p, bool vec, int nb, const float *x, const float *w, const float *bias,
                          float *y, hipStream_t st) {
-    constexpr int CC = ST == 2 ? (R * S == 9 ? 4 : 8) : (R * S == 1 ? 16 : 8);
+    constexpr int CC = flat_chunk_c(R, S, ST);
     const size_t lds = 2 * (size_t)p.xi * 64 * (vec ? 4 : 1) * sizeof(float);
     const dim3 g1((unsigned)p.n_wg);
     clear_stale_launch_error();
     if (vec) {
         if (nb == 2)
-            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 2>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 2, DIL>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
         else
-            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 1>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+            hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, true, ST, 1, DIL>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
         return hipGetLastError();
     }
     if (nb == 2)
-        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 2>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 2, DIL>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
     else
-        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 1>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
+        hipLaunchKernelGGL((igemm_flat_kernel<R, S, CC, false, ST, 1, DIL>), g1, dim3(kBlock), lds, st, x, w, bias, y, p);
     return hipGetLastError();
 }
 
 // Flattened-pixel tiles where the row x column tiles (area per image, in
-// pixels) leave too many lanes idle and the plan applies; returns false to
-// keep the tiles.
+// pixels; 0 where the tile kernel does not take the geometry) leave too many
+// lanes idle and the plan applies; returns false to keep the tiles.
 bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, const float *w, const float *bias,
                      float *y, hipStream_t st, hipError_t *err) {
-    if (100LL * d->Ho * d->Wo >= kFlatBelowPercent * tile_area) return false;
+    if (tile_area > 0 && 100LL * d->Ho * d->Wo >= kFlatBelowPercent * tile_area) return false;
     // 16-byte band pieces unless their column shift widens the pitch (a
     // 28-wide 3x3 layer with padding 1 needs 33 columns for them, 30 for
     // 4-byte loads: 64 against 32, and measured 7 % slower)
     FlatParams p, pv, p4;
+    // (or where only the 16-byte plan fits)
     const bool vec = d->W % 4 == 0 && (((uintptr_t)x & 15u) == 0) && flat_plan(d, 1, true, pv) &&
-                     flat_plan(d, 1, false, p4) && pv.lp == p4.lp;
+                     (!flat_plan(d, 1, false, p4) || pv.lp == p4.lp);
     int nb = 2;
     if (!flat_plan(d, 2, vec, p) || p.n_wg < kFlatTwoBlockWorkgroups) {
         nb = 1;
         if (!flat_plan(d, 1, vec, p)) return false;
     }
     p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
-    const int rs = d->R * 16 + d->S;
-    if (d->stride_h == 1)
-        *err = rs == 1 * 16 + 1 ? launch_flat_t<1, 1, 1>(p, vec, nb, x, w, bias, y, st)
-                                : launch_flat_t<3, 3, 1>(p, vec, nb, x, w, bias, y, st);
-    else
-        *err = rs == 1 * 16 + 1 ? launch_flat_t<1, 1, 2>(p, vec, nb, x, w, bias, y, st)
-                                : launch_flat_t<3, 3, 2>(p, vec, nb, x, w, bias, y, st);
+    const bool s1 = d->stride_h == 1, d2 = flat_dil(d) == 2;
+    switch (d->R) {
+        case 1:
+            *err = s1 ? launch_flat_t<1, 1, 1, 1>(p, vec, nb, x, w, bias, y, st)
+                      : launch_flat_t<1, 1, 2, 1>(p, vec, nb, x, w, bias, y, st);
+            break;
+        case 3:
+            if (d2)
+                *err = s1 ? launch_flat_t<3, 3, 1, 2>(p, vec, nb, x, w, bias, y, st)
+                          : launch_flat_t<3, 3, 2, 2>(p, vec, nb, x, w, bias, y, st);
+            else
+                *err = s1 ? launch_flat_t<3, 3, 1, 1>(p, vec, nb, x, w, bias, y, st)
+                          : launch_flat_t<3, 3, 2, 1>(p, vec, nb, x, w, bias, y, st);
+            break;
+        case 5: *err = launch_flat_t<5, 5, 2, 1>(p, vec, nb, x, w, bias, y, st); break;
+        default: *err = launch_flat_t<7, 7, 2, 1>(p, vec, nb, x, w, bias, y, st); break;
+    }
     return true;
 }
 
 }  // namespace
 
-bool igemm_supported(const gconv_desc *d) {
+namespace {
+
+// The tile kernels (and the fused chain's chunked kernel): dilation 1,
+// stride 1, or stride 2 on both axes at 1x1 and 3x3.
+bool igemm_tile_supported(const gconv_desc *d) {
     // buffer offsets are signed 32-bit: one group's input channels of one
     // image must stay below 2 GB
-    // stride 1, or stride 2 on both axes at 1x1 and 3x3
     const bool stride_ok = d->stride_h == d->stride_w &&
                            (d->stride_h == 1 || (d->stride_h == 2 && d->R == d->S && (d->R == 1 || d->R == 3)));
     return stride_ok && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
            d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
+
+// Geometries only the flattened-pixel kernel takes (3x3 at dilation 2, 5x5
+// and 7x7 at stride 2), where its plan fits: with 16-byte band pieces when W
+// is a multiple of 4 (a call whose x is not 16-byte aligned, and whose
+// 4-byte plan does not fit, runs the direct kernel), else with 4-byte loads.
+bool igemm_flat_only(const gconv_desc *d) {
+    FlatParams p;
+    return !igemm_tile_supported(d) && (flat_plan(d, 1, false, p) || (d->W % 4 == 0 && flat_plan(d, 1, true, p)));
+}
+
+}  // namespace
+
+bool igemm_supported(const gconv_desc *d) { return igemm_tile_supported(d) || igemm_flat_only(d); }
 
 bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // every output channel of every 32*MB block must exist, and a GroupNorm
@@ -1189,7 +1251,7 @@ bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // its grid is (tiles, group x channel block, n), within the hardware's
     // 65535 limit on y and z
     const long long gy = (long long)d->groups * ((d->cout + 32 * pick_mb(d) - 1) / (32 * pick_mb(d)));
-    return igemm_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
+    return igemm_tile_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
            gy <= 65535 && d->N <= 65535;
 }
 
@@ -1200,6 +1262,11 @@ int igemm_fused_parts_per_group(const gconv_desc *d, int) {
 hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, const float *bias,
                         float *y, hipStream_t st) {
     if (!igemm_supported(d)) return hipErrorInvalidValue;
+    if (!igemm_tile_supported(d)) {
+        hipError_t err = hipErrorInvalidValue;
+        if (!try_launch_flat(d, 0, x, w, bias, y, st, &err)) return launch_direct(d, x, w, bias, y, st);
+        return err;
+    }
     // one 32-channel block per workgroup (kPlainMB): each input band is
     // read once per block, in exchange for no register spills
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;

@@ -173,8 +173,9 @@ EXTRA_WORKLOADS = {
 }
 
 # Dense and 32-channel-group layers on the implicit GEMM (ResNet- and
-# ResNeXt-style shapes at batch 16), 3x3 at stride 1 and 2 and a 1x1
-# reduction; x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
+# ResNeXt-style shapes at batch 16), 3x3 at stride 1 and 2, a 1x1
+# reduction, and the geometries of the flattened-pixel kernel (3x3 at
+# dilation 2, 5x5 and 7x7 at stride 2); x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
 IGEMM_WORKLOADS = {
     "g3s2_cpg32_1024x28": Workload("g3s2_cpg32_1024x28", 16, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32, 901,
                                    ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
@@ -186,6 +187,14 @@ IGEMM_WORKLOADS = {
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
     "dense1_256x56": Workload("dense1_256x56", 16, 256, 56, 56, 64, 1, 1, 1, 0, 1, 1, 906,
                               ("uniform", -1.0, 1.0), _u(1 / 16.0)),
+    # geometries on the flattened-pixel kernel only: a dilated 3x3 (a
+    # DeepLab-style dilated stage), dense 5x5 and 7x7 at stride 2
+    "dense3d2_256x28": Workload("dense3d2_256x28", 16, 256, 28, 28, 256, 3, 3, 1, 2, 2, 1, 907,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(256 * 9))),
+    "dense5s2_64x56": Workload("dense5s2_64x56", 16, 64, 56, 56, 64, 5, 5, 2, 2, 1, 1, 908,
+                               ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 25))),
+    "dense7s2_16x112": Workload("dense7s2_16x112", 16, 16, 112, 112, 64, 7, 7, 2, 3, 1, 1, 909,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(16 * 49))),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

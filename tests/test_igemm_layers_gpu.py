@@ -1,7 +1,8 @@
 """GPU parity of the implicit GEMM on dense and 32-channel-group layers at
 full size (ResNet- and ResNeXt-style shapes at batch 16: 3x3 at stride 1 and
-2, a 1x1 reduction), through the C ABI, against the CPU oracle on sampled
-outputs: random ones plus every border pixel of three planes.
+2, a 1x1 reduction; a dilated 3x3, dense 5x5 and 7x7 at stride 2), through
+the C ABI, against the CPU oracle on sampled outputs: random ones plus every
+border pixel of three planes.
 
 Bar: |y_gpu - y_oracle| <= 1e-4 * A + 1e-6 per output, A = sum |x * w| over
 the output's receptive field.  Outputs start as NaN, so an element no kernel

@@ -517,6 +517,19 @@ EDGE = [
     synth.Workload("igemm_flat_s2_vec_1x1", 2, 16, 24, 24, 32, 1, 1, 2, 0, 1, 1, 96, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_nb2_1x1", 16, 512, 14, 14, 1024, 1, 1, 1, 0, 1, 128, 97, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_nb2_vec_1x1", 16, 512, 16, 16, 1024, 1, 1, 1, 0, 1, 128, 98, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # geometries only the flattened-pixel kernel takes: 3x3 at dilation 2
+    # (stride 1 and 2, "same" and narrower padding, 16-byte and 4-byte
+    # bands, 32 channels per group), 5x5 and 7x7 at stride 2 (partial
+    # chunks, 7x7's 98-weight chunks on 4-byte weight loads)
+    synth.Workload("igemm_flat_dil2_vec", 2, 32, 20, 20, 40, 3, 3, 1, 2, 2, 1, 99, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil2_s2_vec", 3, 16, 32, 32, 32, 3, 3, 2, 2, 2, 1, 100, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil2_p1", 2, 8, 15, 15, 16, 3, 3, 1, 1, 2, 1, 101, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil2_cpg32", 2, 64, 14, 14, 64, 3, 3, 1, 2, 2, 2, 102, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil2_s2", 2, 8, 29, 29, 16, 3, 3, 2, 2, 2, 1, 108, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_5x5_s2", 2, 12, 23, 23, 40, 5, 5, 2, 2, 1, 1, 103, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_5x5_s2_vec", 2, 16, 24, 24, 32, 5, 5, 2, 2, 1, 1, 104, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_7x7_s2", 2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1, 105, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_7x7_s2_vec", 1, 4, 40, 40, 32, 7, 7, 2, 3, 1, 1, 106, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
