@@ -657,18 +657,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // The band holds whole input rows of "virtual" row numbers: the batch's
 // images stacked with their zero padding, image n's padded row ihp (input row
 // ihp - pad_h) being virtual row n*HV + ihp, HV = H + 2*pad_h.  Output pixel
-// (n, oh, ow) at kernel row r reads virtual row n*HV + ST*oh + r, so each
+// (n, oh, ow) at kernel row r reads virtual row n*HV + ST*oh + r*DIL, so each
 // lane's operands sit at a fixed offset from the band's first row, which is
 // that of the tile's first pixel.  The host bounds the band's height (tih
-// rows, at most 64) over every tile.
+// rows, at most 64) over every tile.  The same addressing serves 1x1 and 3x3
+// at stride 1 and 2, 3x3 at dilation 2, and 5x5 and 7x7 at stride 2.
 //
 // Band layout: [band row][channel of the chunk][pitch], the pitch a power of
 // two so that a lane finds its element with shifts:
 //  - band column c holds input column c - pad_w - ds, where ds (0..3) makes
 //    pad_w + ds a multiple of 4, so 16-byte pieces of the band are 16-byte
 //    pieces of x (VEC: W % 4 == 0, x 16-byte aligned); pixel ow's tap s is
-//    column ST*ow + s + ds (at stride 2 the 32 lanes of a block read every
-//    other word);
+//    column ST*ow + s*DIL + ds (at stride 2 the 32 lanes of a block read
+//    every other word);
 //  - stride 2 with 4-byte loads (W % 4 != 0 or x unaligned): two phases as
 //    in the tile kernel, band column c < pitch/2 holding padded column 2c
 //    and pitch/2 + c padded column 2c+1, so a block reads consecutive words.

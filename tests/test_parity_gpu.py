@@ -500,6 +500,13 @@ EDGE = [
     synth.Workload("igemm_n_w12_5x5_vec", 1, 8, 16, 16, 32, 5, 5, 1, 0, 1, 1, 85, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_w28_cpg32", 2, 64, 28, 28, 64, 3, 3, 1, 1, 1, 2, 86, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_w15_7x7", 1, 6, 9, 15, 16, 7, 7, 1, 3, 1, 1, 87, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # 1x1 with 16-channel chunks on 8x64 tiles (512 workgroups; 70 KB of
+    # LDS, beyond the 64 KB a workgroup's static LDS took before), with the
+    # 16-byte band loads and without
+    synth.Workload("igemm_n_1x1_c16_tile8x64_vec", 16, 16, 64, 124, 64, 1, 1, 1, 0, 1, 1, 109,
+                   ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_1x1_c16_tile8x64", 16, 16, 64, 126, 64, 1, 1, 1, 0, 1, 1, 110,
+                   ("uniform", -1, 1), ("uniform", -1, 1)),
     # flattened-pixel tiles (1x1 and 3x3 outputs that fill under 80 % of the
     # row x column tiles): blocks of 32 pixels running over rows and images,
     # 4-byte and 16-byte bands (a column shift of 3 for padding 1), stride 1
