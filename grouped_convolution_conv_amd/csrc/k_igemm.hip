@@ -1072,8 +1072,14 @@ IgParams make_params(const gconv_desc *d, int MB) {
 // while 56-wide and 28-wide dense layers, their tiles 87.5 % full, ran
 // 5-25 % slower flattened)
 constexpr int kFlatBelowPercent = 80;
-// two blocks per wave once the grid still has this many workgroups
+// two blocks per wave once the grid still has this many workgroups, or on
+// reductions of this many channel chunks, whose length amortizes a
+// workgroup's set-up and first loads (measured on MI355X, batch 16: a
+// dilated 3x3 C256 28x28 layer, 32 chunks, 214 -> 181 us at 392 instead of
+// 784 workgroups; a 28x28 32-channel-group layer, 4 chunks, 48.1 -> 52.5 us
+// the other way)
 constexpr long long kFlatTwoBlockWorkgroups = 1024;
+constexpr int kFlatTwoBlockChunks = 16;
 constexpr long long kFlatMaxLds = 64 * 1024;
 
 // channels per chunk: as in the tile kernel (16 at 1x1 stride 1), and 4 at
@@ -1192,7 +1198,8 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
     const bool vec = d->W % 4 == 0 && (((uintptr_t)x & 15u) == 0) && flat_plan(d, 1, true, pv) &&
                      (!flat_plan(d, 1, false, p4) || pv.lp == p4.lp);
     int nb = 2;
-    if (!flat_plan(d, 2, vec, p) || p.n_wg < kFlatTwoBlockWorkgroups) {
+    const int nchunks = (d->cin + flat_chunk_c(d->R, d->S, d->stride_h) - 1) / flat_chunk_c(d->R, d->S, d->stride_h);
+    if (!flat_plan(d, 2, vec, p) || (p.n_wg < kFlatTwoBlockWorkgroups && nchunks < kFlatTwoBlockChunks)) {
         nb = 1;
         if (!flat_plan(d, 1, vec, p)) return false;
     }
