@@ -179,9 +179,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 }
 
 // LDS-staged form (W a multiple of 4 and x 16-byte aligned): a workgroup of
-// 4 waves owns 4*RBW output rows x 64 columns of one (image, group); RBW = 1
-// output row per wave.  Its band (the group's 16 channels x 4*RBW + 2 input
-// rows x 72 columns from column ow0 - 4, in whole 16-byte pieces) goes
+// 4 waves owns 4*RBW output rows x 16*NBW columns of one (image, group);
+// RBW = 1 output row per wave, NBW = 4 blocks of 16 columns, or 2 on rows at
+// most 32 wide (a 28-wide row filled 28 of 64 columns).  Its band (the
+// group's 16 channels x 4*RBW + 2 input rows x 16*NBW + 8 columns from
+// column ow0 - 4, in whole 16-byte pieces) goes
 // straight from memory into LDS by buffer loads with the LDS bit (lane l of
 // an instruction writes its 16 bytes at the instruction's LDS base + 16 l;
 // pieces outside the image read zero), channels 0-7 first, then 8-15.  Each
@@ -196,24 +198,24 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // workgroups per CU (measured on MI355X, cold buffers: N8 C256 112x112 86.1
 // -> 83.3 us, 56x56 27.4 -> 25.0, N1 C64 56x56 8.5 -> 6.1; 8-row tiles in the
 // same form, three per CU by LDS, were no faster than before).
-constexpr int kLPitch = 72;         // band row pitch (floats): columns ow0-4 .. ow0+67
 constexpr int kG16RowsPerWave = 1;
 
 struct GlParams {
     int C, H, W, K, G;
-    int n_seg;    // 64-column segments per row
+    int n_seg;    // column segments (16*NBW columns) per row
     int n_rb;     // row blocks (4 * kG16RowsPerWave rows) per image
     int wgs;      // workgroups: N * G * n_rb * n_seg
 };
 
-template <int RBW>
+template <int RBW, int NBW>
 __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float *__restrict__ x,
                                                                     const float *__restrict__ w,
                                                                     const float *__restrict__ bias,
                                                                     float *__restrict__ y, GlParams p) {
     constexpr int TH = 4 * RBW;
     constexpr int LROWS = TH + 2;
-    constexpr int P4 = kLPitch / 4;                         // 16-byte pieces per band row
+    constexpr int PITCH = 16 * NBW + 8;                     // band row: columns ow0-4 .. ow0+16*NBW+3
+    constexpr int P4 = PITCH / 4;                           // 16-byte pieces per band row
     constexpr int HPIECES = 8 * LROWS * P4;                 // pieces of a half band (8 channels)
     constexpr int HI = ((HPIECES + 63) / 64 + 3) / 4 * 4;  // DMA instructions per half, whole rounds of 4 waves
     constexpr int HIW = HI / 4;                             // per wave and half
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     const int rb = t % p.n_rb;
     t /= p.n_rb;
     const int g = t % p.G, n = t / p.G;
-    const int oh0 = TH * rb, ow0 = 64 * seg;
+    const int oh0 = TH * rb, ow0 = 16 * NBW * seg;
     const int j = lane & 15, kq = lane >> 4;
     const int HW = p.H * p.W;
 
@@ -280,18 +282,18 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    floatx4 acc[RBW][4];
+    floatx4 acc[RBW][NBW];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int rr = 0; rr < RBW; ++rr)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[rr][b][v] = bv[v];
+            for (int b = 0; b < NBW; ++b) acc[rr][b][v] = bv[v];
 
     // ---- MFMAs: B of (quad q, output row rr, tap (r, s), block b) is band
     //      half q/2, channel 4(q%2) + kq, row RBW*wave + rr + r, column
     //      16b + j + s - 1 + 4
-    const float *bl = band + (kq * LROWS + RBW * wave) * kLPitch + j + 3;
+    const float *bl = band + (kq * LROWS + RBW * wave) * PITCH + j + 3;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         // The waits and barriers are written out: a workgroup-scope release
@@ -302,21 +304,23 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
         if (q == 0) {
             // this wave's first half has landed (its second half's HIW loads
             // may still be in flight); after the barrier, every wave's has
-            static_assert(HIW == 4 || HIW == 6, "a wait count for this tile");
-            if constexpr (HIW == 4)
+            static_assert(HIW == 2 || HIW == 4 || HIW == 6, "a wait count for this tile");
+            if constexpr (HIW == 2)
+                asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");
+            else if constexpr (HIW == 4)
                 asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
         }
         if (q == 2) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-        float B[RBW + 2][4][3];
+        float B[RBW + 2][NBW][3];
 #pragma unroll
         for (int i = 0; i < RBW + 2; ++i)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int s = 0; s < 3; ++s)
-                    B[i][b][s] = bl[(q >> 1) * HI * 256 + (4 * (q & 1) * LROWS + i) * kLPitch + 16 * b + s];
+                    B[i][b][s] = bl[(q >> 1) * HI * 256 + (4 * (q & 1) * LROWS + i) * PITCH + 16 * b + s];
 #pragma unroll
         for (int r = 0; r < 3; ++r)
 #pragma unroll
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
 #pragma unroll
                 for (int rr = 0; rr < RBW; ++rr)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
+                    for (int b = 0; b < NBW; ++b)
                         acc[rr][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[q][r * 3 + s], B[rr + r][b][s],
                                                                           acc[rr][b], 0, 0, 0);
     }
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(kBlock) void grouped16_mfma_lds_kernel(const float 
     for (int rr = 0; rr < RBW; ++rr) {
         const int oh = oh0 + RBW * wave + rr;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NBW; ++b) {
             const int ow = ow0 + 16 * b + j;
             const int vo = (oh < p.H && ow < p.W) ? ((4 * kq) * HW + oh * p.W + ow) * (int)sizeof(float)
                                                   : kRowOutOfRange;
@@ -389,14 +393,19 @@ hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const floa
     if (d->W % 4 == 0 && ((uintptr_t)x & 15u) == 0) {
         GlParams q;
         q.C = d->C; q.H = d->H; q.W = d->W; q.K = d->K; q.G = d->groups;
-        q.n_seg = (d->W + 63) / 64;
+        const int nbw = d->W <= 32 ? 2 : 4;
+        q.n_seg = (d->W + 16 * nbw - 1) / (16 * nbw);
         q.n_rb = (d->H + 4 * kG16RowsPerWave - 1) / (4 * kG16RowsPerWave);
         const long long wgs = (long long)d->N * d->groups * q.n_rb * q.n_seg;
         if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         q.wgs = (int)wgs;
         clear_stale_launch_error();
-        hipLaunchKernelGGL(grouped16_mfma_lds_kernel<kG16RowsPerWave>, dim3((unsigned)q.wgs), dim3(kBlock), 0, st, x,
-                           w, bias, y, q);
+        if (nbw == 2)
+            hipLaunchKernelGGL((grouped16_mfma_lds_kernel<kG16RowsPerWave, 2>), dim3((unsigned)q.wgs), dim3(kBlock), 0,
+                               st, x, w, bias, y, q);
+        else
+            hipLaunchKernelGGL((grouped16_mfma_lds_kernel<kG16RowsPerWave, 4>), dim3((unsigned)q.wgs), dim3(kBlock), 0,
+                               st, x, w, bias, y, q);
         return hipGetLastError();
     }
     const int NB = pick_nb(d->W);
