@@ -16,7 +16,7 @@
 // loads and reads every B operand from LDS.  grouped16_mfma_kernel (any
 // other W or alignment) reads B straight from memory, described next.
 // Measured on the 16 cpg-16 shapes of the grouped 3x3 grid, the two beat the
-// VALU register kernel everywhere (N8 C256 112x112: 83 us against 126;
+// VALU register kernel everywhere (N8 C256 112x112: 78 us against 126;
 // N8 C256 14x14: 6.5 against 18.9); the direct-load form alone was slower
 // than the VALU kernel at N8 C256 112x112 (129 against 125 us): its dword
 // load per B operand keeps the texture address units and the load latency,
@@ -180,13 +180,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 
 // LDS-staged form (W a multiple of 4 and x 16-byte aligned): a workgroup of
 // 4 waves owns 4*RBW output rows x 16*NBW columns of one (image, group);
-// RBW = 1 output row per wave, NBW = 4 blocks of 16 columns, or 2 on rows at
-// most 32 wide (a 28-wide row filled 28 of 64 columns).  Its band (the
-// group's 16 channels x 4*RBW + 2 input rows x 16*NBW + 8 columns from
-// column ow0 - 4, in whole 16-byte pieces) goes
-// straight from memory into LDS by buffer loads with the LDS bit (lane l of
-// an instruction writes its 16 bytes at the instruction's LDS base + 16 l;
-// pieces outside the image read zero), channels 0-7 first, then 8-15.  Each
+// RBW = 1 output row per wave, NBW = 4 blocks of 16 columns, 2 on rows at
+// most 32 wide (a 28-wide row filled 28 of 64 columns), or 7 on 112-wide
+// rows of large grids.  Its band (the group's 16 channels x 4*RBW + 2 input
+// rows x 16*NBW + 8 columns from column ow0 - 4, in whole 16-byte pieces)
+// goes straight from memory into LDS by buffer loads with the LDS bit (lane
+// l of an instruction writes its 16 bytes at the instruction's LDS base +
+// 16 l; pieces outside the image read zero), channels 0-7 first, then 8-15.  Each
 // wave waits for its own first half (the loads count down in issue order),
 // one barrier admits quads 0 and 1 while channels 8-15 land, a second one
 // quads 2 and 3; every B operand is an LDS read at a compile-time offset
@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // -> 83.3 us, 56x56 27.4 -> 25.0, N1 C64 56x56 8.5 -> 6.1; 8-row tiles in the
 // same form, three per CU by LDS, were no faster than before).
 constexpr int kG16RowsPerWave = 1;
+constexpr long long kG16WideRowWorkgroups = 1024;
 
 struct GlParams {
     int C, H, W, K, G;
@@ -393,14 +394,23 @@ hipError_t launch_grouped16_mfma(const gconv_desc *d, const float *x, const floa
     if (d->W % 4 == 0 && ((uintptr_t)x & 15u) == 0) {
         GlParams q;
         q.C = d->C; q.H = d->H; q.W = d->W; q.K = d->K; q.G = d->groups;
-        const int nbw = d->W <= 32 ? 2 : 4;
-        q.n_seg = (d->W + 16 * nbw - 1) / (16 * nbw);
+        // blocks of 16 columns per wave: 2 on rows at most 32 wide; 7 on rows
+        // of 97-112 columns (one segment, not two of 64 with 16 idle) when
+        // the grid still has kG16WideRowWorkgroups workgroups (measured: N8
+        // C256 112x112 83.4 -> 77.6 us, while N1 C64 112x112, 112
+        // workgroups, went 6.6 -> 8.5 us); else 4
         q.n_rb = (d->H + 4 * kG16RowsPerWave - 1) / (4 * kG16RowsPerWave);
+        int nbw = d->W <= 32 ? 2 : 4;
+        if (d->W > 96 && d->W <= 112 && (long long)d->N * d->groups * q.n_rb >= kG16WideRowWorkgroups) nbw = 7;
+        q.n_seg = (d->W + 16 * nbw - 1) / (16 * nbw);
         const long long wgs = (long long)d->N * d->groups * q.n_rb * q.n_seg;
         if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
         q.wgs = (int)wgs;
         clear_stale_launch_error();
-        if (nbw == 2)
+        if (nbw == 7)
+            hipLaunchKernelGGL((grouped16_mfma_lds_kernel<kG16RowsPerWave, 7>), dim3((unsigned)q.wgs), dim3(kBlock), 0,
+                               st, x, w, bias, y, q);
+        else if (nbw == 2)
             hipLaunchKernelGGL((grouped16_mfma_lds_kernel<kG16RowsPerWave, 2>), dim3((unsigned)q.wgs), dim3(kBlock), 0,
                                st, x, w, bias, y, q);
         else
