@@ -802,9 +802,10 @@ def test_graph_capture_of_onepass_variant():
 
 def test_graph_capture_of_every_kernel_family():
     """One conv per kernel family captured in a single HIP graph (grouped
-    register and band kernels, matrix-core 16/16 groups, depthwise aligned,
-    ragged and packed, implicit GEMM at stride 1, stride 2 and on a narrow
-    small grid, the direct kernel); every replay equals the eager runs."""
+    register and band kernels, matrix-core 16/16 groups at 64- and 32-column
+    segments, depthwise aligned, ragged and packed, implicit GEMM at stride 1
+    and 2 and on flattened pixels (narrow, dilated, 7x7 stride 2), the direct
+    kernel); every replay equals the eager runs."""
     shapes = [  # (N, C, H, W, K, R, stride, pad, dil, groups)
         (2, 16, 20, 32, 16, 3, 1, 1, 1, 4),       # grouped register kernel
         (2, 16, 13, 30, 16, 3, 1, 1, 1, 4),       # grouped band kernel (W % 4 != 0)
@@ -814,7 +815,10 @@ def test_graph_capture_of_every_kernel_family():
         (16, 1024, 7, 7, 1024, 3, 1, 1, 1, 1024), # depthwise 3x3 small planes, packed
         (2, 8, 20, 70, 40, 3, 1, 1, 1, 1),        # implicit GEMM, stride 1
         (2, 8, 19, 70, 40, 3, 2, 1, 1, 1),        # implicit GEMM, stride 2
-        (1, 64, 14, 14, 64, 3, 1, 1, 1, 2),       # implicit GEMM, narrow small grid
+        (1, 64, 14, 14, 64, 3, 1, 1, 1, 2),       # implicit GEMM, flattened pixels (narrow output)
+        (2, 16, 20, 20, 32, 3, 1, 2, 2, 1),       # implicit GEMM, flattened, dilation 2
+        (2, 6, 29, 29, 64, 7, 2, 3, 1, 1),        # implicit GEMM, flattened, 7x7 stride 2
+        (2, 64, 16, 28, 64, 3, 1, 1, 1, 4),       # 16 in / 16 out, 32-column segments
         (2, 6, 11, 13, 9, 3, 2, 1, 2, 3),         # direct kernel
     ]
     runs = []
