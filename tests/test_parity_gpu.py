@@ -431,6 +431,43 @@ def test_conv_geometry_fuzz(wl):
         check_conv(y, y_ref, A, "%s %s" % (wl, gc.ALGO_NAMES[algo]))
 
 
+
+def _flat_cases(n, seed):
+    """Geometries for the flattened-pixel implicit GEMM: square 1x1-7x7
+    kernels, stride 1 and 2, dilation 1 and 2 (3x3), any padding up to 3,
+    small ragged images whose 128-pixel tiles span rows and images, 4-12
+    input and 8-40 output channels per group."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        R = int(rng.choice([1, 3, 3, 5, 7]))
+        st = int(rng.integers(1, 3))
+        dil = int(rng.choice([1, 2])) if R == 3 else 1
+        pad = int(rng.integers(0, 4))
+        H, W_ = int(rng.integers(5, 41)), int(rng.integers(5, 41))
+        if H + 2 * pad - dil * (R - 1) - 1 < 0 or W_ + 2 * pad - dil * (R - 1) - 1 < 0:
+            continue
+        groups = int(rng.choice([1, 1, 2, 3]))
+        cin, cout = int(rng.integers(4, 13)), int(rng.choice([8, 16, 33, 40]))
+        out.append(synth.Workload("flat%d_r%d_s%d_d%d" % (len(out), R, st, dil), int(rng.integers(1, 6)), groups * cin,
+                                  H, W_, groups * cout, R, R, st, pad, dil, groups, 7000 + len(out),
+                                  ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _flat_cases(30, 17), ids=lambda w: w.name)
+def test_flattened_implicit_gemm_fuzz(wl):
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    for algo in (gc.ALGO_AUTO, gc.ALGO_IGEMM):
+        d = _desc(wl)
+        try:
+            gc.conv_desc_set_algo(d, algo)
+        except gc.GconvError:
+            continue
+        y, _ = gpu_conv(wl, inp, algo)
+        check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
+
 EDGE = [
     synth.Workload("one_pixel", 2, 4, 1, 1, 4, 3, 3, 1, 1, 1, 4, 41, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("w5_tail", 1, 8, 7, 5, 8, 3, 3, 1, 1, 1, 2, 42, ("uniform", -1, 1), ("uniform", -1, 1)),
