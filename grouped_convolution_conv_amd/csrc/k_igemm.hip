@@ -1,6 +1,7 @@
 // k_igemm.hip -- FP32 MFMA implicit GEMM for dense and wide-group
-// convolution (dilation 1, any padding; stride 1, and stride 2 at 1x1 and
-// 3x3 in the DMA-staged kernel).
+// convolution (any padding and number of input channels; dilation 1 with
+// stride 1, or stride 2 at square 1x1-7x7, in the DMA-staged tile kernel;
+// 3x3 at dilation 2 in the flattened-pixel kernel).
 //
 // The implicit-GEMM view of the POPCORNBENCH traces ("Kimi-K2.6 l2_p21",
 // GEMM framing; "Kimi-K2.6 l1_p62", output-channel blocking): per group,
@@ -58,10 +59,11 @@ struct IgParams {
     int vec;           // W, pad multiples of 4 and x 16-byte aligned: 16-byte band loads
     int G;             // groups
     int n_wg;          // workgroups of the DMA kernel's 1-D grid: N * G * n_tiles * n_kb
-    int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1 and 3x3
+    int st;            // stride (both axes): 1, or 2 for the DMA kernel at 1x1, 3x3, 5x5 and 7x7
     int nbc;           // 32-column blocks per wave row of the DMA kernel (1 on outputs at most 32 wide)
     int nbr;           // output rows per wave of the DMA kernel (1 at stride 2 and on small grids)
     int wvec;          // C/G*R*S a multiple of 4 and w 16-byte aligned: 16-byte weight loads
+    int ds;            // stride 2 with 16-byte band loads: the band's column shift (0..3)
 };
 
 template <int R, int S, int MB, int CC, bool FUSED>
@@ -335,18 +337,21 @@ __device__ __forceinline__ void lds_barrier() {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // ST: stride (1 or 2, both axes).  At stride 2 the band holds the input rows
-// ST*oh0 - pad ... of the tile, and each row's columns in two phases, even
-// input columns first, then odd ones (HW2 of each): output column ow at tap s
-// reads input column 2*ow + s, which is phase s%2, position ow + s/2, so the
-// 32 lanes of a block still read 32 consecutive LDS words.  Stride 2 takes
-// the 4-byte (gather) band loads.
+// ST*oh0 - pad ... of the tile.  With 4-byte (gather) band loads each row's
+// columns are in two phases, even input columns first, then odd ones (HW2 of
+// each): output column ow at tap s reads input column 2*ow + s, which is
+// phase s%2, position ow + s/2, so the 32 lanes of a block still read 32
+// consecutive LDS words.  With 16-byte band loads (VEC: W % 4 == 0, x
+// 16-byte aligned) the columns stay in order from input column 2*ow0 - pad_w
+// - ds, ds (0..3) aligning it to a 16-byte piece: output column ow at tap s
+// is band column 2*(ow - ow0) + s + ds, and a block reads every other word.
 // NBR output rows per wave (a 4*NBR-row tile): 2, or 1 at stride 2 and on
 // grids too small to fill the chip.
 template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC, int NBR>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
-    static_assert(ST == 1 || (ST == 2 && !VEC), "stride 2 gathers its band with 4-byte loads");
+    static_assert(ST == 1 || ST == 2, "stride 1 or 2");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
     constexpr int TH = 4 * NBR;
@@ -354,7 +359,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int TW = 32 * NBC;
     constexpr int TIH = ST * (TH - 1) + R;
     constexpr int HW2 = TW + (S - 1) / 2;   // stride 2: columns per phase
-    constexpr int TIW = ST == 1 ? TW + S - 1 : 2 * HW2;
+    constexpr int TIW = ST == 1 ? TW + S - 1 : VEC ? 2 * (TW - 1) + S + 3 : 2 * HW2;
     constexpr int PITCH = (TIW + 3) & ~3;    // band row pitch: whole 16-byte pieces
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CC * TIH * P4;       // 16-byte pieces of a chunk's band
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
                 const int f = ii * 64 + lane;
                 const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
                 const int lr = rem / P4, c4 = rem - lr * P4;
-                const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + 4 * c4;
+                const int ih = ST * oh0 - p.pad_h + lr, iw = ST * ow0 - p.pad_w - (ST == 2 ? p.ds : 0) + 4 * c4;
                 const bool ok = f < XE4 && c0 + cl < p.cin && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;
                 const int off = ok ? ((c0 + cl) * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(xs, (lds_void_t *)(xb4 + ii * 64), 16, off, 0, 0, 0);
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             const int f = ii * 64 + lane;
             const int cl = f / (TIH * P4), rem = f - cl * (TIH * P4);
             const int lr = rem / P4, c4 = rem - lr * P4;
-            const int ih = oh0 - p.pad_h + lr, iw = ow0 - p.pad_w + 4 * c4;
+            const int ih = ST * oh0 - p.pad_h + lr, iw = ST * ow0 - p.pad_w - (ST == 2 ? p.ds : 0) + 4 * c4;
             const bool ok = f < XE4 && ih >= 0 && ih < p.H && iw >= 0 && iw < p.W;  // then cl < CC
             xo[t] = ok ? (cl * HW + ih * p.W + iw) * (int)sizeof(float) : kOutOfRange;
         } else {
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
-            const float *xq = xin + (cl * TIH + ST * wave * NBR) * PITCH + j;
+            const float *xq = xin + (cl * TIH + ST * wave * NBR) * PITCH + (ST == 2 && VEC ? 2 * j + p.ds : j);
             const float *wq = WK ? wb + j * WQP + cl * RS : wb + cl * RS * KW + j;
             // kernel rows one at a time: unrolling them all lets the compiler
             // hoist every row's LDS reads and spill with two output blocks
@@ -593,7 +598,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 #pragma unroll
                         for (int bc = 0; bc < NBC; ++bc)
                             b[br * NBC + bc] = xq[(ST * br + r) * PITCH +
-                                                   (ST == 1 ? bc * 32 + s : (s & 1) * HW2 + bc * 32 + (s >> 1))];
+                                                   (ST == 1 ? bc * 32 + s
+                                                    : VEC    ? 64 * bc + s
+                                                             : (s & 1) * HW2 + bc * 32 + (s >> 1))];
 #pragma unroll
                     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -965,15 +972,24 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
         clear_stale_launch_error();
         if (p.st == 2) {
             // a stride-2 band is twice as wide per channel: fewer channels
-            // per chunk at 3x3 keep the two buffers within 64 KB
-            if constexpr ((R == 1 && S == 1) || (R == 3 && S == 3)) {
-                constexpr int CC2 = R * S == 1 ? 8 : 4;
-                if (p.nbc == 1)
+            // per chunk at 3x3 keep the two buffers within 64 KB (5x5 and 7x7
+            // keep their stride-1 chunks of 4 and 2)
+            if constexpr (R == S && (R == 1 || R == 3 || R == 5 || R == 7)) {
+                constexpr int CC2 = R * S == 1 ? 8 : R * S == 9 ? 4 : CC;
+                if (p.vec) {
+                    if (p.nbc == 1)
+                        hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, true, 2, 1, 1>), g1, dim3(kBlock), 0, st,
+                                           x, w, bias, y, p);
+                    else
+                        hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, true, 2, kNBC, 1>), g1, dim3(kBlock), 0,
+                                           st, x, w, bias, y, p);
+                } else if (p.nbc == 1) {
                     hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, 1, 1>), g1, dim3(kBlock), 0, st, x,
                                        w, bias, y, p);
-                else
+                } else {
                     hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC2, false, 2, kNBC, 1>), g1, dim3(kBlock), 0, st,
                                        x, w, bias, y, p);
+                }
             } else {
                 return hipErrorInvalidValue;
             }
@@ -1057,6 +1073,7 @@ IgParams make_params(const gconv_desc *d, int MB) {
     p.n_wg = 0;
     p.st = d->stride_h;
     p.wvec = 0;
+    p.ds = 0;
     return p;
 }
 
@@ -1089,8 +1106,8 @@ constexpr int flat_chunk_c(int R, int S, int ST) {
 }
 
 // Geometries with a flattened-pixel kernel: square 1x1 and 3x3 at stride 1
-// and 2, 3x3 at dilation 2, and 5x5 and 7x7 at stride 2 (which the tile
-// kernel does not take).  A 1x1 kernel's dilation changes nothing.
+// and 2, 3x3 at dilation 2 (which the tile kernel does not take), and 5x5
+// and 7x7 at stride 2.  A 1x1 kernel's dilation changes nothing.
 int flat_dil(const gconv_desc *d) { return d->R == 1 && d->S == 1 ? 1 : d->dil_h; }
 
 bool flat_geometry(const gconv_desc *d) {
@@ -1111,7 +1128,7 @@ bool flat_geometry(const gconv_desc *d) {
 // offsets past int32.
 bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     const int ST = d->stride_h;
-    if (!flat_geometry(d) || d->cin < 4 || d->cout < 8) return false;
+    if (!flat_geometry(d) || d->cout < 8) return false;
     const int dil = flat_dil(d);
     const long long T = 128LL * NB;
     const long long np = (long long)d->N * d->Ho * d->Wo;
@@ -1229,13 +1246,16 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
 namespace {
 
 // The tile kernels (and the fused chain's chunked kernel): dilation 1,
-// stride 1, or stride 2 on both axes at 1x1 and 3x3.
+// stride 1, or stride 2 on both axes at 1x1, 3x3, 5x5 and 7x7.
 bool igemm_tile_supported(const gconv_desc *d) {
     // buffer offsets are signed 32-bit: one group's input channels of one
-    // image must stay below 2 GB
+    // image must stay below 2 GB.  Any number of input channels: a chunk's
+    // channels past C/G read zero (a 3-channel first layer fills 3 of a
+    // 4-channel chunk).
     const bool stride_ok = d->stride_h == d->stride_w &&
-                           (d->stride_h == 1 || (d->stride_h == 2 && d->R == d->S && (d->R == 1 || d->R == 3)));
-    return stride_ok && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 4 &&
+                           (d->stride_h == 1 ||
+                            (d->stride_h == 2 && d->R == d->S && (d->R == 1 || d->R == 3 || d->R == 5 || d->R == 7)));
+    return stride_ok && d->dil_h == 1 && d->dil_w == 1 && rs_instantiated(d->R, d->S) && d->cin >= 1 &&
            d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
 
@@ -1259,7 +1279,7 @@ bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // its grid is (tiles, group x channel block, n), within the hardware's
     // 65535 limit on y and z
     const long long gy = (long long)d->groups * ((d->cout + 32 * pick_mb(d) - 1) / (32 * pick_mb(d)));
-    return igemm_tile_supported(d) && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
+    return igemm_tile_supported(d) && d->cin >= 4 && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
            gy <= 65535 && d->N <= 65535;
 }
 
@@ -1279,7 +1299,11 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     // read once per block, in exchange for no register spills
     const int MB = kPlainMB == 2 ? pick_mb(d) : 1;
     IgParams p = make_params(d, MB);
-    p.vec = d->stride_h == 1 && (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+    // 16-byte band loads: at stride 1 when W and the padding are multiples of
+    // 4, at stride 2 when W is (the band then starts pad_w + ds columns left
+    // of 2*ow0, a 16-byte boundary)
+    p.vec = (d->W % 4 == 0) && (((uintptr_t)x & 15u) == 0) && (d->stride_h == 2 || d->pad_w % 4 == 0);
+    p.ds = d->stride_h == 2 ? (4 - d->pad_w % 4) % 4 : 0;
     p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
     // the DMA kernel's tile: 8 rows (4 at stride 2) by 64 columns, or by one
     // 32-column block on outputs at most 32 wide; 4 rows as well when 8-row

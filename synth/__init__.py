@@ -174,8 +174,8 @@ EXTRA_WORKLOADS = {
 
 # Dense and 32-channel-group layers on the implicit GEMM (ResNet- and
 # ResNeXt-style shapes at batch 16), 3x3 at stride 1 and 2, a 1x1
-# reduction, and the geometries of the flattened-pixel kernel (3x3 at
-# dilation 2, 5x5 and 7x7 at stride 2); x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
+# reduction, 3x3 at dilation 2, 5x5 and 7x7 at stride 2, and two 3-channel
+# first layers; x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
 IGEMM_WORKLOADS = {
     "g3s2_cpg32_1024x28": Workload("g3s2_cpg32_1024x28", 16, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32, 901,
                                    ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
@@ -195,6 +195,12 @@ IGEMM_WORKLOADS = {
                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 25))),
     "dense7s2_16x112": Workload("dense7s2_16x112", 16, 16, 112, 112, 64, 7, 7, 2, 3, 1, 1, 909,
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(16 * 49))),
+    # first layers with 3 input channels: a ResNet-style stem (7x7 stride 2)
+    # and a 3x3 stride-2 stem
+    "stem7s2_3x224": Workload("stem7s2_3x224", 16, 3, 224, 224, 64, 7, 7, 2, 3, 1, 1, 910,
+                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(3 * 49))),
+    "stem3s2_3x224": Workload("stem3s2_3x224", 16, 3, 224, 224, 32, 3, 3, 2, 1, 1, 1, 911,
+                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(3 * 9))),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

@@ -165,15 +165,16 @@ def test_dispatch_of_stride2_dense_and_wide_groups():
     for geom in [(2, 64, 56, 56, 64, 3, 3, 2, 1, 1, 1), (2, 256, 56, 56, 128, 1, 1, 2, 0, 1, 1),
                  (2, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32), (1, 8, 5, 600, 16, 3, 3, 2, 1, 1, 2)]:
         assert gc.conv_desc_get_algo(gc.conv_desc_create(*geom)) == gc.ALGO_IGEMM, geom
-    # on its flattened-pixel kernel: 3x3 at dilation 2 (stride 1 and 2), 5x5
-    # and 7x7 at stride 2, where the band fits its 64 KB of LDS
+    # 5x5 and 7x7 at stride 2, and 3x3 at dilation 2 (stride 1 and 2, on the
+    # flattened-pixel kernel where its band fits its 64 KB of LDS); fewer
+    # than 4 input channels (a ResNet-style stem, a 3-channel first layer)
     for geom in [(2, 16, 20, 20, 32, 3, 3, 1, 2, 2, 1), (3, 16, 32, 32, 32, 3, 3, 2, 2, 2, 1),
-                 (2, 64, 56, 56, 64, 5, 5, 2, 2, 1, 1), (2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1)]:
+                 (2, 64, 56, 56, 64, 5, 5, 2, 2, 1, 1), (2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1),
+                 (2, 16, 20, 20, 32, 5, 5, 2, 2, 1, 1), (16, 3, 224, 224, 64, 7, 7, 2, 3, 1, 1),
+                 (16, 3, 224, 224, 32, 3, 3, 2, 1, 1, 1)]:
         assert gc.conv_desc_get_algo(gc.conv_desc_create(*geom)) == gc.ALGO_IGEMM, geom
-    # not there: a 5x5 stride-2 band over the LDS budget (10-column output,
-    # 39 band rows), stride 3, dilation 3, unequal strides
-    for geom in [(2, 16, 20, 20, 32, 5, 5, 2, 2, 1, 1), (2, 16, 20, 20, 32, 3, 3, 3, 1, 1, 1),
-                 (2, 16, 20, 20, 32, 3, 3, 1, 3, 3, 1)]:
+    # not there: stride 3, dilation 3, unequal strides
+    for geom in [(2, 16, 20, 20, 32, 3, 3, 3, 1, 1, 1), (2, 16, 20, 20, 32, 3, 3, 1, 3, 3, 1)]:
         d = gc.conv_desc_create(*geom)
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DIRECT, geom
         with pytest.raises(gc.GconvError) as ei:

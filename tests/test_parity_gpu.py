@@ -574,6 +574,16 @@ EDGE = [
     synth.Workload("igemm_flat_5x5_s2_vec", 2, 16, 24, 24, 32, 5, 5, 2, 2, 1, 1, 104, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_7x7_s2", 2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1, 105, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_7x7_s2_vec", 1, 4, 40, 40, 32, 7, 7, 2, 3, 1, 1, 106, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # the tile kernel at 5x5 and 7x7 stride 2 (wide outputs, 64-column
+    # tiles), and with fewer than 4 input channels: a 3-channel stem (7x7
+    # stride 2), a 3-channel 3x3 stride-2 first layer, 2 and 3 channels at
+    # stride 1 (partial chunks only)
+    synth.Workload("igemm_s2_5x5_tile", 2, 8, 70, 140, 40, 5, 5, 2, 2, 1, 1, 111, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_7x7_tile", 1, 6, 40, 150, 32, 7, 7, 2, 3, 1, 1, 112, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_7x7_stem_c3", 2, 3, 64, 160, 64, 7, 7, 2, 3, 1, 1, 113, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_s2_3x3_c3", 2, 3, 40, 144, 32, 3, 3, 2, 1, 1, 1, 114, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_5x5_c2", 2, 2, 20, 70, 16, 5, 5, 1, 2, 1, 1, 115, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_7x7_c3", 1, 3, 18, 90, 40, 7, 7, 1, 3, 1, 1, 116, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
