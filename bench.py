@@ -759,7 +759,7 @@ def workload_text(names, known):
     if names == [n for n in known if n in names] and all(n in ROW_TEXT for n in names):
         return "one pass over the shape rows " + ", ".join(names) + " (" + "; ".join(ROW_TEXT[n] for n in names) + ")"
     return "one pass over the shape rows " + "; ".join(
-        "%s: N%d C%d->%d %dx%d %dx%d stride %d pad %d dil %d groups %d" % (
+        "%s: N%d C%d->%d %dx%d %dx%d stride %d pad %s dil %d groups %d" % (
             n, known[n].N, known[n].C, known[n].K, known[n].H, known[n].W, known[n].R, known[n].S,
             known[n].stride, known[n].pad, known[n].dil, known[n].groups) for n in names)
 

@@ -141,6 +141,11 @@ class ConvDesc:
 
 
 def conv_desc_create(N, C, H, W, K, R, S, stride=1, pad=0, dilation=1, groups=1) -> ConvDesc:
+    """Descriptor with symmetric stride, padding and dilation; any of them
+    given as an (h, w) pair goes to conv_desc_create_2d."""
+    if any(isinstance(v, (tuple, list)) for v in (stride, pad, dilation)):
+        pair = lambda v: tuple(v) if isinstance(v, (tuple, list)) else (v, v)
+        return conv_desc_create_2d(N, C, H, W, K, R, S, pair(stride), pair(pad), pair(dilation), groups)
     h = ctypes.c_void_p()
     _check("conv_desc_create", _lib.conv_desc_create(ctypes.byref(h), N, C, H, W, K, R, S, stride, pad,
                                                      dilation, groups))

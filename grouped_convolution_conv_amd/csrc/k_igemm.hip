@@ -1044,13 +1044,30 @@ hipError_t launch_rs(const gconv_desc *d, const IgParams &p, int MB, dim3 grid, 
         case 5 * 16 + 5: return launch_mb<5, 5, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
         case 5 * 16 + 9: return launch_mb<5, 9, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
         case 7 * 16 + 7: return launch_mb<7, 7, FUSED>(MB, p, grid, x, w, bias, y, ep, st);
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    // the factorized kernels of Inception-style blocks, plain convolution only
+    if constexpr (!FUSED) {
+        switch (rs) {
+            case 1 * 16 + 3: return launch_mb<1, 3, false>(MB, p, grid, x, w, bias, y, ep, st);
+            case 3 * 16 + 1: return launch_mb<3, 1, false>(MB, p, grid, x, w, bias, y, ep, st);
+            case 1 * 16 + 7: return launch_mb<1, 7, false>(MB, p, grid, x, w, bias, y, ep, st);
+            case 7 * 16 + 1: return launch_mb<7, 1, false>(MB, p, grid, x, w, bias, y, ep, st);
+            default: break;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+// kernel sizes of the fused chain's chunked kernel, and of the tile kernel,
+// which adds the 1x3, 3x1, 1x7 and 7x1 of factorized (Inception-style) blocks
+bool rs_fused_instantiated(int R, int S) {
+    return (R == 1 && S == 1) || (R == 3 && S == 3) || (R == 5 && S == 5) || (R == 5 && S == 9) ||
+           (R == 7 && S == 7);
 }
 
 bool rs_instantiated(int R, int S) {
-    return (R == 1 && S == 1) || (R == 3 && S == 3) || (R == 5 && S == 5) || (R == 5 && S == 9) ||
-           (R == 7 && S == 7);
+    return rs_fused_instantiated(R, S) || (R == 1 && (S == 3 || S == 7)) || (S == 1 && (R == 3 || R == 7));
 }
 
 int pick_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
@@ -1279,7 +1296,7 @@ bool igemm_fused_supported(const gconv_desc *d, int gn_groups) {
     // its grid is (tiles, group x channel block, n), within the hardware's
     // 65535 limit on y and z
     const long long gy = (long long)d->groups * ((d->cout + 32 * pick_mb(d) - 1) / (32 * pick_mb(d)));
-    return igemm_tile_supported(d) && d->cin >= 4 && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
+    return igemm_tile_supported(d) && rs_fused_instantiated(d->R, d->S) && d->cin >= 4 && d->stride_h == 1 && d->cout % (32 * pick_mb(d)) == 0 && d->K / gn_groups == 4 &&
            gy <= 65535 && d->N <= 65535;
 }
 

@@ -57,7 +57,7 @@ class Workload:
     R: int
     S: int
     stride: int
-    pad: int
+    pad: object  # an int, or an (h, w) pair
     dil: int
     groups: int
     seed: int
@@ -174,8 +174,9 @@ EXTRA_WORKLOADS = {
 
 # Dense and 32-channel-group layers on the implicit GEMM (ResNet- and
 # ResNeXt-style shapes at batch 16), 3x3 at stride 1 and 2, a 1x1
-# reduction, 3x3 at dilation 2, 5x5 and 7x7 at stride 2, and two 3-channel
-# first layers; x ~ U[-1, 1], w ~ U[+-1/sqrt(cin * R * S)].
+# reduction, 3x3 at dilation 2, 5x5 and 7x7 at stride 2, two 3-channel
+# first layers and an Inception-style 1x7 / 7x1 pair; x ~ U[-1, 1],
+# w ~ U[+-1/sqrt(cin * R * S)].
 IGEMM_WORKLOADS = {
     "g3s2_cpg32_1024x28": Workload("g3s2_cpg32_1024x28", 16, 1024, 28, 28, 1024, 3, 3, 2, 1, 1, 32, 901,
                                    ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
@@ -201,6 +202,11 @@ IGEMM_WORKLOADS = {
                               ("uniform", -1.0, 1.0), _u(1 / math.sqrt(3 * 49))),
     "stem3s2_3x224": Workload("stem3s2_3x224", 16, 3, 224, 224, 32, 3, 3, 2, 1, 1, 1, 911,
                               ("uniform", -1.0, 1.0), _u(1 / math.sqrt(3 * 9))),
+    # the factorized 7x7 of an Inception-style 17x17 block: 1x7 then 7x1
+    "incep1x7_160x17": Workload("incep1x7_160x17", 16, 160, 17, 17, 160, 1, 7, 1, (0, 3), 1, 1, 912,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(160 * 7))),
+    "incep7x1_160x17": Workload("incep7x1_160x17", 16, 160, 17, 17, 160, 7, 1, 1, (3, 0), 1, 1, 913,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(160 * 7))),
 }
 
 # Grouped 3x3 shape grid (stride 1, padding 1, dilation 1, no bias, the

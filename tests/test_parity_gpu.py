@@ -584,6 +584,13 @@ EDGE = [
     synth.Workload("igemm_s2_3x3_c3", 2, 3, 40, 144, 32, 3, 3, 2, 1, 1, 1, 114, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_5x5_c2", 2, 2, 20, 70, 16, 5, 5, 1, 2, 1, 1, 115, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_7x7_c3", 1, 3, 18, 90, 40, 7, 7, 1, 3, 1, 1, 116, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # the factorized kernels of Inception-style blocks at stride 1, with
+    # per-axis padding: 1x7 and 1x3 (4-byte bands: padding 3 and 1 across),
+    # 7x1 and 3x1 (16-byte bands), a partial chunk and two output blocks
+    synth.Workload("igemm_n_1x7_p03", 2, 12, 13, 40, 40, 1, 7, 1, (0, 3), 1, 1, 117, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_7x1_p30_vec", 2, 16, 30, 36, 32, 7, 1, 1, (3, 0), 1, 1, 118, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_1x3_p01", 3, 8, 9, 70, 16, 1, 3, 1, (0, 1), 1, 1, 119, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_n_3x1_p10_vec", 1, 20, 33, 64, 64, 3, 1, 1, (1, 0), 1, 1, 120, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
