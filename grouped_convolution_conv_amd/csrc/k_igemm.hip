@@ -668,7 +668,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // lane's operands sit at a fixed offset from the band's first row, which is
 // that of the tile's first pixel.  The host bounds the band's height (tih
 // rows, at most 64) over every tile.  The same addressing serves 1x1 and 3x3
-// at stride 1 and 2, 3x3 at dilation 2, and 5x5 and 7x7 at stride 2.
+// at stride 1 and 2, 3x3 at dilation 2, 5x5 and 7x7 at stride 2, and 1x3,
+// 3x1, 1x7 and 7x1 at stride 1.
 //
 // Band layout: [band row][channel of the chunk][pitch], the pitch a power of
 // two so that a lane finds its element with shifts:
@@ -1108,27 +1109,34 @@ IgParams make_params(const gconv_desc *d, int MB) {
 constexpr int kFlatBelowPercent = 80;
 // two blocks per wave once the grid still has this many workgroups, or on
 // reductions of this many channel chunks, whose length amortizes a
-// workgroup's set-up and first loads (measured on MI355X, batch 16: a
-// dilated 3x3 C256 28x28 layer, 32 chunks, 214 -> 181 us at 392 instead of
-// 784 workgroups; a 28x28 32-channel-group layer, 4 chunks, 48.1 -> 52.5 us
-// the other way)
+// workgroup's set-up and first loads, while the grid keeps one workgroup per
+// CU (measured on MI355X, batch 16: a dilated 3x3 C256 28x28 layer, 32
+// chunks, 214 -> 181 us at 392 instead of 784 workgroups; a 28x28
+// 32-channel-group layer, 4 chunks, 48.1 -> 52.5 us the other way; a 1x7
+// C160 17x17 layer, 20 chunks, 30.6 us at 185 workgroups, 49.2 at 95)
 constexpr long long kFlatTwoBlockWorkgroups = 1024;
 constexpr int kFlatTwoBlockChunks = 16;
+constexpr long long kFlatTwoBlockMinWorkgroups = 256;
 constexpr long long kFlatMaxLds = 64 * 1024;
 
-// channels per chunk: as in the tile kernel (16 at 1x1 stride 1), and 4 at
-// 5x5, 2 at 7x7
+// channels per chunk: as in the tile kernel (16 at 1x1 stride 1; 8 at 3x3
+// and the 1x3, 3x1, 1x7 and 7x1 of factorized blocks), and 4 at 5x5, 2 at 7x7
 constexpr int flat_chunk_c(int R, int S, int ST) {
-    return R * S == 1 ? (ST == 1 ? 16 : 8) : R * S == 9 ? (ST == 1 ? 8 : 4) : R * S == 25 ? 4 : 2;
+    return R * S == 1 ? (ST == 1 ? 16 : 8) : R * S <= 9 ? (ST == 1 ? 8 : 4) : R * S <= 25 ? 4 : 2;
 }
 
 // Geometries with a flattened-pixel kernel: square 1x1 and 3x3 at stride 1
-// and 2, 3x3 at dilation 2 (which the tile kernel does not take), and 5x5
-// and 7x7 at stride 2.  A 1x1 kernel's dilation changes nothing.
+// and 2, 3x3 at dilation 2 (which the tile kernel does not take), 5x5 and
+// 7x7 at stride 2, and the 1x3, 3x1, 1x7 and 7x1 of factorized blocks at
+// stride 1.  A 1x1 kernel's dilation changes nothing.
 int flat_dil(const gconv_desc *d) { return d->R == 1 && d->S == 1 ? 1 : d->dil_h; }
 
+bool flat_factorized(int R, int S) { return (R == 1 && (S == 3 || S == 7)) || (S == 1 && (R == 3 || R == 7)); }
+
 bool flat_geometry(const gconv_desc *d) {
-    if (d->stride_h != d->stride_w || d->dil_h != d->dil_w || d->R != d->S) return false;
+    if (d->stride_h != d->stride_w || d->dil_h != d->dil_w) return false;
+    if (flat_factorized(d->R, d->S)) return d->stride_h == 1 && d->dil_h == 1;
+    if (d->R != d->S) return false;
     if (d->stride_h != 1 && d->stride_h != 2) return false;
     const int dil = flat_dil(d);
     switch (d->R) {
@@ -1233,12 +1241,21 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
                      (!flat_plan(d, 1, false, p4) || pv.lp == p4.lp);
     int nb = 2;
     const int nchunks = (d->cin + flat_chunk_c(d->R, d->S, d->stride_h) - 1) / flat_chunk_c(d->R, d->S, d->stride_h);
-    if (!flat_plan(d, 2, vec, p) || (p.n_wg < kFlatTwoBlockWorkgroups && nchunks < kFlatTwoBlockChunks)) {
+    if (!flat_plan(d, 2, vec, p) ||
+        (p.n_wg < kFlatTwoBlockWorkgroups && (nchunks < kFlatTwoBlockChunks || p.n_wg < kFlatTwoBlockMinWorkgroups))) {
         nb = 1;
         if (!flat_plan(d, 1, vec, p)) return false;
     }
     p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
     const bool s1 = d->stride_h == 1, d2 = flat_dil(d) == 2;
+    if (flat_factorized(d->R, d->S)) {
+        const int rs = d->R * 16 + d->S;
+        *err = rs == 1 * 16 + 3   ? launch_flat_t<1, 3, 1, 1>(p, vec, nb, x, w, bias, y, st)
+               : rs == 3 * 16 + 1 ? launch_flat_t<3, 1, 1, 1>(p, vec, nb, x, w, bias, y, st)
+               : rs == 1 * 16 + 7 ? launch_flat_t<1, 7, 1, 1>(p, vec, nb, x, w, bias, y, st)
+                                  : launch_flat_t<7, 1, 1, 1>(p, vec, nb, x, w, bias, y, st);
+        return true;
+    }
     switch (d->R) {
         case 1:
             *err = s1 ? launch_flat_t<1, 1, 1, 1>(p, vec, nb, x, w, bias, y, st)

@@ -468,6 +468,35 @@ def test_flattened_implicit_gemm_fuzz(wl):
         y, _ = gpu_conv(wl, inp, algo)
         check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
 
+def _factorized_cases(n, seed):
+    """Factorized kernels (1x3, 3x1, 1x7, 7x1) at stride 1: padding chosen per
+    axis up to 4, small ragged images (either the row x column tiles or the
+    flattened-pixel tiles), 3-12 input and 8-40 output channels per group."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        R, S = [(1, 3), (3, 1), (1, 7), (7, 1)][int(rng.integers(0, 4))]
+        ph, pw = int(rng.integers(0, 5)), int(rng.integers(0, 5))
+        H, W_ = int(rng.integers(3, 41)), int(rng.integers(3, 72))
+        if H + 2 * ph - R < 0 or W_ + 2 * pw - S < 0:
+            continue
+        groups = int(rng.choice([1, 1, 2]))
+        cin, cout = int(rng.integers(3, 13)), int(rng.choice([8, 16, 33, 40]))
+        out.append(synth.Workload("fact%d_%dx%d_p%d%d" % (len(out), R, S, ph, pw), int(rng.integers(1, 5)),
+                                  groups * cin, H, W_, groups * cout, R, S, 1, (ph, pw), 1, groups, 7500 + len(out),
+                                  ("uniform", -1.0, 1.0), ("uniform", -0.5, 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("wl", _factorized_cases(16, 29), ids=lambda w: w.name)
+def test_factorized_implicit_gemm_fuzz(wl):
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    for algo in (gc.ALGO_AUTO, gc.ALGO_IGEMM):
+        y, _ = gpu_conv(wl, inp, algo)
+        check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
+
+
 EDGE = [
     synth.Workload("one_pixel", 2, 4, 1, 1, 4, 3, 3, 1, 1, 1, 4, 41, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("w5_tail", 1, 8, 7, 5, 8, 3, 3, 1, 1, 1, 2, 42, ("uniform", -1, 1), ("uniform", -1, 1)),
@@ -591,6 +620,15 @@ EDGE = [
     synth.Workload("igemm_n_7x1_p30_vec", 2, 16, 30, 36, 32, 7, 1, 1, (3, 0), 1, 1, 118, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_1x3_p01", 3, 8, 9, 70, 16, 1, 3, 1, (0, 1), 1, 1, 119, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_n_3x1_p10_vec", 1, 20, 33, 64, 64, 3, 1, 1, (1, 0), 1, 1, 120, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # factorized kernels whose row x column tiles are at least 80 % full stay
+    # on the tile kernel (the cases above take flattened-pixel tiles)
+    synth.Workload("igemm_t_1x7_p03_full", 2, 12, 16, 64, 40, 1, 7, 1, (0, 3), 1, 1, 121, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_t_7x1_p30_full", 1, 16, 16, 32, 32, 7, 1, 1, (3, 0), 1, 1, 122, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_t_1x3_p01_full", 2, 9, 8, 30, 24, 1, 3, 1, (0, 1), 1, 1, 123, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # factorized kernels on flattened-pixel tiles with two blocks per wave
+    # (grids of 2432 and 4096 workgroups): 16-row and 22-row bands, 4-byte loads
+    synth.Workload("igemm_flat_nb2_1x7", 16, 512, 17, 17, 1024, 1, 7, 1, (0, 3), 1, 128, 124, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_nb2_7x1_w30", 16, 512, 17, 30, 1024, 7, 1, 1, (3, 0), 1, 128, 125, ("uniform", -1, 1), ("uniform", -1, 1)),
 ]
 
 
@@ -600,7 +638,7 @@ def test_conv_edge_cases(wl):
     y_ref, A = oracle_conv(wl, inp)
     y, algo = gpu_conv(wl, inp)
     _say("[parity] edge", wl.name, gc.ALGO_NAMES[algo])
-    if wl.name.startswith(("igemm_s2", "igemm_n_", "igemm_flat")):
+    if wl.name.startswith(("igemm_s2", "igemm_n_", "igemm_t_", "igemm_flat")):
         assert algo == gc.ALGO_IGEMM, gc.ALGO_NAMES[algo]
     check_conv(y, y_ref, A, wl.name)
     # an output pointer that is only 4-byte aligned takes the scalar stores
