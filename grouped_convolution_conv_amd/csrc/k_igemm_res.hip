@@ -23,6 +23,9 @@
 //    vmcnt) instead of for every outstanding load and store;
 //  - the barriers between tiles order LDS only, so no wave waits for its own
 //    output stores before starting the next tile.
+// The fused 3x3 passes with 32 output channels (WG) multiply in the Winograd
+// form F(2x2, 3x3) instead (see winograd_tile below): 16 products per 2x2
+// outputs and input channel, against 36 for the direct sum.
 // Epilogue modes:
 //  kPlain       y = acc (+ bias)
 //  kStats       v = sigmoid((acc + bias) * scale) and, per wave (two rows of
@@ -210,8 +213,31 @@ __device__ __forceinline__ void onepass_merge_image(const Partial *parts, int st
     if (lane == 0) __hip_atomic_store(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int R, int S, int MB, int CP, int MODE, bool VEC>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 && MODE != kOnePass ? kResWaves : 2))) void igemm_res_kernel(const float *__restrict__ x,
+// Winograd F(2x2, 3x3) weights of one (output channel, input channel):
+// U = G g G^T with G = [1 0 0; 1/2 1/2 1/2; 1/2 -1/2 1/2; 0 0 1], in FP32.
+// (Lavin and Gray, "Fast Algorithms for Convolutional Neural Networks".)
+// U[u][v] goes to out[4 * v + u]: the four row positions u of one column
+// position v are one 16-byte piece.
+__device__ __forceinline__ void winograd_weights(const float (&g)[9], float *out) {
+    float t[4][3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+        t[0][s] = g[s];
+        t[1][s] = 0.5f * (g[s] + g[3 + s] + g[6 + s]);
+        t[2][s] = 0.5f * (g[s] - g[3 + s] + g[6 + s]);
+        t[3][s] = g[6 + s];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        out[0 * 4 + u] = t[u][0];
+        out[1 * 4 + u] = 0.5f * (t[u][0] + t[u][1] + t[u][2]);
+        out[2 * 4 + u] = 0.5f * (t[u][0] - t[u][1] + t[u][2]);
+        out[3 * 4 + u] = t[u][2];
+    }
+}
+
+template <int R, int S, int MB, int CP, int MODE, bool VEC, bool WG = false>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 && MODE != kOnePass && !WG ? kResWaves : 2))) void igemm_res_kernel(const float *__restrict__ x,
                                                            const float *__restrict__ w,
                                                            float *__restrict__ y, ResParams p,
                                                            ResEpilogue ep) {
@@ -226,15 +252,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     constexpr int P4 = PITCH / 4;
     constexpr int XE4 = CP * TIH * P4;        // 16-byte pieces of a tile's band
     constexpr int NSLOT = (XE4 + kBlock - 1) / kBlock;
-    constexpr int WP = (CP * RS) | 1;         // weight row pitch (odd)
+    // weight row pitch: odd (direct form, 32 lanes reading 32 output
+    // channels' weight q hit 32 banks), or 16*CP + 4 (Winograd form, 16-byte
+    // reads of 32 channels at a pitch of 4 mod 64 words)
+    constexpr int WP = WG ? 16 * CP + 4 : (CP * RS) | 1;
     constexpr int NB = kNBR * NBC;
     constexpr int HALF = CP / 2;
     constexpr int NWAVE = kBlock / 64;
     constexpr int NGS = 16 * MB;              // kNormalize: floats of (mean, rstd) per image
     constexpr bool kStatsMode = MODE == kStats || MODE == kStatsStore || MODE == kOnePass;
     static_assert(MODE != kOnePass || MB == 1, "one-pass chain: 32 output channels, 8 groups of 4");
+    static_assert(!WG || (R == 3 && S == 3 && MB == 1 && MODE != kOnePass && MODE != kPlain),
+                  "Winograd form: 3x3, 32 output channels, the statistics and normalize passes");
 
-    __shared__ float wl[KW * WP];
+    __shared__ __attribute__((aligned(16))) float wl[KW * WP];
     // per-channel constants, staged once: LDS reads in the epilogue count on
     // lgkmcnt, whereas per-lane global loads would count on vmcnt and make
     // the epilogue wait for the next tile's loads
@@ -258,12 +289,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     const int plane = p.Ho * p.Wo;
 
     // ---- weights, once: w[k][c][r][s] for k < cout, c < cin, zero elsewhere
-    for (int e = tid; e < KW * CP * RS; e += kBlock) {
-        const int k = e / (CP * RS), q = e - k * (CP * RS);
-        const int c = q / RS;
-        float v = 0.0f;
-        if (k < p.cout && c < p.cin) v = w[((size_t)k * p.cin + c) * RS + (q - c * RS)];
-        wl[k * WP + q] = v;
+    if constexpr (WG) {
+        // one (output channel, input channel) per thread: its 16 Winograd
+        // weights at wl[k * WP + c * 16 ..]
+        for (int e = tid; e < KW * CP; e += kBlock) {
+            const int k = e / CP, c = e - k * CP;
+            float g[9];
+#pragma unroll
+            for (int q = 0; q < 9; ++q)
+                g[q] = (k < p.cout && c < p.cin) ? w[((size_t)k * p.cin + c) * 9 + q] : 0.0f;
+            winograd_weights(g, wl + k * WP + c * 16);
+        }
+    } else {
+        for (int e = tid; e < KW * CP * RS; e += kBlock) {
+            const int k = e / (CP * RS), q = e - k * (CP * RS);
+            const int c = q / RS;
+            float v = 0.0f;
+            if (k < p.cout && c < p.cin) v = w[((size_t)k * p.cin + c) * RS + (q - c * RS)];
+            wl[k * WP + q] = v;
+        }
     }
     for (int k = tid; k < KW; k += kBlock) {
         float b = 0.0f, sc = 1.0f, ga = 1.0f, be = 0.0f;
@@ -404,7 +448,88 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
 
     // ---- MFMAs of the tile whose band is in LDS
     floatx16 accs[1][MB][NB];
+    // Winograd form: lane j of a wave owns the 2x2 outputs (rows 0-1 of the
+    // wave's rows, columns 2j, 2j+1), acc[0][2a + b] the output at row a,
+    // column 2j + b, for the 32 channels of the MFMA layout.  Per column
+    // position v of the 4x4 transform domain, and per input channel, the
+    // lane forms the four B operands V[u][v] = (B^T d B)[u][v] of its 4x4
+    // input patch d (B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1]: the
+    // column combination s[r] of two patch columns, then the same combination
+    // down the rows), and four MFMA chains accumulate M[u][v] = sum over input
+    // channels of U[u][v] V[u][v].  The output transform A^T M A (A^T =
+    // [1 1 1 0; 0 1 -1 -1]) is then folded in per v: T_a = sum_u A^T[a][u]
+    // M[u][v] and out[a][b] += A^T[b][v] T_a, in a fixed order.
+    auto winograd_tile = [&](const float4 *buf4, floatx16 (&acc)[MB][NB]) __attribute__((always_inline)) {
+        const float *band = reinterpret_cast<const float *>(buf4);
+        // the lane's band and weight offsets, opaque so that the compiler
+        // forms each channel's address in the loop instead of keeping one
+        // register per channel (and buffer) across the tile loop
+        int xb = (h * HALF * TIH + wave * kNBR) * PITCH + 2 * j;
+        int wb = j * WP + h * HALF * 16;
+        asm volatile("" : "+v"(xb), "+v"(wb));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            // patch columns of column position v and their combination
+            constexpr int kc0[4] = {0, 1, 1, 1};
+            constexpr int kc1[4] = {2, 2, 2, 3};
+            floatx16 mv[4];
+#pragma unroll
+            for (int ci = 0; ci < HALF; ++ci) {
+                const float *xq = band + xb + ci * TIH * PITCH;
+                float sr[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float d0 = xq[r * PITCH + kc0[v]], d1 = xq[r * PITCH + kc1[v]];
+                    sr[r] = v == 0 ? d0 - d1 : v == 1 ? d0 + d1 : v == 2 ? d1 - d0 : d0 - d1;
+                }
+                const float vb[4] = {sr[0] - sr[2], sr[1] + sr[2], sr[2] - sr[1], sr[1] - sr[3]};
+                const float4 a4 = *reinterpret_cast<const float4 *>(wl + wb + ci * 16 + v * 4);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    if (ci == 0) {
+                        const floatx16 zero = {};
+                        mv[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], vb[u], zero, 0, 0, 0);
+                    } else {
+                        mv[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], vb[u], mv[u], 0, 0, 0);
+                    }
+                }
+            }
+            // T_0 = M0 + M1 + M2, T_1 = M1 - M2 - M3
+            const floatx16 t0 = (mv[0] + mv[1]) + mv[2];
+            const floatx16 t1 = (mv[1] - mv[2]) - mv[3];
+            if (v == 0) {
+                acc[0][0] = t0;
+                acc[0][2] = t1;
+            } else if (v == 1) {
+                acc[0][0] += t0;
+                acc[0][2] += t1;
+                acc[0][1] = t0;
+                acc[0][3] = t1;
+            } else if (v == 2) {
+                acc[0][0] += t0;
+                acc[0][2] += t1;
+                acc[0][1] -= t0;
+                acc[0][3] -= t1;
+            } else {
+                acc[0][1] -= t0;
+                acc[0][3] -= t1;
+            }
+            // one column position's four chains live at a time: the fold is
+            // pinned here (without the empty asm the compiler sinks it to the
+            // epilogue, keeping all sixteen positions' 256 accumulator
+            // registers live, and spills)
+            if (v == 0)
+                asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][2]));
+            else
+                asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]));
+        }
+    };
     auto mfma_tile = [&](const float4 *buf4, floatx16 (&acc)[MB][NB]) __attribute__((always_inline)) {
+        if constexpr (WG) {
+            winograd_tile(buf4, acc);
+            return;
+        }
         const float *band = reinterpret_cast<const float *>(buf4);
 #pragma unroll
         for (int m = 0; m < MB; ++m)
@@ -460,7 +585,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         for (int br = 0; br < kNBR; ++br)
 #pragma unroll
             for (int bc = 0; bc < NBC; ++bc) {
-                const int oh = oh0 + br, ow = ow0 + bc * 32 + j;
+                // direct form: column block bc, lane j; Winograd form: the
+                // lane's 2x2 outputs, column 2j + bc
+                const int oh = oh0 + br, ow = ow0 + (WG ? 2 * j + bc : bc * 32 + j);
                 pix[br * NBC + bc] = (oh < p.Ho && ow < p.Wo) ? (oh * p.Wo + ow) * (int)sizeof(float) : -1;
             }
         auto store = [&](int nb, int k, float val) __attribute__((always_inline)) {
@@ -876,11 +1003,16 @@ __global__ __launch_bounds__(kBlock) void onepass_fixup_kernel(float *__restrict
 constexpr int kMaxResLds = 80 * 1024;  // keep at least two workgroups per CU
 constexpr int kMaxDevices = 64;
 
-template <int R, int S, int MB, int CP, int MODE>
+template <int R, int S, int MB, int CP, int MODE, bool WG>
 constexpr int res_lds_bytes() {
-    return 4 * (32 * MB * ((CP * R * S) | 1) + 2 * (CP * (kTH + R - 1) * ((kTW + S - 1 + 3) & ~3) + 16 * MB)) +
+    return 4 * (32 * MB * (WG ? 16 * CP + 4 : (CP * R * S) | 1) +
+                2 * (CP * (kTH + R - 1) * ((kTW + S - 1 + 3) & ~3) + 16 * MB)) +
            2 * 8 * 32 * MB + (MODE == kOnePass ? 16 * (kBlock / 64) * 8 : 0);
 }
+
+// The fused statistics and normalize passes of a 3x3 conv with one block of
+// 32 output channels multiply in the Winograd form.
+constexpr bool kResWinograd = true;
 
 // one GroupNorm partial per (tile of kTH rows x kTW columns, wave, group)
 int res_parts_per_group(const gconv_desc *d) {
@@ -913,11 +1045,11 @@ bool res_vec(const gconv_desc *d, const float *x) {
 int res_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
 int res_cp(const gconv_desc *d) { return d->cin <= 4 ? 4 : 8; }
 
-template <int R, int S, int MB, int CP, int MODE, bool VEC>
+template <int R, int S, int MB, int CP, int MODE, bool VEC, bool WG = false>
 hipError_t launch_t(const ResParams &p, const float *x, const float *w, float *y, const ResEpilogue &ep,
                     hipStream_t st) {
-    static_assert(res_lds_bytes<R, S, MB, CP, MODE>() <= kMaxResLds, "LDS budget");
-    auto kern = igemm_res_kernel<R, S, MB, CP, MODE, VEC>;
+    static_assert(res_lds_bytes<R, S, MB, CP, MODE, WG>() <= kMaxResLds, "LDS budget");
+    auto kern = igemm_res_kernel<R, S, MB, CP, MODE, VEC, WG>;
     // resident workgroups per device for this kernel: queried once per
     // device and kept (the query costs host time on every launch otherwise)
     static std::atomic<int> capacity[kMaxDevices];
@@ -964,6 +1096,11 @@ hipError_t launch_mode_v(const gconv_desc *d, const ResParams &p, const float *x
         return hipErrorInvalidValue;
     } else {
         if (d->R == 3 && d->S == 3) {
+            if constexpr (kResWinograd && MODE != kPlain) {
+                if (mb == 1)
+                    return cp == 4 ? launch_t<3, 3, 1, 4, MODE, VEC, true>(p, x, w, y, ep, st)
+                                   : launch_t<3, 3, 1, 8, MODE, VEC, true>(p, x, w, y, ep, st);
+            }
             if (mb == 1)
                 return cp == 4 ? launch_t<3, 3, 1, 4, MODE, VEC>(p, x, w, y, ep, st)
                                : launch_t<3, 3, 1, 8, MODE, VEC>(p, x, w, y, ep, st);

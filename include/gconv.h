@@ -180,7 +180,13 @@ int conv_fused_gn_workspace_size(gconv_desc_t desc, int gn_groups, size_t *bytes
  * its counters, runs the conv once (each image's statistics are merged by
  * the wave that completes them, in a fixed order, and tiles are normalized
  * from registers), then normalizes in place whatever the conv pass left
- * (see conv_desc_set_fused_wait). */
+ * (see conv_desc_set_fused_wait).  On the resident-weight kernel, a 3x3 conv
+ * with 32 output channels runs its STORE and RECOMPUTE conv passes in the
+ * Winograd form F(2x2, 3x3) (Lavin and Gray, "Fast Algorithms for
+ * Convolutional Neural Networks"): the same function, rounded differently
+ * from the direct sum (the variants then differ by a few units in the last
+ * place of the conv; every variant stays within 1e-4 of the exact chain on
+ * the inputs the tests draw). */
 int conv_fused_gn_fwd(gconv_desc_t desc, const float *x, const float *w, const float *bias,
                       const float *scale, const float *gamma, const float *beta, int gn_groups,
                       float eps, float *y, void *workspace, size_t workspace_bytes, void *stream);

@@ -280,6 +280,29 @@ def test_fused_other_geometries():
             check_gn(out, ref, "%s %s" % (wl, gc.FUSED_NAMES[variant]))
 
 
+def test_fused_winograd_geometries():
+    """The fused 3x3 passes with 32 output channels multiply in the Winograd
+    form F(2x2, 3x3): 4- and 8-channel chunks (4, 5 and 8 input channels),
+    16-byte and 4-byte band loads, ragged tiles, a random GroupNorm affine and
+    wider value ranges, in the recompute and store organisations, compared
+    whole with the oracle (the implicit GEMM forced: with 4 input channels and
+    padding AUTO takes the register kernel)."""
+    base = W["c5_fused_gn"]
+    cases = [base.with_(N=2, C=4, H=30, W=68),
+             base.with_(N=2, C=4, H=27, W=45, pad=1),
+             base.with_(N=1, C=5, H=70, W=133),
+             base.with_(N=2, C=8, H=35, W=36, x_dist=("uniform", -4.0, 4.0), w_dist=("uniform", -0.3, 0.3)),
+             base.with_(N=1, C=7, H=66, W=20, pad=1, seed=base.seed + 7)]
+    for wl in cases:
+        inp = synth.make_inputs(wl)
+        inp["gamma"] = synth.uniform((wl.K,), 0.5, 1.5, wl.seed, 16)
+        inp["beta"] = synth.uniform((wl.K,), -0.5, 0.5, wl.seed, 17)
+        ref = oracle_fused(wl, inp)
+        for variant in (gc.FUSED_RECOMPUTE, gc.FUSED_STORE):
+            _say("[parity] fused Winograd form", wl, gc.FUSED_NAMES[variant])
+            check_gn(gpu_fused(wl, inp, gc.ALGO_IGEMM, variant=variant), ref, "%s %s" % (wl, gc.FUSED_NAMES[variant]))
+
+
 _FUSED_FULL_REF = {}
 
 
