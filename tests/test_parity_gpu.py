@@ -292,7 +292,12 @@ def test_fused_winograd_geometries():
              base.with_(N=2, C=4, H=27, W=45, pad=1),
              base.with_(N=1, C=5, H=70, W=133),
              base.with_(N=2, C=8, H=35, W=36, x_dist=("uniform", -4.0, 4.0), w_dist=("uniform", -0.3, 0.3)),
-             base.with_(N=1, C=7, H=66, W=20, pad=1, seed=base.seed + 7)]
+             base.with_(N=1, C=7, H=66, W=20, pad=1, seed=base.seed + 7),
+             # one output pixel; exactly one 64-column tile; a single output row
+             base.with_(N=2, C=8, H=3, W=3, seed=base.seed + 8),
+             base.with_(N=3, C=6, H=4, W=66, seed=base.seed + 9),
+             base.with_(N=2, C=8, H=1, W=90, pad=1, seed=base.seed + 10),
+             base.with_(N=1, C=8, H=3, W=68, seed=base.seed + 11)]
     for wl in cases:
         inp = synth.make_inputs(wl)
         inp["gamma"] = synth.uniform((wl.K,), 0.5, 1.5, wl.seed, 16)
