@@ -1,7 +1,8 @@
 // k_igemm.hip -- FP32 MFMA implicit GEMM for dense and wide-group
 // convolution (any padding and number of input channels; dilation 1 with
 // stride 1, or stride 2 at square 1x1-7x7, in the DMA-staged tile kernel;
-// 3x3 at dilation 2 in the flattened-pixel kernel).
+// 3x3 at dilation 2, and at stride 1 dilation 3 and 4, in the
+// flattened-pixel kernel).
 //
 // The implicit-GEMM view of the POPCORNBENCH traces ("Kimi-K2.6 l2_p21",
 // GEMM framing; "Kimi-K2.6 l1_p62", output-channel blocking): per group,
@@ -668,8 +669,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 // lane's operands sit at a fixed offset from the band's first row, which is
 // that of the tile's first pixel.  The host bounds the band's height (tih
 // rows, at most 64) over every tile.  The same addressing serves 1x1 and 3x3
-// at stride 1 and 2, 3x3 at dilation 2, 5x5 and 7x7 at stride 2, and 1x3,
-// 3x1, 1x7 and 7x1 at stride 1.
+// at stride 1 and 2, 3x3 at dilation 2 (and 3 and 4 at stride 1), 5x5 and
+// 7x7 at stride 2, and 1x3, 3x1, 1x7 and 7x1 at stride 1.
 //
 // Band layout: [band row][channel of the chunk][pitch], the pitch a power of
 // two so that a lane finds its element with shifts:
@@ -718,7 +719,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, FlatParams p) {
     static_assert(ST == 1 || ST == 2, "stride 1 or 2");
-    static_assert(DIL == 1 || DIL == 2, "dilation 1 or 2");
+    static_assert(DIL >= 1 && DIL <= 4, "dilation 1 to 4");
     static_assert((CC & (CC - 1)) == 0, "the chunk is a power of two");
     constexpr int RS = R * S;
     constexpr int KW = 32;
@@ -1120,15 +1121,18 @@ constexpr long long kFlatTwoBlockMinWorkgroups = 256;
 constexpr long long kFlatMaxLds = 64 * 1024;
 
 // channels per chunk: as in the tile kernel (16 at 1x1 stride 1; 8 at 3x3
-// and the 1x3, 3x1, 1x7 and 7x1 of factorized blocks), and 4 at 5x5, 2 at 7x7
-constexpr int flat_chunk_c(int R, int S, int ST) {
-    return R * S == 1 ? (ST == 1 ? 16 : 8) : R * S <= 9 ? (ST == 1 ? 8 : 4) : R * S <= 25 ? 4 : 2;
+// and the 1x3, 3x1, 1x7 and 7x1 of factorized blocks), and 4 at 5x5, 2 at
+// 7x7; 4 at 3x3 dilation 3 and 4, whose bands are taller
+constexpr int flat_chunk_c(int R, int S, int ST, int DIL) {
+    return R * S == 1 ? (ST == 1 ? 16 : 8)
+                      : R * S <= 9 ? (ST == 1 && DIL <= 2 ? 8 : 4) : R * S <= 25 ? 4 : 2;
 }
 
 // Geometries with a flattened-pixel kernel: square 1x1 and 3x3 at stride 1
-// and 2, 3x3 at dilation 2 (which the tile kernel does not take), 5x5 and
-// 7x7 at stride 2, and the 1x3, 3x1, 1x7 and 7x1 of factorized blocks at
-// stride 1.  A 1x1 kernel's dilation changes nothing.
+// and 2, 3x3 at dilation 2 (which the tile kernel does not take) and, at
+// stride 1, dilation 3 and 4, 5x5 and 7x7 at stride 2, and the 1x3, 3x1, 1x7
+// and 7x1 of factorized blocks at stride 1.  A 1x1 kernel's dilation changes
+// nothing.
 int flat_dil(const gconv_desc *d) { return d->R == 1 && d->S == 1 ? 1 : d->dil_h; }
 
 bool flat_factorized(int R, int S) { return (R == 1 && (S == 3 || S == 7)) || (S == 1 && (R == 3 || R == 7)); }
@@ -1141,7 +1145,7 @@ bool flat_geometry(const gconv_desc *d) {
     const int dil = flat_dil(d);
     switch (d->R) {
         case 1: return true;
-        case 3: return dil == 1 || dil == 2;
+        case 3: return dil == 1 || dil == 2 || (d->stride_h == 1 && (dil == 3 || dil == 4));
         case 5:
         case 7: return dil == 1 && d->stride_h == 2;
         default: return false;
@@ -1159,7 +1163,7 @@ bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
     const long long np = (long long)d->N * d->Ho * d->Wo;
     const long long xbytes = (long long)d->N * d->C * d->H * d->W * (long long)sizeof(float);
     if (np + T > INT_MAX || xbytes > INT_MAX - 64) return false;
-    const int CC = flat_chunk_c(d->R, d->S, ST);
+    const int CC = flat_chunk_c(d->R, d->S, ST, dil);
     // band rows: T consecutive pixels span at most dmax + 1 output rows of
     // the batch; each step down a row moves ST virtual rows, and a step into
     // the next image hv - ST*Ho more (at most cross such steps); the last
@@ -1208,7 +1212,7 @@ bool flat_plan(const gconv_desc *d, int NB, bool vec, FlatParams &p) {
 template <int R, int S, int ST, int DIL>
 hipError_t launch_flat_t(const FlatParams &p, bool vec, int nb, const float *x, const float *w, const float *bias,
                          float *y, hipStream_t st) {
-    constexpr int CC = flat_chunk_c(R, S, ST);
+    constexpr int CC = flat_chunk_c(R, S, ST, DIL);
     const size_t lds = 2 * (size_t)p.xi * 64 * (vec ? 4 : 1) * sizeof(float);
     const dim3 g1((unsigned)p.n_wg);
     clear_stale_launch_error();
@@ -1240,14 +1244,16 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
     const bool vec = d->W % 4 == 0 && (((uintptr_t)x & 15u) == 0) && flat_plan(d, 1, true, pv) &&
                      (!flat_plan(d, 1, false, p4) || pv.lp == p4.lp);
     int nb = 2;
-    const int nchunks = (d->cin + flat_chunk_c(d->R, d->S, d->stride_h) - 1) / flat_chunk_c(d->R, d->S, d->stride_h);
+    const int cc = flat_chunk_c(d->R, d->S, d->stride_h, flat_dil(d));
+    const int nchunks = (d->cin + cc - 1) / cc;
     if (!flat_plan(d, 2, vec, p) ||
         (p.n_wg < kFlatTwoBlockWorkgroups && (nchunks < kFlatTwoBlockChunks || p.n_wg < kFlatTwoBlockMinWorkgroups))) {
         nb = 1;
         if (!flat_plan(d, 1, vec, p)) return false;
     }
     p.wvec = (d->cin * d->R * d->S) % 4 == 0 && (((uintptr_t)w & 15u) == 0);
-    const bool s1 = d->stride_h == 1, d2 = flat_dil(d) == 2;
+    const bool s1 = d->stride_h == 1;
+    const int dil = flat_dil(d);
     if (flat_factorized(d->R, d->S)) {
         const int rs = d->R * 16 + d->S;
         *err = rs == 1 * 16 + 3   ? launch_flat_t<1, 3, 1, 1>(p, vec, nb, x, w, bias, y, st)
@@ -1262,7 +1268,11 @@ bool try_launch_flat(const gconv_desc *d, long long tile_area, const float *x, c
                       : launch_flat_t<1, 1, 2, 1>(p, vec, nb, x, w, bias, y, st);
             break;
         case 3:
-            if (d2)
+            if (dil == 4)
+                *err = launch_flat_t<3, 3, 1, 4>(p, vec, nb, x, w, bias, y, st);
+            else if (dil == 3)
+                *err = launch_flat_t<3, 3, 1, 3>(p, vec, nb, x, w, bias, y, st);
+            else if (dil == 2)
                 *err = s1 ? launch_flat_t<3, 3, 1, 2>(p, vec, nb, x, w, bias, y, st)
                           : launch_flat_t<3, 3, 2, 2>(p, vec, nb, x, w, bias, y, st);
             else
@@ -1293,8 +1303,8 @@ bool igemm_tile_supported(const gconv_desc *d) {
            d->cout >= 8 && (long long)d->cin * d->H * d->W * (long long)sizeof(float) < 0x7fffffffLL - 64;
 }
 
-// Geometries only the flattened-pixel kernel takes (3x3 at dilation 2, 5x5
-// and 7x7 at stride 2), where its plan fits: with 16-byte band pieces when W
+// Geometries only the flattened-pixel kernel takes (3x3 at dilation 2 to 4,
+// 5x5 and 7x7 at stride 2), where its plan fits: with 16-byte band pieces when W
 // is a multiple of 4 (a call whose x is not 16-byte aligned, and whose
 // 4-byte plan does not fit, runs the direct kernel), else with 4-byte loads.
 bool igemm_flat_only(const gconv_desc *d) {

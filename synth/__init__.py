@@ -192,6 +192,8 @@ IGEMM_WORKLOADS = {
     # DeepLab-style dilated stage), dense 5x5 and 7x7 at stride 2
     "dense3d2_256x28": Workload("dense3d2_256x28", 16, 256, 28, 28, 256, 3, 3, 1, 2, 2, 1, 907,
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(256 * 9))),
+    "dense3d4_256x28": Workload("dense3d4_256x28", 16, 256, 28, 28, 256, 3, 3, 1, 4, 4, 1, 914,
+                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(256 * 9))),
     "dense5s2_64x56": Workload("dense5s2_64x56", 16, 64, 56, 56, 64, 5, 5, 2, 2, 1, 1, 908,
                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 25))),
     "dense7s2_16x112": Workload("dense7s2_16x112", 16, 16, 112, 112, 64, 7, 7, 2, 3, 1, 1, 909,

@@ -171,10 +171,13 @@ def test_dispatch_of_stride2_dense_and_wide_groups():
     for geom in [(2, 16, 20, 20, 32, 3, 3, 1, 2, 2, 1), (3, 16, 32, 32, 32, 3, 3, 2, 2, 2, 1),
                  (2, 64, 56, 56, 64, 5, 5, 2, 2, 1, 1), (2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1),
                  (2, 16, 20, 20, 32, 5, 5, 2, 2, 1, 1), (16, 3, 224, 224, 64, 7, 7, 2, 3, 1, 1),
-                 (16, 3, 224, 224, 32, 3, 3, 2, 1, 1, 1)]:
+                 (16, 3, 224, 224, 32, 3, 3, 2, 1, 1, 1),
+                 # 3x3 at dilation 3 and 4, stride 1
+                 (2, 16, 20, 20, 32, 3, 3, 1, 3, 3, 1), (16, 256, 28, 28, 256, 3, 3, 1, 4, 4, 1)]:
         assert gc.conv_desc_get_algo(gc.conv_desc_create(*geom)) == gc.ALGO_IGEMM, geom
-    # not there: stride 3, dilation 3, unequal strides
-    for geom in [(2, 16, 20, 20, 32, 3, 3, 3, 1, 1, 1), (2, 16, 20, 20, 32, 3, 3, 1, 3, 3, 1)]:
+    # not there: stride 3, dilation 5, dilation 3 at stride 2, unequal strides
+    for geom in [(2, 16, 20, 20, 32, 3, 3, 3, 1, 1, 1), (2, 16, 20, 20, 32, 3, 3, 1, 5, 5, 1),
+                 (2, 16, 20, 20, 32, 3, 3, 2, 3, 3, 1)]:
         d = gc.conv_desc_create(*geom)
         assert gc.conv_desc_get_algo(d) == gc.ALGO_DIRECT, geom
         with pytest.raises(gc.GconvError) as ei:

@@ -627,6 +627,13 @@ EDGE = [
     synth.Workload("igemm_flat_dil2_p1", 2, 8, 15, 15, 16, 3, 3, 1, 1, 2, 1, 101, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_dil2_cpg32", 2, 64, 14, 14, 64, 3, 3, 1, 2, 2, 2, 102, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_dil2_s2", 2, 8, 29, 29, 16, 3, 3, 2, 2, 2, 1, 108, ("uniform", -1, 1), ("uniform", -1, 1)),
+    # dilation 3 and 4 at stride 1: 4-channel chunks, 16-byte and 4-byte
+    # bands, a ragged last chunk, grouped, tiles over image boundaries
+    synth.Workload("igemm_flat_dil3_vec", 2, 16, 20, 20, 40, 3, 3, 1, 3, 3, 1, 126, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil3_p1", 3, 10, 17, 19, 33, 3, 3, 1, 1, 3, 1, 127, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil4_vec", 2, 12, 24, 24, 32, 3, 3, 1, 4, 4, 1, 128, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil4_cpg32", 2, 64, 14, 14, 64, 3, 3, 1, 4, 4, 2, 129, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("igemm_flat_dil4_p2", 4, 9, 13, 22, 16, 3, 3, 1, 2, 4, 1, 130, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_5x5_s2", 2, 12, 23, 23, 40, 5, 5, 2, 2, 1, 1, 103, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_5x5_s2_vec", 2, 16, 24, 24, 32, 5, 5, 2, 2, 1, 1, 104, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("igemm_flat_7x7_s2", 2, 6, 29, 29, 64, 7, 7, 2, 3, 1, 1, 105, ("uniform", -1, 1), ("uniform", -1, 1)),
