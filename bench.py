@@ -779,7 +779,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of this build "
+        print("bench.py: this library runs on one GPU; runs on more than one GPU are not supported "
               "(got --gpus %d, WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
