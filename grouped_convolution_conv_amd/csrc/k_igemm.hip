@@ -348,11 +348,24 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // is band column 2*(ow - ow0) + s + ds, and a block reads every other word.
 // NBR output rows per wave (a 4*NBR-row tile): 2, or 1 at stride 2 and on
 // grids too small to fill the chip.
-template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC, int NBR>
+//
+// WG: the columns in the Winograd form F(2, 3) (Lavin and Gray, "Fast
+// Algorithms for Convolutional Neural Networks"), for kernels 3 wide at
+// stride 1 on 64-column tiles with one row per wave.  Lane j owns output
+// columns 2j and 2j+1 of its row; for each kernel row r and input channel
+// the lane forms the four B operands V = B^T d of its 4-column input patch
+// d (B^T = [1 0 -1 0; 0 1 1 0; 0 -1 1 0; 0 1 0 -1]) and the four A operands
+// U = G g of the kernel row's 3 weights (G = [1 0 0; 1/2 1/2 1/2; 1/2 -1/2
+// 1/2; 0 0 1]), and four MFMA chains accumulate M[u] = sum over kernel rows
+// and channels of U[u] V[u].  The output transform A^T M (A^T = [1 1 1 0;
+// 0 1 -1 -1]) runs once, in the epilogue: 12 MFMAs per kernel row and
+// channel pair where the direct form takes 18 for the same 64 outputs.
+template <int R, int S, int MB, int CC, bool VEC, int ST, int NBC, int NBR, bool WG = false>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) void igemm_dma_kernel(
     const float *__restrict__ x, const float *__restrict__ w, const float *__restrict__ bias,
     float *__restrict__ y, IgParams p) {
     static_assert(ST == 1 || ST == 2, "stride 1 or 2");
+    static_assert(!WG || (ST == 1 && S == 3 && MB == 1 && NBC == 2 && NBR == 1), "Winograd columns: 3 wide, stride 1");
     constexpr int RS = R * S;
     constexpr int KW = 32 * MB;
     constexpr int TH = 4 * NBR;
@@ -383,7 +396,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     constexpr int WI4 = (WL + 63) / 64;      // (WK) 4-byte weight DMA instructions
     constexpr int WPW = (WI16 + 3) / 4;      // (WK) 16-byte weight DMA instructions per wave
     constexpr int WCAP = WK ? WI16 * 256 : WI * 64;
-    constexpr int NB = NBR * NBC;
+    // accumulator blocks: NBR x NBC of 32 pixels, or (WG) the four Winograd
+    // positions of 32 column pairs
+    constexpr int NB = WG ? 4 : NBR * NBC;
     constexpr int HALF = CC / 2;
     constexpr int NWAVE = kBlock / 64;
 
@@ -580,6 +595,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
             for (int v = 0; v < 16; ++v) acc[m][b][v] = 0.0f;
     auto mfma_chunk = [&](const float4 *xb4, const float *wb) __attribute__((always_inline)) {
         const float *xin = reinterpret_cast<const float *>(xb4);
+        if constexpr (WG) {
+#pragma unroll
+            for (int ci = 0; ci < HALF; ++ci) {
+                const int cl = h * HALF + ci;
+                // band row (wave's output row) + r, columns 2j .. 2j+3
+                const float *xq = xin + (cl * TIH + wave) * PITCH + 2 * j;
+                const float *wq = WK ? wb + j * WQP + cl * RS : wb + cl * RS * KW + j;
+                // kernel rows one at a time, as in the direct form
+#pragma unroll 1
+                for (int r = 0; r < R; ++r) {
+                    float d[4], g[3];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) d[c] = xq[r * PITCH + c];
+#pragma unroll
+                    for (int s = 0; s < 3; ++s) g[s] = WK ? wq[r * 3 + s] : wq[(r * 3 + s) * KW];
+                    const float vb[4] = {d[0] - d[2], d[1] + d[2], d[2] - d[1], d[1] - d[3]};
+                    const float t = g[0] + g[2];
+                    const float ua[4] = {g[0], 0.5f * (t + g[1]), 0.5f * (t - g[1]), g[2]};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        acc[0][u] = __builtin_amdgcn_mfma_f32_32x32x2f32(ua[u], vb[u], acc[0][u], 0, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int ci = 0; ci < HALF; ++ci) {
             const int cl = h * HALF + ci;
@@ -630,6 +670,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // ---- epilogue
     const size_t plane = (size_t)p.Ho * p.Wo;
     float *yb = y + ((size_t)n * p.K + k0) * plane;
+    if constexpr (WG) {
+        // output transform: column 2j gets M0 + M1 + M2, column 2j+1 gets
+        // M1 - M2 - M3
+        const int oh = oh0 + wave;
+        if (oh < p.Ho) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int ow = ow0 + 2 * j + b;
+                if (ow >= p.Wo) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (k < kvalid) {
+                        float o = b == 0 ? (acc[0][0][v] + acc[0][1][v]) + acc[0][2][v]
+                                         : (acc[0][1][v] - acc[0][2][v]) - acc[0][3][v];
+                        if (bias) o += bias[k0 + k];
+                        yb[(size_t)k * plane + (size_t)oh * p.Wo + ow] = o;
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -959,6 +1022,14 @@ size_t lds_bytes(int R, int S, int MB, int CC, int pitch) {
     return sizeof(float) * ((size_t)CC * (kTH + R - 1) * pitch + (size_t)((CC * R * S) | 1) * 32 * MB);
 }
 
+// Plain convs 3 wide (1x3, 3x3) at stride 1 take Winograd columns on
+// 64-column tiles (see igemm_dma_kernel).
+constexpr bool kIgWinograd = true;
+template <int R, int S, int MB>
+constexpr bool ig_winograd() {
+    return kIgWinograd && S == 3 && (R == 1 || R == 3) && MB == 1;
+}
+
 template <int R, int S, int MB, bool FUSED>
 hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w, const float *bias,
                     float *y, const FusedEpilogue &ep, hipStream_t st) {
@@ -994,6 +1065,15 @@ hipError_t launch_t(const IgParams &p, dim3 grid, const float *x, const float *w
                 }
             } else {
                 return hipErrorInvalidValue;
+            }
+        } else if (ig_winograd<R, S, MB>() && p.nbc == kNBC && p.nbr == 1) {
+            if constexpr (ig_winograd<R, S, MB>()) {
+                if (p.vec)
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC1, true, 1, kNBC, 1, true>), g1, dim3(kBlock), 0,
+                                       st, x, w, bias, y, p);
+                else
+                    hipLaunchKernelGGL((igemm_dma_kernel<R, S, MB, CC1, false, 1, kNBC, 1, true>), g1, dim3(kBlock),
+                                       0, st, x, w, bias, y, p);
             }
         } else if (p.vec) {
             if (p.nbc == 1)
@@ -1355,6 +1435,9 @@ hipError_t launch_igemm(const gconv_desc *d, const float *x, const float *w, con
     // workgroups keep more loads in flight)
     p.nbc = d->Wo <= 32 ? 1 : kNBC;
     p.nbr = d->stride_h == 2 ? 1 : kNBR;
+    // kernels 3 wide at stride 1 on 64-column tiles take Winograd columns,
+    // which run one row per wave
+    if (kIgWinograd && d->S == 3 && (d->R == 1 || d->R == 3) && d->stride_h == 1 && p.nbc == kNBC) p.nbr = 1;
     const long long gy = (long long)d->groups * p.n_kb;
     auto tiles = [&]() {
         const int th = 4 * p.nbr, tw = 32 * p.nbc;

@@ -50,6 +50,14 @@
  *    descriptor may be used from several host threads only if none of them
  *    changes the algorithm concurrently.
  *  - Every function returns a status code and never throws across the ABI.
+ *  - Arithmetic is FP32 with FP32 accumulation.  Most kernels reorder the
+ *    direct sum; plain convs 3 wide at stride 1 on the implicit GEMM's
+ *    64-column tiles, and the fused chain's 3x3 passes, use Winograd forms
+ *    (F(2, 3) along the columns, F(2x2, 3x3); Lavin and Gray, "Fast
+ *    Algorithms for Convolutional Neural Networks"), exact in exact
+ *    arithmetic and rounded differently.  Results are repeatable bit for
+ *    bit for a given descriptor and algorithm; integer-valued inputs of
+ *    small magnitude give exact results on every path of conv_fwd.
  */
 #ifndef GCONV_H
 #define GCONV_H

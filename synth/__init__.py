@@ -184,6 +184,8 @@ IGEMM_WORKLOADS = {
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(32 * 9))),
     "dense3_64x56": Workload("dense3_64x56", 16, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 904,
                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 9))),
+    "dense3_128x112": Workload("dense3_128x112", 16, 128, 112, 112, 128, 3, 3, 1, 1, 1, 1, 915,
+                               ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
     "dense3s2_128x56": Workload("dense3s2_128x56", 16, 128, 56, 56, 128, 3, 3, 2, 1, 1, 1, 905,
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
     "dense1_256x56": Workload("dense1_256x56", 16, 256, 56, 56, 64, 1, 1, 1, 0, 1, 1, 906,

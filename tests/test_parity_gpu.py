@@ -525,6 +525,33 @@ def test_factorized_implicit_gemm_fuzz(wl):
         check_conv(y, y_ref, A, "%s %s" % (wl.name, gc.ALGO_NAMES[algo]))
 
 
+WINO_COLUMNS = [
+    # kernels 3 wide at stride 1 on 64-column tiles: Winograd columns
+    synth.Workload("wgcol_3x3_p1", 2, 20, 12, 64, 40, 3, 3, 1, 1, 1, 1, 131, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wgcol_3x3_vec", 2, 16, 10, 64, 32, 3, 3, 1, 0, 1, 1, 132, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wgcol_3x3_odd_w", 1, 12, 9, 63, 33, 3, 3, 1, 0, 1, 1, 133, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wgcol_1x3", 2, 12, 8, 64, 32, 1, 3, 1, (0, 1), 1, 1, 134, ("uniform", -1, 1), ("uniform", -1, 1)),
+    synth.Workload("wgcol_cpg32", 1, 64, 16, 128, 64, 3, 3, 1, 1, 1, 2, 135, ("uniform", -1, 1), ("uniform", -1, 1)),
+]
+
+
+@pytest.mark.parametrize("wl", WINO_COLUMNS, ids=lambda w: w.name)
+def test_winograd_columns_whole_output(wl):
+    """Plain convs 3 wide at stride 1 on 64-column tiles run the implicit
+    GEMM with Winograd columns: every output against the oracle, and integer
+    inputs bit for bit (the transforms' halves are exact there)."""
+    inp = synth.make_inputs(wl)
+    y_ref, A = oracle_conv(wl, inp)
+    y, algo = gpu_conv(wl, inp)
+    assert algo == gc.ALGO_IGEMM, gc.ALGO_NAMES[algo]
+    check_conv(y, y_ref, A, wl.name)
+    wi = wl.with_(x_dist=("int", -2, 2), w_dist=("int", -2, 2), seed=wl.seed + 500)
+    inp = synth.make_inputs(wi)
+    y, _ = gpu_conv(wi, inp)
+    y_ref, _ = oracle_conv(wi, inp)
+    assert np.array_equal(y.astype(np.float64), y_ref), wl.name + " integer inputs"
+
+
 EDGE = [
     synth.Workload("one_pixel", 2, 4, 1, 1, 4, 3, 3, 1, 1, 1, 4, 41, ("uniform", -1, 1), ("uniform", -1, 1)),
     synth.Workload("w5_tail", 1, 8, 7, 5, 8, 3, 3, 1, 1, 1, 2, 42, ("uniform", -1, 1), ("uniform", -1, 1)),
