@@ -186,6 +186,10 @@ IGEMM_WORKLOADS = {
                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(64 * 9))),
     "dense3_128x112": Workload("dense3_128x112", 16, 128, 112, 112, 128, 3, 3, 1, 1, 1, 1, 915,
                                ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
+    "dense3_128x28": Workload("dense3_128x28", 16, 128, 28, 28, 128, 3, 3, 1, 1, 1, 1, 916,
+                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
+    "dense3_256x14": Workload("dense3_256x14", 16, 256, 14, 14, 256, 3, 3, 1, 1, 1, 1, 917,
+                              ("uniform", -1.0, 1.0), _u(1 / math.sqrt(256 * 9))),
     "dense3s2_128x56": Workload("dense3s2_128x56", 16, 128, 56, 56, 128, 3, 3, 2, 1, 1, 1, 905,
                                 ("uniform", -1.0, 1.0), _u(1 / math.sqrt(128 * 9))),
     "dense1_256x56": Workload("dense1_256x56", 16, 256, 56, 56, 64, 1, 1, 1, 0, 1, 1, 906,
