@@ -674,7 +674,29 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
         // output transform: column 2j gets M0 + M1 + M2, column 2j+1 gets
         // M1 - M2 - M3
         const int oh = oh0 + wave;
-        if (oh < p.Ho) {
+        // an even output width with y 8-byte aligned: the lane's two columns
+        // are neighbours, inside or outside the output together, and one
+        // 8-byte store writes both (each store instruction then covers whole
+        // lines instead of every other word)
+        if (oh < p.Ho && p.Wo % 2 == 0 && ((uintptr_t)yb & 7u) == 0) {
+            const int ow = ow0 + 2 * j;
+            if (ow < p.Wo) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (k < kvalid) {
+                        float2 o = make_float2((acc[0][0][v] + acc[0][1][v]) + acc[0][2][v],
+                                               (acc[0][1][v] - acc[0][2][v]) - acc[0][3][v]);
+                        if (bias) {
+                            const float bk = bias[k0 + k];
+                            o.x += bk;
+                            o.y += bk;
+                        }
+                        *reinterpret_cast<float2 *>(yb + (size_t)k * plane + (size_t)oh * p.Wo + ow) = o;
+                    }
+                }
+            }
+        } else if (oh < p.Ho) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
                 const int ow = ow0 + 2 * j + b;

@@ -86,6 +86,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct ResParams {
     int C, H, W, K, Ho, Wo;
@@ -291,14 +292,21 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
     // ---- weights, once: w[k][c][r][s] for k < cout, c < cin, zero elsewhere
     if constexpr (WG) {
         // one (output channel, input channel) per thread: its 16 Winograd
-        // weights at wl[k * WP + c * 16 ..]
+        // weights at wl[k * WP + c * 16 ..], times the channel's sigmoid
+        // slope -scale * log2(e), so that the accumulators hold the
+        // exponent of the sigmoid (its offset enters as a chain's start
+        // value, see winograd_tile)
         for (int e = tid; e < KW * CP; e += kBlock) {
             const int k = e / CP, c = e - k * CP;
             float g[9];
 #pragma unroll
             for (int q = 0; q < 9; ++q)
                 g[q] = (k < p.cout && c < p.cin) ? w[((size_t)k * p.cin + c) * 9 + q] : 0.0f;
-            winograd_weights(g, wl + k * WP + c * 16);
+            float *uk = wl + k * WP + c * 16;
+            winograd_weights(g, uk);
+            const float slope = k < p.cout ? -ep.scale[k] * kLog2e : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) uk[q] *= slope;
         }
     } else {
         for (int e = tid; e < KW * CP * RS; e += kBlock) {
@@ -446,6 +454,15 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
         }
     };
 
+    // The sigmoid's offset -bias * scale * log2(e) per accumulator row, the
+    // start value of the chain of M[1][1]: A^T[a][1] = A^T[b][1] = 1 for
+    // every output (a, b) of the block, so each output receives it once.
+    floatx16 offs = {};
+    if constexpr (WG) {
+        lds_barrier();
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) offs[vv] = chan_bs[8 * (vv >> 2) + 4 * h + (vv & 3)].y;
+    }
     // ---- MFMAs of the tile whose band is in LDS
     floatx16 accs[1][MB][NB];
     // Winograd form: lane j of a wave owns the 2x2 outputs (rows 0-1 of the
@@ -487,7 +504,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                 const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    if (ci == 0) {
+                    if (ci == 0 && v == 1 && u == 1) {
+                        mv[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], vb[u], offs, 0, 0, 0);
+                    } else if (ci == 0) {
                         const floatx16 zero = {};
                         mv[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], vb[u], zero, 0, 0, 0);
                     } else {
@@ -608,6 +627,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
             const int so = (m * 32 + 8 * (vv >> 2) + (vv & 3)) * plane * (int)sizeof(float);
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, val), ys, vofs[nb], so, 0);
         };
+        // Winograd form with an even output width and y 8-byte aligned (VEC):
+        // the lane's two outputs of a row, columns 2j and 2j + 1, are
+        // neighbours and inside or outside the output together, so one 8-byte
+        // store writes both and each store instruction covers whole lines
+        auto store_pair = [&](int nb, int m, int vv, float v0, float v1) __attribute__((always_inline)) {
+            const int so = (m * 32 + 8 * (vv >> 2) + (vv & 3)) * plane * (int)sizeof(float);
+            const u32x2 pv = {__builtin_bit_cast(unsigned int, v0), __builtin_bit_cast(unsigned int, v1)};
+            __builtin_amdgcn_raw_buffer_store_b64(pv, ys, vofs[nb], so, 0);
+        };
+        constexpr bool kPairStore = WG && VEC && (MODE == kStatsStore || MODE == kNormalize);
         // accumulator register v of block m holds channel m*32 + 8(v/4) +
         // 4h + v%4, local GroupNorm group lg = 8m + 2(v/4) + h (4 channels
         // per group)
@@ -629,16 +658,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                         gk = gst[m][vv >> 2].y * gb.x;
                         ck = fmaf(-gst[m][vv >> 2].x, gk, gb.y);
                     }
+                    float o[NB];
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
-                        const float e2 = __builtin_amdgcn_exp2f(fmaf(acc[m][nb][vv], bs.x, bs.y));
+                        // the Winograd form has the slope and offset in the accumulator
+                        const float e2 = __builtin_amdgcn_exp2f(WG ? acc[m][nb][vv] : fmaf(acc[m][nb][vv], bs.x, bs.y));
                         const float val = __builtin_amdgcn_rcpf(1.0f + e2);
-                        if constexpr (kStatsMode) {
-                            acc[m][nb][vv] = val;
-                            if constexpr (MODE == kStatsStore) store_fast(nb, m, vv, val);
-                        } else {
-                            store_fast(nb, m, vv, fmaf(val, gk, ck));
-                        }
+                        if constexpr (kStatsMode) acc[m][nb][vv] = val;
+                        o[nb] = MODE == kNormalize ? fmaf(val, gk, ck) : val;
+                        if constexpr (!kPairStore && (MODE == kStatsStore || MODE == kNormalize))
+                            store_fast(nb, m, vv, o[nb]);
+                    }
+                    if constexpr (kPairStore) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; nb += 2) store_pair(nb, m, vv, o[nb], o[nb + 1]);
                     }
                 }
             }
@@ -1038,8 +1071,12 @@ ResParams make_params(const gconv_desc *d, int gn_groups) {
     return p;
 }
 
-bool res_vec(const gconv_desc *d, const float *x) {
-    return (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0);
+// 16-byte band loads; in the fused modes also y 8-byte aligned, for the
+// paired stores of the Winograd form (W % 4 == 0 and pad_w % 4 == 0 make the
+// output width of a 3x3 conv even)
+bool res_vec(const gconv_desc *d, const float *x, const float *y, bool fused) {
+    return (d->W % 4 == 0) && (d->pad_w % 4 == 0) && (((uintptr_t)x & 15u) == 0) &&
+           (!fused || ((uintptr_t)y & 7u) == 0);
 }
 
 int res_mb(const gconv_desc *d) { return d->cout > 32 ? 2 : 1; }
@@ -1121,7 +1158,7 @@ hipError_t launch_mode_v(const gconv_desc *d, const ResParams &p, const float *x
 template <int MODE>
 hipError_t launch_mode(const gconv_desc *d, const ResParams &p, const float *x, const float *w, float *y,
                        const ResEpilogue &ep, hipStream_t st) {
-    return res_vec(d, x) ? launch_mode_v<MODE, true>(d, p, x, w, y, ep, st)
+    return res_vec(d, x, y, MODE != kPlain) ? launch_mode_v<MODE, true>(d, p, x, w, y, ep, st)
                          : launch_mode_v<MODE, false>(d, p, x, w, y, ep, st);
 }
 
