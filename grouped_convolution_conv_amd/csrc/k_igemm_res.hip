@@ -122,6 +122,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int byt
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, kBufferWord3);
 }
 
+// Sum over one 32-lane half of a wavefront; every lane of the half gets the
+// same total.  The steps inside a 16-lane row (partner lanes xor 1 and xor 2,
+// then the mirrored lane within 8 and within 16) are DPP operands of the
+// additions themselves; only the step between the half's two rows is a lane
+// shuffle.  The two lanes of every exchange add the same two partial sums in
+// swapped order, so the totals agree bit for bit.
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_sum_dpp(float v) {
+    v += dpp_from<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+    v += dpp_from<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+    v += dpp_from<0x141>(v);  // row_half_mirror
+    v += dpp_from<0x140>(v);  // row_mirror
+    return v + __shfl_xor(v, 16, 64);
+}
+
 // Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
 // wait for the wave's outstanding global loads and stores.
 __device__ __forceinline__ void lds_barrier() {
@@ -702,7 +720,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                                 const float v = acc[m][nb][4 * q + uu];
                                 sq += kMask ? (pix[nb] >= 0 ? v : 0.0f) : v;
                             }
-                        const float mu = half_wave_sum(sq) * inv;
+                        const float mu = half_sum_dpp(sq) * inv;
                         float tq = 0.0f;
 #pragma unroll
                         for (int nb = 0; nb < NB; ++nb) {
@@ -713,7 +731,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(MB == 1 
                                 tq = fmaf(dv, dv, tq);
                             }
                         }
-                        const float m2 = half_wave_sum(tq);
+                        const float m2 = half_sum_dpp(tq);
                         const int idx = (8 * m + 2 * q + h) * p.parts_stride + t * NWAVE + wave;
                         const u32x4 pt = {__builtin_bit_cast(unsigned int, count), __builtin_bit_cast(unsigned int, mu),
                                           __builtin_bit_cast(unsigned int, m2), 0u};
