@@ -51,7 +51,7 @@ def gpu_conv(wl, inp, algo=gc.ALGO_AUTO, bias=None, y_offset=0):
     return y.view(wl.N, wl.K, ho, wo).cpu().numpy(), gc.conv_desc_get_algo(d)
 
 
-def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO, wait_us=None):
+def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO, wait_us=None, y_offset=0):
     gn_groups = gn_groups or wl.gn_groups
     d = _desc(wl)
     gc.conv_desc_set_algo(d, algo)
@@ -61,10 +61,14 @@ def gpu_fused(wl, inp, algo=gc.ALGO_AUTO, gn_groups=None, variant=gc.FUSED_AUTO,
     ho, wo = gc.conv_desc_get_output_dims(d)
     ws = torch.empty(max(1, gc.conv_fused_gn_workspace_size(d, gn_groups)), dtype=torch.uint8, device="cuda")
     ws.fill_(0xFF)  # the kernels must not rely on its contents
-    y = torch.full((wl.N, wl.K, ho, wo), float("nan"), device="cuda")
+    # y_offset floats into a larger buffer: an output that is not 8- or
+    # 16-byte aligned
+    ybuf = torch.full((wl.N * wl.K * ho * wo + y_offset,), float("nan"), device="cuda")
+    y = ybuf[y_offset:].view(wl.N, wl.K, ho, wo)
     gc.conv_fused_gn_fwd(d, _dev(inp["x"]), _dev(inp["w"]), _dev(inp["bias"]), _dev(inp["scale"]),
                          _dev(inp.get("gamma")), _dev(inp.get("beta")), gn_groups, wl.eps, y, ws)
     torch.cuda.synchronize()
+    assert y_offset == 0 or bool(torch.isnan(ybuf[:y_offset]).all()), "write before the output"
     return y.cpu().numpy()
 
 
@@ -355,6 +359,21 @@ def test_fused_mid_size_vec_resident():
         check_gn(gpu_fused(wl, inp, variant=variant), ref, "fused vec " + gc.FUSED_NAMES[variant])
 
 
+@pytest.mark.parametrize("y_offset", [1, 2, 3])
+def test_fused_output_alignment(y_offset):
+    """The Winograd passes store a lane's two neighbouring columns with one
+    8-byte store only when y is 8-byte aligned; an output 4 or 12 bytes off
+    (odd offsets) takes the 4-byte stores, 8 bytes off the paired ones.  Every
+    organisation, compared whole, and nothing written before the output."""
+    wl = W["c5_fused_gn"].with_(N=2, H=42, W=68)
+    inp = synth.make_inputs(wl)
+    ref = oracle_fused(wl, inp)
+    for variant in (gc.FUSED_RECOMPUTE, gc.FUSED_STORE, gc.FUSED_ONEPASS):
+        _say("[parity] fused, y offset %d floats," % y_offset, gc.FUSED_NAMES[variant])
+        check_gn(gpu_fused(wl, inp, variant=variant, y_offset=y_offset), ref,
+                 "fused y+%d %s" % (y_offset, gc.FUSED_NAMES[variant]))
+
+
 @pytest.mark.parametrize("case", ["small", "mid vec", "mid ragged", "full"])
 def test_onepass_normalizes_the_same_bits_on_every_path(case):
     """The one-pass variant normalizes a tile in the conv pass once its
@@ -550,6 +569,9 @@ def test_winograd_columns_whole_output(wl):
     y, _ = gpu_conv(wi, inp)
     y_ref, _ = oracle_conv(wi, inp)
     assert np.array_equal(y.astype(np.float64), y_ref), wl.name + " integer inputs"
+    # an output 4 bytes off 8-byte alignment: the 4-byte stores
+    y1, _ = gpu_conv(wi, inp, y_offset=1)
+    assert np.array_equal(y1.astype(np.float64), y_ref), wl.name + " integer inputs, y offset 1 float"
 
 
 EDGE = [
