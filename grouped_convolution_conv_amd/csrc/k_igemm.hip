@@ -655,16 +655,32 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
     // DMA has landed and every wave is done with chunk c-1's buffer) ->
     // DMA chunk c+1 into that buffer -> MFMAs of chunk c.
     dma_any(0, xA4, wA);
-    for (int c = 0; c < nchunks; c += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (c + 1 < nchunks) dma_any(c + 1, xB4, wB);
-        mfma_chunk(xA4, wA);
-        if (c + 1 >= nchunks) break;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (c + 2 < nchunks) dma_any(c + 2, xA4, wA);
-        mfma_chunk(xB4, wB);
+    if constexpr (ST == 1 && R * S > 1) {
+        // One call site of the MFMA loop, the buffers chosen by the chunk's
+        // parity: with a call per buffer the compiler gave each inlined
+        // kernel-row loop its own accumulator registers and copied all of
+        // them in and out around every chunk (64 moves after an MFMA drain).
+        // The 1x1 and stride-2 chunks are short, and keep two chunks per
+        // iteration (measured faster there).
+        for (int c = 0; c < nchunks; ++c) {
+            const bool odd = c & 1;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 1 < nchunks) dma_any(c + 1, odd ? xA4 : xB4, odd ? wA : wB);
+            mfma_chunk(odd ? xB4 : xA4, odd ? wB : wA);
+        }
+    } else {
+        for (int c = 0; c < nchunks; c += 2) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 1 < nchunks) dma_any(c + 1, xB4, wB);
+            mfma_chunk(xA4, wA);
+            if (c + 1 >= nchunks) break;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 2 < nchunks) dma_any(c + 2, xA4, wA);
+            mfma_chunk(xB4, wB);
+        }
     }
 
     // ---- epilogue
@@ -1001,16 +1017,28 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     // the tile kernel's two-buffer chunk pipeline
     dma(0, bandA, wA);
-    for (int c = 0; c < nchunks; c += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (c + 1 < nchunks) dma(c + 1, bandB, wB);
-        mfma_chunk(bandA, wA);
-        if (c + 1 >= nchunks) break;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (c + 2 < nchunks) dma(c + 2, bandA, wA);
-        mfma_chunk(bandB, wB);
+    if constexpr (ST == 1 && R * S > 1 && DIL == 1) {
+        // one call site of the MFMA loop, as in igemm_dma_kernel (dilated
+        // kernels keep two chunks per iteration: measured faster there)
+        for (int c = 0; c < nchunks; ++c) {
+            const bool odd = c & 1;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 1 < nchunks) dma(c + 1, odd ? bandA : bandB, odd ? wA : wB);
+            mfma_chunk(odd ? bandB : bandA, odd ? wB : wA);
+        }
+    } else {
+        for (int c = 0; c < nchunks; c += 2) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 1 < nchunks) dma(c + 1, bandB, wB);
+            mfma_chunk(bandA, wA);
+            if (c + 1 >= nchunks) break;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (c + 2 < nchunks) dma(c + 2, bandA, wA);
+            mfma_chunk(bandB, wB);
+        }
     }
 
     // ---- epilogue: lanes j of a block store 32 consecutive pixels of the
